@@ -1,0 +1,324 @@
+"""Plain fp64 CPU oracle of the ISPA hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check
+and the CPU-baseline leg of the benchmark may import this module.  The HIP
+library does not use it, and it imports nothing from the HIP library.
+
+Every function restates a definition from the pages about "Towards
+Memory-Efficient Autoregressive Video Generation via Instance-Specific
+Parametric Absorption" (arXiv 2607.00712).  Short names for the pages:
+
+* EN review  -- the English papernotes review ("Key Designs" 1-3, "A Worked
+  Example", "Loss & Training", the Table 2 excerpts under "Main Results"
+  and "Ablation Study").
+* ZH review  -- the Chinese papernotes review (same structure, "关键设计").
+* DE summary -- the gist.science technical summary, section 2 "Methodik":
+  the printed objective and the printed closed form for Delta W.
+* gptget     -- the gptget.net summary ("Methodology", ZH "Methodology").
+
+Everything is float64 on whatever the inputs hold (bf16 inputs are decoded
+exactly).  Steps that are a plain library primitive (a matrix product, an
+exponential, a sort) use numpy for that step only; nothing is blocked, fused
+or reordered beyond the definition.  Where the pages leave a step open the
+docstring states the reading taken.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "as_f64",
+    "group_attention",
+    "lse_merge",
+    "dual_stream_attention",
+    "residual_target",
+    "accumulate_stats",
+    "ridge_lambda",
+    "cholesky_lower",
+    "forward_substitution",
+    "backward_substitution",
+    "solve_dw",
+    "epsilon_from_stats",
+    "epsilon_direct",
+    "select_layers",
+    "local_attn_proj",
+    "stream_groups",
+    "kv_bytes_retained",
+    "remaining_kv_fraction",
+]
+
+
+def as_f64(x) -> np.ndarray:
+    """Decode any array-like (numpy, or a CPU torch tensor of any float
+    dtype including bfloat16) to a float64 numpy array, exactly."""
+    if hasattr(x, "detach"):  # torch tensor: widen on the torch side first
+        x = x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Attention of one key group, and the log-sum-exp merge
+# ---------------------------------------------------------------------------
+
+def group_attention(q, k, v, scale: float):
+    """Softmax attention of every query over ONE group of keys, returning the
+    value-weighted output and the group's log-sum-exp.
+
+    EN review, Key Design 1 (ZH review, 关键设计 1): the same current query
+    attends to each disjoint KV group, and each group returns its weighted
+    value output together with the LSE of its softmax normalisation.
+
+    q: [n_q, H, d]; k, v: [n_k, H, d].  Returns (o [n_q, H, d],
+    lse [n_q, H]) with s_j = scale * <q, k_j>, lse = ln sum_j exp(s_j) and
+    o = sum_j exp(s_j - lse) v_j.  An empty group gives o = 0, lse = -inf
+    (its softmax mass is zero).
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    n_q, H, d = q.shape
+    n_k = k.shape[0]
+    if n_k == 0:
+        return np.zeros((n_q, H, d)), np.full((n_q, H), -np.inf)
+    # scores per head: [H, n_q, n_k]  (matrix product primitive)
+    s = scale * np.matmul(q.transpose(1, 0, 2), k.transpose(1, 2, 0))
+    m = s.max(axis=2, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=2, keepdims=True)
+    o = np.matmul(e / l, v.transpose(1, 0, 2))  # [H, n_q, d]
+    lse = (m + np.log(l))[:, :, 0]  # [H, n_q]
+    return o.transpose(1, 0, 2), lse.T
+
+
+def lse_merge(o_parts, lse_parts):
+    """Combine per-group attention results into attention over their union.
+
+    EN review, Key Design 1: the full activation is recovered from the two
+    branches with weights given by their normalisation constants, not by a
+    plain average.  Written out: lse = ln sum_p exp(lse_p) and
+    o = sum_p exp(lse_p - lse) o_p.  Parts with lse = -inf carry no mass;
+    if every part is empty the result is o = 0, lse = -inf.
+
+    Returns (o_full, lse_full, a0, delta) where a0 = o_parts[0] (the local
+    activation A_loc when part 0 is the local group) and
+    delta = o_full - a0 (A_full - A_loc).
+    """
+    os_ = [as_f64(o) for o in o_parts]
+    ls_ = [as_f64(l) for l in lse_parts]
+    stack_l = np.stack(ls_)  # [P, n_q, H]
+    m = stack_l.max(axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    tot = np.zeros_like(m)
+    for l in ls_:
+        tot += np.where(np.isfinite(l), np.exp(l - m_safe), 0.0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    o = np.zeros_like(os_[0])
+    for op, l in zip(os_, ls_):
+        wgt = np.where(np.isfinite(l) & finite, np.exp(l - np.where(finite, lse, 0.0)), 0.0)
+        o += wgt[..., None] * op
+    return o, lse, os_[0], o - os_[0]
+
+
+def dual_stream_attention(q, k_loc, v_loc, k_hist, v_hist, scale: float):
+    """Dual-stream warmup attention (EN review, Key Design 1; DE summary,
+    "Dual-Stream Warmup"): attention over the local group and the history
+    group separately, then the LSE merge.  Returns a dict with o_loc,
+    lse_loc, o_hist, lse_hist, a_full, lse_full, a_loc and delta."""
+    o_l, l_l = group_attention(q, k_loc, v_loc, scale)
+    o_h, l_h = group_attention(q, k_hist, v_hist, scale)
+    a_full, lse_full, a_loc, delta = lse_merge([o_l, o_h], [l_l, l_h])
+    return dict(o_loc=o_l, lse_loc=l_l, o_hist=o_h, lse_hist=l_h,
+                a_full=a_full, lse_full=lse_full, a_loc=a_loc, delta=delta)
+
+
+# ---------------------------------------------------------------------------
+# Regression statistics
+# ---------------------------------------------------------------------------
+
+def residual_target(a_loc, a_full, w):
+    """R = (A_full - A_loc) W (EN review, Key Design 2, the residual
+    equation).  Rows are tokens; W is [D_in, D_out] acting on row vectors."""
+    return (as_f64(a_full) - as_f64(a_loc)) @ as_f64(w)
+
+
+def accumulate_stats(a_loc, delta_a, w):
+    """One step's contribution to the sufficient statistics.
+
+    EN review, Key Design 2: activation outer products and activation-residual
+    cross statistics can be accumulated during the forward passes.  With rows
+    a_i of A_loc (one per query token, all heads concatenated, width D) and
+    r_i = delta_i W the matching residual rows:
+        G = sum_i a_i a_i^T = A_loc^T A_loc       (D x D)
+        C = sum_i a_i r_i^T = A_loc^T R           (D x D)
+        r2 = sum_i |r_i|^2  = ||R||_F^2
+    Statistics are sums over rows (not means); the warmup total is the sum of
+    the per-step contributions.  Returns (G, C, r2).
+    """
+    a = as_f64(a_loc)
+    r = as_f64(delta_a) @ as_f64(w)
+    return a.T @ a, a.T @ r, float(np.sum(r * r))
+
+
+# ---------------------------------------------------------------------------
+# Ridge solve
+# ---------------------------------------------------------------------------
+
+def ridge_lambda(G, lambda_abs: float, lambda_rel: float) -> float:
+    """Regularisation weight.  The pages give lambda = 0.001 (EN review, Loss &
+    Training) without saying whether G is a sum or a mean; the reading taken
+    is lambda = lambda_abs + lambda_rel * tr(G) / D, with lambda_rel = 1e-3 and
+    lambda_abs = 0 for the workloads (the relative form makes Delta W the same
+    for summed or averaged statistics)."""
+    G = as_f64(G)
+    return float(lambda_abs + lambda_rel * np.trace(G) / G.shape[0])
+
+
+def cholesky_lower(a):
+    """Lower-triangular L with L L^T = a, column by column (Cholesky-Crout).
+
+    Returns (L, info): info = 0 on success, else the 1-based index of the
+    first pivot that is not positive (L is then incomplete)."""
+    a = as_f64(a)
+    n = a.shape[0]
+    L = np.zeros_like(a)
+    for j in range(n):
+        piv = a[j, j] - np.dot(L[j, :j], L[j, :j])
+        if not piv > 0.0:
+            return L, j + 1
+        L[j, j] = math.sqrt(piv)
+        if j + 1 < n:
+            L[j + 1:, j] = (a[j + 1:, j] - L[j + 1:, :j] @ L[j, :j]) / L[j, j]
+    return L, 0
+
+
+def forward_substitution(L, B):
+    """Solve L Y = B for lower-triangular L, one row at a time."""
+    L, B = as_f64(L), as_f64(B)
+    Y = np.zeros_like(B)
+    for i in range(L.shape[0]):
+        Y[i] = (B[i] - L[i, :i] @ Y[:i]) / L[i, i]
+    return Y
+
+
+def backward_substitution(L, Y):
+    """Solve L^T X = Y for lower-triangular L, one row at a time."""
+    L, Y = as_f64(L), as_f64(Y)
+    n = L.shape[0]
+    X = np.zeros_like(Y)
+    for i in range(n - 1, -1, -1):
+        X[i] = (Y[i] - L[i + 1:, i] @ X[i + 1:]) / L[i, i]
+    return X
+
+
+def solve_dw(G, C, lam: float):
+    """Closed-form ridge absorption.
+
+    DE summary, Methodik: Delta W minimises
+    ||A_loc (W + Delta W) - A_full W||^2 + lambda ||Delta W||^2, and the
+    printed closed form is Delta W = (A_loc^T A_loc + lambda I)^-1
+    A_loc^T (A_full - A_loc) W = (G + lambda I)^-1 C.  The pages call this a
+    single D x D inversion (EN review, Key Design 2); it is solved here as
+    (G + lambda I) = L L^T followed by two triangular solves, which gives the
+    same matrix without forming the inverse.
+
+    Returns (dW, info); info > 0 means G + lambda I was not positive
+    definite (first failing pivot, 1-based) and dW is NaN.
+    """
+    G, C = as_f64(G), as_f64(C)
+    A = G + lam * np.eye(G.shape[0])
+    L, info = cholesky_lower(A)
+    if info:
+        return np.full_like(C, np.nan), info
+    return backward_substitution(L, forward_substitution(L, C)), 0
+
+
+def epsilon_from_stats(G, C, r2: float, dW) -> float:
+    """Reconstruction error from the statistics.
+
+    EN review, Key Design 2 defines eps = ||A_loc (W + dW) - A_full W||_F^2 =
+    ||A_loc dW - R||_F^2.  Expanding the square over the warmup rows:
+    eps = r2 - 2 <dW, C> + <dW, G dW>, with the unregularised G (the penalty
+    term is not part of eps)."""
+    G, C, dW = as_f64(G), as_f64(C), as_f64(dW)
+    return float(r2 - 2.0 * np.sum(dW * C) + np.sum(dW * (G @ dW)))
+
+
+def epsilon_direct(a_loc, a_full, w, dW) -> float:
+    """eps straight from its definition on stored rows (EN review, Key
+    Design 2): ||A_loc (W + dW) - A_full W||_F^2."""
+    a_loc, a_full, w, dW = as_f64(a_loc), as_f64(a_full), as_f64(w), as_f64(dW)
+    e = a_loc @ (w + dW) - a_full @ w
+    return float(np.sum(e * e))
+
+
+# ---------------------------------------------------------------------------
+# Layer selection
+# ---------------------------------------------------------------------------
+
+def select_layers(eps, K: int):
+    """Instance-specific layer selection (EN review, Key Design 3): sort the N
+    layers by increasing eps and take the K lowest as L-Layers.  Ties go to
+    the lower layer index (stable sort).  A NaN eps is an error.
+
+    Returns (selected [K] int32 in ascending-eps order, is_local [N] uint8,
+    status): status 0 on success, 1 if any eps is NaN (outputs then zero)."""
+    eps = [float(e) for e in as_f64(eps).ravel()]
+    N = len(eps)
+    if any(math.isnan(e) for e in eps):
+        return np.zeros(K, np.int32), np.zeros(N, np.uint8), 1
+    order = sorted(range(N), key=lambda i: (eps[i], i))
+    sel = np.array(order[:K], dtype=np.int32)
+    is_local = np.zeros(N, np.uint8)
+    is_local[sel] = 1
+    return sel, is_local, 0
+
+
+# ---------------------------------------------------------------------------
+# Post-switch layers
+# ---------------------------------------------------------------------------
+
+def local_attn_proj(q, k, v, w_proj, scale: float):
+    """Post-switch layer output (EN review, Key Design 2 and 3; DE summary,
+    "Speichereffiziente Inferenz"): attention over the retained keys, then the
+    output projection.  An L-Layer passes its local keys (sink + current) and
+    W + Delta W; an F-Layer passes all its keys and W.  Returns [n_q, D]."""
+    o, _ = group_attention(q, k, v, scale)
+    n_q = o.shape[0]
+    return o.reshape(n_q, -1) @ as_f64(w_proj)
+
+
+# ---------------------------------------------------------------------------
+# Key grouping and KV accounting
+# ---------------------------------------------------------------------------
+
+def stream_groups(c: int, chunk_tokens: int):
+    """Key groups at chunk step c of a chunked stream (EN review, Overall
+    Architecture and Key Design 1): the local group is the initial sink plus
+    the current chunk, history is everything in between.
+
+    Reading taken: chunk 0 is the sink; at c = 0 the local group is chunk 0
+    alone and history is empty; at c >= 1 local = {chunk 0, chunk c} and
+    history = chunks 1 .. c-1.  Returns (local, history) as lists of
+    half-open token ranges (start, stop) into the layer's key sequence."""
+    T = chunk_tokens
+    if c == 0:
+        return [(0, T)], []
+    local = [(0, T), (c * T, (c + 1) * T)]
+    hist = [(T, c * T)] if c >= 2 else []
+    return local, hist
+
+
+def kv_bytes_retained(n_keys_per_layer, D: int, bytes_per_elem: int = 2) -> int:
+    """KV bytes held: K and V of width D for every retained key of every
+    layer (EN review, Key Design 3: L-Layers keep sink and current entries,
+    F-Layers keep their whole history)."""
+    return int(sum(2 * int(n) * D * bytes_per_elem for n in n_keys_per_layer))
+
+
+def remaining_kv_fraction(x: float, r: float) -> float:
+    """Remaining KV relative to keeping every layer full, when a fraction x of
+    the layers keep only a fraction r of their keys: 1 - x (1 - r).  (EN
+    review, Key Design 3: ISPA-x converts K = xN layers; converted layers
+    still keep sink and current entries.)"""
+    return 1.0 - x * (1.0 - r)
