@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Throughput of the ISPA hot path on one MI355X.
+
+One step is one full cycle of the Wan-1.3B-shaped single-layer workload
+(12 heads x 128 = 1536 wide, 4680 queries per chunk, a 4680-key sink, a
+28080-key history, fresh current chunk each step):
+
+  8 warmup chunk steps, each ispa_dual_attn -> ispa_lse_merge -> ispa_accum_stats
+  the switch: ispa_solve_dw (dW, eps, W + dW) -> ispa_select_layers (K = 1 of 1)
+  one post-switch chunk of the (local) layer: ispa_local_attn_proj with W + dW
+
+All inputs are generated on the GPU before the timed region.  Prints one JSON
+line; the headline value is dual-stream attention + LSE merge TFLOP/s (QK^T
+and PV flops, 4 n_q n_k D per chunk, over the time of the two calls), with
+Gram-statistics TFLOP/s and ms per warmup chunk beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def _fail_multi(n):
+    print(json.dumps({"error": f"--gpus {n}: this build runs on one GPU only; "
+                      "multi-GPU sharding is described in DESIGN.md, not implemented"}))
+    sys.exit(2)
+
+
+def _src_hash(name):
+    with open(os.path.join(ROOT, "kv_cache_absorption_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel_file, src):
+    """HBM bytes per launch measured with rocprofv3 counters for the current
+    source of the kernel, or None if no measurement matches this source."""
+    path = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic_bytes_per_launch:"):
+                rec["bytes"] = float(line.split(":", 1)[1])
+            if line.startswith("source_sha256_16:"):
+                rec["sha"] = line.split(":", 1)[1].strip()
+    if rec.get("sha") != _src_hash(src) or "bytes" not in rec:
+        return None
+    return rec["bytes"]
+
+
+def cpu_baseline(g, q, kc, vc, rows_target_s=15.0):
+    """The oracle timed on host cores on a bounded sample: dual-stream
+    attention + merge for a subset of query rows of one warmup chunk."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing
+        cores = os.cpu_count()
+    k_loc = torch.cat([g.sink_k, kc]).cpu()
+    v_loc = torch.cat([g.sink_v, vc]).cpu()
+    k_h, v_h = g.hist_k.cpu(), g.hist_v.cpu()
+    qh = q.cpu()
+    n_k = k_loc.shape[0] + k_h.shape[0]
+    D = g.D
+    rows_done, t_tot, chunk = 0, 0.0, 64
+    while t_tot < rows_target_s and rows_done + chunk <= qh.shape[0]:
+        t0 = time.perf_counter()
+        O.dual_stream_attention(qh[rows_done:rows_done + chunk], k_loc, v_loc, k_h, v_h, g.d ** -0.5)
+        t_tot += time.perf_counter() - t0
+        rows_done += chunk
+    flops = 4.0 * rows_done * n_k * D
+    return {"value": flops / t_tot / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, dual-stream attention + LSE merge of {rows_done} of 4680 "
+                      f"query rows (all 12 heads, {n_k} keys) of one warmup chunk; {t_tot:.1f} s",
+            "seconds": t_tot}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        _fail_multi(max(args.gpus, world))
+
+    import torch
+    sys.path.insert(0, ROOT)
+    import kv_cache_absorption_amd as K
+    from kv_cache_absorption_amd import _lib as B
+    import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = B.lib()  # raises if libispa.so is missing: no fallback path exists
+
+    # ---------------- inputs (resident in HBM before timing)
+    g = synth.wan13b_single_layer(seed=args.seed, device=dev)
+    n_q, H, d, D = g.n_q, g.H, g.d, g.D
+    n_warm = 8
+    steps_in = [g.step(i) for i in range(n_warm)]
+    q_post, k_post, v_post = g.step(n_warm)
+    scale = d ** -0.5
+    n_loc, n_hist = 2 * n_q, g.hist_k.shape[0]
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    # ---------------- preallocated outputs, state and workspaces
+    f32 = dict(dtype=torch.float32, device=dev)
+    o_loc = torch.empty((n_q, H, d), **f32)
+    o_hist = torch.empty_like(o_loc)
+    lse_loc = torch.empty((n_q, H), **f32)
+    lse_hist = torch.empty_like(lse_loc)
+    a_loc = torch.empty((n_q, D), dtype=torch.float16, device=dev)
+    delta = torch.empty_like(a_loc)
+    G = torch.zeros((D, D), **f32)
+    C = torch.zeros((D, D), **f32)
+    r2 = torch.zeros(1, dtype=torch.float64, device=dev)
+    dW = torch.empty((D, D), **f32)
+    eps = torch.empty(1, dtype=torch.float64, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    w_eff = torch.empty_like(g.w)
+    sel = torch.empty(1, dtype=torch.int32, device=dev)
+    is_local = torch.empty(1, dtype=torch.uint8, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    y_post = torch.empty((n_q, D), dtype=torch.bfloat16, device=dev)
+
+    def segs(pairs):
+        return B._segs(pairs, H, d)
+
+    seg_tables = []
+    for (q, kc, vc) in steps_in:
+        ls, nl = segs([(g.sink_k, g.sink_v), (kc, vc)])
+        hs, nh = segs([(g.hist_k, g.hist_v)])
+        seg_tables.append((q, ls, nl, hs, nh))
+    ws_attn_b = L.ispa_dual_attn_workspace_bytes(B.ISPA_BF16, n_q, H, d, seg_tables[0][1], 2,
+                                                 seg_tables[0][3], 1)
+    ws_stats_b = L.ispa_accum_stats_workspace_bytes(B.ISPA_F16, n_q, D)
+    ws_solve_b = L.ispa_solve_dw_workspace_bytes(1, D)
+    post_segs, post_n = segs([(g.sink_k, g.sink_v), (k_post, v_post)])
+    ws_post_b = L.ispa_local_attn_proj_workspace_bytes(B.ISPA_BF16, n_q, H, d, post_segs, post_n)
+    ws = torch.empty(max(ws_attn_b, ws_stats_b, ws_solve_b, ws_post_b, 256), dtype=torch.uint8, device=dev)
+    wsp, wsn = ws.data_ptr(), ws.numel()
+    op = (ctypes.c_void_p * 2)(o_loc.data_ptr(), o_hist.data_ptr())
+    lp = (ctypes.c_void_p * 2)(lse_loc.data_ptr(), lse_hist.data_ptr())
+
+    def ck(st):
+        if st != 0:
+            raise B.IspaError(st, L.ispa_last_error().decode())
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    rec = {"attn": [], "merge": [], "stats": [], "switch": [], "post": []}
+
+    def cycle(timed):
+        G.zero_()
+        C.zero_()
+        r2.zero_()
+        marks = []
+        for (q, ls, nl, hs, nh) in seg_tables:
+            e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+            e0.record(stream)
+            ck(L.ispa_dual_attn(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
+                                o_loc.data_ptr(), lse_loc.data_ptr(), o_hist.data_ptr(), lse_hist.data_ptr(),
+                                wsp, wsn, sh))
+            e1.record(stream)
+            ck(L.ispa_lse_merge(2, op, lp, n_q, H, d, None, None, a_loc.data_ptr(), delta.data_ptr(),
+                                B.ISPA_F16, sh))
+            e2.record(stream)
+            ck(L.ispa_accum_stats(B.ISPA_F16, B.ISPA_BF16, n_q, D, a_loc.data_ptr(), delta.data_ptr(),
+                                  g.w.data_ptr(), G.data_ptr(), C.data_ptr(), r2.data_ptr(), wsp, wsn, sh))
+            e3.record(stream)
+            marks.append((e0, e1, e2, e3))
+        s0, s1, s2 = ev(), ev(), ev()
+        s0.record(stream)
+        ck(L.ispa_solve_dw(1, D, G.data_ptr(), C.data_ptr(), r2.data_ptr(), D * D, 0.0, 1e-3, dW.data_ptr(),
+                           eps.data_ptr(), info.data_ptr(), g.w.data_ptr(), B.ISPA_BF16, w_eff.data_ptr(),
+                           wsp, wsn, sh))
+        ck(L.ispa_select_layers(1, 1, eps.data_ptr(), sel.data_ptr(), is_local.data_ptr(), status.data_ptr(), sh))
+        s1.record(stream)
+        ck(L.ispa_local_attn_proj(B.ISPA_BF16, n_q, H, d, scale, q_post.data_ptr(), q_post.stride(0), post_segs,
+                                  post_n, w_eff.data_ptr(), B.ISPA_BF16, y_post.data_ptr(), B.ISPA_BF16, wsp,
+                                  wsn, sh))
+        s2.record(stream)
+        if timed:
+            rec["_pending"] = rec.get("_pending", []) + [(marks, (s0, s1, s2))]
+
+    for _ in range(args.warmup):
+        cycle(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        cycle(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for marks, (s0, s1, s2) in rec.pop("_pending", []):
+        for e0, e1, e2, e3 in marks:
+            rec["attn"].append(e0.elapsed_time(e1))
+            rec["merge"].append(e1.elapsed_time(e2))
+            rec["stats"].append(e2.elapsed_time(e3))
+        rec["switch"].append(s0.elapsed_time(s1))
+        rec["post"].append(s1.elapsed_time(s2))
+    if int(info[0]) != 0 or int(status[0]) != 0 or not torch.isfinite(eps).all():
+        raise RuntimeError(f"solve failed: info={int(info[0])} status={int(status[0])} eps={float(eps[0])}")
+
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    attn_flops = 4.0 * n_q * (n_loc + n_hist) * D
+    stats_flops = 5.0 * n_q * D * D + 3.0 * n_q * D
+    merge_bytes = 2 * (4 * n_q * D + 4 * n_q * H) + 2 * 2 * n_q * D
+    t_attn = mean(rec["attn"]) * 1e-3
+    t_merge = mean(rec["merge"]) * 1e-3
+    t_stats = mean(rec["stats"]) * 1e-3
+    value = attn_flops / (t_attn + t_merge) / 1e12
+    achieved = attn_flops / t_attn / 1e12
+    traffic = _traffic("attn_bf16_wan13b_traffic.txt", "attn.hip")
+    out = {
+        "metric": "dual-stream attn+LSE-merge TFLOP/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Wan-1.3B-shaped layer, full ISPA cycle: 8 warmup chunks (4680 queries, "
+                               "12 heads x 128, 9360 local + 28080 history keys) + ridge solve + "
+                               "selection + 1 post-switch local chunk",
+                   "n_q": n_q, "heads": H, "head_dim": d, "local_keys": n_loc, "history_keys": n_hist,
+                   "warmup_chunks": n_warm, "stats_operands": "fp16", "seed": args.seed},
+        "also": {
+            "Gram-stat TFLOP/s": round(stats_flops / t_stats / 1e12, 2),
+            "ms/chunk (1 GPU)": round((t_attn + t_merge + t_stats) * 1e3, 4),
+            "merge GB/s": round(merge_bytes / t_merge / 1e9, 1),
+            "switch ms (solve+select)": round(mean(rec["switch"]), 4),
+            "post-switch chunk ms (local attn + W+dW)": round(mean(rec["post"]), 4),
+            "dual_attn call ms": round(t_attn * 1e3, 4),
+            "merge call ms": round(t_merge * 1e3, 4),
+            "stats call ms": round(t_stats * 1e3, 4),
+            "eps": float(eps[0]),
+        },
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "ispa_dual_attn call (attn_bf16_kernel<128> + history-split combine)"},
+        "roofline_other": [
+            {"kernel": "ispa_lse_merge", "bound": "hbm", "achieved": round(merge_bytes / t_merge / 1e9, 1),
+             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_bytes / t_merge / 1e9 / PEAK_HBM_GBS, 4)},
+            {"kernel": "ispa_accum_stats", "bound": "mfma",
+             "achieved": round(stats_flops / t_stats / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(stats_flops / t_stats / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        ],
+    }
+    if not args.no_cpu_baseline:
+        q, kc, vc = steps_in[0]
+        out["cpu_baseline"] = cpu_baseline(g, q, kc, vc)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * libispa -- the data-parallel hot path of Instance-Specific Parametric
+ * Absorption (ISPA) for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited below (all about arXiv 2607.00712, "Towards Memory-Efficient
+ * Autoregressive Video Generation via Instance-Specific Parametric
+ * Absorption"):
+ *   EN review  -- English papernotes review: "Key Designs" 1-3.
+ *   DE summary -- gist.science technical summary, section 2 "Methodik":
+ *                 the objective and the closed form for Delta W.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer argument that names a tensor is DEVICE memory owned by
+ *    the caller; the library never allocates, frees or keeps a pointer after
+ *    the call returns.  Host arrays (segment tables, part lists) are read
+ *    during the call only.
+ *  - Calls are asynchronous and ordered on the caller's stream; none of them
+ *    synchronises.  A null stream is the legacy default stream.
+ *  - Layouts are row-major.  A token row holds all heads: Q and O are
+ *    [n_q, H, d] = [n_q, D] with D = H*d; a key/value segment is [n, H, d]
+ *    with a row stride in elements (>= H*d).  LSE is [n_q, H], natural log.
+ *    W is [D_in, D_out] acting on row vectors (y = a W): pass the transpose of
+ *    a torch.nn.Linear weight.  G, C, dW are [D, D].
+ *  - Return codes: ISPA_OK, or an error detected on the host before anything
+ *    was launched (ISPA_ERR_INVALID_ARG, ISPA_ERR_UNSUPPORTED,
+ *    ISPA_ERR_WORKSPACE), or ISPA_ERR_HIP when a launch failed.  On error
+ *    ispa_last_error() (thread-local) holds a message.  Numeric failures found
+ *    on the device are reported through device outputs (info, status).
+ *  - Workspace: calls that need scratch take (ws, ws_bytes), device memory
+ *    of at least the size returned by the matching *_workspace_bytes query
+ *    with the same shape arguments, aligned to 256 bytes.  Calls sharing a
+ *    workspace must not overlap in time.
+ *  - Stateless and thread-safe: no global flags, no hidden caches.
+ */
+#ifndef ISPA_H
+#define ISPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ISPA_VERSION 10000 /* 1.0.0 */
+
+typedef int32_t ispa_status;
+enum {
+  ISPA_OK = 0,
+  ISPA_ERR_INVALID_ARG = 1, /* null pointer, bad size, K > N, stride < row */
+  ISPA_ERR_UNSUPPORTED = 2, /* head_dim or dtype combination not built    */
+  ISPA_ERR_WORKSPACE = 3,   /* workspace missing or too small             */
+  ISPA_ERR_HIP = 4          /* launch or runtime error                    */
+};
+
+typedef int32_t ispa_dtype;
+enum { ISPA_F32 = 0, ISPA_BF16 = 1, ISPA_F16 = 2 };
+
+/* Maximum segments in one key group. */
+#define ISPA_MAX_SEGS 8
+
+/* One contiguous run of keys and values: rows [0, n) of k and v, each row
+ * [H, d] of the call's dtype, rows k_stride / v_stride elements apart. */
+typedef struct {
+  const void* k;
+  const void* v;
+  int64_t n;
+  int64_t k_stride;
+  int64_t v_stride;
+} ispa_seg;
+
+int32_t ispa_version(void);
+const char* ispa_status_str(ispa_status s);
+const char* ispa_last_error(void);
+
+/*
+ * ispa_dual_attn -- dual-stream attention (EN review, Key Design 1: the
+ * same query attends to the disjoint local and history groups, and each
+ * group returns its value-weighted output and its log-sum-exp).
+ *
+ * For every query row i and head h, and each group g in {loc, hist} (the
+ * concatenation of that group's segments):
+ *   s_j = scale * <q_ih, k_jh>,  lse_g = ln sum_j exp(s_j),
+ *   o_g = sum_j exp(s_j - lse_g) v_jh.
+ * No mask inside a group.  An empty group (no keys) writes o = 0 and
+ * lse = -inf.
+ *   dt        ISPA_BF16 (MFMA path, d in {64,128}) or ISPA_F32 (d in {64,128}).
+ *   q         [n_q, H, d] of dt, rows q_stride elements apart.
+ *   loc,hist  host arrays of n_loc / n_hist segments (0 <= n <= ISPA_MAX_SEGS).
+ *   o_loc,o_hist     fp32 [n_q, H, d] (dense, D per row).
+ *   lse_loc,lse_hist fp32 [n_q, H].
+ */
+size_t ispa_dual_attn_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d,
+                                      const ispa_seg* loc, int32_t n_loc,
+                                      const ispa_seg* hist, int32_t n_hist);
+ispa_status ispa_dual_attn(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale,
+                           const void* q, int64_t q_stride,
+                           const ispa_seg* loc, int32_t n_loc,
+                           const ispa_seg* hist, int32_t n_hist,
+                           float* o_loc, float* lse_loc, float* o_hist, float* lse_hist,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ispa_lse_merge -- n-way log-sum-exp merge (EN review, Key Design 1: the
+ * full activation is recovered from the groups' outputs weighted by their
+ * normalisation constants; a plain average would be wrong).
+ *   lse = m + ln sum_p exp(lse_p - m), m = max_p lse_p,
+ *   o   = sum_p exp(lse_p - lse) o_p.
+ * Parts with lse = -inf get weight 0; if every part is -inf, o = 0 and
+ * lse = -inf.
+ *   o_parts, lse_parts  host arrays of n_parts (1..16) device pointers to
+ *                       fp32 [n_q, H, d] and fp32 [n_q, H].
+ *   o_full   fp32 [n_q, H, d] or NULL;  lse_full fp32 [n_q, H] or NULL.
+ *   a0_out   part 0 converted to out_dt, [n_q, D], or NULL (A_loc when part
+ *            0 is the local group).
+ *   delta_out  (o - o_parts[0]) computed in fp32, converted to out_dt, or
+ *            NULL (A_full - A_loc).
+ *   out_dt   ISPA_F32, ISPA_BF16 or ISPA_F16 (round to nearest even).
+ */
+ispa_status ispa_lse_merge(int32_t n_parts, const float* const* o_parts,
+                           const float* const* lse_parts, int64_t n_q, int32_t H, int32_t d,
+                           float* o_full, float* lse_full, void* a0_out, void* delta_out,
+                           ispa_dtype out_dt, hipStream_t stream);
+
+/*
+ * ispa_accum_stats -- in-place accumulation of the regression statistics
+ * (EN review, Key Design 2: activation outer products and activation-residual
+ * cross statistics are accumulated over the warmup forward passes).
+ *   R  = delta_a W                  (fp32 accumulation)
+ *   r2 += ||R||_F^2                 (from the fp32 R, summed in fp64)
+ *   G  += a_loc^T a_loc             (UPPER triangle i <= j only; entries
+ *                                    below the diagonal are not touched)
+ *   C  += a_loc^T R                 (R rounded to a_dt before this product)
+ *   a_dt   type of a_loc and delta_a: ISPA_F32, ISPA_BF16 or ISPA_F16.  With
+ *          BF16/F16 the products run on MFMA in that type; W is converted to
+ *          a_dt on load (w_dt may differ).  ISPA_F32 requires w_dt = F32.
+ *   a_loc, delta_a  [n, D] row-major; w [D, D]; G, C fp32 [D, D]; r2 one fp64.
+ *   D must be a multiple of 64; n >= 0 (n = 0 is a no-op).
+ * The caller zeroes G, C and r2 when a warmup starts.
+ */
+size_t ispa_accum_stats_workspace_bytes(ispa_dtype a_dt, int64_t n, int32_t D);
+ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_t D,
+                             const void* a_loc, const void* delta_a, const void* w,
+                             float* G, float* C, double* r2,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ispa_solve_dw -- closed-form ridge absorption and reconstruction error,
+ * batched over layers (DE summary, Methodik: Delta W minimises
+ * ||A_loc (W + dW) - A_full W||^2 + lambda ||dW||^2, closed form
+ * dW = (A_loc^T A_loc + lambda I)^-1 A_loc^T (A_full - A_loc) W; EN review,
+ * Key Design 2 for eps).  Per layer l (matrices mat_stride elements apart):
+ *   lambda = lambda_abs + lambda_rel * tr(G) / D
+ *   G + lambda I = L L^T (fp64 Cholesky, G read from its upper triangle)
+ *   dW  = L^-T L^-1 C                    (fp64, stored fp32)
+ *   eps = r2 - <dW, C> - lambda ||dW||^2 (= ||A_loc dW - R||^2 at the ridge
+ *                                         optimum, penalty excluded)
+ *   info = 0, or the 1-based index of the first non-positive pivot (then dW
+ *          and eps are NaN).
+ *   w, w_eff  optional (both NULL or both set): w_eff = w + dW rounded once
+ *          to w_dt (BF16, F16 or F32), same layout as w.
+ *   D must be a multiple of 64.
+ */
+size_t ispa_solve_dw_workspace_bytes(int32_t n_layers, int32_t D);
+ispa_status ispa_solve_dw(int32_t n_layers, int32_t D, const float* G, const float* C,
+                          const double* r2, int64_t mat_stride, double lambda_abs,
+                          double lambda_rel, float* dW, double* eps, int32_t* info,
+                          const void* w, ispa_dtype w_dt, void* w_eff,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ispa_select_layers -- instance-specific layer selection (EN review, Key
+ * Design 3: sort layers by increasing eps and take the K lowest as L-Layers;
+ * K = x N for ISPA-x).  Stable: equal eps go to the lower layer index.
+ *   eps       fp64 [n_layers] (device), 1 <= n_layers <= 1024, 0 <= K <= n.
+ *   selected  int32 [K]: layer indices in ascending-eps order.
+ *   is_local  uint8 [n_layers]: 1 for selected layers.
+ *   status    int32 [1]: 0, or 1 if any eps is NaN (outputs then zero).
+ */
+ispa_status ispa_select_layers(int32_t n_layers, int32_t K, const double* eps,
+                               int32_t* selected, uint8_t* is_local, int32_t* status,
+                               hipStream_t stream);
+
+/*
+ * ispa_local_attn_proj -- post-switch layer (EN review, Key Designs 2-3: an
+ * L-Layer attends to its retained sink and current keys only and projects
+ * with W + dW; an F-Layer keeps full attention over its history with W).
+ *   y = softmax(scale q k^T) v  over all keys of the segments, then y W.
+ * Long key sets are split into blocks whose partial (o, lse) are merged by
+ * the LSE rule before the projection.
+ *   dt      ISPA_BF16 (d in {64,128}) or ISPA_F32.
+ *   w_proj  [D, D] of w_dt (W + dW for L-Layers, W for F-Layers); with
+ *           dt = BF16, w_dt must be BF16 or F16 (products on MFMA in bf16);
+ *           with dt = F32, w_dt must be F32.
+ *   y       [n_q, D] of y_dt (ISPA_F32 or ISPA_BF16).
+ *   n_segs  1..ISPA_MAX_SEGS; an empty key set gives y = 0.
+ */
+size_t ispa_local_attn_proj_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d,
+                                            const ispa_seg* segs, int32_t n_segs);
+ispa_status ispa_local_attn_proj(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d,
+                                 float scale, const void* q, int64_t q_stride,
+                                 const ispa_seg* segs, int32_t n_segs,
+                                 const void* w_proj, ispa_dtype w_dt,
+                                 void* y, ispa_dtype y_dt,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISPA_H */

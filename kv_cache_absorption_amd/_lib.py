@@ -1,0 +1,255 @@
+"""ctypes binding of libispa.
+
+Thin marshalling only: every function takes torch tensors that live on the
+GPU, allocates its outputs and workspace with torch, passes raw device
+pointers and the current HIP stream to the C ABI declared in include/ispa.h,
+and raises IspaError on a non-zero status.  All arithmetic happens in the
+HIP kernels of libispa.so; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libispa.so")
+
+ISPA_OK, ISPA_ERR_INVALID_ARG, ISPA_ERR_UNSUPPORTED, ISPA_ERR_WORKSPACE, ISPA_ERR_HIP = range(5)
+ISPA_F32, ISPA_BF16, ISPA_F16 = 0, 1, 2
+ISPA_MAX_SEGS = 8
+
+EXPORTED = [
+    "ispa_version", "ispa_status_str", "ispa_last_error",
+    "ispa_dual_attn_workspace_bytes", "ispa_dual_attn",
+    "ispa_lse_merge",
+    "ispa_accum_stats_workspace_bytes", "ispa_accum_stats",
+    "ispa_solve_dw_workspace_bytes", "ispa_solve_dw",
+    "ispa_select_layers",
+    "ispa_local_attn_proj_workspace_bytes", "ispa_local_attn_proj",
+]
+
+_DT = {torch.float32: ISPA_F32, torch.bfloat16: ISPA_BF16, torch.float16: ISPA_F16}
+_TORCH_DT = {v: k for k, v in _DT.items()}
+
+
+class IspaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libispa status {status}: {msg}")
+        self.status = status
+
+
+class Seg(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("k_stride", ctypes.c_int64), ("v_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libispa.so (built in-tree by kv_cache_absorption_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m kv_cache_absorption_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        f32, f64 = ctypes.c_float, ctypes.c_double
+        segp = ctypes.POINTER(Seg)
+        sig = {
+            "ispa_version": (i32, []),
+            "ispa_status_str": (ctypes.c_char_p, [i32]),
+            "ispa_last_error": (ctypes.c_char_p, []),
+            "ispa_dual_attn_workspace_bytes": (sz, [i32, i64, i32, i32, segp, i32, segp, i32]),
+            "ispa_dual_attn": (i32, [i32, i64, i32, i32, f32, vp, i64, segp, i32, segp, i32,
+                                     vp, vp, vp, vp, vp, sz, vp]),
+            "ispa_lse_merge": (i32, [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, i32,
+                                     vp, vp, vp, vp, i32, vp]),
+            "ispa_accum_stats_workspace_bytes": (sz, [i32, i64, i32]),
+            "ispa_accum_stats": (i32, [i32, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ispa_solve_dw_workspace_bytes": (sz, [i32, i32]),
+            "ispa_solve_dw": (i32, [i32, i32, vp, vp, vp, i64, f64, f64, vp, vp, vp, vp, i32, vp,
+                                    vp, sz, vp]),
+            "ispa_select_layers": (i32, [i32, i32, vp, vp, vp, vp, vp]),
+            "ispa_local_attn_proj_workspace_bytes": (sz, [i32, i64, i32, i32, segp, i32]),
+            "ispa_local_attn_proj": (i32, [i32, i64, i32, i32, f32, vp, i64, segp, i32, vp, i32,
+                                           vp, i32, vp, sz, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != ISPA_OK:
+        raise IspaError(status, lib().ispa_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _segs(pairs, H: int, d: int):
+    """[(k, v), ...] with k, v of shape [n, H, d] (rows may be strided) -> Seg array."""
+    arr = (Seg * max(1, len(pairs)))()
+    for i, (k, v) in enumerate(pairs):
+        for t in (k, v):
+            if t.dim() != 3 or t.shape[1] != H or t.shape[2] != d or t.stride(2) != 1 or t.stride(1) != d:
+                raise ValueError("segments must be [n, H, d] with contiguous [H, d] rows")
+        if k.shape[0] != v.shape[0]:
+            raise ValueError("k and v of a segment differ in length")
+        arr[i] = Seg(k.data_ptr(), v.data_ptr(), k.shape[0], k.stride(0), v.stride(0))
+    return arr, len(pairs)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _q_args(q: torch.Tensor):
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [n_q, H, d] with contiguous [H, d] rows")
+    return q.shape[0], q.shape[1], q.shape[2], q.stride(0)
+
+
+# ---------------------------------------------------------------------------
+def ispa_dual_attn(q, loc, hist, scale: float | None = None):
+    """Dual-stream attention.  q [n_q, H, d]; loc / hist lists of (k, v)
+    segments.  Returns (o_loc, lse_loc, o_hist, lse_hist), fp32."""
+    n_q, H, d, qs = _q_args(q)
+    dt = _DT[q.dtype]
+    scale = d ** -0.5 if scale is None else scale
+    ls, nl = _segs(loc, H, d)
+    hs, nh = _segs(hist, H, d)
+    dev = q.device
+    o_loc = torch.empty((n_q, H, d), dtype=torch.float32, device=dev)
+    o_hist = torch.empty_like(o_loc)
+    lse_loc = torch.empty((n_q, H), dtype=torch.float32, device=dev)
+    lse_hist = torch.empty_like(lse_loc)
+    L = lib()
+    wsb = L.ispa_dual_attn_workspace_bytes(dt, n_q, H, d, ls, nl, hs, nh)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_dual_attn(dt, n_q, H, d, scale, q.data_ptr(), qs, ls, nl, hs, nh,
+                            o_loc.data_ptr(), lse_loc.data_ptr(), o_hist.data_ptr(),
+                            lse_hist.data_ptr(), _ptr(ws), wsb, _stream(dev)))
+    return o_loc, lse_loc, o_hist, lse_hist
+
+
+def ispa_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],
+                   out_dtype=torch.float32, want_full=True, want_a0=True, want_delta=True):
+    """n-way LSE merge.  Returns (o_full, lse_full, a0, delta); a0/delta are
+    [n_q, D] of out_dtype, any of them None when not requested."""
+    o0 = o_parts[0]
+    n_q, H, d = o0.shape
+    dev = o0.device
+    for t in list(o_parts) + list(lse_parts):
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("parts must be contiguous fp32")
+    P = len(o_parts)
+    op = (ctypes.c_void_p * P)(*[t.data_ptr() for t in o_parts])
+    lp = (ctypes.c_void_p * P)(*[t.data_ptr() for t in lse_parts])
+    o_full = torch.empty((n_q, H, d), dtype=torch.float32, device=dev) if want_full else None
+    lse_full = torch.empty((n_q, H), dtype=torch.float32, device=dev) if want_full else None
+    a0 = torch.empty((n_q, H * d), dtype=out_dtype, device=dev) if want_a0 else None
+    delta = torch.empty((n_q, H * d), dtype=out_dtype, device=dev) if want_delta else None
+    _check(lib().ispa_lse_merge(P, op, lp, n_q, H, d, _ptr(o_full), _ptr(lse_full), _ptr(a0),
+                                _ptr(delta), _DT[out_dtype], _stream(dev)))
+    return o_full, lse_full, a0, delta
+
+
+def ispa_accum_stats(a_loc, delta_a, w, G, C, r2):
+    """In place: G (upper triangle) += a^T a, C += a^T (delta W), r2 += ||delta W||^2."""
+    n, D = a_loc.shape
+    for t in (a_loc, delta_a, w, G, C, r2):
+        if not t.is_contiguous():
+            raise ValueError("accum_stats operands must be contiguous")
+    if G.dtype != torch.float32 or C.dtype != torch.float32 or r2.dtype != torch.float64:
+        raise ValueError("G, C must be fp32 and r2 fp64")
+    dev = a_loc.device
+    L = lib()
+    adt = _DT[a_loc.dtype]
+    wsb = L.ispa_accum_stats_workspace_bytes(adt, n, D)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_accum_stats(adt, _DT[w.dtype], n, D, a_loc.data_ptr(), delta_a.data_ptr(),
+                              w.data_ptr(), G.data_ptr(), C.data_ptr(), r2.data_ptr(), _ptr(ws), wsb,
+                              _stream(dev)))
+
+
+def ispa_solve_dw(G, C, r2, lambda_abs=0.0, lambda_rel=1e-3, w=None, w_eff_dtype=None):
+    """Batched ridge solve.  G, C fp32 [L, D, D] (or [D, D]); r2 fp64 [L].
+    Returns (dW fp32, eps fp64 [L], info int32 [L], w_eff or None)."""
+    squeeze = G.dim() == 2
+    if squeeze:
+        G, C = G.unsqueeze(0), C.unsqueeze(0)
+        r2 = r2.reshape(1)
+        if w is not None:
+            w = w.unsqueeze(0)
+    nl, D, _ = G.shape
+    dev = G.device
+    for t in (G, C, r2):
+        if not t.is_contiguous():
+            raise ValueError("solve operands must be contiguous")
+    dW = torch.empty_like(G)
+    eps = torch.empty(nl, dtype=torch.float64, device=dev)
+    info = torch.empty(nl, dtype=torch.int32, device=dev)
+    w_eff = None
+    if w is not None:
+        w = w.contiguous()
+        w_eff = torch.empty_like(w, dtype=w_eff_dtype or w.dtype)
+        if w_eff.dtype != w.dtype:
+            raise ValueError("w_eff has the dtype of w")
+    L = lib()
+    wsb = L.ispa_solve_dw_workspace_bytes(nl, D)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_solve_dw(nl, D, G.data_ptr(), C.data_ptr(), r2.data_ptr(), D * D, lambda_abs,
+                           lambda_rel, dW.data_ptr(), eps.data_ptr(), info.data_ptr(), _ptr(w),
+                           _DT[w.dtype] if w is not None else 0, _ptr(w_eff), _ptr(ws), wsb,
+                           _stream(dev)))
+    if squeeze:
+        dW = dW[0]
+        if w_eff is not None:
+            w_eff = w_eff[0]
+    return dW, eps, info, w_eff
+
+
+def ispa_select_layers(eps, K: int):
+    """Returns (selected int32 [K], is_local uint8 [N], status int32 [1])."""
+    N = eps.shape[0]
+    dev = eps.device
+    eps = eps.contiguous()
+    sel = torch.empty(max(K, 1), dtype=torch.int32, device=dev)
+    is_local = torch.empty(N, dtype=torch.uint8, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().ispa_select_layers(N, K, eps.data_ptr(), sel.data_ptr(), is_local.data_ptr(),
+                                    status.data_ptr(), _stream(dev)))
+    return sel[:K], is_local, status
+
+
+def ispa_local_attn_proj(q, segs, w_proj, scale: float | None = None, out_dtype=torch.bfloat16):
+    """Attention over the segments then y @ w_proj.  Returns y [n_q, D]."""
+    n_q, H, d, qs = _q_args(q)
+    dt = _DT[q.dtype]
+    scale = d ** -0.5 if scale is None else scale
+    ss, ns = _segs(segs, H, d)
+    dev = q.device
+    if not w_proj.is_contiguous():
+        raise ValueError("w_proj must be contiguous")
+    y = torch.empty((n_q, H * d), dtype=out_dtype, device=dev)
+    L = lib()
+    wsb = L.ispa_local_attn_proj_workspace_bytes(dt, n_q, H, d, ss, ns)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_local_attn_proj(dt, n_q, H, d, scale, q.data_ptr(), qs, ss, ns,
+                                  w_proj.data_ptr(), _DT[w_proj.dtype], y.data_ptr(),
+                                  _DT[out_dtype], _ptr(ws), wsb, _stream(dev)))
+    return y

@@ -1,0 +1,316 @@
+// C ABI of libispa: argument validation, workspace sizing and dispatch.
+// Nothing here allocates device memory; every kernel runs on the caller's
+// stream.
+#include <stdio.h>
+
+#include <string>
+
+#include "attn.hpp"
+#include "gemm.hpp"
+#include "internal.hpp"
+
+namespace ispa {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+ispa_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return ISPA_ERR_HIP;
+  }
+  return ISPA_OK;
+}
+
+namespace {
+
+ispa_status fail(ispa_status s, const std::string& msg) {
+  set_error(msg);
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// validate a key group; bf16 path needs 16-byte aligned rows
+ispa_status check_group(const char* name, ispa_dtype dt, int32_t H, int32_t d, const ispa_seg* segs,
+                        int32_t n) {
+  if (n < 0 || n > ISPA_MAX_SEGS)
+    return fail(ISPA_ERR_INVALID_ARG, std::string(name) + ": segment count out of range");
+  if (n > 0 && !segs) return fail(ISPA_ERR_INVALID_ARG, std::string(name) + ": null segment table");
+  const int64_t row = (int64_t)H * d;
+  const size_t al = dt == ISPA_BF16 ? 16 : 4;
+  for (int i = 0; i < n; ++i) {
+    const ispa_seg& s = segs[i];
+    if (s.n < 0) return fail(ISPA_ERR_INVALID_ARG, std::string(name) + ": negative segment length");
+    if (s.n == 0) continue;
+    if (!s.k || !s.v) return fail(ISPA_ERR_INVALID_ARG, std::string(name) + ": null k/v pointer");
+    if (s.k_stride < row || s.v_stride < row)
+      return fail(ISPA_ERR_INVALID_ARG, std::string(name) + ": row stride smaller than H*d");
+    if (!aligned(s.k, al) || !aligned(s.v, al) || (dt == ISPA_BF16 && (s.k_stride % 8 || s.v_stride % 8)))
+      return fail(ISPA_ERR_INVALID_ARG, std::string(name) + ": k/v rows must be 16-byte aligned");
+  }
+  return ISPA_OK;
+}
+
+ispa_status check_attn_common(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, const void* q,
+                              int64_t q_stride) {
+  if (dt != ISPA_BF16 && dt != ISPA_F32) return fail(ISPA_ERR_UNSUPPORTED, "attention dtype must be BF16 or F32");
+  if (d != 64 && d != 128) return fail(ISPA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (n_q < 0 || H < 1) return fail(ISPA_ERR_INVALID_ARG, "n_q must be >= 0 and H >= 1");
+  if (n_q > 0 && !q) return fail(ISPA_ERR_INVALID_ARG, "null q");
+  if (q_stride < (int64_t)H * d) return fail(ISPA_ERR_INVALID_ARG, "q_stride smaller than H*d");
+  if (dt == ISPA_BF16 && (!aligned(q, 16) || q_stride % 8))
+    return fail(ISPA_ERR_INVALID_ARG, "q rows must be 16-byte aligned");
+  if (dt == ISPA_F32 && !aligned(q, 4)) return fail(ISPA_ERR_INVALID_ARG, "q must be 4-byte aligned");
+  return ISPA_OK;
+}
+
+size_t gemm_r_blocks(int64_t n, int32_t D) {
+  return (size_t)((n + kGemmBM - 1) / kGemmBM) * (size_t)((D + kGemmBN - 1) / kGemmBN);
+}
+int64_t rt_ld(int64_t n) { return (n + 7) / 8 * 8; }
+
+}  // namespace
+}  // namespace ispa
+
+using namespace ispa;
+
+extern "C" {
+
+int32_t ispa_version(void) { return ISPA_VERSION; }
+
+const char* ispa_status_str(ispa_status s) {
+  switch (s) {
+    case ISPA_OK: return "ok";
+    case ISPA_ERR_INVALID_ARG: return "invalid argument";
+    case ISPA_ERR_UNSUPPORTED: return "unsupported";
+    case ISPA_ERR_WORKSPACE: return "workspace too small";
+    case ISPA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* ispa_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------- dual_attn
+size_t ispa_dual_attn_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, const ispa_seg* loc,
+                                      int32_t n_loc, const ispa_seg* hist, int32_t n_hist) {
+  (void)dt;
+  if (n_q <= 0 || H < 1 || n_loc < 0 || n_hist < 0 || n_loc > ISPA_MAX_SEGS || n_hist > ISPA_MAX_SEGS)
+    return 0;
+  HostGroup g[2] = {{loc, n_loc}, {hist, n_hist}};
+  const SplitPlan plan = plan_splits(n_q, H, g, 2);
+  return split_workspace_bytes(n_q, H, d, plan, 2);
+}
+
+ispa_status ispa_dual_attn(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale, const void* q,
+                           int64_t q_stride, const ispa_seg* loc, int32_t n_loc, const ispa_seg* hist,
+                           int32_t n_hist, float* o_loc, float* lse_loc, float* o_hist, float* lse_hist,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  ispa_status st = check_attn_common(dt, n_q, H, d, q, q_stride);
+  if (st) return st;
+  if ((st = check_group("loc", dt, H, d, loc, n_loc))) return st;
+  if ((st = check_group("hist", dt, H, d, hist, n_hist))) return st;
+  if (n_q > 0 && (!o_loc || !lse_loc || !o_hist || !lse_hist))
+    return fail(ISPA_ERR_INVALID_ARG, "null output pointer");
+  if (!aligned(o_loc, 16) || !aligned(o_hist, 16)) return fail(ISPA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(ISPA_ERR_INVALID_ARG, "scale must be finite");
+  const size_t need = ispa_dual_attn_workspace_bytes(dt, n_q, H, d, loc, n_loc, hist, n_hist);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(ISPA_ERR_WORKSPACE, "dual_attn workspace too small or misaligned");
+  if (n_q == 0) return ISPA_OK;
+  HostGroup g[2] = {{loc, n_loc}, {hist, n_hist}};
+  float* o[2] = {o_loc, o_hist};
+  float* l[2] = {lse_loc, lse_hist};
+  return run_group_attention(dt, n_q, H, d, scale, q, q_stride, g, 2, o, l, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- lse_merge
+ispa_status ispa_lse_merge(int32_t n_parts, const float* const* o_parts, const float* const* lse_parts,
+                           int64_t n_q, int32_t H, int32_t d, float* o_full, float* lse_full, void* a0_out,
+                           void* delta_out, ispa_dtype out_dt, hipStream_t stream) {
+  if (n_parts < 1 || n_parts > 16) return fail(ISPA_ERR_INVALID_ARG, "n_parts must be 1..16");
+  if (!o_parts || !lse_parts) return fail(ISPA_ERR_INVALID_ARG, "null part table");
+  if (n_q < 0 || H < 1 || d < 4 || d % 4) return fail(ISPA_ERR_INVALID_ARG, "bad shape (d must be a multiple of 4)");
+  if (!valid_dtype(out_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad out_dt");
+  for (int i = 0; i < n_parts; ++i) {
+    if (n_q > 0 && (!o_parts[i] || !lse_parts[i])) return fail(ISPA_ERR_INVALID_ARG, "null part pointer");
+    if (!aligned(o_parts[i], 16)) return fail(ISPA_ERR_INVALID_ARG, "parts must be 16-byte aligned");
+  }
+  if (!aligned(o_full, 16) || !aligned(a0_out, 16) || !aligned(delta_out, 16))
+    return fail(ISPA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  MergeParams p{};
+  p.n_parts = n_parts;
+  p.d = d;
+  p.n_rows = n_q * H;
+  for (int i = 0; i < n_parts; ++i) {
+    p.o[i] = o_parts[i];
+    p.lse[i] = lse_parts[i];
+  }
+  p.o_full = o_full;
+  p.lse_full = lse_full;
+  p.a0 = a0_out;
+  p.delta = delta_out;
+  p.out_dt = out_dt;
+  return launch_merge(p, stream);
+}
+
+// ---------------------------------------------------------------- accum_stats
+size_t ispa_accum_stats_workspace_bytes(ispa_dtype a_dt, int64_t n, int32_t D) {
+  if (n <= 0 || D <= 0) return 0;
+  if (a_dt == ISPA_F32) return align256((size_t)n * D * 4) + align256(64 * 8);
+  return align256((size_t)D * rt_ld(n) * 2) + align256(gemm_r_blocks(n, D) * 8);
+}
+
+ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_t D, const void* a_loc,
+                             const void* delta_a, const void* w, float* G, float* C, double* r2, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(a_dt) || !valid_dtype(w_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad dtype");
+  if (a_dt == ISPA_F32 && w_dt != ISPA_F32) return fail(ISPA_ERR_UNSUPPORTED, "F32 statistics need F32 W");
+  if (a_dt != ISPA_F32 && w_dt == ISPA_F32) return fail(ISPA_ERR_UNSUPPORTED, "16-bit statistics need 16-bit W");
+  if (D <= 0 || D % 64) return fail(ISPA_ERR_INVALID_ARG, "D must be a positive multiple of 64");
+  if (n < 0) return fail(ISPA_ERR_INVALID_ARG, "n must be >= 0");
+  if (!G || !C || !r2 || !w) return fail(ISPA_ERR_INVALID_ARG, "null G/C/r2/w");
+  if (n > 0 && (!a_loc || !delta_a)) return fail(ISPA_ERR_INVALID_ARG, "null activations");
+  const size_t al = a_dt == ISPA_F32 ? 4 : 16;
+  if (!aligned(a_loc, al) || !aligned(delta_a, al) || !aligned(w, 4))
+    return fail(ISPA_ERR_INVALID_ARG, "misaligned activations or W");
+  if (n == 0) return ISPA_OK;
+  const size_t need = ispa_accum_stats_workspace_bytes(a_dt, n, D);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "accum_stats workspace too small or misaligned");
+  if (a_dt == ISPA_F32)
+    return launch_stats_f32(n, D, (const float*)a_loc, (const float*)delta_a, (const float*)w, G, C, r2, ws,
+                            stream);
+  const int64_t ldr = rt_ld(n);
+  uint16_t* Rt = (uint16_t*)ws;
+  double* partials = (double*)((char*)ws + align256((size_t)D * ldr * 2));
+  // R = delta W  (stored transposed, 16-bit) and per-workgroup ||R||^2
+  GemmParams r{};
+  r.M = n;
+  r.N = D;
+  r.K = D;
+  r.x = GemmOperand{delta_a, D, a_dt, kDirect};
+  r.y = GemmOperand{w, D, w_dt, kTrans};
+  r.epi = kStoreRt;
+  r.out = Rt;
+  r.ld_out = ldr;
+  r.tiles_m = (int)((n + kGemmBM - 1) / kGemmBM);
+  r.tiles_n = (int)((D + kGemmBN - 1) / kGemmBN);
+  r.sq_partials = partials;
+  int nblk = 0;
+  ispa_status st = launch_gemm(r, a_dt, stream, &nblk);
+  if (st) return st;
+  if ((st = launch_reduce_add(partials, nblk, r2, stream))) return st;
+  // G += A^T A (upper triangle), then C += A^T R
+  GemmParams g{};
+  g.M = D;
+  g.N = D;
+  g.K = n;
+  g.x = GemmOperand{a_loc, D, a_dt, kTrans};
+  g.y = GemmOperand{a_loc, D, a_dt, kTrans};
+  g.epi = kAccum;
+  g.out = G;
+  g.ld_out = D;
+  g.tiles_m = g.tiles_n = (int)((D + kGemmBM - 1) / kGemmBM);
+  g.tri = 1;
+  if ((st = launch_gemm(g, a_dt, stream, nullptr))) return st;
+  GemmParams c = g;
+  c.y = GemmOperand{Rt, ldr, a_dt, kDirect};
+  c.out = C;
+  c.tri = 0;
+  return launch_gemm(c, a_dt, stream, nullptr);
+}
+
+// ---------------------------------------------------------------- solve_dw
+size_t ispa_solve_dw_workspace_bytes(int32_t n_layers, int32_t D) {
+  if (n_layers <= 0 || D <= 0) return 0;
+  return solve_ws_bytes(n_layers, D);
+}
+
+ispa_status ispa_solve_dw(int32_t n_layers, int32_t D, const float* G, const float* C, const double* r2,
+                          int64_t mat_stride, double lambda_abs, double lambda_rel, float* dW, double* eps,
+                          int32_t* info, const void* w, ispa_dtype w_dt, void* w_eff, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (n_layers < 1) return fail(ISPA_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (D <= 0 || D % 64) return fail(ISPA_ERR_INVALID_ARG, "D must be a positive multiple of 64");
+  if (mat_stride < (int64_t)D * D) return fail(ISPA_ERR_INVALID_ARG, "mat_stride smaller than D*D");
+  if (!G || !C || !r2 || !dW || !eps || !info) return fail(ISPA_ERR_INVALID_ARG, "null pointer");
+  if ((w == nullptr) != (w_eff == nullptr)) return fail(ISPA_ERR_INVALID_ARG, "w and w_eff must both be set or null");
+  if (w && !valid_dtype(w_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad w_dt");
+  if (!std::isfinite(lambda_abs) || !std::isfinite(lambda_rel) || lambda_abs < 0 || lambda_rel < 0)
+    return fail(ISPA_ERR_INVALID_ARG, "lambda must be finite and >= 0");
+  const size_t need = ispa_solve_dw_workspace_bytes(n_layers, D);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "solve_dw workspace too small or misaligned");
+  return run_solve(n_layers, D, G, C, r2, mat_stride, lambda_abs, lambda_rel, dW, eps, info, w, w_dt, w_eff,
+                   ws, stream);
+}
+
+// ---------------------------------------------------------------- select
+ispa_status ispa_select_layers(int32_t n_layers, int32_t K, const double* eps, int32_t* selected,
+                               uint8_t* is_local, int32_t* status, hipStream_t stream) {
+  if (n_layers < 1 || n_layers > 1024) return fail(ISPA_ERR_INVALID_ARG, "n_layers must be 1..1024");
+  if (K < 0 || K > n_layers) return fail(ISPA_ERR_INVALID_ARG, "K must be in 0..n_layers");
+  if (!eps || !is_local || !status || (K > 0 && !selected)) return fail(ISPA_ERR_INVALID_ARG, "null pointer");
+  return launch_select(n_layers, K, eps, selected, is_local, status, stream);
+}
+
+// ---------------------------------------------------------------- local_attn_proj
+size_t ispa_local_attn_proj_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d,
+                                            const ispa_seg* segs, int32_t n_segs) {
+  (void)dt;
+  if (n_q <= 0 || H < 1 || n_segs < 0 || n_segs > ISPA_MAX_SEGS) return 0;
+  HostGroup g[1] = {{segs, n_segs}};
+  const SplitPlan plan = plan_splits(n_q, H, g, 1);
+  return align256((size_t)n_q * H * d * 4) + align256((size_t)n_q * H * 4) +
+         split_workspace_bytes(n_q, H, d, plan, 1);
+}
+
+ispa_status ispa_local_attn_proj(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale, const void* q,
+                                 int64_t q_stride, const ispa_seg* segs, int32_t n_segs, const void* w_proj,
+                                 ispa_dtype w_dt, void* y, ispa_dtype y_dt, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  ispa_status st = check_attn_common(dt, n_q, H, d, q, q_stride);
+  if (st) return st;
+  if (n_segs < 1) return fail(ISPA_ERR_INVALID_ARG, "n_segs must be >= 1");
+  if ((st = check_group("segs", dt, H, d, segs, n_segs))) return st;
+  if (!valid_dtype(w_dt) || !valid_dtype(y_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad w_dt or y_dt");
+  if (dt == ISPA_F32 && w_dt != ISPA_F32) return fail(ISPA_ERR_UNSUPPORTED, "F32 attention needs F32 W");
+  if (dt == ISPA_BF16 && w_dt == ISPA_F32) return fail(ISPA_ERR_UNSUPPORTED, "BF16 attention needs 16-bit W");
+  if (!w_proj || (n_q > 0 && !y)) return fail(ISPA_ERR_INVALID_ARG, "null w_proj or y");
+  if (!aligned(w_proj, 4) || !aligned(y, 4)) return fail(ISPA_ERR_INVALID_ARG, "misaligned w_proj or y");
+  if (!std::isfinite(scale)) return fail(ISPA_ERR_INVALID_ARG, "scale must be finite");
+  if (n_q == 0) return ISPA_OK;
+  const size_t need = ispa_local_attn_proj_workspace_bytes(dt, n_q, H, d, segs, n_segs);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "local_attn_proj workspace too small or misaligned");
+  const int32_t D = H * d;
+  float* O = (float*)ws;
+  float* lse = (float*)((char*)ws + align256((size_t)n_q * D * 4));
+  char* rest = (char*)lse + align256((size_t)n_q * H * 4);
+  HostGroup g[1] = {{segs, n_segs}};
+  float* oo[1] = {O};
+  float* ll[1] = {lse};
+  st = run_group_attention(dt, n_q, H, d, scale, q, q_stride, g, 1, oo, ll, rest,
+                           ws_bytes - (size_t)(rest - (char*)ws), stream);
+  if (st) return st;
+  if (dt == ISPA_F32) return launch_proj_f32(n_q, D, O, (const float*)w_proj, y, y_dt, stream);
+  GemmParams p{};
+  p.M = n_q;
+  p.N = D;
+  p.K = D;
+  p.x = GemmOperand{O, D, ISPA_F32, kDirect};
+  p.y = GemmOperand{w_proj, D, w_dt, kTrans};
+  p.epi = kStore;
+  p.out_dt = y_dt;
+  p.out = y;
+  p.ld_out = D;
+  p.tiles_m = (int)((n_q + kGemmBM - 1) / kGemmBM);
+  p.tiles_n = (int)((D + kGemmBN - 1) / kGemmBN);
+  return launch_gemm(p, ISPA_BF16, stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Attention kernels: parameter block and host launchers.
+#pragma once
+
+#include "common.hpp"
+
+namespace ispa {
+
+// One segment of a key group as the kernels see it.
+struct AttnSeg {
+  const void* k;
+  const void* v;
+  int64_t n;
+  int64_t ks;  // row strides in elements
+  int64_t vs;
+};
+
+// One unit of key work: keys [kbeg, kend) of group `group` (positions in the
+// concatenation of that group's segments), written as normalised o and lse.
+struct AttnJob {
+  int32_t group;
+  int32_t pad;
+  int64_t kbeg;
+  int64_t kend;
+  float* o;    // [n_q, H, d]
+  float* lse;  // [n_q, H]
+};
+
+constexpr int kMaxJobs = 32;
+
+struct AttnParams {
+  const void* q;
+  int64_t q_stride;
+  int64_t n_q;
+  int32_t H;
+  int32_t n_qtiles;
+  float c;  // scale * log2(e)
+  int32_t n_jobs;
+  int32_t n_segs[2];
+  AttnSeg segs[2][ISPA_MAX_SEGS];
+  AttnJob jobs[kMaxJobs];
+};
+
+// A group description on the host.
+struct HostGroup {
+  const ispa_seg* segs;
+  int32_t n_segs;
+  int64_t n_keys() const {
+    int64_t t = 0;
+    for (int i = 0; i < n_segs; ++i) t += segs[i].n;
+    return t;
+  }
+};
+
+// Plan of how a group's keys are cut into jobs.
+struct SplitPlan {
+  int n_splits[2];
+  int64_t split_len[2];
+};
+
+// Choose splits so the launch has enough equal-sized work units.
+SplitPlan plan_splits(int64_t n_q, int32_t H, const HostGroup* groups, int n_groups);
+
+// Workspace bytes for the partial (o, lse) of the split groups.
+size_t split_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan& plan, int n_groups);
+
+// Run attention for n_groups (1 or 2) groups.  For each group the final
+// normalised o / lse go to o_out[g] / lse_out[g]; split groups use ws for
+// partials and are merged with the LSE rule.
+ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale,
+                                const void* q, int64_t q_stride, const HostGroup* groups,
+                                int n_groups, float* const* o_out, float* const* lse_out,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+// n-way merge used both by the public call and by split combining.
+struct MergeParams {
+  int32_t n_parts;
+  int32_t d;
+  int64_t n_rows;  // n_q * H
+  const float* o[16];
+  const float* lse[16];
+  float* o_full;
+  float* lse_full;
+  void* a0;
+  void* delta;
+  int32_t out_dt;
+};
+ispa_status launch_merge(const MergeParams& p, hipStream_t stream);
+
+}  // namespace ispa

@@ -1,0 +1,137 @@
+"""CPU checks of the C ABI: the library loads, exports what include/ispa.h
+declares, and rejects bad arguments on the host before launching anything.
+Also the host-side stream layout against the oracle's grouping."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    try:
+        from kv_cache_absorption_amd import _lib as m
+        return m, m.lib()
+    except (ImportError, OSError) as e:  # libamdhip64 missing or library not built
+        pytest.skip(f"libispa not loadable here: {e}")
+
+
+def test_exports_match_header():
+    m, L = _lib()
+    hdr = open(os.path.join(ROOT, "include", "ispa.h")).read()
+    declared = set(re.findall(r"\b(ispa_[a-z_]+)\s*\(", hdr))
+    assert declared == set(m.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.ispa_version() == 10000
+    assert L.ispa_status_str(m.ISPA_ERR_WORKSPACE) == b"workspace too small"
+
+
+def _seg(n, H=2, d=128, ptr=256):
+    return (n and ptr, n and ptr, n, H * d, H * d)
+
+
+def _segarr(m, specs):
+    arr = (m.Seg * max(1, len(specs)))()
+    for i, s in enumerate(specs):
+        arr[i] = m.Seg(*s)
+    return arr
+
+
+FAKE = 4096  # a non-null, aligned address that is never dereferenced
+
+
+def test_dual_attn_rejects_bad_args():
+    m, L = _lib()
+    segs = _segarr(m, [_seg(10, ptr=FAKE)])
+    args = dict(dt=m.ISPA_BF16, n_q=4, H=2, d=128, scale=0.1, q=FAKE, qs=256)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.ispa_dual_attn(a["dt"], a["n_q"], a["H"], a["d"], a["scale"], a["q"], a["qs"],
+                                segs, kw.get("nl", 1), segs, kw.get("nh", 1), FAKE, FAKE, FAKE, FAKE,
+                                None, 0, None)
+    assert call(d=96) == m.ISPA_ERR_UNSUPPORTED
+    assert call(dt=m.ISPA_F16) == m.ISPA_ERR_UNSUPPORTED
+    assert call(q=None) == m.ISPA_ERR_INVALID_ARG
+    assert call(qs=100) == m.ISPA_ERR_INVALID_ARG
+    assert call(nl=9) == m.ISPA_ERR_INVALID_ARG
+    assert call(q=FAKE + 2) == m.ISPA_ERR_INVALID_ARG  # misaligned bf16 rows
+    assert call(scale=float("nan")) == m.ISPA_ERR_INVALID_ARG
+    assert b"finite" in L.ispa_last_error()
+    bad = _segarr(m, [(0, FAKE, 10, 256, 256)])
+    assert L.ispa_dual_attn(m.ISPA_BF16, 4, 2, 128, 0.1, FAKE, 256, bad, 1, segs, 1,
+                            FAKE, FAKE, FAKE, FAKE, None, 0, None) == m.ISPA_ERR_INVALID_ARG
+
+
+def test_workspace_queries_and_errors():
+    m, L = _lib()
+    # Wan-1.3B layer: 37 q-tiles x 12 heads x 2 groups is below the split target,
+    # so the history group is split and needs workspace
+    loc = _segarr(m, [_seg(4680, 12, 128, FAKE), _seg(4680, 12, 128, FAKE)])
+    hist = _segarr(m, [_seg(28080, 12, 128, FAKE)])
+    need = L.ispa_dual_attn_workspace_bytes(m.ISPA_BF16, 4680, 12, 128, loc, 2, hist, 1)
+    assert need > 0
+    st = L.ispa_dual_attn(m.ISPA_BF16, 4680, 12, 128, 0.1, FAKE, 1536, loc, 2, hist, 1,
+                          FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == m.ISPA_ERR_WORKSPACE
+    # 14B shape: enough work units, no split
+    loc40 = _segarr(m, [_seg(4680, 40, 128, FAKE), _seg(4680, 40, 128, FAKE)])
+    hist40 = _segarr(m, [_seg(79560, 40, 128, FAKE)])
+    assert L.ispa_dual_attn_workspace_bytes(m.ISPA_BF16, 4680, 40, 128, loc40, 2, hist40, 1) == 0
+    assert L.ispa_accum_stats_workspace_bytes(m.ISPA_F16, 4680, 1536) >= 1536 * 4680 * 2
+    assert L.ispa_solve_dw_workspace_bytes(2, 128) >= 2 * 2 * 128 * 128 * 8
+
+
+def test_stats_solve_select_reject_bad_args():
+    m, L = _lib()
+    F = FAKE
+    assert L.ispa_accum_stats(m.ISPA_BF16, m.ISPA_BF16, 10, 100, F, F, F, F, F, F, F, 1 << 20, None) \
+        == m.ISPA_ERR_INVALID_ARG  # D not a multiple of 64
+    assert L.ispa_accum_stats(m.ISPA_F32, m.ISPA_BF16, 10, 128, F, F, F, F, F, F, F, 1 << 20, None) \
+        == m.ISPA_ERR_UNSUPPORTED
+    assert L.ispa_accum_stats(m.ISPA_BF16, m.ISPA_BF16, 10, 128, F, F, F, F, F, F, None, 0, None) \
+        == m.ISPA_ERR_WORKSPACE
+    assert L.ispa_accum_stats(m.ISPA_BF16, m.ISPA_BF16, 0, 128, F, F, F, F, F, F, None, 0, None) \
+        == m.ISPA_OK  # empty step: nothing to do, nothing launched
+    assert L.ispa_solve_dw(1, 128, F, F, F, 128 * 128, 0.0, 1e-3, F, F, F, None, 0, None, None, 0,
+                           None) == m.ISPA_ERR_WORKSPACE
+    assert L.ispa_solve_dw(1, 128, F, F, F, 100, 0.0, 1e-3, F, F, F, None, 0, None, F, 1 << 30,
+                           None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_solve_dw(1, 128, F, F, F, 128 * 128, 0.0, -1.0, F, F, F, None, 0, None, F, 1 << 30,
+                           None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_solve_dw(1, 128, F, F, F, 128 * 128, 0.0, 1e-3, F, F, F, F, m.ISPA_BF16, None, F,
+                           1 << 30, None) == m.ISPA_ERR_INVALID_ARG  # w without w_eff
+    assert L.ispa_select_layers(30, 31, F, F, F, F, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_select_layers(0, 0, F, F, F, F, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_select_layers(2000, 1, F, F, F, F, None) == m.ISPA_ERR_INVALID_ARG
+    op = (ctypes.c_void_p * 1)(F)
+    assert L.ispa_lse_merge(0, op, op, 4, 2, 128, F, F, F, F, m.ISPA_F32, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_lse_merge(1, op, op, 4, 2, 6, F, F, F, F, m.ISPA_F32, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_lse_merge(1, op, op, 4, 2, 128, F, F, F, F, 7, None) == m.ISPA_ERR_UNSUPPORTED
+    segs = _segarr(m, [_seg(10, ptr=F)])
+    assert L.ispa_local_attn_proj(m.ISPA_BF16, 4, 2, 128, 0.1, F, 256, segs, 1, F, m.ISPA_F32, F,
+                                  m.ISPA_BF16, F, 1 << 20, None) == m.ISPA_ERR_UNSUPPORTED
+    assert L.ispa_local_attn_proj(m.ISPA_BF16, 4, 2, 128, 0.1, F, 256, segs, 0, F, m.ISPA_BF16, F,
+                                  m.ISPA_BF16, F, 1 << 20, None) == m.ISPA_ERR_INVALID_ARG
+
+
+def test_stream_layout_matches_oracle_grouping():
+    from kv_cache_absorption_amd.stream import chunk_segments, keys_retained, kv_bytes
+    from oracle import kv_bytes_retained, stream_groups
+    T, H, d = 5, 2, 4
+    cache = torch.arange(12 * T * H * d, dtype=torch.float32).reshape(12 * T, H, d)
+    for c in range(12):
+        loc, hist = chunk_segments(cache, cache, c, T)
+        oloc, ohist = stream_groups(c, T)
+        for got, want in ((loc, oloc), (hist, ohist)):
+            assert len(got) == len(want)
+            for (k, v), (a, b) in zip(got, want):
+                assert torch.equal(k, cache[a:b]) and k.data_ptr() == cache[a:b].data_ptr()
+    flags = [1, 0, 1, 1, 0]
+    for c in (0, 1, 7):
+        n = keys_retained(c, T, flags)
+        assert kv_bytes(n, 1536) == kv_bytes_retained(n, 1536)

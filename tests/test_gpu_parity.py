@@ -1,0 +1,362 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Bars: attention output rel-L2 <= 5e-3 and LSE abs <= 2e-3 with bf16 inputs;
+merge vs monolithic attention <= 1e-5 relative in fp32 mode; dW
+rel-Frobenius <= 1e-3; identical selection wherever the eps gap at the
+K-th boundary exceeds 1e-4 relative.  Other bars are derived in each test.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    _need_gpu()
+    torch.manual_seed(0)
+    print(flush=True)
+
+
+def K():
+    import kv_cache_absorption_amd as k
+    return k
+
+
+def h64(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+def rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def rel_fro_upper(G_gpu, G_ref):
+    iu = np.triu_indices(G_ref.shape[0])
+    return rel(G_gpu[iu], G_ref[iu])
+
+
+# ---------------------------------------------------------------- attention
+def _cache(n, H, d, seed, dtype=torch.bfloat16, pad=0):
+    """[n, H, d] rows with row stride H*d + pad (a view into a wider buffer)."""
+    x = synth.normal((n, H * d + pad), seed, DEV, dtype=dtype)
+    return x[:, : H * d].unflatten(1, (H, d))
+
+
+@pytest.mark.parametrize("d,H,n_q,n_sink,n_hist,pad", [
+    (128, 2, 200, 70, 300, 0),     # ragged q tile, ragged key tiles
+    (128, 3, 129, 64, 1000, 64),   # strided rows, one query past a tile
+    (64, 4, 77, 5, 190, 0),        # d = 64, tiny sink
+    (128, 1, 1, 1, 1, 0),          # degenerate single query/key
+    (128, 2, 100, 64, 9000, 0),    # history split into ragged pieces + merge
+])
+def test_dual_attn_bf16_parity(d, H, n_q, n_sink, n_hist, pad):
+    print(f"dual_attn bf16 d={d} H={H} n_q={n_q} sink={n_sink} hist={n_hist} pad={pad}", flush=True)
+    seed = 1000 + d + H
+    q = _cache(n_q, H, d, seed, pad=pad)
+    ks, vs = _cache(n_sink, H, d, seed + 1, pad=pad), _cache(n_sink, H, d, seed + 2, pad=pad)
+    kc, vc = _cache(n_q, H, d, seed + 3, pad=pad), _cache(n_q, H, d, seed + 4, pad=pad)
+    kh = _cache(n_hist, H, d, seed + 5, pad=pad) + 0.5
+    vh = _cache(n_hist, H, d, seed + 6, pad=pad)
+    scale = d ** -0.5
+    o_l, l_l, o_h, l_h = K().ispa_dual_attn(q, [(ks, vs), (kc, vc)], [(kh, vh)], scale)
+    torch.cuda.synchronize()
+    ref = O.dual_stream_attention(q.cpu(), torch.cat([ks, kc]).cpu(), torch.cat([vs, vc]).cpu(),
+                                  kh.cpu(), vh.cpu(), scale)
+    assert rel(h64(o_l), ref["o_loc"]) <= 5e-3
+    assert rel(h64(o_h), ref["o_hist"]) <= 5e-3
+    assert np.abs(h64(l_l) - ref["lse_loc"]).max() <= 2e-3
+    assert np.abs(h64(l_h) - ref["lse_hist"]).max() <= 2e-3
+
+
+def test_dual_attn_empty_history_and_zero_query():
+    print("dual_attn empty history / zero query", flush=True)
+    H, d, n = 2, 128, 150
+    q = torch.zeros((n, H, d), dtype=torch.bfloat16, device=DEV)
+    k, v = _cache(300, H, d, 7), _cache(300, H, d, 8)
+    o_l, l_l, o_h, l_h = K().ispa_dual_attn(q, [(k, v)], [], d ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.all(o_h == 0) and torch.all(torch.isneginf(l_h))
+    # q = 0: uniform softmax, o = mean of v, lse = ln n
+    np.testing.assert_allclose(h64(l_l), math.log(300), atol=1e-5)
+    mean_v = h64(v).mean(axis=0)
+    assert rel(h64(o_l), np.broadcast_to(mean_v, (n, H, d))) <= 1e-5
+
+
+def test_dual_attn_wan13b_sampled_rows():
+    """Wan-1.3B layer at full size (4680 queries, 12 heads, 9360 local and
+    28080 history keys): every output row is computed on the GPU, a sample of
+    64 query rows is checked against the oracle."""
+    print("dual_attn wan1.3b full size, sampled rows", flush=True)
+    g = synth.wan13b_single_layer(seed=3, device=DEV)
+    q, kc, vc = g.step(0)
+    o_l, l_l, o_h, l_h = K().ispa_dual_attn(q, [(g.sink_k, g.sink_v), (kc, vc)], [(g.hist_k, g.hist_v)])
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(4680, 64, replace=False))
+    rows = np.concatenate([rows, [4679, 4608, 0]])  # include the ragged last q tile
+    ref = O.dual_stream_attention(q[rows].cpu(), torch.cat([g.sink_k, kc]).cpu(),
+                                  torch.cat([g.sink_v, vc]).cpu(), g.hist_k.cpu(), g.hist_v.cpu(),
+                                  128 ** -0.5)
+    assert rel(h64(o_l[rows]), ref["o_loc"]) <= 5e-3
+    assert rel(h64(o_h[rows]), ref["o_hist"]) <= 5e-3
+    assert np.abs(h64(l_l[rows]) - ref["lse_loc"]).max() <= 2e-3
+    assert np.abs(h64(l_h[rows]) - ref["lse_hist"]).max() <= 2e-3
+    # history carries substantial mass (the offset keys make the merge matter)
+    s = 1 / (1 + np.exp(-(ref["lse_hist"] - ref["lse_loc"])))
+    assert 0.3 < s.mean() < 0.95
+
+
+def test_dual_attn_f32_and_merge_tiny():
+    """fp32 mode on the tiny workload: merged output vs monolithic attention
+    <= 1e-5 relative."""
+    print("dual_attn f32 tiny + merge", flush=True)
+    g = synth.tiny_fp32(seed=11, device=DEV)
+    q, kc, vc = g.step(0)
+    o_l, l_l, o_h, l_h = K().ispa_dual_attn(q, [(g.sink_k, g.sink_v), (kc, vc)], [(g.hist_k, g.hist_v)],
+                                            64 ** -0.5)
+    o_f, l_f, a0, dl = K().ispa_lse_merge([o_l, o_h], [l_l, l_h], torch.float32)
+    torch.cuda.synchronize()
+    mono_o, mono_l = O.group_attention(q.cpu(), torch.cat([g.sink_k, kc, g.hist_k]).cpu(),
+                                       torch.cat([g.sink_v, vc, g.hist_v]).cpu(), 64 ** -0.5)
+    assert rel(h64(o_f), mono_o) <= 1e-5
+    assert np.abs(h64(l_f) - mono_l).max() <= 1e-5 * np.abs(mono_l).max()
+    assert torch.equal(a0.view(-1), o_l.view(-1))
+    ref_delta = mono_o.reshape(64, -1) - h64(o_l).reshape(64, -1)
+    assert rel(h64(dl), ref_delta) <= 1e-4
+
+
+# ---------------------------------------------------------------- merge
+def test_merge_parts_from_oracle():
+    print("merge: oracle parts, 3-way and empty", flush=True)
+    rng = np.random.default_rng(21)
+    n_q, H, d = 37, 3, 128
+    qn = rng.normal(size=(n_q, H, d))
+    ks = [rng.normal(size=(n, H, d)) + s for n, s in ((20, 0.0), (50, 0.5), (7, -0.3))]
+    vs = [rng.normal(size=(n, H, d)) for n in (20, 50, 7)]
+    parts = [O.group_attention(qn, k, v, 0.09) for k, v in zip(ks, vs)]
+    mono_o, mono_l = O.group_attention(qn, np.concatenate(ks), np.concatenate(vs), 0.09)
+    t = lambda a: torch.tensor(a, dtype=torch.float32, device=DEV).contiguous()  # noqa: E731
+    o_f, l_f, a0, dl = K().ispa_lse_merge([t(p[0]) for p in parts], [t(p[1]) for p in parts],
+                                          torch.float32)
+    torch.cuda.synchronize()
+    assert rel(h64(o_f), mono_o) <= 1e-5
+    assert np.abs(h64(l_f) - mono_l).max() <= 1e-5 * np.abs(mono_l).max()
+    # bf16 / f16 outputs are the fp32 values rounded once
+    for dt in (torch.bfloat16, torch.float16):
+        _, _, a0h, dlh = K().ispa_lse_merge([t(p[0]) for p in parts], [t(p[1]) for p in parts], dt,
+                                            want_full=False)
+        torch.cuda.synchronize()
+        assert torch.equal(a0h.cpu(), a0.cpu().to(dt))
+        assert torch.equal(dlh.cpu(), dl.cpu().to(dt))
+    # empty parts get no weight; all-empty gives o = 0, lse = -inf
+    z = torch.zeros((n_q, H, d), device=DEV)
+    ninf = torch.full((n_q, H), -math.inf, device=DEV)
+    o2, l2, _, d2 = K().ispa_lse_merge([t(parts[0][0]), z], [t(parts[0][1]), ninf])
+    o3, l3, _, _ = K().ispa_lse_merge([z, z], [ninf, ninf])
+    torch.cuda.synchronize()
+    assert torch.allclose(o2, t(parts[0][0]), rtol=1e-6, atol=0) and torch.all(d2 == 0)
+    assert torch.all(o3 == 0) and torch.all(torch.isneginf(l3))
+
+
+# ---------------------------------------------------------------- statistics
+@pytest.mark.parametrize("dt,n,D,steps", [
+    (torch.bfloat16, 300, 256, 2),
+    (torch.float16, 777, 128, 3),
+    (torch.float16, 4680, 1536, 1),   # one Wan-1.3B warmup step
+    (torch.float32, 64, 128, 4),      # tiny fp32 workload
+])
+def test_accum_stats_parity(dt, n, D, steps):
+    print(f"accum_stats {dt} n={n} D={D} steps={steps}", flush=True)
+    G = torch.zeros((D, D), dtype=torch.float32, device=DEV)
+    C = torch.zeros_like(G)
+    r2 = torch.zeros(1, dtype=torch.float64, device=DEV)
+    w = synth.normal((D, D), 77, DEV, std=D ** -0.5, dtype=torch.bfloat16 if dt != torch.float32 else dt)
+    Gr = np.zeros((D, D)); Cr = np.zeros((D, D)); rr = 0.0
+    for s in range(steps):
+        a = synth.normal((n, D), 100 + s, DEV, std=0.3, dtype=dt)
+        dl = synth.normal((n, D), 200 + s, DEV, std=0.1, dtype=dt)
+        K().ispa_accum_stats(a, dl, w, G, C, r2)
+        g, c, r = O.accumulate_stats(a.cpu(), dl.cpu(), w.cpu())
+        Gr += g; Cr += c; rr += r
+    torch.cuda.synchronize()
+    Gg = h64(G)
+    assert rel_fro_upper(Gg, Gr) <= 1e-5
+    assert np.all(np.tril(Gg, -1) == 0)  # lower triangle untouched
+    # C: R is rounded to the operand type before A^T R (derived bar: one
+    # rounding of R, 2^-9 relative for bf16, 2^-12 for f16, averaged over n)
+    assert rel(h64(C), Cr) <= (2e-3 if dt == torch.bfloat16 else 5e-4)
+    assert abs(float(r2.item()) - rr) <= 1e-5 * rr
+
+
+# ---------------------------------------------------------------- solve
+def _stats_for_solve(D, n, seed, planted=False):
+    rng = np.random.default_rng(seed)
+    a = rng.normal(size=(n, D)) * 0.5
+    w = rng.normal(size=(D, D)) / math.sqrt(D)
+    dl = rng.normal(size=(n, D)) * 0.2 + 0.3 * a @ (rng.normal(size=(D, D)) / math.sqrt(D))
+    G, C, r2 = O.accumulate_stats(a, dl, w)
+    return G.astype(np.float32), C.astype(np.float32), r2, w
+
+
+@pytest.mark.parametrize("D,L", [(128, 3), (256, 1), (1536, 1)])
+def test_solve_parity(D, L):
+    print(f"solve_dw D={D} layers={L}", flush=True)
+    Gs, Cs, rs, ws = zip(*[_stats_for_solve(D, 3 * D, 50 + l) for l in range(L)])
+    G = torch.tensor(np.stack(Gs), device=DEV)
+    C = torch.tensor(np.stack(Cs), device=DEV)
+    r2 = torch.tensor(rs, dtype=torch.float64, device=DEV)
+    W = torch.tensor(np.stack(ws), dtype=torch.bfloat16, device=DEV)
+    dW, eps, info, w_eff = K().ispa_solve_dw(G, C, r2, 0.0, 1e-3, w=W)
+    torch.cuda.synchronize()
+    assert torch.all(info == 0)
+    for l in range(L):
+        Gl, Cl = Gs[l].astype(np.float64), Cs[l].astype(np.float64)
+        # the GPU reads the upper triangle of G: give the oracle the same matrix
+        Gsym = np.triu(Gl) + np.triu(Gl, 1).T
+        lam = O.ridge_lambda(Gsym, 0.0, 1e-3)
+        ref, rinfo = O.solve_dw(Gsym, Cl, lam)
+        assert rinfo == 0
+        assert rel(h64(dW[l]), ref) <= 1e-3
+        assert rel(h64(dW[l]), ref) <= 1e-6  # fp64 solve, fp32 output
+        e_ref = O.epsilon_from_stats(Gsym, Cl, rs[l], ref)
+        assert abs(float(eps[l]) - e_ref) <= 1e-6 * rs[l]
+        weff_ref = (W[l].float().cpu() + torch.tensor(ref, dtype=torch.float32)).to(torch.bfloat16)
+        assert (w_eff[l].cpu().float() - weff_ref.float()).abs().max() <= \
+            2 ** -7 * weff_ref.float().abs().max()
+
+
+def test_solve_non_spd_reports_pivot():
+    print("solve_dw non-SPD", flush=True)
+    D = 128
+    G = torch.eye(D, device=DEV)
+    G[70, 70] = -1.0
+    C = torch.ones((D, D), device=DEV)
+    r2 = torch.ones(1, dtype=torch.float64, device=DEV)
+    dW, eps, info, _ = K().ispa_solve_dw(G, C, r2, 0.0, 0.0)
+    torch.cuda.synchronize()
+    assert int(info[0]) == 71
+    assert torch.isnan(eps[0]) and torch.all(torch.isnan(dW))
+
+
+def test_solve_planted_and_large_lambda():
+    print("solve_dw planted", flush=True)
+    D, n = 256, 1024
+    rng = np.random.default_rng(9)
+    a = rng.normal(size=(n, D))
+    dWs = 0.05 * rng.normal(size=(D, D))
+    w = rng.normal(size=(D, D)) / math.sqrt(D)
+    delta = a @ dWs @ np.linalg.inv(w)
+    G, C, r2 = O.accumulate_stats(a, delta, w)
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device=DEV)  # noqa: E731
+    r = torch.tensor([r2], dtype=torch.float64, device=DEV)
+    dW, eps, info, _ = K().ispa_solve_dw(t(G), t(C), r, 0.0, 1e-9)
+    dWb, epsb, _, _ = K().ispa_solve_dw(t(G), t(C), r, 1e12, 0.0)
+    torch.cuda.synchronize()
+    assert rel(h64(dW), dWs) <= 1e-3  # exactly linear target: dW* recovered
+    assert float(eps[0]) <= 1e-4 * r2
+    assert float(dWb.abs().max()) < 1e-6 and abs(float(epsb[0]) - r2) <= 1e-6 * r2
+
+
+# ---------------------------------------------------------------- selection
+def test_select_parity():
+    print("select_layers", flush=True)
+    rng = np.random.default_rng(3)
+    for N, Kk in ((30, 15), (40, 20), (1, 1), (7, 0), (1024, 100)):
+        eps = rng.uniform(size=N)
+        if N > 5:
+            eps[2] = eps[5]  # a tie: lower index first
+        sel, is_local, st = K().ispa_select_layers(torch.tensor(eps, device=DEV), Kk)
+        torch.cuda.synchronize()
+        rsel, rloc, rst = O.select_layers(eps, Kk)
+        assert int(st[0]) == rst == 0
+        assert sel.cpu().numpy().tolist() == rsel.tolist()
+        assert is_local.cpu().numpy().tolist() == rloc.tolist()
+    bad = torch.tensor([0.1, float("nan"), 0.2], dtype=torch.float64, device=DEV)
+    _, _, st = K().ispa_select_layers(bad, 1)
+    torch.cuda.synchronize()
+    assert int(st[0]) == 1
+
+
+# ---------------------------------------------------------------- post-switch
+@pytest.mark.parametrize("H,d,n_q,seg_lens,y_dt", [
+    (2, 128, 300, [64, 300], torch.float32),        # L-layer: sink + current
+    (2, 128, 130, [64, 500, 700, 130], torch.bfloat16),  # F-layer, several segments
+    (4, 64, 200, [5000], torch.float32),             # long single segment (split)
+])
+def test_local_attn_proj_parity(H, d, n_q, seg_lens, y_dt):
+    print(f"local_attn_proj H={H} d={d} n_q={n_q} segs={seg_lens} {y_dt}", flush=True)
+    D = H * d
+    q = _cache(n_q, H, d, 31)
+    segs = [(_cache(n, H, d, 40 + i), _cache(n, H, d, 60 + i)) for i, n in enumerate(seg_lens)]
+    w = synth.normal((D, D), 90, DEV, std=D ** -0.5)
+    y = K().ispa_local_attn_proj(q, segs, w, d ** -0.5, out_dtype=y_dt)
+    torch.cuda.synchronize()
+    ref = O.local_attn_proj(q.cpu(), torch.cat([s[0] for s in segs]).cpu(),
+                            torch.cat([s[1] for s in segs]).cpu(), w.cpu(), d ** -0.5)
+    assert rel(h64(y), ref) <= 5e-3
+
+
+def test_local_attn_proj_f32_tiny():
+    print("local_attn_proj f32", flush=True)
+    g = synth.tiny_fp32(seed=4, device=DEV)
+    q, kc, vc = g.step(1)
+    y = K().ispa_local_attn_proj(q, [(g.sink_k, g.sink_v), (kc, vc)], g.w, 64 ** -0.5,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.local_attn_proj(q.cpu(), torch.cat([g.sink_k, kc]).cpu(), torch.cat([g.sink_v, vc]).cpu(),
+                            g.w.cpu(), 64 ** -0.5)
+    assert rel(h64(y), ref) <= 1e-5
+
+
+# ---------------------------------------------------------------- end to end
+def test_end_to_end_tiny_fp32():
+    """The tiny workload through every call in fp32 mode, against the oracle
+    run on the same seeded Q, K, V, W: 4 warmup steps, solve, selection, one
+    post-switch chunk."""
+    print("end-to-end tiny fp32", flush=True)
+    k = K()
+    g = synth.tiny_fp32(seed=1, device=DEV)
+    D = g.D
+    G = torch.zeros((D, D), device=DEV)
+    C = torch.zeros_like(G)
+    r2 = torch.zeros(1, dtype=torch.float64, device=DEV)
+    Gr = np.zeros((D, D)); Cr = np.zeros((D, D)); rr = 0.0
+    for s in range(4):
+        q, kc, vc = g.step(s)
+        o_l, l_l, o_h, l_h = k.ispa_dual_attn(q, [(g.sink_k, g.sink_v), (kc, vc)], [(g.hist_k, g.hist_v)],
+                                              64 ** -0.5)
+        _, _, a_loc, delta = k.ispa_lse_merge([o_l, o_h], [l_l, l_h], torch.float32, want_full=False)
+        k.ispa_accum_stats(a_loc, delta, g.w, G, C, r2)
+        ref = O.dual_stream_attention(q.cpu(), torch.cat([g.sink_k, kc]).cpu(), torch.cat([g.sink_v, vc]).cpu(),
+                                      g.hist_k.cpu(), g.hist_v.cpu(), 64 ** -0.5)
+        gg, cc, r = O.accumulate_stats(ref["a_loc"].reshape(64, D), ref["delta"].reshape(64, D), g.w.cpu())
+        Gr += gg; Cr += cc; rr += r
+    dW, eps, info, w_eff = k.ispa_solve_dw(G, C, r2, 0.0, 1e-3, w=g.w)
+    sel, is_local, st = k.ispa_select_layers(eps, 1)
+    torch.cuda.synchronize()
+    lam = O.ridge_lambda(Gr, 0.0, 1e-3)
+    dW_ref, _ = O.solve_dw(Gr, Cr, lam)
+    assert int(info[0]) == 0 and int(st[0]) == 0 and int(sel[0]) == 0
+    assert rel(h64(dW), dW_ref) <= 1e-3
+    e_ref = O.epsilon_from_stats(Gr, Cr, rr, dW_ref)
+    assert abs(float(eps[0]) - e_ref) <= 1e-3 * e_ref
+    q, kc, vc = g.step(4)
+    y = k.ispa_local_attn_proj(q, [(g.sink_k, g.sink_v), (kc, vc)], w_eff, 64 ** -0.5, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y_ref = O.local_attn_proj(q.cpu(), torch.cat([g.sink_k, kc]).cpu(), torch.cat([g.sink_v, vc]).cpu(),
+                              g.w.cpu().double().numpy() + dW_ref, 64 ** -0.5)
+    assert rel(h64(y), y_ref) <= 1e-4
