@@ -97,11 +97,10 @@ const char* ispa_last_error(void) { return g_last_error.c_str(); }
 // ---------------------------------------------------------------- dual_attn
 size_t ispa_dual_attn_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, const ispa_seg* loc,
                                       int32_t n_loc, const ispa_seg* hist, int32_t n_hist) {
-  (void)dt;
   if (n_q <= 0 || H < 1 || n_loc < 0 || n_hist < 0 || n_loc > ISPA_MAX_SEGS || n_hist > ISPA_MAX_SEGS)
     return 0;
   HostGroup g[2] = {{loc, n_loc}, {hist, n_hist}};
-  const SplitPlan plan = plan_splits(n_q, H, g, 2);
+  const SplitPlan plan = plan_splits(attn_block_q(dt, d), n_q, H, g, 2);
   return split_workspace_bytes(n_q, H, d, plan, 2);
 }
 
@@ -261,10 +260,9 @@ ispa_status ispa_select_layers(int32_t n_layers, int32_t K, const double* eps, i
 // ---------------------------------------------------------------- local_attn_proj
 size_t ispa_local_attn_proj_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d,
                                             const ispa_seg* segs, int32_t n_segs) {
-  (void)dt;
   if (n_q <= 0 || H < 1 || n_segs < 0 || n_segs > ISPA_MAX_SEGS) return 0;
   HostGroup g[1] = {{segs, n_segs}};
-  const SplitPlan plan = plan_splits(n_q, H, g, 1);
+  const SplitPlan plan = plan_splits(attn_block_q(dt, d), n_q, H, g, 1);
   return align256((size_t)n_q * H * d * 4) + align256((size_t)n_q * H * 4) +
          split_workspace_bytes(n_q, H, d, plan, 1);
 }

@@ -71,6 +71,19 @@ __device__ __forceinline__ bool cursor_next(const AttnParams& p, int g, int64_t 
   return cursor_seek(p, g, cur.seg + 1, kbeg, kend, cur);
 }
 
+template <int BK>
+__device__ __forceinline__ bool cursor_seek_bk(const AttnParams& p, int g, int seg, int64_t kbeg, int64_t kend,
+                                               TileCursor& cur) {
+  return cursor_seek(p, g, seg, kbeg, kend, cur);
+}
+template <int BK>
+__device__ __forceinline__ bool cursor_next_bk(const AttnParams& p, int g, int64_t kbeg, int64_t kend,
+                                               TileCursor& cur) {
+  cur.row += BK;
+  if (cur.row < cur.end) return true;
+  return cursor_seek(p, g, cur.seg + 1, kbeg, kend, cur);
+}
+
 template <int DH>
 struct BfTile {
   static constexpr int CH = DH / 8;          // 16-byte chunks per key row
@@ -303,6 +316,383 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnParams p) {
   }
 }
 
+// ---- d = 128 pipelined kernel ----------------------------------------------
+//
+// 4 waves x 64 queries (two 32-query blocks per wave, so every K or V^T
+// fragment read from LDS feeds two MFMAs); key tiles of 32.
+//   * K and V tiles go from global memory straight into LDS (buffer loads with
+//     the LDS flag, no VGPR staging), row-major with the 16-byte chunks of a
+//     row XOR-swizzled (see swz) so that both the 16-byte K fragment reads and
+//     the transposing V reads are free of bank conflicts.
+//   * The V^T fragment of O^T = V^T P^T is read with ds_read_b64_tr_b16: in each
+//     16-lane group, lane 4r + c reads 4 consecutive d of key row r and the
+//     transpose hands lane j the 4 keys at d = 4*(j/4) + j%4.  Two such reads give
+//     the 8 keys of one MFMA slot set, in the order the score accumulator holds
+//     them.
+//   * Software pipeline of one tile: in iteration j the MFMAs of P_{j-1} V_{j-1}
+//     and of K_{j+1} Q^T are issued while the softmax of tile j runs on the
+//     VALU.  Tiles are loaded three iterations ahead into a ring of five LDS
+//     buffers; one barrier per iteration.
+namespace d128 {
+constexpr int DH = 128;
+constexpr int BQ = 256;
+constexpr int BK = 32;
+constexpr int PD = 3;                  // tiles loaded ahead
+constexpr int NBUF = PD + 2;           // live: V_{j-1}, V_j, K_{j+1}, two in flight
+constexpr int ROWB = DH * 2;           // bytes per key row in LDS
+constexpr int TILEB = BK * ROWB;       // 8 KB per K (or V) tile
+constexpr int LPW = TILEB / 1024 / 4;  // 1 KB load instructions per wave per tensor per tile
+constexpr int LOADS_PER_TILE = 2 * LPW;
+}  // namespace d128
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Tile cursor of the d = 128 kernel: the current segment's K/V row pointers (head
+// applied) and byte strides are cached so a step touches kernel arguments only
+// when it crosses into the next segment.
+struct SegCursor {
+  int seg;
+  int64_t row, end;          // tile start row and one past the job's last row in this segment
+  const char* kp;            // row 0 of the segment, this head
+  const char* vp;
+  int64_t ksb, vsb;          // row strides in bytes
+};
+
+__device__ __forceinline__ bool segc_seek(const AttnParams& p, int g, int head, int seg, int64_t kbeg,
+                                          int64_t kend, SegCursor& c) {
+  int64_t st = 0;
+  for (int s = 0; s < p.n_segs[g]; ++s) {
+    const AttnSeg sg = p.segs[g][s];
+    const int64_t a = kbeg > st ? kbeg : st;
+    const int64_t b = kend < st + sg.n ? kend : st + sg.n;
+    if (s >= seg && a < b) {
+      c.seg = s;
+      c.row = a - st;
+      c.end = b - st;
+      c.ksb = sg.ks * 2;
+      c.vsb = sg.vs * 2;
+      c.kp = (const char*)sg.k + (int64_t)head * 256;
+      c.vp = (const char*)sg.v + (int64_t)head * 256;
+      return true;
+    }
+    st += sg.n;
+  }
+  return false;
+}
+
+template <int BK>
+__device__ __forceinline__ void segc_next(const AttnParams& p, int g, int head, int64_t kbeg, int64_t kend,
+                                          SegCursor& c) {
+  c.row += BK;
+  if (c.row >= c.end) segc_seek(p, g, head, c.seg + 1, kbeg, kend, c);
+}
+
+// 16-byte slot of chunk `ch` of key row `row` in an LDS tile: XOR with a
+// permutation of (row mod 16) that sends rows 0..15 to distinct values (16-byte
+// K reads of 16 consecutive rows hit 16 different slots) and rows 4a..4a+3 to
+// values differing in bits 2-3 (the transposing V reads of 4 rows x 4 chunks hit
+// 16 different slots).
+__device__ __forceinline__ int swz(int row, int ch) { return ch ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
+#define ISPA_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt with vmcnt = n (n in {0, LOADS_PER_TILE}), expcnt/lgkmcnt untouched
+  if (n == 0)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70 | d128::LOADS_PER_TILE);
+}
+
+// One 16-byte-per-lane buffer load written straight to LDS at lds_off + 16*lane.
+// Issued as a plain instruction so that the compiler does not serialise later
+// LDS reads of other ring buffers behind it; completion is awaited explicitly
+// with wait_vmcnt before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_off, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_off), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+__global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(const AttnParams p) {
+  using namespace d128;
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int lq = lane & 31;
+  const int g16 = lane >> 4;  // 16-lane group
+  const int s16 = lane & 15;
+
+  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int qtile = logical % p.n_qtiles;
+  const uint32_t rest = logical / p.n_qtiles;
+  const int head = rest % p.H;
+  const int jidx = rest / p.H;
+  const AttnJob job = p.jobs[jidx];
+  const int g = job.group;
+
+  // ---- this lane's queries (B operand of S^T = K Q^T): block qb, slice s
+  const int64_t qrow0 = (int64_t)qtile * BQ + wave * 64 + lq;
+  bf16x8 qf[2][DH / 16];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t qrow = qrow0 + qb * 32;
+    const uint16_t* qp = (const uint16_t*)p.q + qrow * p.q_stride + (int64_t)head * DH + hh * 8;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+      u32x4 v = {0, 0, 0, 0};
+      if (qrow < p.n_q) v = *(const u32x4*)(qp + s * 16);
+      qf[qb][s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // ---- tiles of this job
+  int n_tiles = 0;
+  {
+    int64_t st = 0;
+    for (int s = 0; s < p.n_segs[g]; ++s) {
+      const int64_t n = p.segs[g][s].n;
+      const int64_t a = job.kbeg > st ? job.kbeg : st;
+      const int64_t b = job.kend < st + n ? job.kend : st + n;
+      if (a < b) n_tiles += (int)((b - a + BK - 1) / BK);
+      st += n;
+    }
+  }
+
+  // load geometry: instruction i of this wave fills LDS rows (wave*LPW + i)*4 + g16,
+  // 16-byte slot s16, which holds global chunk swz(row, s16)
+  const uint32_t lds0 = lds_addr(lds);
+
+  auto issue = [&](const SegCursor& cur, int buf) {
+    const int nvalid = (int)min<int64_t>(BK, cur.end - cur.row);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(cur.kp + cur.row * cur.ksb), 0, (int)(nvalid * cur.ksb), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(cur.vp + cur.row * cur.vsb), 0, (int)(nvalid * cur.vsb), 0x00020000);
+    const uint32_t kdst = lds0 + (buf * 2 + 0) * TILEB;
+    const uint32_t vdst = lds0 + (buf * 2 + 1) * TILEB;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int lrow = (wave * LPW + i) * 4 + g16;
+      const int row = lrow < nvalid ? lrow : nvalid - 1;  // rows past the end reload a valid row
+      const int chunk = swz(lrow, s16);
+      const uint32_t dst = (wave * LPW + i) * 1024;
+      lds_dma16(rk, kdst + dst, (int)(row * cur.ksb) + chunk * 16);
+      lds_dma16(rv, vdst + dst, (int)(row * cur.vsb) + chunk * 16);
+    }
+  };
+
+  // K fragment for slice s: row lq, 16-byte chunk 2s + hh (swizzled)
+  auto k_frag = [&](const char* kb, int s) {
+    return *(const bf16x8*)(kb + lq * ROWB + swz(lq, 2 * s + hh) * 16);
+  };
+  // V^T fragment for key slice gp (16 keys), d-tile dt: two transposing reads
+  auto v_frag = [&](const char* vb, int gp, int dt) {
+    const int r = s16 >> 2, cc = s16 & 3;
+    const int colb = dt * 64 + (g16 & 1) * 32 + cc * 8;  // byte column of the 4 d values
+    const int row0 = gp * 16 + (g16 >> 1) * 4 + r;
+    const int row1 = row0 + 8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        ISPA_LDS_PTR(s16x4, vb + row0 * ROWB + (swz(row0, colb >> 4) << 4) + (colb & 15)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        ISPA_LDS_PTR(s16x4, vb + row1 * ROWB + (swz(row1, colb >> 4) << 4) + (colb & 15)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  f32x16 o[2][DH / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < DH / 32; ++i) o[qb][i] = (f32x16){};
+  float m_c[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.0f, 0.0f};
+  const float c = p.c;
+
+  // ---- prologue: issue tiles 0 .. PD-1, wait for tiles 0 and 1
+  SegCursor lcur, ccur;
+  segc_seek(p, g, head, 0, job.kbeg, job.kend, lcur);
+  ccur = lcur;
+  int issued = 0, lbuf = 0;  // tiles issued so far; ring slot of the next issue
+  for (; issued < PD && issued < n_tiles; ++issued) {
+    issue(lcur, lbuf);
+    lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
+    segc_next<BK>(p, g, head, job.kbeg, job.kend, lcur);
+  }
+  wait_vmcnt(issued > 2 ? LOADS_PER_TILE : 0);
+  __syncthreads();
+
+  f32x16 S_a[2], S_b[2];
+  bf16x8 P_a[2][2], P_b[2][2];
+  {
+    const char* kb = lds;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+      const bf16x8 a = k_frag(kb, s);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        S_a[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], s == 0 ? (f32x16){} : S_a[qb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) P_b[qb][gp] = (bf16x8){};  // P_{-1} = 0: the first PV adds nothing
+  }
+
+  // One pipeline step for tile j: O += V_{j-1}^T P_{j-1} and S_{j+1} = K_{j+1} Q^T
+  // on the matrix cores while the VALU turns S_j into P_j.
+  int cbuf = 0;  // ring slot of tile j
+  auto step = [&](int j, f32x16 (&s_in)[2], f32x16 (&s_out)[2], const bf16x8 (&p_in)[2][2],
+                  bf16x8 (&p_out)[2][2]) {
+    const int nv = (int)min<int64_t>(BK, ccur.end - ccur.row);
+    segc_next<BK>(p, g, head, job.kbeg, job.kend, ccur);
+    if (issued < n_tiles) {
+      issue(lcur, lbuf);
+      lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
+      segc_next<BK>(p, g, head, job.kbeg, job.kend, lcur);
+      ++issued;
+    }
+    const int pbuf = j == 0 ? 0 : (cbuf == 0 ? NBUF - 1 : cbuf - 1);  // tile j-1 (tile 0 when j = 0)
+    const int nbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;                  // tile j+1
+    if (nv < BK) {  // last tile of a segment: keys past its end score -inf
+      const int lim = nv - hh * 4;  // element i is a valid key iff (i/4)*8 + i%4 < lim
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s_in[qb][i] = ((i >> 2) * 8 + (i & 3) < lim) ? s_in[qb][i] : -INFINITY;
+    }
+    // (A) P_{j-1} V_{j-1} (tile 0's V with P = 0 when j = 0) + mask + row max
+    {
+      const char* vb = lds + (pbuf * 2 + 1) * TILEB;
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) {
+          const bf16x8 a = v_frag(vb, gp, dt);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p_in[qb][gp], o[qb][dt], 0, 0, 0);
+        }
+    }
+    float mxc[2];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = s_in[qb][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s_in[qb][i]);
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      mxc[qb] = mx * c;
+      need |= mxc[qb] > m_c[qb] + 8.0f;
+    }
+    // rare: raise the running maximum and rescale O and l
+    if (__any(need)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = fmaxf(m_c[qb], mxc[qb]);
+        if (m_new != -INFINITY) {
+          const float alpha = (m_c[qb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_c[qb] - m_new);
+          l_part[qb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < DH / 32; ++i) o[qb][i] *= alpha;
+          m_c[qb] = m_new;
+        }
+      }
+    }
+    // (B) S_{j+1} = K_{j+1} Q^T (discarded after the last tile) + P_j = exp2(S_j c - m)
+    {
+      const char* kb = lds + (nbuf * 2 + 0) * TILEB;
+#pragma unroll
+      for (int s = 0; s < DH / 16; ++s) {
+        const bf16x8 a = k_frag(kb, s);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s_out[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], s == 0 ? (f32x16){} : s_out[qb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m_use = (m_c[qb] == -INFINITY) ? 0.0f : m_c[qb];
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        u32x4 w;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int i = gp * 8 + 2 * m;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_in[qb][i], c, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_in[qb][i + 1], c, -m_use));
+          const uint32_t pk = pack_bf16(p0, p1);
+          l_part[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                                       __builtin_bit_cast(bf16x2, 0x3f803f80u), l_part[qb], false);
+          w[m] = pk;
+        }
+        p_out[qb][gp] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    // tile j+2 must be in LDS for the next step; newer loads may stay in flight
+    wait_vmcnt(issued > j + 3 ? LOADS_PER_TILE : 0);
+    __syncthreads();
+    cbuf = nbuf;
+  };
+
+  auto final_pv = [&](const bf16x8 (&pl)[2][2]) {
+    const char* vb = lds + (((n_tiles - 1) % NBUF) * 2 + 1) * TILEB;  // tile n-1
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) {
+        const bf16x8 a = v_frag(vb, gp, dt);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pl[qb][gp], o[qb][dt], 0, 0, 0);
+      }
+  };
+
+  int j = 0;
+  for (; j + 2 <= n_tiles; j += 2) {
+    step(j, S_a, S_b, P_b, P_a);
+    step(j + 1, S_b, S_a, P_a, P_b);
+  }
+  if (j < n_tiles) {
+    step(j, S_a, S_b, P_b, P_a);
+    final_pv(P_a);
+  } else if (n_tiles > 0) {
+    final_pv(P_b);
+  }
+
+  // ---- finalise
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[qb]), __float_as_uint(l_part[qb]), false, false);
+    const float l_tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const int64_t qrow = qrow0 + qb * 32;
+    if (qrow >= p.n_q) continue;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float* op = job.o + (qrow * p.H + head) * (int64_t)DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = dt * 32 + g4 * 8 + hh * 4;
+        f32x4 v = {o[qb][dt][g4 * 4 + 0] * inv, o[qb][dt][g4 * 4 + 1] * inv, o[qb][dt][g4 * 4 + 2] * inv,
+                   o[qb][dt][g4 * 4 + 3] * inv};
+        *(f32x4*)(op + d0) = v;
+      }
+    }
+    if (hh == 0) job.lse[qrow * p.H + head] = l_tot > 0.0f ? (m_c[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 // fp32 reference-precision path: one thread per (query, head, job).
 template <int DH>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
@@ -407,7 +797,9 @@ ispa_status launch_merge(const MergeParams& p, hipStream_t stream) {
   return check_launch("merge_kernel");
 }
 
-SplitPlan plan_splits(int64_t n_q, int32_t H, const HostGroup* groups, int n_groups) {
+int attn_block_q(ispa_dtype dt, int32_t d) { return (dt == ISPA_BF16 && d == 128) ? d128::BQ : kBQ; }
+
+SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, int n_groups) {
   SplitPlan plan;
   int64_t shortest = 0;
   int nonempty = 0;
@@ -420,7 +812,7 @@ SplitPlan plan_splits(int64_t n_q, int32_t H, const HostGroup* groups, int n_gro
       shortest = shortest == 0 ? n : std::min(shortest, n);
     }
   }
-  const int64_t qtiles = (n_q + kBQ - 1) / kBQ;
+  const int64_t qtiles = (n_q + bq - 1) / bq;
   const int64_t wgs = qtiles * H * std::max(nonempty, 1);
   // Enough workgroups already (several per CU slot): no split.
   constexpr int64_t kTargetWgs = 2048, kMinPiece = 2048;
@@ -470,7 +862,8 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
   p.q_stride = q_stride;
   p.n_q = n_q;
   p.H = H;
-  p.n_qtiles = (int)((n_q + kBQ - 1) / kBQ);
+  const int bq = attn_block_q(dt, d);
+  p.n_qtiles = (int)((n_q + bq - 1) / bq);
   p.c = scale * kLog2e;
   for (int g = 0; g < n_groups; ++g) {
     p.n_segs[g] = groups[g].n_segs;
@@ -479,7 +872,7 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
       p.segs[g][s] = AttnSeg{sg.k, sg.v, sg.n, sg.k_stride, sg.v_stride};
     }
   }
-  const SplitPlan plan = plan_splits(n_q, H, groups, n_groups);
+  const SplitPlan plan = plan_splits(bq, n_q, H, groups, n_groups);
   if (split_workspace_bytes(n_q, H, d, plan, n_groups) > ws_bytes) {
     set_error("attention workspace too small");
     return ISPA_ERR_WORKSPACE;
@@ -532,7 +925,7 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
   if (dt == ISPA_BF16) {
     const int64_t blocks = (int64_t)p.n_qtiles * H * nj;
     if (d == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {

@@ -57,8 +57,11 @@ struct SplitPlan {
   int64_t split_len[2];
 };
 
+// Queries per workgroup of the kernel that runs (dtype, head_dim).
+int attn_block_q(ispa_dtype dt, int32_t d);
+
 // Choose splits so the launch has enough equal-sized work units.
-SplitPlan plan_splits(int64_t n_q, int32_t H, const HostGroup* groups, int n_groups);
+SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, int n_groups);
 
 // Workspace bytes for the partial (o, lse) of the split groups.
 size_t split_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan& plan, int n_groups);

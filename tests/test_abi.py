@@ -78,10 +78,10 @@ def test_workspace_queries_and_errors():
     st = L.ispa_dual_attn(m.ISPA_BF16, 4680, 12, 128, 0.1, FAKE, 1536, loc, 2, hist, 1,
                           FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
     assert st == m.ISPA_ERR_WORKSPACE
-    # 14B shape: enough work units, no split
-    loc40 = _segarr(m, [_seg(4680, 40, 128, FAKE), _seg(4680, 40, 128, FAKE)])
-    hist40 = _segarr(m, [_seg(79560, 40, 128, FAKE)])
-    assert L.ispa_dual_attn_workspace_bytes(m.ISPA_BF16, 4680, 40, 128, loc40, 2, hist40, 1) == 0
+    # enough work units (many heads, short history): no split, no workspace
+    loc64 = _segarr(m, [_seg(4680, 64, 128, FAKE), _seg(4680, 64, 128, FAKE)])
+    hist64 = _segarr(m, [_seg(9360, 64, 128, FAKE)])
+    assert L.ispa_dual_attn_workspace_bytes(m.ISPA_BF16, 4680, 64, 128, loc64, 2, hist64, 1) == 0
     assert L.ispa_accum_stats_workspace_bytes(m.ISPA_F16, 4680, 1536) >= 1536 * 4680 * 2
     assert L.ispa_solve_dw_workspace_bytes(2, 128) >= 2 * 2 * 128 * 128 * 8
 
