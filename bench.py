@@ -97,6 +97,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--attn-only", type=int, default=0,
+                    help="only run this many dual-attention calls of the workload (counter runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -113,6 +117,13 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes}))
+        return
     L = B.lib()  # raises if libispa.so is missing: no fallback path exists
 
     # ---------------- inputs (resident in HBM before timing)
@@ -162,6 +173,17 @@ def main():
     ws_post_b = L.ispa_local_attn_proj_workspace_bytes(B.ISPA_BF16, n_q, H, d, post_segs, post_n)
     ws = torch.empty(max(ws_attn_b, ws_stats_b, ws_solve_b, ws_post_b, 256), dtype=torch.uint8, device=dev)
     wsp, wsn = ws.data_ptr(), ws.numel()
+    if args.attn_only:
+        q, ls, nl, hs, nh = seg_tables[0]
+        for _ in range(args.attn_only):
+            st = L.ispa_dual_attn(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
+                                  o_loc.data_ptr(), lse_loc.data_ptr(), o_hist.data_ptr(), lse_hist.data_ptr(),
+                                  wsp, wsn, sh)
+            if st:
+                raise B.IspaError(st, L.ispa_last_error().decode())
+        torch.cuda.synchronize()
+        print(json.dumps({"attn_only_calls": args.attn_only}))
+        return
     op = (ctypes.c_void_p * 2)(o_loc.data_ptr(), o_hist.data_ptr())
     lp = (ctypes.c_void_p * 2)(lse_loc.data_ptr(), lse_hist.data_ptr())
 

@@ -3,6 +3,7 @@
 // stream.
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "attn.hpp"
@@ -70,7 +71,8 @@ ispa_status check_attn_common(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, 
 size_t gemm_r_blocks(int64_t n, int32_t D) {
   return (size_t)((n + kGemmBM - 1) / kGemmBM) * (size_t)((D + kGemmBN - 1) / kGemmBN);
 }
-int64_t rt_ld(int64_t n) { return (n + 7) / 8 * 8; }
+// workgroups the statistics launch aims for (several per CU)
+constexpr int64_t kStatsTargetWgs = 1024;
 
 }  // namespace
 }  // namespace ispa
@@ -160,7 +162,7 @@ ispa_status ispa_lse_merge(int32_t n_parts, const float* const* o_parts, const f
 size_t ispa_accum_stats_workspace_bytes(ispa_dtype a_dt, int64_t n, int32_t D) {
   if (n <= 0 || D <= 0) return 0;
   if (a_dt == ISPA_F32) return align256((size_t)n * D * 4) + align256(64 * 8);
-  return align256((size_t)D * rt_ld(n) * 2) + align256(gemm_r_blocks(n, D) * 8);
+  return align256((size_t)n * D * 2) + align256(gemm_r_blocks(n, D) * 8);
 }
 
 ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_t D, const void* a_loc,
@@ -183,10 +185,9 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   if (a_dt == ISPA_F32)
     return launch_stats_f32(n, D, (const float*)a_loc, (const float*)delta_a, (const float*)w, G, C, r2, ws,
                             stream);
-  const int64_t ldr = rt_ld(n);
-  uint16_t* Rt = (uint16_t*)ws;
-  double* partials = (double*)((char*)ws + align256((size_t)D * ldr * 2));
-  // R = delta W  (stored transposed, 16-bit) and per-workgroup ||R||^2
+  uint16_t* R = (uint16_t*)ws;
+  double* partials = (double*)((char*)ws + align256((size_t)n * D * 2));
+  // R = delta W  (stored row-major in the operand type) and per-workgroup ||R||^2
   GemmParams r{};
   r.M = n;
   r.N = D;
@@ -194,33 +195,39 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   r.x = GemmOperand{delta_a, D, a_dt, kDirect};
   r.y = GemmOperand{w, D, w_dt, kTrans};
   r.epi = kStoreRt;
-  r.out = Rt;
-  r.ld_out = ldr;
+  r.out = R;
+  r.ld_out = D;
   r.tiles_m = (int)((n + kGemmBM - 1) / kGemmBM);
   r.tiles_n = (int)((D + kGemmBN - 1) / kGemmBN);
+  r.ksplit = 1;
+  r.kchunk = (D + kGemmBK - 1) / kGemmBK * kGemmBK;
   r.sq_partials = partials;
   int nblk = 0;
   ispa_status st = launch_gemm(r, a_dt, stream, &nblk);
   if (st) return st;
   if ((st = launch_reduce_add(partials, nblk, r2, stream))) return st;
-  // G += A^T A (upper triangle), then C += A^T R
+  // one launch: G += A^T A (upper-triangle tiles) and C += A^T R (all tiles), K split so
+  // that the launch has several workgroups per CU; split partials are added atomically
   GemmParams g{};
   g.M = D;
   g.N = D;
   g.K = n;
   g.x = GemmOperand{a_loc, D, a_dt, kTrans};
   g.y = GemmOperand{a_loc, D, a_dt, kTrans};
+  g.y2 = GemmOperand{R, D, a_dt, kTrans};
   g.epi = kAccum;
   g.out = G;
+  g.out2 = C;
   g.ld_out = D;
   g.tiles_m = g.tiles_n = (int)((D + kGemmBM - 1) / kGemmBM);
   g.tri = 1;
-  if ((st = launch_gemm(g, a_dt, stream, nullptr))) return st;
-  GemmParams c = g;
-  c.y = GemmOperand{Rt, ldr, a_dt, kDirect};
-  c.out = C;
-  c.tri = 0;
-  return launch_gemm(c, a_dt, stream, nullptr);
+  g.two_kinds = 1;
+  const int64_t tiles = (int64_t)g.tiles_m * (g.tiles_m + 1) / 2 + (int64_t)g.tiles_m * g.tiles_n;
+  const int64_t stages = (n + kGemmBK - 1) / kGemmBK;
+  int64_t split = std::max<int64_t>(1, std::min<int64_t>((kStatsTargetWgs + tiles - 1) / tiles, stages / 8));
+  g.kchunk = (stages + split - 1) / split * kGemmBK;
+  g.ksplit = (int)((n + g.kchunk - 1) / g.kchunk);
+  return launch_gemm(g, a_dt, stream, nullptr);
 }
 
 // ---------------------------------------------------------------- solve_dw
@@ -308,6 +315,8 @@ ispa_status ispa_local_attn_proj(ispa_dtype dt, int64_t n_q, int32_t H, int32_t 
   p.ld_out = D;
   p.tiles_m = (int)((n_q + kGemmBM - 1) / kGemmBM);
   p.tiles_n = (int)((D + kGemmBN - 1) / kGemmBN);
+  p.ksplit = 1;
+  p.kchunk = (D + kGemmBK - 1) / kGemmBK * kGemmBK;
   return launch_gemm(p, ISPA_BF16, stream, nullptr);
 }
 

@@ -168,24 +168,34 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmParams p) {
   const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, lq = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- which tile
-  uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  // ---- which tile and which K range: blocks are (split, tile) with the tile
+  // fastest, so the workgroups sharing an XCD work on neighbouring tiles
+  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t n_kind0 = p.tri ? (uint32_t)(p.tiles_m * (p.tiles_m + 1) / 2) : (uint32_t)(p.tiles_m * p.tiles_n);
+  const uint32_t n_tiles = n_kind0 + (p.two_kinds ? (uint32_t)(p.tiles_m * p.tiles_n) : 0u);
+  const uint32_t split = bid / n_tiles;
+  uint32_t t = bid - split * n_tiles;
+  const bool kind1 = t >= n_kind0;
+  if (kind1) t -= n_kind0;
   int tm, tn;
-  if (p.tri) {
+  if (p.tri && !kind1) {
     // upper-triangle tiles (tm <= tn), row by row
     tm = 0;
-    uint32_t rem = bid;
-    while (rem >= (uint32_t)(p.tiles_n - tm)) {
-      rem -= p.tiles_n - tm;
+    while (t >= (uint32_t)(p.tiles_n - tm)) {
+      t -= p.tiles_n - tm;
       ++tm;
     }
-    tn = tm + (int)rem;
+    tn = tm + (int)t;
   } else {
-    tm = bid / p.tiles_n;
-    tn = bid % p.tiles_n;
+    tm = t / p.tiles_n;
+    tn = t % p.tiles_n;
   }
+  const void* yp = kind1 ? p.y2.p : p.y.p;
+  const int64_t yld = kind1 ? p.y2.ld : p.y.ld;
   const int64_t m0 = (int64_t)tm * kGemmBM, n0 = (int64_t)tn * kGemmBN;
-  const int nk = (int)((p.K + kGemmBK - 1) / kGemmBK);
+  const int64_t kb = (int64_t)split * p.kchunk;
+  const int64_t ke = min(p.K, kb + p.kchunk);
+  const int nk = ke > kb ? (int)((ke - kb + kGemmBK - 1) / kGemmBK) : 0;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -196,8 +206,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmParams p) {
   StageRegs<XL, XF32> xr;
   StageRegs<YL, false> yr;
   if (nk > 0) {
-    load_stage(p.x.p, p.x.ld, p.M, p.K, m0, 0, tid, xr);
-    load_stage(p.y.p, p.y.ld, p.N, p.K, n0, 0, tid, yr);
+    load_stage(p.x.p, p.x.ld, p.M, ke, m0, kb, tid, xr);
+    load_stage(yp, yld, p.N, ke, n0, kb, tid, yr);
     store_stage<MT>(p.x.dt, tid, xr, Xs[0]);
     store_stage<MT>(p.y.dt, tid, yr, Ys[0]);
   }
@@ -206,8 +216,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmParams p) {
   for (int kt = 0; kt < nk; ++kt) {
     const bool next = kt + 1 < nk;
     if (next) {
-      load_stage(p.x.p, p.x.ld, p.M, p.K, m0, (int64_t)(kt + 1) * kGemmBK, tid, xr);
-      load_stage(p.y.p, p.y.ld, p.N, p.K, n0, (int64_t)(kt + 1) * kGemmBK, tid, yr);
+      load_stage(p.x.p, p.x.ld, p.M, ke, m0, kb + (int64_t)(kt + 1) * kGemmBK, tid, xr);
+      load_stage(yp, yld, p.N, ke, n0, kb + (int64_t)(kt + 1) * kGemmBK, tid, yr);
     }
     const uint16_t* xs = Xs[buf];
     const uint16_t* ys = Ys[buf];
@@ -235,37 +245,25 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmParams p) {
 
   // ---- epilogue
   if (p.epi == kStoreRt) {
+    // R row-major as 16-bit (mfma type), plus this workgroup's sum of squares
     double ss = 0.0;
-    float ssf = 0.0f;
     uint16_t* out = (uint16_t*)p.out;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t n = n0 + wn * 64 + j * 32 + lq;
+        float ssf = 0.0f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t mb = m0 + wm * 64 + i * 32 + g * 8 + hh * 4;
-          const float v0 = acc[i][j][g * 4 + 0], v1 = acc[i][j][g * 4 + 1];
-          const float v2 = acc[i][j][g * 4 + 2], v3 = acc[i][j][g * 4 + 3];
-          if (n < p.N) {
-            if (mb + 3 < p.M) {
-              *(u32x2*)(out + n * p.ld_out + mb) = (u32x2){to_pair<MT>(v0, v1), to_pair<MT>(v2, v3)};
-              ssf += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
-            } else {
-              const float vv[4] = {v0, v1, v2, v3};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (mb + e < p.M) {
-                  out[n * p.ld_out + mb + e] = (uint16_t)(to_pair<MT>(vv[e], 0.0f) & 0xffffu);
-                  ssf += vv[e] * vv[e];
-                }
-              }
-            }
+        for (int e = 0; e < 16; ++e) {
+          const int64_t m = m0 + wm * 64 + i * 32 + (e >> 2) * 8 + hh * 4 + (e & 3);
+          if (m < p.M && n < p.N) {
+            const float v = acc[i][j][e];
+            out[m * p.ld_out + n] = (uint16_t)(to_pair<MT>(v, 0.0f) & 0xffffu);
+            ssf += v * v;
           }
         }
         ss += (double)ssf;
-        ssf = 0.0f;
       }
     }
     // workgroup sum of squares
@@ -277,8 +275,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmParams p) {
     return;
   }
 
-  float* outf = (float*)p.out;
-  const bool tri_tile = p.tri;
+  float* outf = (float*)(kind1 ? p.out2 : p.out);
+  const bool tri_tile = p.tri && !kind1;
+  const bool atomic = p.ksplit > 1;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -290,7 +289,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmParams p) {
         if (m >= p.M || n >= p.N) continue;
         if (p.epi == kAccum) {
           if (tri_tile && m > n) continue;
-          outf[m * p.ld_out + n] += acc[i][j][e];
+          if (atomic)
+            unsafeAtomicAdd(outf + m * p.ld_out + n, acc[i][j][e]);
+          else
+            outf[m * p.ld_out + n] += acc[i][j][e];
         } else {
           store_from_f32(p.out, m * p.ld_out + n, acc[i][j][e], p.out_dt);
         }
@@ -364,8 +366,13 @@ __global__ void reduce_add_kernel(const double* partials, int64_t n, double* r2)
 }  // namespace
 
 ispa_status launch_gemm(const GemmParams& p, int mfma_dt, hipStream_t stream, int* n_blocks_out) {
-  const int64_t blocks = p.tri ? (int64_t)p.tiles_m * (p.tiles_m + 1) / 2 : (int64_t)p.tiles_m * p.tiles_n;
+  const int64_t n0 = p.tri ? (int64_t)p.tiles_m * (p.tiles_m + 1) / 2 : (int64_t)p.tiles_m * p.tiles_n;
+  const int64_t blocks = (n0 + (p.two_kinds ? (int64_t)p.tiles_m * p.tiles_n : 0)) * p.ksplit;
   if (n_blocks_out) *n_blocks_out = (int)blocks;
+  if (p.ksplit < 1 || p.kchunk % kGemmBK || (int64_t)p.ksplit * p.kchunk < p.K) {
+    set_error("gemm: bad K split");
+    return ISPA_ERR_INVALID_ARG;
+  }
   if (blocks == 0) return ISPA_OK;
   const bool xf32 = p.x.dt == ISPA_F32;
   if (p.x.layout == kTrans && (xf32 || p.y.dt == ISPA_F32)) {

@@ -12,8 +12,8 @@ enum { kDirect = 0, kTrans = 1 };
 
 // Epilogues.
 enum {
-  kStoreRt = 0,     // write acc^T as 16-bit (mfma type) to out[n][m] (ld_out) + sum of squares
-  kAccum = 1,       // out[m][n] += acc (fp32, ld_out); upper triangle only if tri
+  kStoreRt = 0,     // write acc as 16-bit (mfma type) to out[m][n] (ld_out) + sum of squares
+  kAccum = 1,       // out[m][n] += acc (fp32, ld_out; atomic when K is split); upper triangle only if tri
   kStore = 2        // out[m][n] = acc as out_dt (fp32 / bf16 / f16)
 };
 
@@ -28,12 +28,17 @@ struct GemmParams {
   int64_t M, N, K;
   GemmOperand x;   // rows = m
   GemmOperand y;   // rows = n
+  GemmOperand y2;  // rows = n of the second kind of tiles (same layout and type as y)
   int32_t epi;
   int32_t out_dt;
   void* out;
+  void* out2;      // output of the second kind of tiles
   int64_t ld_out;
   int32_t tiles_m, tiles_n;
-  int32_t tri;     // only the upper-triangle tiles (tm <= tn) and entries m <= n
+  int32_t tri;     // first-kind tiles: upper triangle only (tm <= tn) and entries m <= n
+  int32_t two_kinds;  // a full tiles_m x tiles_n grid of second-kind tiles follows
+  int32_t ksplit;  // K split into ksplit ranges of kchunk (multiple of kGemmBK)
+  int64_t kchunk;
   double* sq_partials;  // per-workgroup sum of squares (kStoreRt)
 };
 
