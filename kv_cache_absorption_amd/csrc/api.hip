@@ -8,6 +8,7 @@
 
 #include "attn.hpp"
 #include "gemm.hpp"
+#include "gram.hpp"
 #include "internal.hpp"
 
 namespace ispa {
@@ -68,11 +69,6 @@ ispa_status check_attn_common(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, 
   return ISPA_OK;
 }
 
-size_t gemm_r_blocks(int64_t n, int32_t D) {
-  return (size_t)((n + kGemmBM - 1) / kGemmBM) * (size_t)((D + kGemmBN - 1) / kGemmBN);
-}
-// workgroups the statistics launch aims for (several per CU)
-constexpr int64_t kStatsTargetWgs = 1024;
 
 }  // namespace
 }  // namespace ispa
@@ -162,7 +158,9 @@ ispa_status ispa_lse_merge(int32_t n_parts, const float* const* o_parts, const f
 size_t ispa_accum_stats_workspace_bytes(ispa_dtype a_dt, int64_t n, int32_t D) {
   if (n <= 0 || D <= 0) return 0;
   if (a_dt == ISPA_F32) return align256((size_t)n * D * 4) + align256(64 * 8);
-  return align256((size_t)n * D * 2) + align256(gemm_r_blocks(n, D) * 8);
+  const int64_t np = (n + kNtBK - 1) / kNtBK * kNtBK;
+  const size_t rblocks = (size_t)((D + kNtBM - 1) / kNtBM) * (size_t)((np + kNtBN - 1) / kNtBN);
+  return 2 * align256((size_t)D * D * 2) + 2 * align256((size_t)D * np * 2) + align256(rblocks * 8);
 }
 
 ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_t D, const void* a_loc,
@@ -176,7 +174,7 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   if (!G || !C || !r2 || !w) return fail(ISPA_ERR_INVALID_ARG, "null G/C/r2/w");
   if (n > 0 && (!a_loc || !delta_a)) return fail(ISPA_ERR_INVALID_ARG, "null activations");
   const size_t al = a_dt == ISPA_F32 ? 4 : 16;
-  if (!aligned(a_loc, al) || !aligned(delta_a, al) || !aligned(w, 4))
+  if (!aligned(a_loc, al) || !aligned(delta_a, al) || !aligned(w, a_dt == ISPA_F32 ? 4 : 8))
     return fail(ISPA_ERR_INVALID_ARG, "misaligned activations or W");
   if (n == 0) return ISPA_OK;
   const size_t need = ispa_accum_stats_workspace_bytes(a_dt, n, D);
@@ -185,49 +183,74 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   if (a_dt == ISPA_F32)
     return launch_stats_f32(n, D, (const float*)a_loc, (const float*)delta_a, (const float*)w, G, C, r2, ws,
                             stream);
-  uint16_t* R = (uint16_t*)ws;
-  double* partials = (double*)((char*)ws + align256((size_t)n * D * 2));
-  // R = delta W  (stored row-major in the operand type) and per-workgroup ||R||^2
-  GemmParams r{};
-  r.M = n;
-  r.N = D;
+  // Workspace: W^T and (if W's type differs) W converted, A_loc^T and R^T with the
+  // token dimension zero-padded to a multiple of the GEMM's K stage, per-workgroup ||R||^2.
+  const int64_t np = (n + kNtBK - 1) / kNtBK * kNtBK;
+  char* wp = (char*)ws;
+  uint16_t* Wt = (uint16_t*)wp;
+  wp += align256((size_t)D * D * 2);
+  uint16_t* Wc = (uint16_t*)wp;
+  wp += align256((size_t)D * D * 2);
+  uint16_t* At = (uint16_t*)wp;
+  wp += align256((size_t)D * np * 2);
+  uint16_t* Rt = (uint16_t*)wp;
+  wp += align256((size_t)D * np * 2);
+  double* partials = (double*)wp;
+  ispa_status st;
+  const void* wsrc = w;
+  if (w_dt != a_dt) {
+    if ((st = launch_convert16(w, (int64_t)D * D, w_dt, Wc, a_dt, stream))) return st;
+    wsrc = Wc;
+  }
+  if ((st = launch_transpose16(wsrc, D, D, D, Wt, D, D, stream))) return st;
+  if ((st = launch_transpose16(a_loc, D, n, D, At, np, np, stream))) return st;
+  // R^T = W^T dA^T, stored with zero padding, and per-workgroup ||R||^2
+  NtGemmParams r{};
+  r.M = D;
+  r.N = np;
   r.K = D;
-  r.x = GemmOperand{delta_a, D, a_dt, kDirect};
-  r.y = GemmOperand{w, D, w_dt, kTrans};
-  r.epi = kStoreRt;
-  r.out = R;
-  r.ld_out = D;
-  r.tiles_m = (int)((n + kGemmBM - 1) / kGemmBM);
-  r.tiles_n = (int)((D + kGemmBN - 1) / kGemmBN);
+  r.x = Wt;
+  r.ldx = D;
+  r.y = delta_a;
+  r.ldy = D;
+  r.y_rows = n;
+  r.epi = kNtStoreT;
+  r.out = Rt;
+  r.ld_out = np;
+  r.n_valid = n;
+  r.tiles_m = (D + kNtBM - 1) / kNtBM;
+  r.tiles_n = (int)((np + kNtBN - 1) / kNtBN);
   r.ksplit = 1;
-  r.kchunk = (D + kGemmBK - 1) / kGemmBK * kGemmBK;
+  r.kchunk = D;
   r.sq_partials = partials;
   int nblk = 0;
-  ispa_status st = launch_gemm(r, a_dt, stream, &nblk);
-  if (st) return st;
+  if ((st = launch_nt_gemm(r, a_dt, stream, &nblk))) return st;
   if ((st = launch_reduce_add(partials, nblk, r2, stream))) return st;
-  // one launch: G += A^T A (upper-triangle tiles) and C += A^T R (all tiles), K split so
-  // that the launch has several workgroups per CU; split partials are added atomically
-  GemmParams g{};
+  // G += A^T A (upper-triangle tiles) and C += A^T R (all tiles) in one launch
+  NtGemmParams g{};
   g.M = D;
   g.N = D;
-  g.K = n;
-  g.x = GemmOperand{a_loc, D, a_dt, kTrans};
-  g.y = GemmOperand{a_loc, D, a_dt, kTrans};
-  g.y2 = GemmOperand{R, D, a_dt, kTrans};
-  g.epi = kAccum;
+  g.K = np;
+  g.x = At;
+  g.ldx = np;
+  g.y = At;
+  g.y2 = Rt;
+  g.ldy = np;
+  g.y_rows = D;
+  g.epi = kNtAccum;
   g.out = G;
   g.out2 = C;
   g.ld_out = D;
-  g.tiles_m = g.tiles_n = (int)((D + kGemmBM - 1) / kGemmBM);
+  g.tiles_m = g.tiles_n = (D + kNtBM - 1) / kNtBM;
   g.tri = 1;
   g.two_kinds = 1;
+  // split the token range when there are fewer tiles than two per CU slot pair
   const int64_t tiles = (int64_t)g.tiles_m * (g.tiles_m + 1) / 2 + (int64_t)g.tiles_m * g.tiles_n;
-  const int64_t stages = (n + kGemmBK - 1) / kGemmBK;
-  int64_t split = std::max<int64_t>(1, std::min<int64_t>((kStatsTargetWgs + tiles - 1) / tiles, stages / 8));
-  g.kchunk = (stages + split - 1) / split * kGemmBK;
-  g.ksplit = (int)((n + g.kchunk - 1) / g.kchunk);
-  return launch_gemm(g, a_dt, stream, nullptr);
+  const int64_t stages = np / kNtBK;
+  const int64_t split = std::max<int64_t>(1, std::min<int64_t>((512 + tiles - 1) / tiles, stages / 8));
+  g.kchunk = (stages + split - 1) / split * kNtBK;
+  g.ksplit = (int)((np + g.kchunk - 1) / g.kchunk);
+  return launch_nt_gemm(g, a_dt, stream, nullptr);
 }
 
 // ---------------------------------------------------------------- solve_dw

@@ -1,0 +1,41 @@
+// K-contiguous ("NT") MFMA GEMM for the statistics, and 16-bit layout helpers.
+#pragma once
+
+#include "common.hpp"
+
+namespace ispa {
+
+enum {
+  kNtAccum = 0,   // out[m][n] += acc (fp32); atomic when K is split; upper triangle for first-kind tiles if tri
+  kNtStoreT = 1   // out[m][n] = acc as 16-bit (mfma type) for n < n_valid, 0 for n_valid <= n < N;
+                  // per-workgroup sum of squares of the stored values
+};
+
+struct NtGemmParams {
+  int64_t M, N, K;   // acc[m][n] = sum_k X[m][k] Y[n][k]; K a multiple of kNtBK
+  const void* x;     // [M][ldx] 16-bit, k contiguous
+  const void* y;     // [y_rows][ldy]
+  const void* y2;    // second-kind tiles' y operand (same ldy)
+  int64_t ldx, ldy;  // elements, multiples of 8
+  int64_t y_rows;    // rows of y that exist (rows past it are not read)
+  int32_t epi;
+  void* out;
+  void* out2;        // second-kind tiles' output
+  int64_t ld_out;
+  int64_t n_valid;   // kNtStoreT: columns at or past n_valid are written as 0
+  int32_t tiles_m, tiles_n;
+  int32_t tri, two_kinds;
+  int32_t ksplit;
+  int64_t kchunk;
+  double* sq_partials;
+};
+
+ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t stream, int* n_blocks_out);
+// out[c][r] = in[r][c] (r < rows), 0 for rows <= r < rows_pad; rows_pad multiple of 4, cols of 4
+ispa_status launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,
+                               int64_t ld_out, int64_t rows_pad, hipStream_t stream);
+ispa_status launch_convert16(const void* in, int64_t n, int in_dt, void* out, int out_dt, hipStream_t stream);
+
+constexpr int kNtBM = 128, kNtBN = 128, kNtBK = 32;
+
+}  // namespace ispa
