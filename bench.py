@@ -13,6 +13,18 @@ All inputs are generated on the GPU before the timed region.  Prints one JSON
 line; the headline value is dual-stream attention + LSE merge TFLOP/s (QK^T
 and PV flops, 4 n_q n_k D per chunk, over the time of the two calls), with
 Gram-statistics TFLOP/s and ms per warmup chunk beside it.
+
+Other workloads (``--workload``), each one pass of a chunked stream through
+IspaStream, timed per chunk with HIP events around the ISPA calls of all
+layers (the chunk's Q, K, V are generated on the GPU before its events):
+
+  wan13b_stream  30 layers x 12 heads x 128, 20 chunks of 4680 tokens:
+                 warmup chunks 0-5, switch (K = 15), post-switch chunks 6-19
+  wan14b_warmup  40 layers x 40 heads x 128, warmup chunks 0-18 (history up
+                 to 79560 keys), switch with 40 ridge solves at D = 5120, K = 20
+  wan14b_post    40 post-switch chunks of the same 40 layers (20 L-Layers on
+                 sink + current, 20 F-Layers on up to 187200 keys), with the
+                 selection and W + dW of an untimed wan14b_warmup pass
 """
 from __future__ import annotations
 
@@ -90,18 +102,194 @@ def cpu_baseline(g, q, kc, vc, rows_target_s=15.0):
             "seconds": t_tot}
 
 
+STREAMS = {
+    # name: layers, heads, head_dim, chunks in the pass, warmup chunks, K, workload id
+    "wan13b_stream": dict(N=30, H=12, d=128, chunks=20, warm=6, K=15, wid=3),
+    "wan14b_warmup": dict(N=40, H=40, d=128, chunks=19, warm=19, K=20, wid=4),
+    "wan14b_post": dict(N=40, H=40, d=128, chunks=40, warm=0, K=20, wid=5),
+}
+TOKENS_PER_CHUNK = 4680  # 3 latent frames of 1560 tokens
+
+
+def _stream_pass(spec, dev, seed, adopt=None, timed=True):
+    """One pass of a chunked stream.  Returns per-chunk records and the stream.
+
+    ``adopt`` = (is_local, W, W + dW) starts the stream after a switch made by
+    another pass (post-switch-only workload)."""
+    import torch
+    import synth
+    from kv_cache_absorption_amd.stream import IspaStream
+
+    N, H, d, T = spec["N"], spec["H"], spec["d"], TOKENS_PER_CHUNK
+    D = H * d
+    si = synth.StreamInputs(N, H, d, T, torch.bfloat16, seed, dev, workload=spec["wid"])
+    if adopt is None:
+        st = IspaStream(N, H, d, T, spec["chunks"], dev)
+        for layer in range(N):
+            st.set_w(layer, si.w(layer))
+    else:
+        is_local, W, w_eff = adopt
+        caps = [2 if f else spec["chunks"] for f in is_local]
+        st = IspaStream(N, H, d, T, caps, dev, with_stats=False)
+        st.W = W
+        st.adopt_switch(is_local, w_eff)
+    stream = torch.cuda.current_stream(dev)
+    qbuf = torch.empty((N, T, H, d), dtype=torch.bfloat16, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    recs = []
+    switch_ev = None
+    for c in range(spec["chunks"]):
+        if c == spec["warm"] and adopt is None:
+            s0, s1 = ev(), ev()
+            s0.record(stream)
+            st.switch(spec["K"])
+            s1.record(stream)
+            switch_ev = (s0, s1)
+        for layer in range(N):
+            k, v = si.kv(layer, c)
+            st.write_kv(layer, c, k, v)
+            qbuf[layer].copy_(si.q(layer, c))
+            del k, v
+        warm = c < spec["warm"]
+        marks = []
+        e_start = ev()
+        e_start.record(stream)
+        for layer in range(N):
+            if warm:
+                st.warmup(layer, c, qbuf[layer])
+            else:
+                st.post(layer, c, qbuf[layer])
+            e = ev()
+            e.record(stream)
+            marks.append(e)
+        # keys each layer's call attends to: local + history during warmup
+        n_keys = [(c + 1) * T] * N if warm else st.keys_held(c)
+        recs.append(dict(c=c, warm=warm, start=e_start, marks=marks, n_keys=n_keys,
+                         kv_held=st.kv_bytes_held(c), kv_alloc=st.kv_bytes_allocated()))
+    if spec["warm"] == spec["chunks"] and adopt is None:  # warmup-only pass ends in the switch
+        s0, s1 = ev(), ev()
+        s0.record(stream)
+        st.switch(spec["K"], evict=False)
+        s1.record(stream)
+        switch_ev = (s0, s1)
+    torch.cuda.synchronize()
+    for r in recs:
+        t, prev = [], r["start"]
+        for e in r["marks"]:
+            t.append(prev.elapsed_time(e))
+            prev = e
+        r["layer_ms"] = t
+        r["ms"] = sum(t)
+        del r["start"], r["marks"]
+    switch_ms = switch_ev[0].elapsed_time(switch_ev[1]) if switch_ev else None
+    return recs, switch_ms, st
+
+
+def run_stream(args, name, dev):
+    import torch
+    spec = STREAMS[name]
+    N, H, d, T = spec["N"], spec["H"], spec["d"], TOKENS_PER_CHUNK
+    D = H * d
+    adopt = None
+    pre = {}
+    if name == "wan14b_post":
+        t0 = time.perf_counter()
+        _, pre_switch_ms, st4 = _stream_pass(STREAMS["wan14b_warmup"], dev, args.seed)
+        adopt = (list(st4.is_local_host), st4.W, st4.w_eff)
+        pre = {"switch_source": "untimed wan14b_warmup pass (same seed)",
+               "switch_ms": round(pre_switch_ms, 3), "setup_s": round(time.perf_counter() - t0, 1)}
+        st4.kv = []
+        st4.G = st4.C = st4.dW = None
+        torch.cuda.empty_cache()
+    for _ in range(args.warmup):
+        _stream_pass(spec, dev, args.seed, adopt)
+        torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    passes = []
+    for _ in range(args.steps):
+        passes.append(_stream_pass(spec, dev, args.seed, adopt))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recs, switch_ms, st = passes[-1]
+    all_recs = [r for p in passes for r in p[0]]
+    chunk_ms = [r["ms"] for r in all_recs]
+    mean = lambda xs: sum(xs) / len(xs) if xs else None  # noqa: E731
+    warm_ms = [r["ms"] for r in all_recs if r["warm"]]
+    post_ms = [r["ms"] for r in all_recs if not r["warm"]]
+    # attention flops of every call in the pass (QK^T and PV only)
+    attn_flops, proj_flops, stats_flops = 0.0, 0.0, 0.0
+    for r in recs:
+        for nk in r["n_keys"]:
+            attn_flops += 4.0 * T * nk * D
+        if r["warm"]:
+            stats_flops += N * (5.0 * T * D * D + 3.0 * T * D)
+        else:
+            proj_flops += N * 2.0 * T * D * D
+    pass_ms = sum(r["ms"] for r in recs)
+    last = recs[-1]
+    c_last = last["c"]
+    full_bytes = 2 * N * (c_last + 1) * T * D * 2
+    value = mean(chunk_ms)
+    achieved = (attn_flops + proj_flops + stats_flops) / (pass_ms * 1e-3) / 1e12
+    out = {
+        "metric": "ms/chunk (1 GPU)",
+        "value": round(value, 3),
+        "unit": "ms/chunk",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "layers": N, "heads": H, "head_dim": d, "tokens_per_chunk": T,
+                   "chunks": spec["chunks"], "warmup_chunks": spec["warm"], "K": spec["K"],
+                   "stats_operands": "fp16", "seed": args.seed,
+                   "timing": "HIP events around each chunk's ISPA calls of all layers; the chunk's "
+                             "synthetic Q/K/V generation sits outside them (ms_per_step is the wall "
+                             "time of the whole pass including that generation)"},
+        "also": {
+            "warmup ms/chunk (mean)": round(mean(warm_ms), 3) if warm_ms else None,
+            "post-switch ms/chunk (mean)": round(mean(post_ms), 3) if post_ms else None,
+            "last chunk ms": round(last["ms"], 3),
+            "switch ms (solve all layers + select)": round(switch_ms, 3) if switch_ms else None,
+            "pass TFLOP/s (attention + statistics + projection flops / ISPA time)": round(achieved, 2),
+            "kv_bytes_held_last_chunk": last["kv_held"],
+            "kv_bytes_all_full_last_chunk": full_bytes,
+            "kv_held_fraction": round(last["kv_held"] / full_bytes, 4),
+            "kv_bytes_allocated_last_chunk": last["kv_alloc"],
+            "L-Layers": [i for i, f in enumerate(st.is_local_host or []) if f],
+            **pre,
+        },
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "all ISPA calls of the pass (attention dominates)"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="default 3 (1 for stream workloads)")
+    ap.add_argument("--warmup", type=int, default=None, help="default 1 (0 for stream workloads)")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--workload", default="wan13b_layer", choices=["wan13b_layer"] + sorted(STREAMS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only run this many dual-attention calls of the workload (counter runs)")
     args = ap.parse_args()
+    is_stream = args.workload != "wan13b_layer"
+    if args.steps is None:
+        args.steps = 1 if is_stream else 3
+    if args.warmup is None:
+        args.warmup = 0 if is_stream else 1
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         _fail_multi(max(args.gpus, world))
@@ -125,6 +313,9 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes}))
         return
     L = B.lib()  # raises if libispa.so is missing: no fallback path exists
+    if args.workload != "wan13b_layer":
+        run_stream(args, args.workload, dev)
+        return
 
     # ---------------- inputs (resident in HBM before timing)
     g = synth.wan13b_single_layer(seed=args.seed, device=dev)

@@ -1,16 +1,25 @@
-"""Host-side layout of a chunked stream: key groups and KV accounting.
+"""Host-side layout and driver of a chunked stream: key groups, KV caches,
+the warmup -> switch -> post-switch sequence, and KV accounting.
 
-A layer's keys and values live in one caller-owned cache of token rows
-[max_tokens, H, d]; chunk c occupies rows [c*T, (c+1)*T).  Chunk 0 holds the
-sink.  At chunk step c >= 1 the local group is {sink, chunk c} and the
-history group is chunks 1 .. c-1 (EN review, Key Design 1: local = initial
-sink frame(s) + current frame(s), history = the frames in between); at c = 0
-the local group is chunk 0 alone.  After the switch an L-Layer keeps only its
-sink and current rows, an F-Layer keeps everything (EN review, Key Design 3).
+A layer's keys and values live in one device cache of token rows
+[capacity, H, d]; while the layer keeps its full history, chunk c occupies
+rows [c*T, (c+1)*T).  Chunk 0 holds the sink.  At chunk step c >= 1 the local
+group is {sink, chunk c} and the history group is chunks 1 .. c-1 (EN review,
+Key Design 1: local = initial sink frame(s) + current frame(s), history = the
+frames in between); at c = 0 the local group is chunk 0 alone.  After the
+switch an L-Layer keeps only its sink and current rows, an F-Layer keeps
+everything (EN review, Key Design 3).
+
+Every arithmetic step runs in libispa; this module only decides which call
+gets which rows, allocates caches and buffers with torch, and counts bytes.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
+
+from . import _lib as B
 
 
 def chunk_segments(k_cache: torch.Tensor, v_cache: torch.Tensor, c: int, T: int):
@@ -50,5 +59,273 @@ class Workspace:
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = None
             self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf
+
+    def release(self):
+        self.buf = None
+
+
+class LayerKV:
+    """K and V rows of one layer.
+
+    While the layer is full, chunk c lives in slot c (rows [cT, (c+1)T)).
+    After :meth:`evict_history` (an L-Layer) the cache shrinks to two slots:
+    the sink stays in slot 0 and every later chunk is written to slot 1,
+    replacing the previous current chunk."""
+
+    def __init__(self, capacity_chunks: int, T: int, H: int, d: int, dtype, device):
+        self.T, self.H, self.d = T, H, d
+        self.dtype, self.device = dtype, device
+        self.local_only = False
+        self._alloc(capacity_chunks)
+
+    def _alloc(self, chunks: int):
+        self.capacity = chunks
+        self.k = torch.empty((chunks * self.T, self.H, self.d), dtype=self.dtype, device=self.device)
+        self.v = torch.empty_like(self.k)
+
+    def slot(self, c: int) -> int:
+        return min(c, 1) if self.local_only else c
+
+    def _rows(self, a: int, b: int):
+        return (self.k[a * self.T:b * self.T], self.v[a * self.T:b * self.T])
+
+    def write(self, c: int, k: torch.Tensor, v: torch.Tensor):
+        """Store chunk c's keys and values (the output of the model's K/V projection)."""
+        s = self.slot(c)
+        if s >= self.capacity:
+            self.grow(max(s + 1, 2 * self.capacity))
+        kk, vv = self._rows(s, s + 1)
+        kk.copy_(k)
+        vv.copy_(v)
+
+    def grow(self, chunks: int):
+        """Reallocate with room for ``chunks`` slots, keeping the rows held."""
+        old_k, old_v, n = self.k, self.v, self.capacity
+        self._alloc(chunks)
+        self.k[:n * self.T].copy_(old_k)
+        self.v[:n * self.T].copy_(old_v)
+
+    def evict_history(self):
+        """Keep the sink (slot 0) only, in a two-slot cache; frees the history rows."""
+        sink_k, sink_v = self._rows(0, 1)
+        sink_k, sink_v = sink_k.clone(), sink_v.clone()
+        self.k = self.v = None
+        self._alloc(2)
+        self.k[:self.T].copy_(sink_k)
+        self.v[:self.T].copy_(sink_v)
+        self.local_only = True
+
+    def warmup_groups(self, c: int):
+        """(local, history) segment lists at warmup chunk c (the layer is full)."""
+        assert not self.local_only
+        return chunk_segments(self.k, self.v, c, self.T)
+
+    def attend_all(self, c: int):
+        """Segments of every key the layer holds at chunk c: for a full layer
+        rows [0, (c+1)T); for an L-Layer the sink and the current chunk (which
+        sit next to each other in slots 0 and 1)."""
+        hi = self.slot(c) + 1
+        return [self._rows(0, hi)]
+
+    def keys_held(self, c: int) -> int:
+        return (self.slot(c) + 1) * self.T
+
+    def bytes_allocated(self) -> int:
+        return 2 * self.k.numel() * self.k.element_size()
+
+
+class IspaStream:
+    """One stream of ``n_layers`` attention layers through the ISPA cycle.
+
+    ``with_stats=False`` skips the statistics (a stream that starts after a
+    switch made elsewhere, see :meth:`adopt_switch`).
+
+    ``capacity`` is the number of chunk slots each layer's cache starts with
+    (an int, or one per layer); a full layer's cache grows when a chunk lands
+    past it.
+
+    Usage: for warmup chunks call :meth:`write_kv` then :meth:`warmup` for
+    each layer; call :meth:`switch` once; afterwards :meth:`write_kv` and
+    :meth:`post` per layer and chunk.  Results of a call live in buffers that
+    the next call on the stream overwrites (views are returned).
+
+    Device state per layer: the KV cache, W (bf16 [D, D], y = a W), the
+    statistics G, C (fp32 [D, D], batched as [N, D, D] so the switch solves all
+    layers in one call) and r2 (fp64).  After the switch: dW (fp32), eps
+    (fp64), W + dW (bf16), the selection and the L/F mask.
+    """
+
+    def __init__(self, n_layers: int, H: int, d: int, T: int, capacity,
+                 device, dtype=torch.bfloat16, stats_dtype=torch.float16,
+                 lambda_abs: float = 0.0, lambda_rel: float = 1e-3, scale: float | None = None,
+                 with_stats: bool = True):
+        if dtype != torch.bfloat16:
+            raise ValueError("streams run on bf16 Q/K/V")
+        self.N, self.H, self.d, self.T = n_layers, H, d, T
+        self.D = H * d
+        self.device, self.dtype, self.stats_dtype = device, dtype, stats_dtype
+        self.lambda_abs, self.lambda_rel = lambda_abs, lambda_rel
+        self.scale = d ** -0.5 if scale is None else scale
+        self.L = B.lib()
+        D, dev = self.D, device
+        f32 = dict(dtype=torch.float32, device=dev)
+        caps = [capacity] * n_layers if isinstance(capacity, int) else list(capacity)
+        if len(caps) != n_layers:
+            raise ValueError("one capacity per layer")
+        self.kv = [LayerKV(cap, T, H, d, dtype, dev) for cap in caps]
+        self.W = torch.empty((n_layers, D, D), dtype=dtype, device=dev)
+        self.G = self.C = self.r2 = None
+        if with_stats:
+            self.G = torch.zeros((n_layers, D, D), **f32)
+            self.C = torch.zeros((n_layers, D, D), **f32)
+            self.r2 = torch.zeros(n_layers, dtype=torch.float64, device=dev)
+        self.o_loc = torch.empty((T, H, d), **f32)
+        self.o_hist = torch.empty_like(self.o_loc)
+        self.lse_loc = torch.empty((T, H), **f32)
+        self.lse_hist = torch.empty_like(self.lse_loc)
+        self.a_loc = torch.empty((T, D), dtype=stats_dtype, device=dev)
+        self.delta = torch.empty_like(self.a_loc)
+        self.y = torch.empty((T, D), dtype=dtype, device=dev)
+        self._op = (ctypes.c_void_p * 2)(self.o_loc.data_ptr(), self.o_hist.data_ptr())
+        self._lp = (ctypes.c_void_p * 2)(self.lse_loc.data_ptr(), self.lse_hist.data_ptr())
+        self.ws = Workspace(dev)
+        self.switched = False
+        self.dW = self.eps = self.info = self.w_eff = None
+        self.selected = self.is_local = self.status = None
+        self.is_local_host = None
+
+    # ------------------------------------------------------------------ helpers
+    def _ck(self, st):
+        if st != B.ISPA_OK:
+            raise B.IspaError(st, self.L.ispa_last_error().decode())
+
+    def _stream(self) -> int:
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def _segs(self, pairs):
+        return B._segs(pairs, self.H, self.d)
+
+    def set_w(self, layer: int, w: torch.Tensor):
+        self.W[layer].copy_(w)
+
+    def write_kv(self, layer: int, c: int, k: torch.Tensor, v: torch.Tensor):
+        self.kv[layer].write(c, k, v)
+
+    # ------------------------------------------------------------------ warmup
+    def warmup(self, layer: int, c: int, q: torch.Tensor):
+        """Chunk c of one layer during warmup: dual-stream attention over the
+        local and history groups, the LSE merge into A_loc and A_full - A_loc,
+        and the statistics update.  Returns (o_loc, lse_loc, o_hist, lse_hist,
+        a_loc, delta) views."""
+        if self.switched or self.G is None:
+            raise RuntimeError("warmup needs the statistics and must come before the switch")
+        if q.shape != (self.T, self.H, self.d) or q.dtype != self.dtype:
+            raise ValueError("q must be [T, H, d] bf16")
+        L, s = self.L, self._stream()
+        loc, hist = self.kv[layer].warmup_groups(c)
+        ls, nl = self._segs(loc)
+        hs, nh = self._segs(hist)
+        n = self.T
+        need = max(L.ispa_dual_attn_workspace_bytes(B.ISPA_BF16, n, self.H, self.d, ls, nl, hs, nh),
+                   L.ispa_accum_stats_workspace_bytes(B._DT[self.stats_dtype], n, self.D))
+        ws = self.ws.get(need)
+        wsp = ws.data_ptr() if ws is not None else None
+        self._ck(L.ispa_dual_attn(B.ISPA_BF16, n, self.H, self.d, self.scale, q.data_ptr(), q.stride(0),
+                                  ls, nl, hs, nh, self.o_loc.data_ptr(), self.lse_loc.data_ptr(),
+                                  self.o_hist.data_ptr(), self.lse_hist.data_ptr(), wsp, need, s))
+        self._ck(L.ispa_lse_merge(2, self._op, self._lp, n, self.H, self.d, None, None,
+                                  self.a_loc.data_ptr(), self.delta.data_ptr(),
+                                  B._DT[self.stats_dtype], s))
+        self._ck(L.ispa_accum_stats(B._DT[self.stats_dtype], B.ISPA_BF16, n, self.D,
+                                    self.a_loc.data_ptr(), self.delta.data_ptr(),
+                                    self.W[layer].data_ptr(), self.G[layer].data_ptr(),
+                                    self.C[layer].data_ptr(), self.r2[layer:layer + 1].data_ptr(),
+                                    wsp, need, s))
+        return self.o_loc, self.lse_loc, self.o_hist, self.lse_hist, self.a_loc, self.delta
+
+    # ------------------------------------------------------------------ switch
+    def switch(self, K: int, evict: bool = True):
+        """Ridge solve of every layer in one batched call (dW, eps, W + dW),
+        selection of the K lowest-eps layers, then (optionally) eviction of the
+        L-Layers' history.  Synchronises once to read the L/F mask on the host,
+        which decides the later calls."""
+        L, s, N, D = self.L, self._stream(), self.N, self.D
+        dev = self.device
+        self.dW = torch.empty((N, D, D), dtype=torch.float32, device=dev)
+        self.eps = torch.empty(N, dtype=torch.float64, device=dev)
+        self.info = torch.empty(N, dtype=torch.int32, device=dev)
+        self.w_eff = torch.empty_like(self.W)
+        need = L.ispa_solve_dw_workspace_bytes(N, D)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self._ck(L.ispa_solve_dw(N, D, self.G.data_ptr(), self.C.data_ptr(), self.r2.data_ptr(), D * D,
+                                 self.lambda_abs, self.lambda_rel, self.dW.data_ptr(), self.eps.data_ptr(),
+                                 self.info.data_ptr(), self.W.data_ptr(), B.ISPA_BF16,
+                                 self.w_eff.data_ptr(), ws.data_ptr(), need, s))
+        self.selected = torch.empty(max(K, 1), dtype=torch.int32, device=dev)
+        self.is_local = torch.empty(N, dtype=torch.uint8, device=dev)
+        self.status = torch.empty(1, dtype=torch.int32, device=dev)
+        self._ck(L.ispa_select_layers(N, K, self.eps.data_ptr(), self.selected.data_ptr(),
+                                      self.is_local.data_ptr(), self.status.data_ptr(), s))
+        self.K = K
+        self.is_local_host = [int(x) for x in self.is_local.cpu()]  # synchronises
+        del ws
+        if int(self.status.cpu()[0]) != 0 or int(self.info.max().cpu()) != 0:
+            raise RuntimeError("switch failed: eps is NaN or a Gram matrix is not positive definite")
+        self.switched = True
+        if evict:
+            self.evict()
+        return self.selected[:K], self.is_local, self.eps
+
+    def evict(self):
+        """Free the history rows of every L-Layer; drop the statistics."""
+        for layer, flag in enumerate(self.is_local_host):
+            if flag:
+                self.kv[layer].evict_history()
+        self.G = self.C = None
+        self.ws.release()
+
+    def adopt_switch(self, is_local, w_eff, dW=None, eps=None):
+        """Start a stream directly in the post-switch phase with a selection
+        and W + dW computed elsewhere (e.g. an earlier stream of the same
+        layers)."""
+        self.is_local_host = [int(x) for x in is_local]
+        self.w_eff = w_eff
+        self.dW, self.eps = dW, eps
+        self.switched = True
+        for layer, flag in enumerate(self.is_local_host):
+            if flag:
+                self.kv[layer].evict_history()
+        self.G = self.C = None
+
+    # ------------------------------------------------------------------ post-switch
+    def post(self, layer: int, c: int, q: torch.Tensor):
+        """Chunk c of one layer after the switch: an L-Layer attends to its
+        sink and current chunk and projects with W + dW; an F-Layer attends to
+        all its keys and projects with W.  Returns the y [T, D] bf16 view."""
+        if not self.switched:
+            raise RuntimeError("post-switch call before the switch")
+        L, s = self.L, self._stream()
+        local = bool(self.is_local_host[layer])
+        segs, ns = self._segs(self.kv[layer].attend_all(c))
+        w = self.w_eff[layer] if local else self.W[layer]
+        need = L.ispa_local_attn_proj_workspace_bytes(B.ISPA_BF16, self.T, self.H, self.d, segs, ns)
+        ws = self.ws.get(need)
+        self._ck(L.ispa_local_attn_proj(B.ISPA_BF16, self.T, self.H, self.d, self.scale, q.data_ptr(),
+                                        q.stride(0), segs, ns, w.data_ptr(), B.ISPA_BF16,
+                                        self.y.data_ptr(), B.ISPA_BF16,
+                                        ws.data_ptr() if ws is not None else None, need, s))
+        return self.y
+
+    # ------------------------------------------------------------------ accounting
+    def keys_held(self, c: int) -> list:
+        return [kv.keys_held(c) for kv in self.kv]
+
+    def kv_bytes_held(self, c: int) -> int:
+        """Bytes of the K and V rows the layers hold at chunk c."""
+        return kv_bytes(self.keys_held(c), self.D, torch.finfo(self.dtype).bits // 8)
+
+    def kv_bytes_allocated(self) -> int:
+        return sum(kv.bytes_allocated() for kv in self.kv)

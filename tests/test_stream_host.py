@@ -1,0 +1,59 @@
+"""Host logic of the chunked stream (no GPU): cache slots, eviction and the
+key accounting against the oracle's grouping."""
+import torch
+
+import oracle as O
+from kv_cache_absorption_amd.stream import LayerKV, keys_retained, kv_bytes
+
+
+def _fill(kv, c, T, H, d):
+    val = torch.full((T, H, d), float(c))
+    kv.write(c, val, -val)
+
+
+def test_layer_cache_groups_follow_oracle():
+    T, H, d = 3, 2, 4
+    kv = LayerKV(2, T, H, d, torch.float32, "cpu")  # grows past two slots
+    for c in range(7):
+        _fill(kv, c, T, H, d)
+        loc, hist = kv.warmup_groups(c)
+        oloc, ohist = O.stream_groups(c, T)
+        for got, want in ((loc, oloc), (hist, ohist)):
+            assert [k.shape[0] for k, _ in got] == [b - a for a, b in want]
+            for (k, v), (a, b) in zip(got, want):
+                # row r of the key sequence holds chunk r // T
+                assert torch.equal(k[:, 0, 0], torch.arange(a, b).div(T, rounding_mode="floor").float())
+                assert torch.equal(v, -k)
+        assert kv.keys_held(c) == (c + 1) * T
+        (k_all, _), = kv.attend_all(c)
+        assert k_all.shape[0] == (c + 1) * T
+    assert kv.capacity >= 7
+
+
+def test_eviction_keeps_sink_and_current():
+    T, H, d = 2, 1, 4
+    kv = LayerKV(6, T, H, d, torch.float32, "cpu")
+    for c in range(6):
+        _fill(kv, c, T, H, d)
+    kv.evict_history()
+    assert kv.capacity == 2 and kv.local_only
+    assert kv.bytes_allocated() == 2 * 2 * T * H * d * 4
+    for c in range(6, 9):
+        _fill(kv, c, T, H, d)
+        (k, v), = kv.attend_all(c)
+        # the local group of chunk c: sink rows then the current chunk's rows
+        assert k[:, 0, 0].tolist() == [0.0] * T + [float(c)] * T
+        oloc, _ = O.stream_groups(c, T)
+        assert kv.keys_held(c) == sum(b - a for a, b in oloc)
+
+
+def test_keys_retained_matches_oracle_bytes():
+    T, D = 4680, 1536
+    flags = [1, 0] * 15
+    for c in (0, 1, 5, 19):
+        n = keys_retained(c, T, flags)
+        oloc, ohist = O.stream_groups(c, T)
+        n_loc = sum(b - a for a, b in oloc)
+        n_full = n_loc + sum(b - a for a, b in ohist)
+        assert n == [n_loc if f else n_full for f in flags]
+        assert kv_bytes(n, D) == O.kv_bytes_retained(n, D)
