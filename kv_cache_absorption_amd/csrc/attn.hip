@@ -6,7 +6,8 @@
 // is the per-group state the dual-stream warmup relies on (EN review, Key
 // Design 1: each group returns its weighted values and its LSE).
 //
-// bf16 path (d = 64 or 128), one workgroup = 4 waves x 32 queries of one head:
+// bf16 path, d = 64: one workgroup = 4 waves x 32 queries of one head (d = 128
+// has its own kernel further down, described there):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the key tile is the A operand
 //     (read row-wise from LDS), the wave's 32 queries are the B operand (kept
 //     in registers).  In the 32x32 accumulator each lane then holds 16 scores
@@ -316,34 +317,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnParams p) {
   }
 }
 
-// ---- d = 128 pipelined kernel ----------------------------------------------
-//
-// 4 waves x 64 queries (two 32-query blocks per wave, so every K or V^T
-// fragment read from LDS feeds two MFMAs); key tiles of 32.
-//   * K and V tiles go from global memory straight into LDS (buffer loads with
-//     the LDS flag, no VGPR staging), row-major with the 16-byte chunks of a
-//     row XOR-swizzled (see swz) so that both the 16-byte K fragment reads and
-//     the transposing V reads are free of bank conflicts.
-//   * The V^T fragment of O^T = V^T P^T is read with ds_read_b64_tr_b16: in each
-//     16-lane group, lane 4r + c reads 4 consecutive d of key row r and the
-//     transpose hands lane j the 4 keys at d = 4*(j/4) + j%4.  Two such reads give
-//     the 8 keys of one MFMA slot set, in the order the score accumulator holds
-//     them.
-//   * Software pipeline of one tile: in iteration j the MFMAs of P_{j-1} V_{j-1}
-//     and of K_{j+1} Q^T are issued while the softmax of tile j runs on the
-//     VALU.  Tiles are loaded three iterations ahead into a ring of five LDS
-//     buffers; one barrier per iteration.
-namespace d128 {
-constexpr int DH = 128;
-constexpr int BQ = 256;
-constexpr int BK = 32;
-constexpr int PD = 3;                  // tiles loaded ahead
-constexpr int NBUF = PD + 2;           // live: V_{j-1}, V_j, K_{j+1}, two in flight
-constexpr int ROWB = DH * 2;           // bytes per key row in LDS
-constexpr int TILEB = BK * ROWB;       // 8 KB per K (or V) tile
-constexpr int LPW = TILEB / 1024 / 4;  // 1 KB load instructions per wave per tensor per tile
-constexpr int LOADS_PER_TILE = 2 * LPW;
-}  // namespace d128
+// ---- helpers of the d = 128 kernel --------------------------------------------
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -395,18 +369,10 @@ __device__ __forceinline__ void segc_next(const AttnParams& p, int g, int head, 
 __device__ __forceinline__ int swz(int row, int ch) { return ch ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
 #define ISPA_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  // s_waitcnt with vmcnt = n (n in {0, LOADS_PER_TILE}), expcnt/lgkmcnt untouched
-  if (n == 0)
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70 | d128::LOADS_PER_TILE);
-}
-
 // One 16-byte-per-lane buffer load written straight to LDS at lds_off + 16*lane.
 // Issued as a plain instruction so that the compiler does not serialise later
 // LDS reads of other ring buffers behind it; completion is awaited explicitly
-// with wait_vmcnt before the barrier that publishes the tile.
+// with s_waitcnt vmcnt before the barrier that publishes the tile.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_off, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
@@ -418,16 +384,66 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
-__global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(const AttnParams p) {
-  using namespace d128;
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
+// ---- d = 128 kernel ----------------------------------------------------------
+//
+// 8 waves x 32 queries (256 queries of one head per workgroup), key tiles of
+// 64.  Waves w and w + 4 share a SIMD and belong to different groups; the two
+// groups run half a tile apart.  The work of a tile is split into an MFMA
+// phase X (S_t = K_t Q^T and O += V_{t-1}^T P_{t-1}^T, with their LDS
+// fragment reads) and a VALU phase Y (P_t = exp2(S_t c - m), row sum, mask of
+// a short tile), and a workgroup barrier closes every phase: group A runs
+// X_0 Y_0 X_1 ..., group B one phase later, so each SIMD has one wave on the
+// matrix core while the other works on its softmax (exp2 overlaps with the
+// other wave's MFMAs; plain VALU work largely does not, so the phases are
+// written to keep VALU instructions per tile low):
+//   * The running row maximum m (log2 units, c = scale * log2(e)) is not
+//     recomputed per tile: P = exp2(S c - m) is formed first and m is raised
+//     only when some P reaches 2 (the exponent MSB of a packed bf16 pair,
+//     tested with one OR per pair; inf and NaN set it too).  Then the rows of
+//     that tile are re-based on their maximum and O, l rescaled.  m starts at
+//     -inf, so the first tile always takes that path and sets m exactly; exp2
+//     arguments stay below 1 and the result is unchanged in exact arithmetic.
+//   * Every LDS fragment address is a per-lane register plus an immediate: K
+//     slots occupy the first 64 KB and V slots the second, and the tile loop
+//     is unrolled by the ring size so the slot offsets are constants.
+//   * K and V tiles go from global memory straight into a ring of NBUF slots
+//     (buffer loads with the LDS flag, rows XOR-swizzled so that the 16-byte K
+//     reads and the transposing V reads are conflict-free); tile u is issued
+//     NBUF - 2 tiles ahead, at the start of the even phase in which its slot
+//     frees (group B's PV of tile u - NBUF ends the phase before).
+//   * S^T = K Q^T puts a query in each lane's accumulator column, so row
+//     statistics are in-register reductions plus one v_permlane32_swap; the V^T
+//     fragments of O^T = V^T P^T come from ds_read_b64_tr_b16 in the key order
+//     of the score accumulator.
+namespace pp {
+constexpr int DH = 128;
+constexpr int WAVES = 8;
+constexpr int BQ = WAVES * 32;
+constexpr int BK = 64;
+constexpr int NBUF = 4;
+constexpr int ROWB = DH * 2;
+constexpr int TILEB = BK * ROWB;           // 16 KB per K (or V) tile
+constexpr int VBASE = NBUF * TILEB;        // V slots follow the K slots
+constexpr int LPW = TILEB / 1024 / WAVES;  // 1 KB load instructions per wave per tensor per tile
+constexpr int LOADS_PER_TILE = 2 * LPW;
+static_assert(LPW * WAVES * 1024 == TILEB, "tile load split");
+static_assert(VBASE + NBUF * TILEB <= 160 * 1024, "LDS budget");
+}  // namespace pp
+
+// XOR mask of the swizzle: swz(row, ch) == ch ^ swz_mask(row)
+__device__ __forceinline__ int swz_mask(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+__global__ __launch_bounds__(512, 1) void attn_bf16_d128_pp_kernel(const AttnParams p) {
+  using namespace pp;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * NBUF * TILEB];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int lq = lane & 31;
-  const int g16 = lane >> 4;  // 16-lane group
+  const int g16 = lane >> 4;
   const int s16 = lane & 15;
 
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -437,23 +453,21 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(const AttnParams
   const int jidx = rest / p.H;
   const AttnJob job = p.jobs[jidx];
   const int g = job.group;
+  const float c = p.c;
 
-  // ---- this lane's queries (B operand of S^T = K Q^T): block qb, slice s
-  const int64_t qrow0 = (int64_t)qtile * BQ + wave * 64 + lq;
-  bf16x8 qf[2][DH / 16];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int64_t qrow = qrow0 + qb * 32;
+  // this lane's query (B operand of S^T = K Q^T), slices of 16 d
+  const int64_t qrow = (int64_t)qtile * BQ + wave * 32 + lq;
+  bf16x8 qf[DH / 16];
+  {
     const uint16_t* qp = (const uint16_t*)p.q + qrow * p.q_stride + (int64_t)head * DH + hh * 8;
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
       u32x4 v = {0, 0, 0, 0};
       if (qrow < p.n_q) v = *(const u32x4*)(qp + s * 16);
-      qf[qb][s] = __builtin_bit_cast(bf16x8, v);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  // ---- tiles of this job
   int n_tiles = 0;
   {
     int64_t st = 0;
@@ -466,18 +480,31 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(const AttnParams
     }
   }
 
-  // load geometry: instruction i of this wave fills LDS rows (wave*LPW + i)*4 + g16,
-  // 16-byte slot s16, which holds global chunk swz(row, s16)
-  const uint32_t lds0 = lds_addr(lds);
+  // per-lane LDS byte offsets of the fragments; slot, key block and key group
+  // offsets are added as immediates
+  uint32_t koff[DH / 16];  // K row lq (of each 32-key block), 16-byte chunk 2s + hh
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s) koff[s] = lq * ROWB + (((2 * s + hh) ^ swz_mask(lq)) << 4);
+  uint32_t voff0[DH / 32], voff1[DH / 32];  // V rows r0, r0 + 8 of each 16-key group, d-tile dt
+  {
+    const int r0 = (g16 >> 1) * 4 + (s16 >> 2), r1 = r0 + 8;
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt) {
+      const int colb = dt * 64 + (g16 & 1) * 32 + (s16 & 3) * 8;
+      voff0[dt] = VBASE + r0 * ROWB + (((colb >> 4) ^ swz_mask(r0)) << 4) + (colb & 15);
+      voff1[dt] = VBASE + r1 * ROWB + (((colb >> 4) ^ swz_mask(r1)) << 4) + (colb & 15);
+    }
+  }
 
+  const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](const SegCursor& cur, int buf) {
     const int nvalid = (int)min<int64_t>(BK, cur.end - cur.row);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(cur.kp + cur.row * cur.ksb), 0, (int)(nvalid * cur.ksb), 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(cur.vp + cur.row * cur.vsb), 0, (int)(nvalid * cur.vsb), 0x00020000);
-    const uint32_t kdst = lds0 + (buf * 2 + 0) * TILEB;
-    const uint32_t vdst = lds0 + (buf * 2 + 1) * TILEB;
+    const uint32_t kdst = lds0 + buf * TILEB;
+    const uint32_t vdst = lds0 + VBASE + buf * TILEB;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int lrow = (wave * LPW + i) * 4 + g16;
@@ -489,208 +516,199 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(const AttnParams
     }
   };
 
-  // K fragment for slice s: row lq, 16-byte chunk 2s + hh (swizzled)
-  auto k_frag = [&](const char* kb, int s) {
-    return *(const bf16x8*)(kb + lq * ROWB + swz(lq, 2 * s + hh) * 16);
-  };
-  // V^T fragment for key slice gp (16 keys), d-tile dt: two transposing reads
-  auto v_frag = [&](const char* vb, int gp, int dt) {
-    const int r = s16 >> 2, cc = s16 & 3;
-    const int colb = dt * 64 + (g16 & 1) * 32 + cc * 8;  // byte column of the 4 d values
-    const int row0 = gp * 16 + (g16 >> 1) * 4 + r;
-    const int row1 = row0 + 8;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        ISPA_LDS_PTR(s16x4, vb + row0 * ROWB + (swz(row0, colb >> 4) << 4) + (colb & 15)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        ISPA_LDS_PTR(s16x4, vb + row1 * ROWB + (swz(row1, colb >> 4) << 4) + (colb & 15)));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-  };
-
-  f32x16 o[2][DH / 32];
+  f32x16 o[DH / 32];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int i = 0; i < DH / 32; ++i) o[qb][i] = (f32x16){};
-  float m_c[2] = {-INFINITY, -INFINITY};
-  float l_part[2] = {0.0f, 0.0f};
-  const float c = p.c;
+  for (int i = 0; i < DH / 32; ++i) o[i] = (f32x16){};
+  f32x16 S[2];
+  bf16x8 P[4];
+  float m = -INFINITY, l_part = 0.0f;
 
-  // ---- prologue: issue tiles 0 .. PD-1, wait for tiles 0 and 1
   SegCursor lcur, ccur;
   segc_seek(p, g, head, 0, job.kbeg, job.kend, lcur);
   ccur = lcur;
-  int issued = 0, lbuf = 0;  // tiles issued so far; ring slot of the next issue
-  for (; issued < PD && issued < n_tiles; ++issued) {
-    issue(lcur, lbuf);
-    lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
+  int issued = 0;
+  for (; issued < NBUF - 1 && issued < n_tiles; ++issued) {
+    issue(lcur, issued);
     segc_next<BK>(p, g, head, job.kbeg, job.kend, lcur);
   }
-  wait_vmcnt(issued > 2 ? LOADS_PER_TILE : 0);
+  auto wait_tile = [&](int u) {  // loads of tiles newer than u may stay in flight
+    if (issued - 1 - u <= 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_TILE);
+  };
+  static_assert(NBUF == 4, "wait_tile covers one newer tile in flight");
+  if (n_tiles > 0) wait_tile(0);
   __syncthreads();
 
-  f32x16 S_a[2], S_b[2];
-  bf16x8 P_a[2][2], P_b[2][2];
-  {
-    const char* kb = lds;
+  // X_t with tile t in ring slot u
+  auto phase_x = [&](const int t, const int u) {
+    if (t >= 1) {  // O += V_{t-1}^T P_{t-1}^T, fragments read one key group ahead
+      const int vs = ((u + NBUF - 1) % NBUF) * TILEB;
+      bf16x8 fa[4], fb[4];
+      auto vfr = [&](int gp, int dt) {
+        const int off = vs + gp * 16 * ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, lds + voff0[dt] + off));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, lds + voff1[dt] + off));
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+      };
 #pragma unroll
-    for (int s = 0; s < DH / 16; ++s) {
-      const bf16x8 a = k_frag(kb, s);
+      for (int dt = 0; dt < 4; ++dt) fa[dt] = vfr(0, dt);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        S_a[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], s == 0 ? (f32x16){} : S_a[qb], 0, 0, 0);
+      for (int gp = 0; gp < 4; ++gp) {
+        bf16x8 (&cur)[4] = (gp & 1) ? fb : fa;
+        bf16x8 (&nxt)[4] = (gp & 1) ? fa : fb;
+        if (gp < 3) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) nxt[dt] = vfr(gp + 1, dt);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[dt], P[gp], o[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    if (t < n_tiles) {  // S_t = K_t Q^T
+      const int ks = u * TILEB;
+      auto kfr = [&](int blk, int s) { return *(const bf16x8*)(lds + koff[s] + ks + blk * 32 * ROWB); };
+      bf16x8 fa[4], fb[4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int i = 0; i < 4; ++i) fa[i] = kfr(0, i);
 #pragma unroll
-      for (int gp = 0; gp < 2; ++gp) P_b[qb][gp] = (bf16x8){};  // P_{-1} = 0: the first PV adds nothing
-  }
+      for (int q4 = 0; q4 < 4; ++q4) {  // groups of 4 (block, slice) pairs
+        bf16x8 (&cur)[4] = (q4 & 1) ? fb : fa;
+        bf16x8 (&nxt)[4] = (q4 & 1) ? fa : fb;
+        if (q4 < 3) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) nxt[i] = kfr((q4 + 1) >> 1, ((q4 + 1) & 1) * 4 + i);
+        }
+        const int blk = q4 >> 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = (q4 & 1) * 4 + i;
+          S[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[i], qf[s], s == 0 ? (f32x16){} : S[blk], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
 
-  // One pipeline step for tile j: O += V_{j-1}^T P_{j-1} and S_{j+1} = K_{j+1} Q^T
-  // on the matrix cores while the VALU turns S_j into P_j.
-  int cbuf = 0;  // ring slot of tile j
-  auto step = [&](int j, f32x16 (&s_in)[2], f32x16 (&s_out)[2], const bf16x8 (&p_in)[2][2],
-                  bf16x8 (&p_out)[2][2]) {
+  // P = exp2(S c - m) packed to bf16 pairs; returns the OR of the pairs
+  auto exp_pack = [&](uint32_t (&w)[16]) {
+    uint32_t orr = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int blk = k >> 3, i = (k & 7) * 2;
+      w[k] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(S[blk][i], c, -m)),
+                       __builtin_amdgcn_exp2f(fmaf(S[blk][i + 1], c, -m)));
+      orr |= w[k];
+    }
+    return orr;
+  };
+
+  // Y_t on S_t
+  auto phase_y = [&]() {
     const int nv = (int)min<int64_t>(BK, ccur.end - ccur.row);
     segc_next<BK>(p, g, head, job.kbeg, job.kend, ccur);
+    if (nv < BK) {  // short last tile of a segment: keys past its end score -inf
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int lim = nv - blk * 32 - hh * 4;  // element i is key blk*32 + (i/4)*8 + hh*4 + i%4
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[blk][i] = ((i >> 2) * 8 + (i & 3) < lim) ? S[blk][i] : -INFINITY;
+      }
+    }
+    uint32_t w[16];
+    const uint32_t orr = exp_pack(w);
+    if (__any((orr & 0x40004000u) != 0u)) {
+      // some P >= 2 (or not finite), or the first tile: raise m to the row maxima
+      float mx = fmaxf(S[0][0], S[1][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(S[0][i], S[1][i]));
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      const float m_new = fmaxf(m, mx * c);
+      if (m_new > m) {
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 when m = -inf
+        m = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < DH / 32; ++i) o[i] *= alpha;
+      }
+      exp_pack(w);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
+                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), l_part, false);
+#pragma unroll
+    for (int gp = 0; gp < 4; ++gp) P[gp] = __builtin_bit_cast(bf16x8, (u32x4){w[4 * gp], w[4 * gp + 1],
+                                                                              w[4 * gp + 2], w[4 * gp + 3]});
+  };
+
+  auto issue_next = [&]() {
     if (issued < n_tiles) {
-      issue(lcur, lbuf);
-      lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
+      issue(lcur, issued % NBUF);
       segc_next<BK>(p, g, head, job.kbeg, job.kend, lcur);
       ++issued;
     }
-    const int pbuf = j == 0 ? 0 : (cbuf == 0 ? NBUF - 1 : cbuf - 1);  // tile j-1 (tile 0 when j = 0)
-    const int nbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;                  // tile j+1
-    if (nv < BK) {  // last tile of a segment: keys past its end score -inf
-      const int lim = nv - hh * 4;  // element i is a valid key iff (i/4)*8 + i%4 < lim
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          s_in[qb][i] = ((i >> 2) * 8 + (i & 3) < lim) ? s_in[qb][i] : -INFINITY;
-    }
-    // (A) P_{j-1} V_{j-1} (tile 0's V with P = 0 when j = 0) + mask + row max
-    {
-      const char* vb = lds + (pbuf * 2 + 1) * TILEB;
-#pragma unroll
-      for (int gp = 0; gp < 2; ++gp)
-#pragma unroll
-        for (int dt = 0; dt < DH / 32; ++dt) {
-          const bf16x8 a = v_frag(vb, gp, dt);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p_in[qb][gp], o[qb][dt], 0, 0, 0);
-        }
-    }
-    float mxc[2];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = s_in[qb][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s_in[qb][i]);
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-      mxc[qb] = mx * c;
-      need |= mxc[qb] > m_c[qb] + 8.0f;
-    }
-    // rare: raise the running maximum and rescale O and l
-    if (__any(need)) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float m_new = fmaxf(m_c[qb], mxc[qb]);
-        if (m_new != -INFINITY) {
-          const float alpha = (m_c[qb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_c[qb] - m_new);
-          l_part[qb] *= alpha;
-#pragma unroll
-          for (int i = 0; i < DH / 32; ++i) o[qb][i] *= alpha;
-          m_c[qb] = m_new;
-        }
-      }
-    }
-    // (B) S_{j+1} = K_{j+1} Q^T (discarded after the last tile) + P_j = exp2(S_j c - m)
-    {
-      const char* kb = lds + (nbuf * 2 + 0) * TILEB;
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s) {
-        const bf16x8 a = k_frag(kb, s);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s_out[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], s == 0 ? (f32x16){} : s_out[qb], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m_use = (m_c[qb] == -INFINITY) ? 0.0f : m_c[qb];
-#pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        u32x4 w;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int i = gp * 8 + 2 * m;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_in[qb][i], c, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_in[qb][i + 1], c, -m_use));
-          const uint32_t pk = pack_bf16(p0, p1);
-          l_part[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
-                                                       __builtin_bit_cast(bf16x2, 0x3f803f80u), l_part[qb], false);
-          w[m] = pk;
-        }
-        p_out[qb][gp] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-    // tile j+2 must be in LDS for the next step; newer loads may stay in flight
-    wait_vmcnt(issued > j + 3 ? LOADS_PER_TILE : 0);
+  };
+  // close phase ph; before closing an odd phase, tile (ph + 1) / 2 must be in LDS
+  auto end_phase = [&](const int ph) {
+    if ((ph & 1) == 1 && (ph + 1) / 2 < n_tiles) wait_tile((ph + 1) / 2);
     __syncthreads();
-    cbuf = nbuf;
   };
-
-  auto final_pv = [&](const bf16x8 (&pl)[2][2]) {
-    const char* vb = lds + (((n_tiles - 1) % NBUF) * 2 + 1) * TILEB;  // tile n-1
+  // phases 0 .. 2 n_tiles + 1; every wave issues its share of the next tile at
+  // the start of each even phase >= 2
+  if (grp == 0) {
+    for (int t0 = 0; t0 <= n_tiles; t0 += NBUF) {
 #pragma unroll
-    for (int gp = 0; gp < 2; ++gp)
-#pragma unroll
-      for (int dt = 0; dt < DH / 32; ++dt) {
-        const bf16x8 a = v_frag(vb, gp, dt);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pl[qb][gp], o[qb][dt], 0, 0, 0);
-      }
-  };
-
-  int j = 0;
-  for (; j + 2 <= n_tiles; j += 2) {
-    step(j, S_a, S_b, P_b, P_a);
-    step(j + 1, S_b, S_a, P_a, P_b);
-  }
-  if (j < n_tiles) {
-    step(j, S_a, S_b, P_b, P_a);
-    final_pv(P_a);
-  } else if (n_tiles > 0) {
-    final_pv(P_b);
-  }
-
-  // ---- finalise
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[qb]), __float_as_uint(l_part[qb]), false, false);
-    const float l_tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    const int64_t qrow = qrow0 + qb * 32;
-    if (qrow >= p.n_q) continue;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* op = job.o + (qrow * p.H + head) * (int64_t)DH;
-#pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = dt * 32 + g4 * 8 + hh * 4;
-        f32x4 v = {o[qb][dt][g4 * 4 + 0] * inv, o[qb][dt][g4 * 4 + 1] * inv, o[qb][dt][g4 * 4 + 2] * inv,
-                   o[qb][dt][g4 * 4 + 3] * inv};
-        *(f32x4*)(op + d0) = v;
+      for (int u = 0; u < NBUF; ++u) {
+        const int t = t0 + u;
+        if (t > n_tiles) break;
+        if (t >= 1) issue_next();
+        phase_x(t, u);
+        end_phase(2 * t);
+        if (t < n_tiles) phase_y();
+        end_phase(2 * t + 1);
       }
     }
-    if (hh == 0) job.lse[qrow * p.H + head] = l_tot > 0.0f ? (m_c[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    end_phase(0);
+    for (int t0 = 0; t0 <= n_tiles; t0 += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int t = t0 + u;
+        if (t > n_tiles) break;
+        phase_x(t, u);
+        end_phase(2 * t + 1);
+        if (t < n_tiles) {
+          issue_next();
+          phase_y();
+          end_phase(2 * t + 2);
+        }
+      }
+    }
   }
+
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+  const float l_tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  if (qrow >= p.n_q) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  float* op = job.o + (qrow * p.H + head) * (int64_t)DH;
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = dt * 32 + g4 * 8 + hh * 4;
+      f32x4 v = {o[dt][g4 * 4 + 0] * inv, o[dt][g4 * 4 + 1] * inv, o[dt][g4 * 4 + 2] * inv,
+                 o[dt][g4 * 4 + 3] * inv};
+      *(f32x4*)(op + d0) = v;
+    }
+  }
+  if (hh == 0) job.lse[qrow * p.H + head] = l_tot > 0.0f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // fp32 reference-precision path: one thread per (query, head, job).
@@ -797,7 +815,10 @@ ispa_status launch_merge(const MergeParams& p, hipStream_t stream) {
   return check_launch("merge_kernel");
 }
 
-int attn_block_q(ispa_dtype dt, int32_t d) { return (dt == ISPA_BF16 && d == 128) ? d128::BQ : kBQ; }
+int attn_block_q(ispa_dtype dt, int32_t d) {
+  if (dt == ISPA_BF16 && d == 128) return pp::BQ;
+  return kBQ;
+}
 
 SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, int n_groups) {
   SplitPlan plan;
@@ -925,7 +946,7 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
   if (dt == ISPA_BF16) {
     const int64_t blocks = (int64_t)p.n_qtiles * H * nj;
     if (d == 128)
-      hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(attn_bf16_d128_pp_kernel, dim3((unsigned)blocks), dim3(512), 0, stream, p);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {
