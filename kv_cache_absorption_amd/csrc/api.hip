@@ -159,8 +159,10 @@ size_t ispa_accum_stats_workspace_bytes(ispa_dtype a_dt, int64_t n, int32_t D) {
   if (n <= 0 || D <= 0) return 0;
   if (a_dt == ISPA_F32) return align256((size_t)n * D * 4) + align256(64 * 8);
   const int64_t np = (n + kNtBK - 1) / kNtBK * kNtBK;
-  const size_t rblocks = (size_t)((D + kNtBM - 1) / kNtBM) * (size_t)((np + kNtBN - 1) / kNtBN);
-  return 2 * align256((size_t)D * D * 2) + 2 * align256((size_t)D * np * 2) + align256(rblocks * 8);
+  const size_t rblocks = (size_t)((D + kNtBM - 1) / kNtBM) * (size_t)((np + 127) / 128);
+  const int64_t split = nt_stats_split(D, np);
+  const size_t part = split > 1 ? align256((size_t)split * 2 * D * D * 4) : 0;
+  return 2 * align256((size_t)D * D * 2) + 2 * align256((size_t)D * np * 2) + align256(rblocks * 8) + part;
 }
 
 ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_t D, const void* a_loc,
@@ -176,6 +178,7 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   const size_t al = a_dt == ISPA_F32 ? 4 : 16;
   if (!aligned(a_loc, al) || !aligned(delta_a, al) || !aligned(w, a_dt == ISPA_F32 ? 4 : 8))
     return fail(ISPA_ERR_INVALID_ARG, "misaligned activations or W");
+  if (!aligned(G, 16) || !aligned(C, 16)) return fail(ISPA_ERR_INVALID_ARG, "G and C must be 16-byte aligned");
   if (n == 0) return ISPA_OK;
   const size_t need = ispa_accum_stats_workspace_bytes(a_dt, n, D);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
@@ -184,7 +187,8 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
     return launch_stats_f32(n, D, (const float*)a_loc, (const float*)delta_a, (const float*)w, G, C, r2, ws,
                             stream);
   // Workspace: W^T and (if W's type differs) W converted, A_loc^T and R^T with the
-  // token dimension zero-padded to a multiple of the GEMM's K stage, per-workgroup ||R||^2.
+  // token dimension zero-padded to a multiple of the GEMM's K stage, per-workgroup
+  // ||R||^2, and (when the token range is split) the partial G and C sums.
   const int64_t np = (n + kNtBK - 1) / kNtBK * kNtBK;
   char* wp = (char*)ws;
   uint16_t* Wt = (uint16_t*)wp;
@@ -196,6 +200,7 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   uint16_t* Rt = (uint16_t*)wp;
   wp += align256((size_t)D * np * 2);
   double* partials = (double*)wp;
+  const size_t rblocks_bytes = (size_t)((D + kNtBM - 1) / kNtBM) * (size_t)((np + 127) / 128) * 8;
   ispa_status st;
   const void* wsrc = w;
   if (w_dt != a_dt) {
@@ -218,8 +223,9 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   r.out = Rt;
   r.ld_out = np;
   r.n_valid = n;
+  r.bn = 128;  // narrower tiles: R has no K split, so fill the CUs with tiles
   r.tiles_m = (D + kNtBM - 1) / kNtBM;
-  r.tiles_n = (int)((np + kNtBN - 1) / kNtBN);
+  r.tiles_n = (int)((np + r.bn - 1) / r.bn);
   r.ksplit = 1;
   r.kchunk = D;
   r.sq_partials = partials;
@@ -241,16 +247,16 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   g.out = G;
   g.out2 = C;
   g.ld_out = D;
+  g.bn = kNtBM;
   g.tiles_m = g.tiles_n = (D + kNtBM - 1) / kNtBM;
   g.tri = 1;
   g.two_kinds = 1;
-  // split the token range when there are fewer tiles than two per CU slot pair
-  const int64_t tiles = (int64_t)g.tiles_m * (g.tiles_m + 1) / 2 + (int64_t)g.tiles_m * g.tiles_n;
   const int64_t stages = np / kNtBK;
-  const int64_t split = std::max<int64_t>(1, std::min<int64_t>((512 + tiles - 1) / tiles, stages / 8));
-  g.kchunk = (stages + split - 1) / split * kNtBK;
-  g.ksplit = (int)((np + g.kchunk - 1) / g.kchunk);
-  return launch_nt_gemm(g, a_dt, stream, nullptr);
+  g.ksplit = (int)nt_stats_split(D, np);
+  g.kchunk = (stages + g.ksplit - 1) / g.ksplit * kNtBK;
+  g.part = g.ksplit > 1 ? (float*)(wp + align256(rblocks_bytes)) : nullptr;
+  if ((st = launch_nt_gemm(g, a_dt, stream, nullptr))) return st;
+  return launch_nt_split_reduce(g, stream);
 }
 
 // ---------------------------------------------------------------- solve_dw

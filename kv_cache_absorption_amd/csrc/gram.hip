@@ -6,16 +6,23 @@
 // input width (R = dA W).  Transposing A_loc and W once per call into the
 // workspace, and writing R transposed, turns every product into this NT form so
 // both operands can be moved straight from global memory into LDS:
-//   * 128 x 128 output tile per workgroup, 4 waves as 2 x 2, each 64 x 64
-//     = 2 x 2 tiles of v_mfma_f32_32x32x16_{f16,bf16};
-//   * K stages of 32: each operand tile is 128 rows x 64 bytes in LDS, filled by
-//     buffer loads with the LDS flag (16 bytes per lane, no VGPR staging), two
-//     stages ahead in a ring of four (64 KB, so two workgroups share a CU and
-//     hide each other's LDS latency); one barrier per stage;
+//   * 256 x (2 WN) output tile per workgroup, 4 waves as 2 x 2, each 128 x WN
+//     (WN = 128 or 64) = 4 x WN/32 tiles of v_mfma_f32_32x32x16_{f16,bf16}
+//     whose accumulators live in the accumulation registers; a fragment read
+//     from LDS feeds WN/32 (or 4) MFMAs, so LDS traffic stays at 0.5-0.75 KB
+//     per MFMA and one wave per SIMD keeps the matrix core busy;
+//   * K stages of 32: each operand tile is 256 (or 2 WN) rows x 64 bytes in LDS,
+//     filled by buffer loads with the LDS flag (16 bytes per lane, no VGPR
+//     staging), PD stages ahead in a ring of PD + 2 (3 and 5 for 256-wide
+//     tiles, 4 and 6 for 128-wide: 96 KB in flight per CU, enough to cover the
+//     L2 and HBM latency at the MFMA rate); one barrier per stage;
 //   * 16-byte chunks of a row are XOR-swizzled with (row / 4) mod 4 so the
 //     16-byte fragment reads of 16 consecutive rows use 16 distinct bank groups;
-//   * the fragments of the next 16-wide k slice are read while the MFMAs of the
-//     current one run;
+//   * the fragments of both 16-wide k slices of a stage are read before its MFMAs
+//     run (the next stage's arrive meanwhile);
+//   * the MFMA takes the Y fragment as its A operand and the X fragment as its B
+//     operand, so each lane's accumulator holds four consecutive output columns
+//     of one row: the epilogue reads, adds and writes 16-byte vectors;
 //   * operand rows past the matrix reload the last valid row (results there
 //     are discarded); the token dimension is zero-padded to a multiple of 32 so
 //     no K masking is needed.
@@ -27,13 +34,9 @@ namespace ispa {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int NBUF = 4, PD = 2;          // ring slots; stages loaded ahead
+constexpr int BM = kNtBM, BK = kNtBK;
 constexpr int ROWB = BK * 2;              // bytes per tile row (64)
 constexpr int RPI = 1024 / ROWB;          // rows per 1 KB load instruction (16)
-constexpr int TILEB = BM * ROWB;          // 8 KB per operand tile
-constexpr int LPW = TILEB / 1024 / 4;     // 1 KB load instructions per wave per operand (2)
-constexpr int LOADS_PER_STAGE = 2 * LPW;  // per wave
 
 __device__ __forceinline__ int gswz(int row, int ch) { return ch ^ ((row >> 2) & 3); }
 
@@ -42,13 +45,6 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds
                :
                : "s"(lds_off), "v"(voff), "s"(r), "s"(soff)
                : "memory", "m0");
-}
-
-__device__ __forceinline__ void wait_stage(bool one_newer) {
-  if (one_newer)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_STAGE);
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 template <int MT>
@@ -61,10 +57,48 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
                                                   0, 0);
 }
 
-template <int MT>
-__global__ __launch_bounds__(256, 2) void nt_gemm_kernel(const NtGemmParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
-  __shared__ double red[4];
+// Tile (tm, tn) of the t-th workgroup of a grid (or of its upper triangle, tm <=
+// tn): columns are taken in groups of eight and, inside a group, rows in order
+// with the group's columns fastest.  Consecutive workgroups, which run at the
+// same time on one XCD, then cover a compact block of tiles (four rows by eight
+// columns) and share its operand rows in that XCD's L2.
+__device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, bool tri, int& tm, int& tn) {
+  constexpr int GC = 8;
+  for (int c0 = 0; c0 < tiles_n; c0 += GC) {
+    const int nc = min(GC, tiles_n - c0);
+    if (!tri) {
+      if (t < tiles_m * nc) {
+        tm = t / nc;
+        tn = c0 + t % nc;
+        return;
+      }
+      t -= tiles_m * nc;
+      continue;
+    }
+    for (int r = 0; r < c0 + nc; ++r) {  // row r holds columns max(c0, r) .. c0 + nc - 1
+      const int w = c0 + nc - max(c0, r);
+      if (t < w) {
+        tm = r;
+        tn = max(c0, r) + t;
+        return;
+      }
+      t -= w;
+    }
+  }
+  tm = tn = 0;  // not reached for t below the tile count
+}
+
+template <int MT, int WN>
+__global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
+  constexpr int BN = 2 * WN;
+  constexpr int NJ = WN / 32;                 // 32-column blocks per wave
+  constexpr int XB = BM * ROWB, YB = BN * ROWB;  // bytes per stage of each operand
+  constexpr int XL = XB / 1024 / 4, YL = YB / 1024 / 4;  // 1 KB loads per wave per stage
+  constexpr int LOADS = XL + YL;
+  constexpr int PD = WN == 128 ? 3 : 4;  // stages loaded ahead
+  constexpr int NBUF = PD + 2;           // ring slots
+  static_assert(NBUF * (XB + YB) <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * (XB + YB)];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hh = lane >> 5, lq = lane & 31;
@@ -80,17 +114,9 @@ __global__ __launch_bounds__(256, 2) void nt_gemm_kernel(const NtGemmParams p) {
   const bool kind1 = t >= n_kind0;
   if (kind1) t -= n_kind0;
   int tm, tn;
-  if (p.tri && !kind1) {
-    tm = 0;
-    while (t >= (uint32_t)(p.tiles_n - tm)) {
-      t -= p.tiles_n - tm;
-      ++tm;
-    }
-    tn = tm + (int)t;
-  } else {
-    tm = t / p.tiles_n;
-    tn = t % p.tiles_n;
-  }
+  grouped_tile((int)t, p.tiles_m, p.tiles_n, p.tri && !kind1, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);  // workgroup-uniform: keeps the buffer
+  tn = __builtin_amdgcn_readfirstlane(tn);  // descriptors in scalar registers
   const char* yp = (const char*)(kind1 ? p.y2 : p.y);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kb = (int64_t)split * p.kchunk;
@@ -103,39 +129,62 @@ __global__ __launch_bounds__(256, 2) void nt_gemm_kernel(const NtGemmParams p) {
       (void*)((const char*)p.x + m0 * p.ldx * 2), 0, (int)(min<int64_t>(BM, xrows - m0) * p.ldx * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(yp + n0 * p.ldy * 2), 0, (int)(min<int64_t>(BN, yrows - n0) * p.ldy * 2), 0x00020000);
-  int xo[LPW], yo[LPW];
+  int xo[XL], yo[YL];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int row = (wave * LPW + i) * RPI + lane / (ROWB / 16);  // RPI rows per 1 KB instruction
-    const int slot = lane % (ROWB / 16);
-    const int ch = gswz(row, slot);
-    const int xr = (int)min<int64_t>(row, xrows - m0 - 1), yr = (int)min<int64_t>(row, yrows - n0 - 1);
-    xo[i] = xr * (int)(p.ldx * 2) + ch * 16;
-    yo[i] = yr * (int)(p.ldy * 2) + ch * 16;
+  for (int i = 0; i < XL; ++i) {
+    const int row = (wave * XL + i) * RPI + lane / (ROWB / 16);  // RPI rows per 1 KB instruction
+    const int xr = (int)min<int64_t>(row, xrows - m0 - 1);
+    xo[i] = xr * (int)(p.ldx * 2) + gswz(row, lane % (ROWB / 16)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < YL; ++i) {
+    const int row = (wave * YL + i) * RPI + lane / (ROWB / 16);
+    const int yr = (int)min<int64_t>(row, yrows - n0 - 1);
+    yo[i] = yr * (int)(p.ldy * 2) + gswz(row, lane % (ROWB / 16)) * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
   auto issue = [&](int s, int buf) {
     const int soff = (int)((kb + (int64_t)s * BK) * 2);
+    const uint32_t xb = lds0 + buf * (XB + YB), yb = xb + XB;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const uint32_t dst = (wave * LPW + i) * 1024;
-      lds_dma16(rx, lds0 + (buf * 2 + 0) * TILEB + dst, xo[i], soff);
-      lds_dma16(ry, lds0 + (buf * 2 + 1) * TILEB + dst, yo[i], soff);
+    for (int i = 0; i < XL; ++i) lds_dma16(rx, xb + (wave * XL + i) * 1024, xo[i], soff);
+#pragma unroll
+    for (int i = 0; i < YL; ++i) lds_dma16(ry, yb + (wave * YL + i) * 1024, yo[i], soff);
+  };
+  // wait until at most `newer` stages of loads are outstanding (0 <= newer < PD)
+  auto wait_stage = [&](int newer) {
+    if constexpr (LOADS == 8) {
+      if (newer <= 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      else if (newer == 1)
+        __builtin_amdgcn_s_waitcnt(0x0F78);
+      else
+        __builtin_amdgcn_s_waitcnt(0x4F70);  // 16: vmcnt bits 5:4 sit in simm16 bits 15:14
+    } else {
+      static_assert(LOADS == 6, "stage load count");
+      if (newer <= 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      else if (newer == 1)
+        __builtin_amdgcn_s_waitcnt(0x0F76);
+      else if (newer == 2)
+        __builtin_amdgcn_s_waitcnt(0x0F7C);
+      else
+        __builtin_amdgcn_s_waitcnt(0x4F72);  // 18
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x16){};
 
   int issued = 0, lbuf = 0;
   for (; issued < PD && issued < ns; ++issued) {
     issue(issued, lbuf);
     lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
   }
-  wait_stage(issued > 1);
+  wait_stage(issued - 1);
   __syncthreads();
 
   int cbuf = 0;
@@ -145,63 +194,72 @@ __global__ __launch_bounds__(256, 2) void nt_gemm_kernel(const NtGemmParams p) {
       lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
       ++issued;
     }
-    const char* xs = lds + (cbuf * 2 + 0) * TILEB;
-    const char* ys = lds + (cbuf * 2 + 1) * TILEB;
-    auto frags = [&](int ks, u32x4 (&a)[2], u32x4 (&b)[2]) {
+    const char* xs = lds + cbuf * (XB + YB);
+    const char* ys = xs + XB;
+    auto frags = [&](int ks, u32x4 (&a)[4], u32x4 (&b)[NJ]) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 64 + i * 32 + lq;
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + lq;
         a[i] = *(const u32x4*)(xs + row * ROWB + gswz(row, 2 * ks + hh) * 16);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wn * 64 + j * 32 + lq;
+      for (int j = 0; j < NJ; ++j) {
+        const int row = wn * WN + j * 32 + lq;
         b[j] = *(const u32x4*)(ys + row * ROWB + gswz(row, 2 * ks + hh) * 16);
       }
     };
-    u32x4 a0[2], b0[2], a1[2], b1[2];
+    u32x4 a0[4], b0[NJ], a1[4], b1[NJ];
     frags(0, a0, b0);
     frags(1, a1, b1);
+    // acc[i][j] holds out^T for row block i and column block j (lane: row lq,
+    // columns (e/4)*8 + hh*4 + e%4)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<MT>(a0[i], b0[j], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma<MT>(b0[j], a0[i], acc[i][j]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<MT>(a1[i], b1[j], acc[i][j]);
-    // stage s+1 must be in LDS for the next iteration; the newer one may stay in flight
-    wait_stage(issued > s + 2);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma<MT>(b1[j], a1[i], acc[i][j]);
+    // stage s+1 must be in LDS for the next iteration; newer ones may stay in flight
+    wait_stage(issued - (s + 2));
     __syncthreads();
     cbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;
   }
 
-  // ---- epilogues
+  // ---- epilogues: lane holds out[m][n .. n+3] in acc[i][j][4 g .. 4 g + 3] with
+  // m = row block i + lq and n = column block j + 8 g + 4 hh
   if (p.epi == kNtStoreT) {
     // out[m][n] (16-bit, ld_out) for n < n_valid, zero for n_valid <= n < N; sum of squares
     uint16_t* out = (uint16_t*)p.out;
     double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 32 + lq;
+      float ssf = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + wn * 64 + j * 32 + lq;
-        float ssf = 0.0f;
+      for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t m = m0 + wm * 64 + i * 32 + (e >> 2) * 8 + hh * 4 + (e & 3);
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + wn * WN + j * 32 + g * 8 + hh * 4;  // N is a multiple of 4
           if (m < p.M && n < p.N) {
-            const bool ok = n < p.n_valid;
-            const float v = ok ? acc[i][j][e] : 0.0f;
-            out[m * p.ld_out + n] = (uint16_t)(MT == ISPA_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v));
-            ssf += v * v;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = n + e < p.n_valid ? acc[i][j][g * 4 + e] : 0.0f;
+              ssf += v[e] * v[e];
+            }
+            const uint32_t lo = MT == ISPA_BF16 ? pack_bf16(v[0], v[1]) : pack_f16(v[0], v[1]);
+            const uint32_t hi = MT == ISPA_BF16 ? pack_bf16(v[2], v[3]) : pack_f16(v[2], v[3]);
+            *(u32x2*)(out + m * p.ld_out + n) = (u32x2){lo, hi};
           }
         }
-        ss += (double)ssf;
       }
+      ss += (double)ssf;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    double* red = (double*)lds;  // the ring is idle after the last stage's barrier
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     if (tid == 0) p.sq_partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
@@ -209,22 +267,57 @@ __global__ __launch_bounds__(256, 2) void nt_gemm_kernel(const NtGemmParams p) {
   }
   float* outf = (float*)(kind1 ? p.out2 : p.out);
   const bool tri_tile = p.tri && !kind1;
-  const bool atomic = p.ksplit > 1;
+  if (p.ksplit > 1) {
+    // partial sums of this split, stored in the output's layout (no triangle mask:
+    // the reduction applies it)
+    float* part = p.part + ((int64_t)split * 2 + (kind1 ? 1 : 0)) * p.M * p.ld_out;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 32 + lq;
+      if (m >= p.M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 32 + lq;
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 64 + i * 32 + (e >> 2) * 8 + hh * 4 + (e & 3);
-        if (m >= p.M || n >= p.N || (tri_tile && m > n)) continue;
-        if (atomic)
-          unsafeAtomicAdd(outf + m * p.ld_out + n, acc[i][j][e]);
-        else
-          outf[m * p.ld_out + n] += acc[i][j][e];
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + wn * WN + j * 32 + g * 8 + hh * 4;
+          if (n < p.N)
+            *(f32x4*)(part + m * p.ld_out + n) =
+                (f32x4){acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
+        }
     }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 128 + i * 32 + lq;
+    if (m >= p.M) continue;
+    float* row = outf + m * p.ld_out;
+    // read all of this row block's vectors first so their latencies overlap
+    f32x4 cur[NJ][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wn * WN + j * 32 + g * 8 + hh * 4;  // N is a multiple of 4
+        cur[j][g] = n < p.N ? *(const f32x4*)(row + n) : (f32x4){};
+      }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wn * WN + j * 32 + g * 8 + hh * 4;
+        if (n >= p.N) continue;
+        f32x4 v = cur[j][g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += acc[i][j][g * 4 + e];
+        if (!tri_tile || m <= n) {
+          *(f32x4*)(row + n) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)  // the diagonal crosses this vector: upper part only
+            if (m <= n + e) row[n + e] = v[e];
+        }
+      }
   }
 }
 
@@ -267,22 +360,74 @@ __global__ void convert16_kernel(const uint16_t* in, int64_t n, int in_dt, uint1
   out[i] = (uint16_t)(out_dt == ISPA_BF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f));
 }
 
+// out[m][n .. n+3] += sum_s part[s][kind][m][n .. n+3]; the first kind keeps the
+// upper triangle (m <= n) only when tri is set
+__global__ __launch_bounds__(256) void split_reduce_kernel(float* out0, float* out1, const float* part, int64_t M,
+                                                           int64_t N, int64_t ld, int ksplit, int tri, int two) {
+  const int64_t vecs_per_row = N / 4;
+  const int64_t per_kind = M * vecs_per_row;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= per_kind * (two ? 2 : 1)) return;
+  const int kind = gid >= per_kind ? 1 : 0;
+  const int64_t v = gid - kind * per_kind;
+  const int64_t m = v / vecs_per_row, n = (v % vecs_per_row) * 4;
+  if (kind == 0 && tri && m > n + 3) return;  // entirely below the diagonal
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < ksplit; ++s) acc += *(const f32x4*)(part + ((int64_t)s * 2 + kind) * M * ld + m * ld + n);
+  float* row = (kind ? out1 : out0) + m * ld;
+  if (kind == 0 && tri && m > n) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (m <= n + e) row[n + e] += acc[e];
+    return;
+  }
+  *(f32x4*)(row + n) += acc;
+}
+
 }  // namespace
 
 ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t stream, int* n_blocks_out) {
   const int64_t n0 = p.tri ? (int64_t)p.tiles_m * (p.tiles_m + 1) / 2 : (int64_t)p.tiles_m * p.tiles_n;
   const int64_t blocks = (n0 + (p.two_kinds ? (int64_t)p.tiles_m * p.tiles_n : 0)) * p.ksplit;
   if (n_blocks_out) *n_blocks_out = (int)blocks;
-  if (p.K % BK || p.kchunk % BK || p.ksplit < 1 || (int64_t)p.ksplit * p.kchunk < p.K || p.ldx % 8 || p.ldy % 8) {
-    set_error("nt_gemm: K, split or leading dimensions not aligned");
+  if (p.K % BK || p.kchunk % BK || p.ksplit < 1 || (int64_t)p.ksplit * p.kchunk < p.K || p.ldx % 8 || p.ldy % 8 ||
+      (p.bn != 256 && p.bn != 128) || (p.tri && p.bn != BM) || p.N % 4 || p.ld_out % 4 ||
+      (p.epi == kNtAccum && p.ksplit > 1 && !p.part)) {
+    set_error("nt_gemm: K, split, tile or leading dimensions not aligned");
     return ISPA_ERR_INVALID_ARG;
   }
   if (blocks == 0) return ISPA_OK;
-  if (mfma_dt == ISPA_BF16)
-    hipLaunchKernelGGL(nt_gemm_kernel<ISPA_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(nt_gemm_kernel<ISPA_F16>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (mfma_dt == ISPA_BF16) {
+    if (p.bn == 256)
+      hipLaunchKernelGGL((nt_gemm_kernel<ISPA_BF16, 128>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((nt_gemm_kernel<ISPA_BF16, 64>), grid, block, 0, stream, p);
+  } else {
+    if (p.bn == 256)
+      hipLaunchKernelGGL((nt_gemm_kernel<ISPA_F16, 128>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((nt_gemm_kernel<ISPA_F16, 64>), grid, block, 0, stream, p);
+  }
   return check_launch("nt_gemm_kernel");
+}
+
+ispa_status launch_nt_split_reduce(const NtGemmParams& p, hipStream_t stream) {
+  if (p.ksplit <= 1) return ISPA_OK;
+  const int64_t items = p.M * (p.N / 4) * (p.two_kinds ? 2 : 1);
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream,
+                     (float*)p.out, (float*)p.out2, p.part, p.M, p.N, p.ld_out, p.ksplit, p.tri, p.two_kinds);
+  return check_launch("split_reduce_kernel");
+}
+
+int64_t nt_stats_split(int32_t D, int64_t np) {
+  // one workgroup per CU: split the token range when there are fewer tiles than CUs
+  const int64_t tm = (D + kNtBM - 1) / kNtBM;
+  const int64_t tiles = tm * (tm + 1) / 2 + tm * tm;
+  const int64_t stages = np / kNtBK;
+  const int64_t split = std::max<int64_t>(1, std::min<int64_t>(256 / tiles, stages / 8));
+  const int64_t kchunk = (stages + split - 1) / split;
+  return (stages + kchunk - 1) / kchunk;
 }
 
 ispa_status launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,

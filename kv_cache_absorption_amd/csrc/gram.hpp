@@ -6,7 +6,8 @@
 namespace ispa {
 
 enum {
-  kNtAccum = 0,   // out[m][n] += acc (fp32); atomic when K is split; upper triangle for first-kind tiles if tri
+  kNtAccum = 0,   // out[m][n] += acc (fp32), upper triangle for first-kind tiles if tri; with a K split the
+                  // workgroups store partial sums to part[split][kind] (layout of out) for nt_split_reduce
   kNtStoreT = 1   // out[m][n] = acc as 16-bit (mfma type) for n < n_valid, 0 for n_valid <= n < N;
                   // per-workgroup sum of squares of the stored values
 };
@@ -23,19 +24,25 @@ struct NtGemmParams {
   void* out2;        // second-kind tiles' output
   int64_t ld_out;
   int64_t n_valid;   // kNtStoreT: columns at or past n_valid are written as 0
-  int32_t tiles_m, tiles_n;
+  int32_t tiles_m, tiles_n;  // tiles of kNtBM x bn
+  int32_t bn;                 // tile width: 256, or 128 (no triangle)
   int32_t tri, two_kinds;
   int32_t ksplit;
   int64_t kchunk;
   double* sq_partials;
+  float* part;        // kNtAccum with ksplit > 1: [ksplit][2][M][ld_out] partial sums
 };
 
 ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t stream, int* n_blocks_out);
+// out (and out2) += sum over splits of the partial sums a kNtAccum launch left in p.part
+ispa_status launch_nt_split_reduce(const NtGemmParams& p, hipStream_t stream);
+// K split of the statistics GEMM over np tokens at width D (tiles of kNtBM)
+int64_t nt_stats_split(int32_t D, int64_t np);
 // out[c][r] = in[r][c] (r < rows), 0 for rows <= r < rows_pad; rows_pad multiple of 4, cols of 4
 ispa_status launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,
                                int64_t ld_out, int64_t rows_pad, hipStream_t stream);
 ispa_status launch_convert16(const void* in, int64_t n, int in_dt, void* out, int out_dt, hipStream_t stream);
 
-constexpr int kNtBM = 128, kNtBN = 128, kNtBK = 32;
+constexpr int kNtBM = 256, kNtBK = 32;
 
 }  // namespace ispa
