@@ -384,62 +384,72 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
+// XOR mask of the swizzle: swz(row, ch) == ch ^ swz_mask(row)
+__device__ __forceinline__ int swz_mask(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
 // ---- d = 128 kernel ----------------------------------------------------------
 //
-// 8 waves x 32 queries (256 queries of one head per workgroup), key tiles of
-// 64.  Waves w and w + 4 share a SIMD and belong to different groups; the two
-// groups run half a tile apart.  The work of a tile is split into an MFMA
-// phase X (S_t = K_t Q^T and O += V_{t-1}^T P_{t-1}^T, with their LDS
-// fragment reads) and a VALU phase Y (P_t = exp2(S_t c - m), row sum, mask of
-// a short tile), and a workgroup barrier closes every phase: group A runs
-// X_0 Y_0 X_1 ..., group B one phase later, so each SIMD has one wave on the
-// matrix core while the other works on its softmax (exp2 overlaps with the
-// other wave's MFMAs; plain VALU work largely does not, so the phases are
-// written to keep VALU instructions per tile low):
-//   * The running row maximum m (log2 units, c = scale * log2(e)) is not
-//     recomputed per tile: P = exp2(S c - m) is formed first and m is raised
-//     only when some P reaches 2 (the exponent MSB of a packed bf16 pair,
-//     tested with one OR per pair; inf and NaN set it too).  Then the rows of
-//     that tile are re-based on their maximum and O, l rescaled.  m starts at
-//     -inf, so the first tile always takes that path and sets m exactly; exp2
-//     arguments stay below 1 and the result is unchanged in exact arithmetic.
+// 8 waves x 32 queries of one head per workgroup (two waves per SIMD), key
+// tiles of 64, one workgroup per CU.  Each wave software-pipelines its tiles
+// so that the matrix core and the vector ALU work on different tiles in the
+// same stretch of code (a wave's VALU instructions issue in the shadow of its
+// own MFMAs).  Iteration t runs in two halves of 16 steps:
+//   1. O += V_{t-1}^T P_{t-1}^T on the matrix core, while the VALU forms
+//      P_t = exp2(S_t c - m) (c = scale * log2(e)) packed to bf16;
+//   2. S_{t+1} = K_{t+1} Q^T on the matrix core (into the registers of S_t,
+//      now consumed), while the VALU adds the row sums of P_t and takes the
+//      row maxima of the first key block of S_{t+1}.
+// Before half 1 the tile's row maxima decide a lazy re-basing: the running
+// maximum m is raised only when the tile exceeds it by more than 8 (log2
+// units), so P < 2^8 and, after the first tile (m starts at -inf), re-basing
+// is rare; it scales l at once and O after half 1.  Any m below the true
+// maximum gives the same result in exact arithmetic.
+//   * One iteration form for every tile: iteration 0 multiplies a zeroed
+//     P_{-1} with a zeroed V slot, and keys past the end of a segment (all keys
+//     of the final iteration) are masked to -inf behind a uniform branch.
 //   * Every LDS fragment address is a per-lane register plus an immediate: K
 //     slots occupy the first 64 KB and V slots the second, and the tile loop
-//     is unrolled by the ring size so the slot offsets are constants.
-//   * K and V tiles go from global memory straight into a ring of NBUF slots
-//     (buffer loads with the LDS flag, rows XOR-swizzled so that the 16-byte K
-//     reads and the transposing V reads are conflict-free); tile u is issued
-//     NBUF - 2 tiles ahead, at the start of the even phase in which its slot
-//     frees (group B's PV of tile u - NBUF ends the phase before).
+//     is unrolled by the ring size so the slot offsets are constants.  Each
+//     step reads its fragment LA steps ahead; a scheduling boundary per step
+//     keeps the compiler from sinking the reads onto their MFMAs.
+//   * K and V tiles go from global memory straight into two rings of four
+//     slots (buffer loads with the LDS flag, rows XOR-swizzled so that the
+//     16-byte K reads and the transposing V reads are conflict-free).  K of
+//     tile u is read in iteration u - 1 and issued in iteration u - 4; V of
+//     tile u is read in iteration u + 1 and issued in iteration u - 2; one
+//     barrier per iteration publishes the loads and frees the slots.
 //   * S^T = K Q^T puts a query in each lane's accumulator column, so row
 //     statistics are in-register reductions plus one v_permlane32_swap; the V^T
 //     fragments of O^T = V^T P^T come from ds_read_b64_tr_b16 in the key order
 //     of the score accumulator.
-namespace pp {
+//   * QB query blocks per wave share each K or V fragment; QB = 1 with 8 waves
+//     measured fastest (QB = 2 with 4 waves leaves one wave per SIMD and
+//     nothing to cover its stalls).
+namespace a5 {
 constexpr int DH = 128;
 constexpr int WAVES = 8;
-constexpr int BQ = WAVES * 32;
+constexpr int QB = 1;                  // 32-query blocks per wave
+constexpr int BQ = WAVES * QB * 32;
 constexpr int BK = 64;
-constexpr int NBUF = 4;
+constexpr int NSLOT = 4;               // ring slots for K and for V
 constexpr int ROWB = DH * 2;
-constexpr int TILEB = BK * ROWB;           // 16 KB per K (or V) tile
-constexpr int VBASE = NBUF * TILEB;        // V slots follow the K slots
-constexpr int LPW = TILEB / 1024 / WAVES;  // 1 KB load instructions per wave per tensor per tile
-constexpr int LOADS_PER_TILE = 2 * LPW;
+constexpr int TILEB = BK * ROWB;       // 16 KB per K (or V) tile
+constexpr int VBASE = NSLOT * TILEB;   // V slots follow the K slots
+constexpr int LPW = TILEB / 1024 / WAVES;  // 1 KB load instructions per wave per tile and tensor
+constexpr int LA = 2;                  // LDS fragments read ahead of their MFMA
 static_assert(LPW * WAVES * 1024 == TILEB, "tile load split");
-static_assert(VBASE + NBUF * TILEB <= 160 * 1024, "LDS budget");
-}  // namespace pp
+static_assert(2 * NSLOT * TILEB <= 160 * 1024, "LDS budget");
+// s_waitcnt immediate that waits until at most n vector memory operations are
+// outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+}  // namespace a5
 
-// XOR mask of the swizzle: swz(row, ch) == ch ^ swz_mask(row)
-__device__ __forceinline__ int swz_mask(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
-__global__ __launch_bounds__(512, 1) void attn_bf16_d128_pp_kernel(const AttnParams p) {
-  using namespace pp;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * NBUF * TILEB];
+__global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const AttnParams p) {
+  using namespace a5;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * NSLOT * TILEB];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int lq = lane & 31;
@@ -455,16 +465,18 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_d128_pp_kernel(const AttnPar
   const int g = job.group;
   const float c = p.c;
 
-  // this lane's query (B operand of S^T = K Q^T), slices of 16 d
-  const int64_t qrow = (int64_t)qtile * BQ + wave * 32 + lq;
-  bf16x8 qf[DH / 16];
-  {
+  // this lane's queries (B operand of S^T = K Q^T): block qb, slices of 16 d
+  const int64_t qrow0 = (int64_t)qtile * BQ + wave * (QB * 32) + lq;
+  bf16x8 qf[QB][DH / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t qrow = qrow0 + qb * 32;
     const uint16_t* qp = (const uint16_t*)p.q + qrow * p.q_stride + (int64_t)head * DH + hh * 8;
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
       u32x4 v = {0, 0, 0, 0};
       if (qrow < p.n_q) v = *(const u32x4*)(qp + s * 16);
-      qf[s] = __builtin_bit_cast(bf16x8, v);
+      qf[qb][s] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
@@ -481,10 +493,10 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_d128_pp_kernel(const AttnPar
   }
 
   // per-lane LDS byte offsets of the fragments; slot, key block and key group
-  // offsets are added as immediates
-  uint32_t koff[DH / 16];  // K row lq (of each 32-key block), 16-byte chunk 2s + hh
-#pragma unroll
-  for (int s = 0; s < DH / 16; ++s) koff[s] = lq * ROWB + (((2 * s + hh) ^ swz_mask(lq)) << 4);
+  // offsets are immediates.  K row lq (of each 32-key block), 16-byte chunk
+  // 2s + hh: the chunk bits sit below the row bits, so the offset of slice s is
+  // kbase ^ (s << 5), one XOR in the VALU-light half of the iteration.
+  const uint32_t kbase = lq * ROWB + ((hh ^ swz_mask(lq)) << 4);
   uint32_t voff0[DH / 32], voff1[DH / 32];  // V rows r0, r0 + 8 of each 16-key group, d-tile dt
   {
     const int r0 = (g16 >> 1) * 4 + (s16 >> 2), r1 = r0 + 8;
@@ -495,220 +507,302 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_d128_pp_kernel(const AttnPar
       voff1[dt] = VBASE + r1 * ROWB + (((colb >> 4) ^ swz_mask(r1)) << 4) + (colb & 15);
     }
   }
+  // fragment i of S = K Q^T: key block i / 8, d slice i % 8
+  auto k_frag = [&](const int ks, const int i) {
+    const uint32_t off = (i & 7) ? (kbase ^ ((uint32_t)(i & 7) << 5)) : kbase;
+    return *(const bf16x8*)(lds + off + ks + (i >> 3) * 32 * ROWB);
+  };
+  auto v_frag = [&](const int vs, const int gp, const int dt) {
+    const int off = vs + gp * 16 * ROWB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, lds + voff0[dt] + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, lds + voff1[dt] + off));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
 
   const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](const SegCursor& cur, int buf) {
+  // this wave's share of one K or V tile into LDS at dst
+  auto issue = [&](const char* base, int64_t rsb, const SegCursor& cur, uint32_t dst) {
     const int nvalid = (int)min<int64_t>(BK, cur.end - cur.row);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(cur.kp + cur.row * cur.ksb), 0, (int)(nvalid * cur.ksb), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(cur.vp + cur.row * cur.vsb), 0, (int)(nvalid * cur.vsb), 0x00020000);
-    const uint32_t kdst = lds0 + buf * TILEB;
-    const uint32_t vdst = lds0 + VBASE + buf * TILEB;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + cur.row * rsb), 0, (int)(nvalid * rsb), 0x00020000);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int lrow = (wave * LPW + i) * 4 + g16;
       const int row = lrow < nvalid ? lrow : nvalid - 1;  // rows past the end reload a valid row
-      const int chunk = swz(lrow, s16);
-      const uint32_t dst = (wave * LPW + i) * 1024;
-      lds_dma16(rk, kdst + dst, (int)(row * cur.ksb) + chunk * 16);
-      lds_dma16(rv, vdst + dst, (int)(row * cur.vsb) + chunk * 16);
+      lds_dma16(r, dst + (wave * LPW + i) * 1024, (int)(row * rsb) + swz(lrow, s16) * 16);
+    }
+  };
+  SegCursor kcur, vcur, ccur;
+  segc_seek(p, g, head, 0, job.kbeg, job.kend, kcur);
+  vcur = ccur = kcur;
+  // iteration i issues K_{i+4} and V_{i+2}
+  auto issue_iter = [&](int i) {
+    if (i + 4 < n_tiles) {
+      issue(kcur.kp, kcur.ksb, kcur, lds0 + ((i + 4) % NSLOT) * TILEB);
+      segc_next<BK>(p, g, head, job.kbeg, job.kend, kcur);
+    }
+    if (i + 2 >= 0 && i + 2 < n_tiles) {
+      issue(vcur.vp, vcur.vsb, vcur, lds0 + VBASE + ((i + 2) % NSLOT) * TILEB);
+      segc_next<BK>(p, g, head, job.kbeg, job.kend, vcur);
+    }
+  };
+  // end of iteration t: K_{t+2} and V_t must be in LDS; the loads of iterations
+  // t - 1 and t (K_{t+3}, V_{t+1}, K_{t+4}, V_{t+2}) may stay in flight
+  auto wait_iter = [&](int t) {
+    const int newer = (t + 3 < n_tiles) + (t + 1 < n_tiles && t + 1 >= 0) + (t + 4 < n_tiles) +
+                      (t + 2 < n_tiles && t + 2 >= 0);
+    switch (newer) {  // LPW load instructions per tile and tensor
+      case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPW)); break;
+      default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW)); break;
     }
   };
 
-  f32x16 o[DH / 32];
+  f32x16 o[QB][DH / 32];
 #pragma unroll
-  for (int i = 0; i < DH / 32; ++i) o[i] = (f32x16){};
-  f32x16 S[2];
-  bf16x8 P[4];
-  float m = -INFINITY, l_part = 0.0f;
-
-  SegCursor lcur, ccur;
-  segc_seek(p, g, head, 0, job.kbeg, job.kend, lcur);
-  ccur = lcur;
-  int issued = 0;
-  for (; issued < NBUF - 1 && issued < n_tiles; ++issued) {
-    issue(lcur, issued);
-    segc_next<BK>(p, g, head, job.kbeg, job.kend, lcur);
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int i = 0; i < DH / 32; ++i) o[qb][i] = (f32x16){};
+  f32x16 S[QB][2];  // [query block][key block]: S_t, then S_{t+1}
+  // P as packed bf16 pairs [buffer][query block][pair]; pairs 4g .. 4g+3 form
+  // the MFMA operand of key group g (32-bit words: the row sums read them one
+  // at a time)
+  uint32_t P[2][QB][16];
+  auto p_frag = [&](const int b, const int qb, const int gp) {
+    return __builtin_bit_cast(bf16x8, (u32x4){P[b][qb][4 * gp], P[b][qb][4 * gp + 1], P[b][qb][4 * gp + 2],
+                                              P[b][qb][4 * gp + 3]});
+  };
+  float m[QB], l_part[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l_part[qb] = 0.0f;
   }
-  auto wait_tile = [&](int u) {  // loads of tiles newer than u may stay in flight
-    if (issued - 1 - u <= 0)
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_TILE);
-  };
-  static_assert(NBUF == 4, "wait_tile covers one newer tile in flight");
-  if (n_tiles > 0) wait_tile(0);
-  __syncthreads();
 
-  // X_t with tile t in ring slot u
-  auto phase_x = [&](const int t, const int u) {
-    if (t >= 1) {  // O += V_{t-1}^T P_{t-1}^T, fragments read one key group ahead
-      const int vs = ((u + NBUF - 1) % NBUF) * TILEB;
-      bf16x8 fa[4], fb[4];
-      auto vfr = [&](int gp, int dt) {
-        const int off = vs + gp * 16 * ROWB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, lds + voff0[dt] + off));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, lds + voff1[dt] + off));
-        typedef short s16x8 __attribute__((ext_vector_type(8)));
-        const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return __builtin_bit_cast(bf16x8, v);
-      };
+  // P pair k of query block qb into P[b] (uses m)
+  auto exp_pair = [&](const int b, const int qb, const int k) {
+    const int blk = k >> 3, i = (k & 7) * 2;
+    P[b][qb][k] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(S[qb][blk][i], c, -m[qb])),
+                            __builtin_amdgcn_exp2f(fmaf(S[qb][blk][i + 1], c, -m[qb])));
+  };
+  // this lane's maximum over the 16 scores of key block blk of query block qb
+  auto blk_max = [&](const int qb, const int blk) {
+    float mx = S[qb][blk][0];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) fa[dt] = vfr(0, dt);
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][blk][i]);
+    return mx;
+  };
+  // Lazy re-basing, decided before P_t is formed from the tile's row maximum
+  // (lanes l and l + 32 hold the two key halves of one query): m is raised to
+  // the row maximum only when that exceeds m by more than kLazy (log2 units),
+  // so P stays below 2^kLazy and re-basing is rare after the first tile (m
+  // starts at -inf, so the first tile always re-bases).  Re-basing scales l at
+  // once and O after this iteration's PV product (which still uses P_{t-1},
+  // formed with the old m).  Returns whether any lane re-based.
+  constexpr float kLazy = 8.0f;
+  float alpha[QB];
+  auto decide = [&](const float (&mx_lane)[QB]) {
+    float mx[QB];
+    bool up[QB], any = false;
 #pragma unroll
-      for (int gp = 0; gp < 4; ++gp) {
-        bf16x8 (&cur)[4] = (gp & 1) ? fb : fa;
-        bf16x8 (&nxt)[4] = (gp & 1) ? fa : fb;
-        if (gp < 3) {
+    for (int qb = 0; qb < QB; ++qb) {
+      const auto r =
+          __builtin_amdgcn_permlane32_swap(__float_as_uint(mx_lane[qb]), __float_as_uint(mx_lane[qb]), false, false);
+      mx[qb] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * c;
+      up[qb] = mx[qb] - m[qb] > kLazy;
+      any = any || up[qb];
+    }
+    if (__any(any)) {
+      asm volatile("" ::: "memory");  // keep the rare path a branch (not speculated)
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) nxt[dt] = vfr(gp + 1, dt);
+      for (int qb = 0; qb < QB; ++qb) {
+        alpha[qb] = up[qb] ? __builtin_amdgcn_exp2f(m[qb] - mx[qb]) : 1.0f;  // 0 when m = -inf
+        m[qb] = up[qb] ? mx[qb] : m[qb];
+        l_part[qb] *= alpha[qb];
+      }
+      return true;
+    }
+    return false;
+  };
+  // Both halves of an iteration run 16 steps of QB MFMAs each (one per query
+  // block, sharing one K or V fragment); the fragment of step i is read LA
+  // steps ahead, and the last LA steps of half 1 read the first K fragments of
+  // half 2 (K_{t+1} has been in LDS since the last barrier).  Every iteration has this one form: iteration 0 multiplies a
+  // zeroed P_{-1} with a zeroed V slot, and scores of keys past the end of a
+  // segment (all keys of iteration n_tiles) are masked to -inf, which makes
+  // their P exactly 0.
+  float mx0[QB];  // this lane's maxima of key block 0 of S_{t+1}, taken in half 2
+  // half 1: step i = O^T += V^T P^T for key group i / 4, d-tile i % 4 (P_{t-1})
+  // on the matrix core; P_t pair i on the VALU
+  auto half1 = [&](const int vs, const int ks, const int cb, bf16x8(&kf)[16]) {
+    bf16x8 vf[16];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) vf[i] = v_frag(vs, i >> 2, i & 3);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + LA < 16) vf[i + LA] = v_frag(vs, (i + LA) >> 2, (i + LA) & 3);
+      else kf[i + LA - 16] = k_frag(ks, i + LA - 16);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        exp_pair(cb, qb, i);
+        o[qb][i & 3] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], p_frag(cb ^ 1, qb, i >> 2), o[qb][i & 3], 0, 0, 0);
+      }
+      // QB MFMAs, 2 LDS reads, 5 VALU per query block (2 FMA, 2 exp, pack); the
+      // step boundary keeps each read LA steps ahead of its MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 5 * QB, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P_t is formed here, not sunk past the re-basing branch into its users
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const uint32_t(&w)[16] = P[cb][qb];
+      asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]),
+                   "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // half 2: step i = S_{t+1} += K Q^T for key block i / 8, d slice i % 8 on the
+  // matrix core; row sum of P_t pair i on the VALU, and from step 10 (two
+  // MFMAs after block 0 is complete) the maximum of block 0
+  auto half2 = [&](const int ks, const int cb, bf16x8(&kf)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i == 10) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          mx0[qb] = blk_max(qb, 0);
+          asm volatile("" ::"v"(mx0[qb]));  // taken here, where the VALU is idle, not at its use
         }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[dt], P[gp], o[dt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
       }
+      if (i + LA < 16) kf[i + LA] = k_frag(ks, i + LA);
+      const int blk = i >> 3, sl = i & 7;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        l_part[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, P[cb][qb][i]),
+                                                     __builtin_bit_cast(bf16x2, 0x3f803f80u), l_part[qb], false);
+        S[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[qb][sl], sl == 0 ? (f32x16){} : S[qb][blk],
+                                                             0, 0, 0);
+      }
+      // QB MFMAs, 1 LDS read, the address XOR and a row sum per query block,
+      // then the block-0 maxima
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < 10) __builtin_amdgcn_sched_group_barrier(0x402, 1 + QB, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x402, 1 + 4 * QB, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (t < n_tiles) {  // S_t = K_t Q^T
-      const int ks = u * TILEB;
-      auto kfr = [&](int blk, int s) { return *(const bf16x8*)(lds + koff[s] + ks + blk * 32 * ROWB); };
-      bf16x8 fa[4], fb[4];
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Iteration t: ring slot u = t mod 4, P_t into buffer cb = t mod 2 (P_{t-1}
+  // is in buffer cb ^ 1).
+  auto run_iter = [&](const int t, const int u, const int cb) {
+    issue_iter(t);
+    int nv = 0;  // keys of tile t
+    if (t < n_tiles) {
+      nv = (int)min<int64_t>(BK, ccur.end - ccur.row);
+      segc_next<BK>(p, g, head, job.kbeg, job.kend, ccur);
+    }
+    if (nv < BK) {  // keys past the end of the segment score -inf
+      asm volatile("" ::: "memory");  // a branch, not a select in every iteration
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = kfr(0, i);
+      for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {  // groups of 4 (block, slice) pairs
-        bf16x8 (&cur)[4] = (q4 & 1) ? fb : fa;
-        bf16x8 (&nxt)[4] = (q4 & 1) ? fa : fb;
-        if (q4 < 3) {
+        for (int blk = 0; blk < 2; ++blk) {
+          const int lim = nv - blk * 32 - hh * 4;  // element i is key blk*32 + (i/4)*8 + hh*4 + i%4
 #pragma unroll
-          for (int i = 0; i < 4; ++i) nxt[i] = kfr((q4 + 1) >> 1, ((q4 + 1) & 1) * 4 + i);
+          for (int i = 0; i < 16; ++i)
+            S[qb][blk][i] = ((i >> 2) * 8 + (i & 3) < lim) ? S[qb][blk][i] : -INFINITY;
         }
-        const int blk = q4 >> 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = (q4 & 1) * 4 + i;
-          S[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[i], qf[s], s == 0 ? (f32x16){} : S[blk], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        mx0[qb] = blk_max(qb, 0);
       }
     }
-  };
-
-  // P = exp2(S c - m) packed to bf16 pairs; returns the OR of the pairs
-  auto exp_pack = [&](uint32_t (&w)[16]) {
-    uint32_t orr = 0;
+    // row maxima of S_t and the re-basing decision, before P_t is formed
+    float mx[QB];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int blk = k >> 3, i = (k & 7) * 2;
-      w[k] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(S[blk][i], c, -m)),
-                       __builtin_amdgcn_exp2f(fmaf(S[blk][i + 1], c, -m)));
-      orr |= w[k];
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(mx0[qb], blk_max(qb, 1));
+    const bool resc = decide(mx);
+    const int ks = ((u + 1) & 3) * TILEB, vs = ((u + 3) & 3) * TILEB;
+    bf16x8 kf[16];
+    half1(vs, ks, cb, kf);
+    if (resc) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) o[qb][dt] *= alpha[qb];
     }
-    return orr;
-  };
-
-  // Y_t on S_t
-  auto phase_y = [&]() {
-    const int nv = (int)min<int64_t>(BK, ccur.end - ccur.row);
-    segc_next<BK>(p, g, head, job.kbeg, job.kend, ccur);
-    if (nv < BK) {  // short last tile of a segment: keys past its end score -inf
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int lim = nv - blk * 32 - hh * 4;  // element i is key blk*32 + (i/4)*8 + hh*4 + i%4
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[blk][i] = ((i >> 2) * 8 + (i & 3) < lim) ? S[blk][i] : -INFINITY;
-      }
-    }
-    uint32_t w[16];
-    const uint32_t orr = exp_pack(w);
-    if (__any((orr & 0x40004000u) != 0u)) {
-      // some P >= 2 (or not finite), or the first tile: raise m to the row maxima
-      float mx = fmaxf(S[0][0], S[1][0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(S[0][i], S[1][i]));
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-      const float m_new = fmaxf(m, mx * c);
-      if (m_new > m) {
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 when m = -inf
-        m = m_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int i = 0; i < DH / 32; ++i) o[i] *= alpha;
-      }
-      exp_pack(w);
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
-                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), l_part, false);
-#pragma unroll
-    for (int gp = 0; gp < 4; ++gp) P[gp] = __builtin_bit_cast(bf16x8, (u32x4){w[4 * gp], w[4 * gp + 1],
-                                                                              w[4 * gp + 2], w[4 * gp + 3]});
-  };
-
-  auto issue_next = [&]() {
-    if (issued < n_tiles) {
-      issue(lcur, issued % NBUF);
-      segc_next<BK>(p, g, head, job.kbeg, job.kend, lcur);
-      ++issued;
-    }
-  };
-  // close phase ph; before closing an odd phase, tile (ph + 1) / 2 must be in LDS
-  auto end_phase = [&](const int ph) {
-    if ((ph & 1) == 1 && (ph + 1) / 2 < n_tiles) wait_tile((ph + 1) / 2);
+    half2(ks, cb, kf);
+    wait_iter(t);
     __syncthreads();
   };
-  // phases 0 .. 2 n_tiles + 1; every wave issues its share of the next tile at
-  // the start of each even phase >= 2
-  if (grp == 0) {
-    for (int t0 = 0; t0 <= n_tiles; t0 += NBUF) {
+
+  if (n_tiles > 0) {
+    // P_{-1} = 0 and a zeroed V slot 3 (read by iteration 0; first loaded by
+    // iteration 1, after iteration 0's closing barrier): iteration 0 adds 0 to O
 #pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        const int t = t0 + u;
-        if (t > n_tiles) break;
-        if (t >= 1) issue_next();
-        phase_x(t, u);
-        end_phase(2 * t);
-        if (t < n_tiles) phase_y();
-        end_phase(2 * t + 1);
-      }
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) P[1][qb][k] = 0u;
+    constexpr int ZB = TILEB / (WAVES * 64);  // bytes zeroed per thread
+    static_assert(ZB % 16 == 0, "V slot zeroing");
+#pragma unroll
+    for (int j = 0; j < ZB; j += 16) *(u32x4*)(lds + VBASE + 3 * TILEB + tid * ZB + j) = (u32x4){0, 0, 0, 0};
+    // prologue: iterations -4 .. -1 issue K_0..K_3, V_0, V_1; S_0 = K_0 Q^T
+    for (int i = -4; i < 0; ++i) issue_iter(i);
+    wait_iter(-1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int blk = i >> 3, sl = i & 7;
+      const bf16x8 kfr = k_frag(0, i);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        S[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[qb][sl], sl == 0 ? (f32x16){} : S[qb][blk],
+                                                             0, 0, 0);
     }
-  } else {
-    end_phase(0);
-    for (int t0 = 0; t0 <= n_tiles; t0 += NBUF) {
 #pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        const int t = t0 + u;
-        if (t > n_tiles) break;
-        phase_x(t, u);
-        end_phase(2 * t + 1);
-        if (t < n_tiles) {
-          issue_next();
-          phase_y();
-          end_phase(2 * t + 2);
-        }
-      }
+    for (int qb = 0; qb < QB; ++qb) mx0[qb] = blk_max(qb, 0);
+    __syncthreads();  // every wave has read K_0 before iteration 0 loads K_4 into its slot
+    // iterations 0 .. n_tiles, unrolled by the ring size
+    for (int t = 0;;) {
+      run_iter(t, 0, 0);
+      if (++t > n_tiles) break;
+      run_iter(t, 1, 1);
+      if (++t > n_tiles) break;
+      run_iter(t, 2, 0);
+      if (++t > n_tiles) break;
+      run_iter(t, 3, 1);
+      if (++t > n_tiles) break;
     }
   }
 
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
-  const float l_tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  if (qrow >= p.n_q) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  float* op = job.o + (qrow * p.H + head) * (int64_t)DH;
 #pragma unroll
-  for (int dt = 0; dt < DH / 32; ++dt) {
+  for (int qb = 0; qb < QB; ++qb) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[qb]), __float_as_uint(l_part[qb]), false, false);
+    const float l_tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const int64_t qrow = qrow0 + qb * 32;
+    if (qrow >= p.n_q) continue;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float* op = job.o + (qrow * p.H + head) * (int64_t)DH;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = dt * 32 + g4 * 8 + hh * 4;
-      f32x4 v = {o[dt][g4 * 4 + 0] * inv, o[dt][g4 * 4 + 1] * inv, o[dt][g4 * 4 + 2] * inv,
-                 o[dt][g4 * 4 + 3] * inv};
-      *(f32x4*)(op + d0) = v;
+    for (int dt = 0; dt < DH / 32; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = dt * 32 + g4 * 8 + hh * 4;
+        f32x4 v = {o[qb][dt][g4 * 4 + 0] * inv, o[qb][dt][g4 * 4 + 1] * inv, o[qb][dt][g4 * 4 + 2] * inv,
+                   o[qb][dt][g4 * 4 + 3] * inv};
+        *(f32x4*)(op + d0) = v;
+      }
     }
+    if (hh == 0) job.lse[qrow * p.H + head] = l_tot > 0.0f ? (m[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
   }
-  if (hh == 0) job.lse[qrow * p.H + head] = l_tot > 0.0f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // fp32 reference-precision path: one thread per (query, head, job).
@@ -816,7 +910,7 @@ ispa_status launch_merge(const MergeParams& p, hipStream_t stream) {
 }
 
 int attn_block_q(ispa_dtype dt, int32_t d) {
-  if (dt == ISPA_BF16 && d == 128) return pp::BQ;
+  if (dt == ISPA_BF16 && d == 128) return a5::BQ;
   return kBQ;
 }
 
@@ -946,7 +1040,7 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
   if (dt == ISPA_BF16) {
     const int64_t blocks = (int64_t)p.n_qtiles * H * nj;
     if (d == 128)
-      hipLaunchKernelGGL(attn_bf16_d128_pp_kernel, dim3((unsigned)blocks), dim3(512), 0, stream, p);
+      hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3((unsigned)blocks), dim3(a5::WAVES * 64), 0, stream, p);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {
