@@ -83,6 +83,43 @@ def test_dual_attn_bf16_parity(d, H, n_q, n_sink, n_hist, pad):
     assert np.abs(h64(l_h) - ref["lse_hist"]).max() <= 2e-3
 
 
+def _staircase_keys(steps, tail, H, d, u, seed):
+    """Keys whose score against queries along u climbs (or drops) by the
+    given log2 offsets tile by tile (64 keys per tile, `tail` keys after the
+    last full tile)."""
+    c = d ** -0.5 * math.log2(math.e)
+    n = 64 * len(steps) + tail
+    k = 0.5 * synth.normal((n, H, d), seed, DEV).float()
+    off = torch.tensor([steps[min(j // 64, len(steps) - 1)] for j in range(n)], device=DEV)
+    k += (off / (c * 4.0))[:, None, None] * u[None]
+    return k.to(torch.bfloat16)
+
+
+def test_dual_attn_rebase_schedule():
+    """Scores planted to step up tile by tile by more and by less than the
+    kernel's lazy re-basing margin, then drop and climb again, in both
+    groups: exercises re-basing on later tiles, P values up to 2^8 between
+    re-basings, and tiles far below the running maximum."""
+    print("dual_attn planted score staircase", flush=True)
+    H, d, n_q = 2, 128, 96
+    u = synth.normal((H, d), 41, DEV).float()
+    u = u / u.norm(dim=1, keepdim=True)
+    q = (0.5 * synth.normal((n_q, H, d), 42, DEV).float() + 4.0 * u[None]).to(torch.bfloat16)
+    steps_l = [0, 3, 12, 14, 40, 41, 20, 90, 91, 200, 0, 205, 210]
+    steps_h = [50, 7.9, 8.1, 60, 68.5, 0, 120, 127, 3]
+    kl, vl = _staircase_keys(steps_l, 20, H, d, u, 43), _cache(64 * len(steps_l) + 20, H, d, 44)
+    kh, vh = _staircase_keys(steps_h, 5, H, d, u, 45), _cache(64 * len(steps_h) + 5, H, d, 46)
+    o_l, l_l, o_h, l_h = K().ispa_dual_attn(q, [(kl[:300], vl[:300]), (kl[300:], vl[300:])], [(kh, vh)],
+                                            d ** -0.5)
+    torch.cuda.synchronize()
+    ref = O.dual_stream_attention(q.cpu(), kl.cpu(), vl.cpu(), kh.cpu(), vh.cpu(), d ** -0.5)
+    assert rel(h64(o_l), ref["o_loc"]) <= 5e-3
+    assert rel(h64(o_h), ref["o_hist"]) <= 5e-3
+    assert np.abs(h64(l_l) - ref["lse_loc"]).max() <= 2e-3
+    assert np.abs(h64(l_h) - ref["lse_hist"]).max() <= 2e-3
+    assert ref["lse_loc"].min() > 100  # the planted offsets dominate the scores
+
+
 def test_dual_attn_empty_history_and_zero_query():
     print("dual_attn empty history / zero query", flush=True)
     H, d, n = 2, 128, 150
