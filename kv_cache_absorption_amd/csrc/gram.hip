@@ -179,14 +179,46 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x16){};
 
+  // fragments of one 16-wide k slice of a stage: the wave's X rows and Y rows
+  auto frags = [&](int buf, int ks, u32x4 (&a)[4], u32x4 (&b)[NJ]) {
+    const char* xs = lds + buf * (XB + YB);
+    const char* ys = xs + XB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + lq;
+      a[i] = *(const u32x4*)(xs + row * ROWB + gswz(row, 2 * ks + hh) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int row = wn * WN + j * 32 + lq;
+      b[j] = *(const u32x4*)(ys + row * ROWB + gswz(row, 2 * ks + hh) * 16);
+    }
+  };
+  // acc[i][j] holds out^T for row block i and column block j (lane: row lq,
+  // columns (e/4)*8 + hh*4 + e%4)
+  auto mfmas = [&](const u32x4 (&a)[4], const u32x4 (&b)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma<MT>(b[j], a[i], acc[i][j]);
+  };
+
   int issued = 0, lbuf = 0;
   for (; issued < PD && issued < ns; ++issued) {
     issue(issued, lbuf);
     lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
   }
-  wait_stage(issued - 1);
-  __syncthreads();
-
+  // The MFMAs of one k slice run from registers while the next slice's
+  // fragments are read between them.  Per stage s: slice 0's MFMAs with slice 1
+  // read; the wait and barrier for stage s + 1; slice 1's MFMAs with stage
+  // s + 1's slice 0 read.  A slot refilled in iteration s held stage
+  // s + PD - NBUF = s - 2, last read in iteration s - 2 before its barrier.
+  u32x4 fa0[4], fb0[NJ], fa1[4], fb1[NJ];
+  if (ns > 0) {
+    wait_stage(issued - 1);
+    __syncthreads();
+    frags(0, 0, fa0, fb0);
+  }
   int cbuf = 0;
   for (int s = 0; s < ns; ++s) {
     if (issued < ns) {
@@ -194,37 +226,16 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
       lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
       ++issued;
     }
-    const char* xs = lds + cbuf * (XB + YB);
-    const char* ys = xs + XB;
-    auto frags = [&](int ks, u32x4 (&a)[4], u32x4 (&b)[NJ]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + lq;
-        a[i] = *(const u32x4*)(xs + row * ROWB + gswz(row, 2 * ks + hh) * 16);
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int row = wn * WN + j * 32 + lq;
-        b[j] = *(const u32x4*)(ys + row * ROWB + gswz(row, 2 * ks + hh) * 16);
-      }
-    };
-    u32x4 a0[4], b0[NJ], a1[4], b1[NJ];
-    frags(0, a0, b0);
-    frags(1, a1, b1);
-    // acc[i][j] holds out^T for row block i and column block j (lane: row lq,
-    // columns (e/4)*8 + hh*4 + e%4)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma<MT>(b0[j], a0[i], acc[i][j]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma<MT>(b1[j], a1[i], acc[i][j]);
-    // stage s+1 must be in LDS for the next iteration; newer ones may stay in flight
-    wait_stage(issued - (s + 2));
-    __syncthreads();
-    cbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;
+    frags(cbuf, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    const int nbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;
+    if (s + 1 < ns) {
+      wait_stage(issued - (s + 2));  // stage s + 1 is in LDS
+      __syncthreads();
+      frags(nbuf, 0, fa0, fb0);
+    }
+    mfmas(fa1, fb1);
+    cbuf = nbuf;
   }
 
   // ---- epilogues: lane holds out[m][n .. n+3] in acc[i][j][4 g .. 4 g + 3] with
@@ -259,7 +270,8 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    double* red = (double*)lds;  // the ring is idle after the last stage's barrier
+    double* red = (double*)lds;
+    __syncthreads();  // every wave is done with the ring
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     if (tid == 0) p.sq_partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
