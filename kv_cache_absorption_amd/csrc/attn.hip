@@ -326,10 +326,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // when it crosses into the next segment.
 struct SegCursor {
   int seg;
-  int64_t row, end;          // tile start row and one past the job's last row in this segment
-  const char* kp;            // row 0 of the segment, this head
-  const char* vp;
-  int64_t ksb, vsb;          // row strides in bytes
+  int64_t row, end;  // tile start row and one past the job's last row in this segment
 };
 
 __device__ __forceinline__ bool segc_seek(const AttnParams& p, int g, int head, int seg, int64_t kbeg,
@@ -343,10 +340,6 @@ __device__ __forceinline__ bool segc_seek(const AttnParams& p, int g, int head, 
       c.seg = s;
       c.row = a - st;
       c.end = b - st;
-      c.ksb = sg.ks * 2;
-      c.vsb = sg.vs * 2;
-      c.kp = (const char*)sg.k + (int64_t)head * 256;
-      c.vp = (const char*)sg.v + (int64_t)head * 256;
       return true;
     }
     st += sg.n;
@@ -508,11 +501,11 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     }
   }
   // fragment i of S = K Q^T: key block i / 8, d slice i % 8
-  auto k_frag = [&](const int ks, const int i) {
+  auto k_frag = [&](const int ks, const int i) __attribute__((always_inline)) {
     const uint32_t off = (i & 7) ? (kbase ^ ((uint32_t)(i & 7) << 5)) : kbase;
     return *(const bf16x8*)(lds + off + ks + (i >> 3) * 32 * ROWB);
   };
-  auto v_frag = [&](const int vs, const int gp, const int dt) {
+  auto v_frag = [&](const int vs, const int gp, const int dt) __attribute__((always_inline)) {
     const int off = vs + gp * 16 * ROWB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, lds + voff0[dt] + off));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, lds + voff1[dt] + off));
@@ -522,45 +515,112 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   };
 
   const uint32_t lds0 = lds_addr(lds);
-  // this wave's share of one K or V tile into LDS at dst
-  auto issue = [&](const char* base, int64_t rsb, const SegCursor& cur, uint32_t dst) {
-    const int nvalid = (int)min<int64_t>(BK, cur.end - cur.row);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + cur.row * rsb), 0, (int)(nvalid * rsb), 0x00020000);
+  // K and V tile streams over the job's rows.  Inside a segment every full tile
+  // takes the short path: a buffer descriptor over the tile's 64 rows, per-lane
+  // offsets fixed for the segment, one 64-bit pointer step and a countdown; a
+  // partial tile (its rows past the end reload a valid row) and the move to the
+  // next segment take the long path.
+  struct Stream {
+    SegCursor c;
+    const char* tile;  // first row of the next tile, this head
+    int64_t sb;        // row stride in bytes
+    int full;          // full tiles left from c.row in this segment
+    int voff[LPW];     // this lane's byte offsets inside a full tile
+  };
+  auto stream_init = [&](Stream& st, const bool is_v) __attribute__((always_inline)) {
+    const AttnSeg sg = p.segs[g][st.c.seg];  // segment pointers and strides, read on segment changes
+    st.sb = (is_v ? sg.vs : sg.ks) * 2;
+    st.tile = (const char*)(is_v ? sg.v : sg.k) + (int64_t)head * 256 + st.c.row * st.sb;
+    st.full = (int)((st.c.end - st.c.row) / BK);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int lrow = (wave * LPW + i) * 4 + g16;
-      const int row = lrow < nvalid ? lrow : nvalid - 1;  // rows past the end reload a valid row
-      lds_dma16(r, dst + (wave * LPW + i) * 1024, (int)(row * rsb) + swz(lrow, s16) * 16);
+      st.voff[i] = lrow * (int)st.sb + swz(lrow, s16) * 16;
     }
   };
-  SegCursor kcur, vcur, ccur;
-  segc_seek(p, g, head, 0, job.kbeg, job.kend, kcur);
-  vcur = ccur = kcur;
-  // iteration i issues K_{i+4} and V_{i+2}
-  auto issue_iter = [&](int i) {
-    if (i + 4 < n_tiles) {
-      issue(kcur.kp, kcur.ksb, kcur, lds0 + ((i + 4) % NSLOT) * TILEB);
-      segc_next<BK>(p, g, head, job.kbeg, job.kend, kcur);
-    }
-    if (i + 2 >= 0 && i + 2 < n_tiles) {
-      issue(vcur.vp, vcur.vsb, vcur, lds0 + VBASE + ((i + 2) % NSLOT) * TILEB);
-      segc_next<BK>(p, g, head, job.kbeg, job.kend, vcur);
-    }
+  // One tile load of this wave, prepared at the start of an iteration and issued
+  // (LPW instructions) in the middle of it: a buffer descriptor, this lane's
+  // byte offsets and the LDS destination.
+  struct Load {
+    __amdgpu_buffer_rsrc_t r;
+    int voff[LPW];
+    uint32_t dst;
   };
-  // end of iteration t: K_{t+2} and V_t must be in LDS; the loads of iterations
-  // t - 1 and t (K_{t+3}, V_{t+1}, K_{t+4}, V_{t+2}) may stay in flight
-  auto wait_iter = [&](int t) {
-    const int newer = (t + 3 < n_tiles) + (t + 1 < n_tiles && t + 1 >= 0) + (t + 4 < n_tiles) +
-                      (t + 2 < n_tiles && t + 2 >= 0);
-    switch (newer) {  // LPW load instructions per tile and tensor
-      case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-      case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW)); break;
-      case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW)); break;
-      case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPW)); break;
-      default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW)); break;
+  // the stream's next tile into LDS at dst (then advance); when `real` is false
+  // an empty descriptor stands in, so that every iteration issues the same
+  // number of loads (they write nothing that is read: their slot is free)
+  auto stream_prep = [&](Stream& st, const bool is_v, const uint32_t dst, const bool real) __attribute__((always_inline)) {
+    Load ld;
+    ld.dst = dst;
+    if (!real) {
+      ld.r = __builtin_amdgcn_make_buffer_rsrc((void*)st.tile, 0, 0, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) ld.voff[i] = 0;
+      return ld;
     }
+    if (st.full > 0) {
+      ld.r = __builtin_amdgcn_make_buffer_rsrc((void*)st.tile, 0, (int)(BK * st.sb), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) ld.voff[i] = st.voff[i];
+      st.tile += BK * st.sb;
+      st.c.row += BK;
+      if (--st.full == 0 && st.c.row >= st.c.end) {
+        asm volatile("" ::: "memory");  // the segment ends on a tile boundary: next segment
+        if (segc_seek(p, g, head, st.c.seg + 1, job.kbeg, job.kend, st.c)) stream_init(st, is_v);
+      }
+      return ld;
+    }
+    asm volatile("" ::: "memory");  // partial tile: rows past the end reload the last valid row
+    const int nvalid = (int)min<int64_t>(BK, st.c.end - st.c.row);
+    ld.r = __builtin_amdgcn_make_buffer_rsrc((void*)st.tile, 0, (int)(nvalid * st.sb), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int lrow = (wave * LPW + i) * 4 + g16;
+      const int row = lrow < nvalid ? lrow : nvalid - 1;
+      ld.voff[i] = (int)(row * st.sb) + swz(lrow, s16) * 16;
+    }
+    st.c.row += BK;
+    if (segc_seek(p, g, head, st.c.seg + 1, job.kbeg, job.kend, st.c)) stream_init(st, is_v);
+    return ld;
   };
+  auto issue_load = [&](const Load& ld, const int i) __attribute__((always_inline)) {
+    lds_dma16(ld.r, ld.dst + (wave * LPW + i) * 1024, ld.voff[i]);
+  };
+  Stream ks_, vs_;
+  SegCursor ccur;
+  int cfull = 0;  // full tiles left from ccur.row in its segment
+  segc_seek(p, g, head, 0, job.kbeg, job.kend, ccur);
+  ks_.c = vs_.c = ccur;
+  stream_init(ks_, false);
+  stream_init(vs_, true);
+  cfull = (int)((ccur.end - ccur.row) / BK);
+  // keys of the next tile in job order (64 for a full tile)
+  auto next_nv = [&]() __attribute__((always_inline)) {
+    if (cfull > 0) {
+      ccur.row += BK;
+      if (--cfull == 0 && ccur.row >= ccur.end) {
+        asm volatile("" ::: "memory");
+        if (segc_seek(p, g, head, ccur.seg + 1, job.kbeg, job.kend, ccur)) cfull = (int)((ccur.end - ccur.row) / BK);
+      }
+      return BK;
+    }
+    asm volatile("" ::: "memory");
+    const int nv = (int)(ccur.end - ccur.row);
+    ccur.row += BK;
+    if (segc_seek(p, g, head, ccur.seg + 1, job.kbeg, job.kend, ccur)) cfull = (int)((ccur.end - ccur.row) / BK);
+    return nv;
+  };
+  // Iteration i (prologue iterations -4 .. -1 included) loads K_{i+4} and, from
+  // i = -2 on, V_{i+2}, real or stand-in, so the load count is the same in every
+  // iteration.  At the end of iteration t, K_{t+2} and V_t (loaded in iteration
+  // t - 2) must be in LDS while the 4 * LPW loads of iterations t - 1 and t
+  // (K_{t+3}, V_{t+1}, K_{t+4}, V_{t+2}) may stay in flight; loads complete in
+  // issue order.
+  auto prep_k = [&](int i) __attribute__((always_inline)) { return stream_prep(ks_, false, lds0 + ((i + 4) % NSLOT) * TILEB, i + 4 < n_tiles); };
+  auto prep_v = [&](int i) __attribute__((always_inline)) {
+    return stream_prep(vs_, true, lds0 + VBASE + ((i + 2) % NSLOT) * TILEB, i + 2 < n_tiles);
+  };
+  auto wait_iter = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW)); };
 
   f32x16 o[QB][DH / 32];
 #pragma unroll
@@ -572,7 +632,7 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   // the MFMA operand of key group g (32-bit words: the row sums read them one
   // at a time)
   uint32_t P[2][QB][16];
-  auto p_frag = [&](const int b, const int qb, const int gp) {
+  auto p_frag = [&](const int b, const int qb, const int gp) __attribute__((always_inline)) {
     return __builtin_bit_cast(bf16x8, (u32x4){P[b][qb][4 * gp], P[b][qb][4 * gp + 1], P[b][qb][4 * gp + 2],
                                               P[b][qb][4 * gp + 3]});
   };
@@ -584,13 +644,13 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   }
 
   // P pair k of query block qb into P[b] (uses m)
-  auto exp_pair = [&](const int b, const int qb, const int k) {
+  auto exp_pair = [&](const int b, const int qb, const int k) __attribute__((always_inline)) {
     const int blk = k >> 3, i = (k & 7) * 2;
     P[b][qb][k] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(S[qb][blk][i], c, -m[qb])),
                             __builtin_amdgcn_exp2f(fmaf(S[qb][blk][i + 1], c, -m[qb])));
   };
   // this lane's maximum over the 16 scores of key block blk of query block qb
-  auto blk_max = [&](const int qb, const int blk) {
+  auto blk_max = [&](const int qb, const int blk) __attribute__((always_inline)) {
     float mx = S[qb][blk][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][blk][i]);
@@ -638,7 +698,7 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   float mx0[QB];  // this lane's maxima of key block 0 of S_{t+1}, taken in half 2
   // half 1: step i = O^T += V^T P^T for key group i / 4, d-tile i % 4 (P_{t-1})
   // on the matrix core; P_t pair i on the VALU
-  auto half1 = [&](const int vs, const int ks, const int cb, bf16x8(&kf)[16]) {
+  auto half1 = [&](const int vs, const int ks, const int cb, bf16x8(&kf)[16]) __attribute__((always_inline)) {
     bf16x8 vf[16];
 #pragma unroll
     for (int i = 0; i < LA; ++i) vf[i] = v_frag(vs, i >> 2, i & 3);
@@ -670,10 +730,18 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   };
   // half 2: step i = S_{t+1} += K Q^T for key block i / 8, d slice i % 8 on the
   // matrix core; row sum of P_t pair i on the VALU, and from step 10 (two
-  // MFMAs after block 0 is complete) the maximum of block 0
-  auto half2 = [&](const int ks, const int cb, bf16x8(&kf)[16]) {
+  // MFMAs after block 0 is complete) the maximum of block 0.  The iteration's
+  // loads are issued here, spread over the half so that the waves do not queue
+  // behind each other on the load path.
+  auto half2 = [&](const int ks, const int cb, bf16x8(&kf)[16], const Load& lk, const Load& lv)
+                   __attribute__((always_inline)) {
+    static_assert(LPW == 2, "load placement in half 2");
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      if (i == 1) issue_load(lk, 0);
+      if (i == 5) issue_load(lk, 1);
+      if (i == 9) issue_load(lv, 0);
+      if (i == 13) issue_load(lv, 1);
       if (i == 10) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -703,13 +771,9 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
 
   // Iteration t: ring slot u = t mod 4, P_t into buffer cb = t mod 2 (P_{t-1}
   // is in buffer cb ^ 1).
-  auto run_iter = [&](const int t, const int u, const int cb) {
-    issue_iter(t);
-    int nv = 0;  // keys of tile t
-    if (t < n_tiles) {
-      nv = (int)min<int64_t>(BK, ccur.end - ccur.row);
-      segc_next<BK>(p, g, head, job.kbeg, job.kend, ccur);
-    }
+  auto run_iter = [&](const int t, const int u, const int cb) __attribute__((always_inline)) {
+    const Load lk = prep_k(t), lv = prep_v(t);
+    const int nv = t < n_tiles ? next_nv() : 0;  // keys of tile t
     if (nv < BK) {  // keys past the end of the segment score -inf
       asm volatile("" ::: "memory");  // a branch, not a select in every iteration
 #pragma unroll
@@ -738,11 +802,10 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
 #pragma unroll
         for (int dt = 0; dt < DH / 32; ++dt) o[qb][dt] *= alpha[qb];
     }
-    half2(ks, cb, kf);
-    wait_iter(t);
+    half2(ks, cb, kf, lk, lv);
+    wait_iter();
     __syncthreads();
   };
-
   if (n_tiles > 0) {
     // P_{-1} = 0 and a zeroed V slot 3 (read by iteration 0; first loaded by
     // iteration 1, after iteration 0's closing barrier): iteration 0 adds 0 to O
@@ -755,8 +818,17 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
 #pragma unroll
     for (int j = 0; j < ZB; j += 16) *(u32x4*)(lds + VBASE + 3 * TILEB + tid * ZB + j) = (u32x4){0, 0, 0, 0};
     // prologue: iterations -4 .. -1 issue K_0..K_3, V_0, V_1; S_0 = K_0 Q^T
-    for (int i = -4; i < 0; ++i) issue_iter(i);
-    wait_iter(-1);
+    for (int i = -4; i < 0; ++i) {
+      const Load lk = prep_k(i);
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) issue_load(lk, j);
+      if (i + 2 >= 0) {
+        const Load lv = prep_v(i);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) issue_load(lv, j);
+      }
+    }
+    wait_iter();  // K_0 and K_1 are in LDS
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -781,6 +853,7 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
       run_iter(t, 3, 1);
       if (++t > n_tiles) break;
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS write in flight when the workgroup ends
   }
 
 #pragma unroll
