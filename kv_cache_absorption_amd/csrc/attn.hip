@@ -649,6 +649,13 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     P[b][qb][k] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(S[qb][blk][i], c, -m[qb])),
                             __builtin_amdgcn_exp2f(fmaf(S[qb][blk][i + 1], c, -m[qb])));
   };
+  // the same in two parts, so that the pack of pair k can go one step after its
+  // exps (a VALU use right after a transcendental costs a wait state)
+  auto exp_two = [&](const int qb, const int k, float (&e)[2]) __attribute__((always_inline)) {
+    const int blk = k >> 3, i = (k & 7) * 2;
+    e[0] = __builtin_amdgcn_exp2f(fmaf(S[qb][blk][i], c, -m[qb]));
+    e[1] = __builtin_amdgcn_exp2f(fmaf(S[qb][blk][i + 1], c, -m[qb]));
+  };
   // this lane's maximum over the 16 scores of key block blk of query block qb
   auto blk_max = [&](const int qb, const int blk) __attribute__((always_inline)) {
     float mx = S[qb][blk][0];
@@ -702,13 +709,16 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     bf16x8 vf[16];
 #pragma unroll
     for (int i = 0; i < LA; ++i) vf[i] = v_frag(vs, i >> 2, i & 3);
+    float e[2][QB][2];  // exps of pairs i (buffer i & 1), packed in step i + 1
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + LA < 16) vf[i + LA] = v_frag(vs, (i + LA) >> 2, (i + LA) & 3);
       else kf[i + LA - 16] = k_frag(ks, i + LA - 16);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        exp_pair(cb, qb, i);
+        exp_two(qb, i, e[i & 1][qb]);
+        if (i > 0) P[cb][qb][i - 1] = pack_bf16(e[(i - 1) & 1][qb][0], e[(i - 1) & 1][qb][1]);
+        if (i == 15) P[cb][qb][15] = pack_bf16(e[1][qb][0], e[1][qb][1]);
         o[qb][i & 3] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], p_frag(cb ^ 1, qb, i >> 2), o[qb][i & 3], 0, 0, 0);
       }
