@@ -437,6 +437,9 @@ static_assert(2 * NSLOT * TILEB <= 160 * 1024, "LDS budget");
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 }  // namespace a5
 
+// kRuns: every job covers at most two runs of consecutive rows (one run per
+// segment it overlaps); tile addresses are then computed from the tile index.
+template <bool kRuns>
 __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const AttnParams p) {
   using namespace a5;
   __shared__ __attribute__((aligned(1024))) char lds[2 * NSLOT * TILEB];
@@ -595,7 +598,7 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   stream_init(vs_, true);
   cfull = (int)((ccur.end - ccur.row) / BK);
   // keys of the next tile in job order (64 for a full tile)
-  auto next_nv = [&]() __attribute__((always_inline)) {
+  auto next_nv_stream = [&]() __attribute__((always_inline)) {
     if (cfull > 0) {
       ccur.row += BK;
       if (--cfull == 0 && ccur.row >= ccur.end) {
@@ -610,15 +613,85 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     if (segc_seek(p, g, head, ccur.seg + 1, job.kbeg, job.kend, ccur)) cfull = (int)((ccur.end - ccur.row) / BK);
     return nv;
   };
+
+  // Two-run addressing: run r of the job starts at row base (this head) with
+  // `tiles` tiles, the last holding `tail` keys.  The load of a tile is a few
+  // scalar selects and one multiply; rows past the run's end reload its last
+  // row (a per-lane min), and tiles past the job's end get an empty descriptor.
+  struct Run {
+    const char* k;
+    const char* v;
+    int ksb, vsb, tiles, tail;
+  };
+  Run r0{}, r1{};
+  if constexpr (kRuns) {
+    int64_t st = 0;
+    int nr = 0;
+    for (int s = 0; s < p.n_segs[g]; ++s) {
+      const AttnSeg sg = p.segs[g][s];
+      const int64_t a = job.kbeg > st ? job.kbeg : st;
+      const int64_t b = job.kend < st + sg.n ? job.kend : st + sg.n;
+      if (a < b) {
+        Run r;
+        r.ksb = (int)(sg.ks * 2);
+        r.vsb = (int)(sg.vs * 2);
+        r.k = (const char*)sg.k + (int64_t)head * 256 + (a - st) * r.ksb;
+        r.v = (const char*)sg.v + (int64_t)head * 256 + (a - st) * r.vsb;
+        r.tiles = (int)((b - a + BK - 1) / BK);
+        r.tail = (int)(b - a) - (r.tiles - 1) * BK;
+        if (nr == 0) r0 = r;
+        else r1 = r;  // the host launches this form only for jobs of at most two runs
+        ++nr;
+      }
+      st += sg.n;
+    }
+  }
+  int swzo[LPW];  // this lane's chunk offset in its load rows
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) swzo[i] = swz((wave * LPW + i) * 4 + g16, s16) * 16;
+  // keys of tile `tile` of the job (0 past its end)
+  auto run_nv = [&](const int tile) __attribute__((always_inline)) {
+    const bool in1 = tile >= r0.tiles;
+    const int tr = in1 ? tile - r0.tiles : tile;
+    const int nv = tr < (in1 ? r1.tiles : r0.tiles) - 1 ? BK : (in1 ? r1.tail : r0.tail);
+    return tile < n_tiles ? nv : 0;
+  };
+  auto run_load = [&](const int tile, const bool is_v, const uint32_t dst) __attribute__((always_inline)) {
+    const bool in1 = tile >= r0.tiles;
+    const int tr = in1 ? tile - r0.tiles : tile;
+    const char* base = is_v ? (in1 ? r1.v : r0.v) : (in1 ? r1.k : r0.k);
+    const int sb = is_v ? (in1 ? r1.vsb : r0.vsb) : (in1 ? r1.ksb : r0.ksb);
+    const int nv = run_nv(tile);
+    Load ld;
+    ld.dst = dst;
+    ld.r = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)tr * (BK * sb)), 0, nv * sb, 0x00020000);
+    const int lastrow = nv > 0 ? nv - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int lrow = (wave * LPW + i) * 4 + g16;
+      ld.voff[i] = min(lrow, lastrow) * sb + swzo[i];
+    }
+    return ld;
+  };
+  auto next_nv = [&](const int t) __attribute__((always_inline)) {
+    if constexpr (kRuns) return run_nv(t);
+    else return t < n_tiles ? next_nv_stream() : 0;
+  };
   // Iteration i (prologue iterations -4 .. -1 included) loads K_{i+4} and, from
   // i = -2 on, V_{i+2}, real or stand-in, so the load count is the same in every
   // iteration.  At the end of iteration t, K_{t+2} and V_t (loaded in iteration
   // t - 2) must be in LDS while the 4 * LPW loads of iterations t - 1 and t
   // (K_{t+3}, V_{t+1}, K_{t+4}, V_{t+2}) may stay in flight; loads complete in
   // issue order.
-  auto prep_k = [&](int i) __attribute__((always_inline)) { return stream_prep(ks_, false, lds0 + ((i + 4) % NSLOT) * TILEB, i + 4 < n_tiles); };
+  auto prep_k = [&](int i) __attribute__((always_inline)) {
+    const uint32_t dst = lds0 + ((i + 4) % NSLOT) * TILEB;
+    if constexpr (kRuns) return run_load(i + 4, false, dst);
+    else return stream_prep(ks_, false, dst, i + 4 < n_tiles);
+  };
   auto prep_v = [&](int i) __attribute__((always_inline)) {
-    return stream_prep(vs_, true, lds0 + VBASE + ((i + 2) % NSLOT) * TILEB, i + 2 < n_tiles);
+    const uint32_t dst = lds0 + VBASE + ((i + 2) % NSLOT) * TILEB;
+    if constexpr (kRuns) return run_load(i + 2, true, dst);
+    else return stream_prep(vs_, true, dst, i + 2 < n_tiles);
   };
   auto wait_iter = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW)); };
 
@@ -783,7 +856,7 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   // is in buffer cb ^ 1).
   auto run_iter = [&](const int t, const int u, const int cb) __attribute__((always_inline)) {
     const Load lk = prep_k(t), lv = prep_v(t);
-    const int nv = t < n_tiles ? next_nv() : 0;  // keys of tile t
+    const int nv = next_nv(t);  // keys of tile t
     if (nv < BK) {  // keys past the end of the segment score -inf
       asm volatile("" ::: "memory");  // a branch, not a select in every iteration
 #pragma unroll
@@ -1117,13 +1190,24 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
     return (a.ke - a.kb) > (b.ke - b.kb);
   });
   p.n_jobs = nj;
+  bool two_runs = true;  // every job overlaps at most two segments
   for (int j = 0; j < nj; ++j) {
     p.jobs[j] = AttnJob{pend[j].g, 0, pend[j].kb, pend[j].ke, pend[j].o, pend[j].lse};
+    int runs = 0;
+    int64_t st = 0;
+    for (int sg = 0; sg < p.n_segs[pend[j].g]; ++sg) {
+      const int64_t n = p.segs[pend[j].g][sg].n;
+      if (std::max(pend[j].kb, st) < std::min(pend[j].ke, st + n)) ++runs;
+      st += n;
+    }
+    two_runs = two_runs && runs <= 2;
   }
   if (dt == ISPA_BF16) {
     const int64_t blocks = (int64_t)p.n_qtiles * H * nj;
-    if (d == 128)
-      hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3((unsigned)blocks), dim3(a5::WAVES * 64), 0, stream, p);
+    if (d == 128 && two_runs)
+      hipLaunchKernelGGL(attn_bf16_d128_kernel<true>, dim3((unsigned)blocks), dim3(a5::WAVES * 64), 0, stream, p);
+    else if (d == 128)
+      hipLaunchKernelGGL(attn_bf16_d128_kernel<false>, dim3((unsigned)blocks), dim3(a5::WAVES * 64), 0, stream, p);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {

@@ -83,6 +83,28 @@ def test_dual_attn_bf16_parity(d, H, n_q, n_sink, n_hist, pad):
     assert np.abs(h64(l_h) - ref["lse_hist"]).max() <= 2e-3
 
 
+def test_dual_attn_many_segments():
+    """Groups of three and four segments with ragged lengths: jobs over more
+    than two segments take the general tile streams (segment changes inside a
+    job), the others the two-run addressing."""
+    print("dual_attn many segments", flush=True)
+    H, d, n_q = 2, 128, 300
+    q = _cache(n_q, H, d, 51)
+    lens_l, lens_h = [100, 64, 333], [1, 700, 129, 64]
+    ks = [_cache(n, H, d, 60 + i) for i, n in enumerate(lens_l)]
+    vs = [_cache(n, H, d, 70 + i) for i, n in enumerate(lens_l)]
+    kh = [_cache(n, H, d, 80 + i) + 0.5 for i, n in enumerate(lens_h)]
+    vh = [_cache(n, H, d, 90 + i) for i, n in enumerate(lens_h)]
+    o_l, l_l, o_h, l_h = K().ispa_dual_attn(q, list(zip(ks, vs)), list(zip(kh, vh)), d ** -0.5)
+    torch.cuda.synchronize()
+    ref = O.dual_stream_attention(q.cpu(), torch.cat(ks).cpu(), torch.cat(vs).cpu(), torch.cat(kh).cpu(),
+                                  torch.cat(vh).cpu(), d ** -0.5)
+    assert rel(h64(o_l), ref["o_loc"]) <= 5e-3
+    assert rel(h64(o_h), ref["o_hist"]) <= 5e-3
+    assert np.abs(h64(l_l) - ref["lse_loc"]).max() <= 2e-3
+    assert np.abs(h64(l_h) - ref["lse_hist"]).max() <= 2e-3
+
+
 def _staircase_keys(steps, tail, H, d, u, seed):
     """Keys whose score against queries along u climbs (or drops) by the
     given log2 offsets tile by tile (64 keys per tile, `tail` keys after the
