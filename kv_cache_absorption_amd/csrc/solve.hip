@@ -2,16 +2,19 @@
 //
 // The closed form dW = (A_loc^T A_loc + lambda I)^-1 A_loc^T (A_full - A_loc) W
 // (DE summary, Methodik) is evaluated as a blocked right-looking Cholesky
-// factorisation G + lambda I = L L^T with 64 x 64 blocks, followed by block
-// forward and backward substitution for all D right-hand sides.  Each step of
-// the factorisation is three launches, all batched over layers:
-//   potrf : factor the diagonal block in LDS and form its triangular inverse
-//   trsm  : panel blocks L_ik = A_ik L_kk^-T  (block product with the inverse)
-//   syrk  : trailing blocks A_ij -= L_ik L_jk^T
-// and each substitution step is two launches (diagonal block, then update of
-// the remaining block rows).  eps uses the identity that holds at the ridge
-// optimum, eps = r2 - <dW, C> - lambda ||dW||^2 (from G dW = C - lambda dW),
-// which is ||A_loc dW - R||^2 without the penalty (EN review, Key Design 2).
+// factorisation G + lambda I = L L^T with 64 x 64 blocks and block forward and
+// backward substitution for all D right-hand sides, every launch batched over
+// layers.  Per block column kb there are two launches: the panel (L_ik =
+// A_ik inv(L_kk)^T, and the forward diagonal step on X's block row kb) and the
+// update (trailing A_ij -= L_ik L_jk^T, forward X_ij -= L_ik X_kb,j, and the
+// factorisation of the next diagonal block by the workgroup that updates it).
+// The backward substitution is one launch per block row, whose workgroups of
+// block row kb - 1 also apply inv(L)^T of that row right after its last
+// update.  Block products are 64 x 64 x 64 fp64 MFMA tiles from LDS; a
+// diagonal block is turned into inv(L_kk) by one wave (chol_inv64).  eps uses
+// the identity that holds at the ridge optimum, eps = r2 - <dW, C> -
+// lambda ||dW||^2 (from G dW = C - lambda dW), which is ||A_loc dW - R||^2
+// without the penalty (EN review, Key Design 2).
 #include <cmath>
 
 #include "common.hpp"
@@ -83,170 +86,240 @@ __global__ void fill_kernel(int D, const float* G, const float* C, int64_t ms, c
   }
 }
 
-// Factor diagonal block kb of every layer and write its inverse.
-__global__ __launch_bounds__(256) void potrf_kernel(int D, int kb, double* Aall, double* Liall,
-                                                    int32_t* info) {
-  __shared__ double a[NB][NB + 1];
-  __shared__ int failed;
-  const int l = blockIdx.x;
-  const int tid = threadIdx.x;
-  double* A = Aall + (int64_t)l * D * D;
-  const int64_t base = (int64_t)kb * NB * D + (int64_t)kb * NB;
-  for (int e = tid; e < NB * NB; e += 256) a[e / NB][e % NB] = A[base + (int64_t)(e / NB) * D + e % NB];
-  if (tid == 0) failed = 0;
-  __syncthreads();
-  for (int j = 0; j < NB; ++j) {
-    const double piv = a[j][j];
-    if (!(piv > 0.0)) {
-      if (tid == 0) {
-        failed = 1;
-        if (info[l] == 0) info[l] = kb * NB + j + 1;
-      }
-      break;
-    }
-    const double d = sqrt(piv);
-    __syncthreads();
-    if (tid == 0) a[j][j] = d;
-    for (int i = j + 1 + tid; i < NB; i += 256) a[i][j] /= d;
-    __syncthreads();
-    const int m = NB - 1 - j;  // trailing size
-    const int cnt = m * (m + 1) / 2;
-    for (int idx = tid; idx < cnt; idx += 256) {
-      // row r (0..m-1), col c (0..r) of the trailing lower triangle
-      int r = (int)((sqrt(8.0 * idx + 1.0) - 1.0) * 0.5);
-      while (r * (r + 1) / 2 > idx) --r;
-      while ((r + 1) * (r + 2) / 2 <= idx) ++r;
-      const int c = idx - r * (r + 1) / 2;
-      const int i = j + 1 + r, k = j + 1 + c;
-      a[i][k] -= a[i][j] * a[k][j];
-    }
-    __syncthreads();
-  }
-  __syncthreads();
-  if (failed) {
-    // leave NaN so every later product of this layer is NaN
-    for (int e = tid; e < NB * NB; e += 256) A[base + (int64_t)(e / NB) * D + e % NB] = NAN;
-    double* Li = Liall + (int64_t)l * D * NB + (int64_t)kb * NB * NB;
-    for (int e = tid; e < NB * NB; e += 256) Li[e] = NAN;
-    return;
-  }
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, k = e % NB;
-    A[base + (int64_t)i * D + k] = k <= i ? a[i][k] : 0.0;
-  }
-  if (tid < NB) {
-    // column tid of L^-1 by forward substitution on e_tid
-    double x[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      double s = (i == tid) ? 1.0 : 0.0;
-#pragma unroll
-      for (int t = 0; t < i; ++t) s -= a[i][t] * x[t];
-      x[i] = s / a[i][i];
-    }
-    double* Li = Liall + (int64_t)l * D * NB + (int64_t)kb * NB * NB;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) Li[i * NB + tid] = x[i];
-  }
-}
+// ---- 64 x 64 fp64 blocks in LDS (row pitch LDP doubles) and their MFMA product
 
-enum { kTrsm = 0, kSyrk = 1, kFwdDiag = 2, kFwdUpd = 3, kBwdDiag = 4, kBwdUpd = 5 };
+constexpr int LDP = NB + 1;  // pitch: the 16 rows of an A fragment fall in distinct banks
 
 struct BlockOp {
   const double* p;  // block top-left
   int64_t ld;
-  int trans;        // operand element (i, k) = p[k*ld + i] if trans else p[i*ld + k]
+  int trans;        // element (r, c) = p[c*ld + r] if trans else p[r*ld + c]
 };
 
-// Out (64 x 64, ld) = [Out -] Aop Bop, K = 64.
-__device__ void block_product(BlockOp A, BlockOp B, double* out, int64_t ld_out, bool subtract) {
-  __shared__ double as[NB][33];
-  __shared__ double bs[32][NB + 1];
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
-  double acc[4][4];
+// dst[r][c] = element (r, c) of o; global reads run along o's contiguous dimension
+__device__ __forceinline__ void stage(double* dst, BlockOp o) {
+  const int t = threadIdx.x;
+  const int u = t & 63, v0 = t >> 6;
+  double x[NB / 4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
-  for (int kh = 0; kh < 2; ++kh) {
-    for (int e = tid; e < NB * 32; e += 256) {
-      const int i = e >> 5, k = e & 31;
-      const int kk = kh * 32 + k;
-      as[i][k] = A.trans ? A.p[(int64_t)kk * A.ld + i] : A.p[(int64_t)i * A.ld + kk];
-    }
-    for (int e = tid; e < 32 * NB; e += 256) {
-      const int k = e >> 6, j = e & 63;
-      const int kk = kh * 32 + k;
-      bs[k][j] = B.trans ? B.p[(int64_t)j * B.ld + kk] : B.p[(int64_t)kk * B.ld + j];
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = as[ty + 16 * r][k];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = bs[k][tx + 16 * c];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = fma(av[r], bv[c], acc[r][c]);
-    }
-    __syncthreads();
+  for (int it = 0; it < NB / 4; ++it) {
+    const int v = v0 + 4 * it;
+    x[it] = o.p[(int64_t)v * o.ld + u];
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      double* o = out + (int64_t)(ty + 16 * r) * ld_out + tx + 16 * c;
-      *o = subtract ? *o - acc[r][c] : acc[r][c];
-    }
+  for (int it = 0; it < NB / 4; ++it) {
+    const int v = v0 + 4 * it;
+    if (o.trans)
+      dst[u * LDP + v] = x[it];
+    else
+      dst[v * LDP + u] = x[it];
+  }
 }
 
-__global__ __launch_bounds__(256) void block_step_kernel(int kind, int D, int kb, double* Aall,
-                                                         double* Xall, const double* Liall) {
+// acc = As * Bs for this wave's 32 x 32 quadrant, as 2 x 2 tiles of
+// v_mfma_f64_16x16x4 (A fragment: lane holds A[l % 16][l / 16]; B fragment:
+// B[l / 16][l % 16]; result element e of lane l: row l / 16 + 4 e, column l % 16)
+__device__ __forceinline__ void mma64(const double* As, const double* Bs, f64x4 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = (wave >> 1) * 32, c0 = (wave & 1) * 32, li = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f64x4){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ks = 0; ks < NB / 4; ++ks) {
+    const double a0 = As[(r0 + li) * LDP + 4 * ks + lk];
+    const double a1 = As[(r0 + 16 + li) * LDP + 4 * ks + lk];
+    const double b0 = Bs[(4 * ks + lk) * LDP + c0 + li];
+    const double b1 = Bs[(4 * ks + lk) * LDP + c0 + 16 + li];
+    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+// Visit this lane's product elements: f(row, col, value)
+template <class F>
+__device__ __forceinline__ void for_acc(const f64x4 (&acc)[2][2], F f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = (wave >> 1) * 32, c0 = (wave & 1) * 32, li = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f(r0 + 16 * ti + lk + 4 * e, c0 + 16 * tj + li, acc[ti][tj][e]);
+}
+
+// out (global, ld) = acc, or out - acc
+__device__ __forceinline__ void store_block(const f64x4 (&acc)[2][2], double* out, int64_t ld, bool subtract) {
+  for_acc(acc, [&](int r, int c, double v) {
+    double* o = out + (int64_t)r * ld + c;
+    *o = subtract ? *o - v : v;
+  });
+}
+
+// dst (LDS) = old (global) - acc
+__device__ __forceinline__ void sub_to_lds(const f64x4 (&acc)[2][2], const double* old, int64_t ld, double* dst) {
+  for_acc(acc, [&](int r, int c, double v) { dst[r * LDP + c] = old[(int64_t)r * ld + c] - v; });
+}
+
+// Inverse of the Cholesky factor of the SPD 64 x 64 block M (LDS), by one wave.
+//
+// Lane a holds column a of the block in registers and eliminates below the
+// diagonal one pivot at a time (right-looking, symmetric Schur complements,
+// so the multipliers of step j are row j, which every lane publishes to LDS).
+// When step j reaches its own column, lane j stops updating: its remaining
+// entries are then column j of the inverse unit factor times -pivot_j, and the
+// later steps update them with the same formula as the matrix columns.  Pivot
+// j of the elimination is the squared diagonal of the Cholesky factor, so
+// inv(L)[i][a] = E[i][a] / sqrt(pivot_i) with E the inverse unit factor.
+// rows: 64 x 64 doubles of LDS.  Writes Li (row-major, 64 wide); returns the
+// first non-positive pivot (1-based) or 0.
+__device__ __forceinline__ int chol_inv64(const double* M, double* rows, double* Li) {
+  const int a = threadIdx.x & 63;
+  double c[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) c[i] = M[i * LDP + a];
+  int bad = 0;
+  rows[a] = c[0];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const double* rj = rows + j * NB;
+    const double piv = rj[j];
+    if (!(piv > 0.0) && bad == 0) bad = j + 1;
+    const double s = a == j ? 0.0 : c[j] / piv;
+    if (j + 1 < NB) {
+      // the next pivot row first, so its publication overlaps this step's tail
+      c[j + 1] = fma(-rj[j + 1], s, c[j + 1]);
+      rows[(j + 1) * NB + a] = c[j + 1];
+    }
+#pragma unroll
+    for (int i = j + 2; i < NB; ++i) c[i] = fma(-rj[i], s, c[i]);
+  }
+  const double pa = rows[a * NB + a];
+  const double ea = -1.0 / pa;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const double isq = 1.0 / sqrt(rows[i * NB + i]);
+    double v = i < a ? 0.0 : (i == a ? isq : c[i] * ea * isq);
+    Li[i * NB + a] = bad ? NAN : v;
+  }
+  return bad;
+}
+
+// factor the block in As (wave 0 only) and record the first failing pivot
+__device__ __forceinline__ void factor_block(const double* As, double* Bs, double* Li, int32_t* info, int base) {
+  if (threadIdx.x >= 64) return;
+  const int bad = chol_inv64(As, Bs, Li);
+  if (bad && threadIdx.x == 0 && *info == 0) *info = base + bad;
+}
+
+enum { kPotrf0 = 0, kPanel = 1, kUpdate = 2, kBwd = 3 };
+
+// One launch of the blocked solve, batched over layers (blockIdx.y).
+//   kPotrf0      : inv(L_00)
+//   kPanel  (kb) : L_ik = A_ik inv(L_kk)^T for i > kb, and the forward diagonal
+//                  step X_kb = inv(L_kk) X_kb (for the last kb also the backward
+//                  one, X_kb = inv(L_kk)^T X_kb)
+//   kUpdate (kb) : A_ij -= L_ik L_jk^T for kb < j <= i, X_ij -= L_ik X_kb,j for
+//                  i > kb; the workgroup of the block (kb+1, kb+1) then factors it
+//   kBwd    (kb) : X_ij -= L_kb,i^T X_kb,j for i < kb; for i = kb - 1 then also
+//                  X_ij = inv(L_ii)^T X_ij
+// Diagonal blocks keep only inv(L_kk) (in Li); the strictly lower blocks of A
+// become L.  Every launch writes blocks that no other workgroup of it reads.
+__global__ __launch_bounds__(256, 2) void solve_step_kernel(int kind, int D, int kb, double* Aall, double* Xall,
+                                                         double* Liall, int32_t* info) {
+  __shared__ double As[NB * LDP], Bs[NB * LDP];
   const int l = blockIdx.y;
   const int nb = D / NB;
+  const int b = blockIdx.x;
   double* A = Aall + (int64_t)l * D * D;
   double* X = Xall + (int64_t)l * D * D;
-  const double* Li = Liall + (int64_t)l * D * NB + (int64_t)kb * NB * NB;
+  double* Li = Liall + (int64_t)l * D * NB;
   auto blk = [&](double* M, int bi, int bj) { return M + (int64_t)bi * NB * D + (int64_t)bj * NB; };
-  const int b = blockIdx.x;
+  auto linv = [&](int k) { return Li + (int64_t)k * NB * NB; };
+  f64x4 acc[2][2];
+  double* fac_li = nullptr;  // set when this workgroup factors a diagonal block (in As)
+  int fac_base = 0;
+  auto product = [&](BlockOp x, BlockOp y) {
+    stage(As, x);
+    stage(Bs, y);
+    __syncthreads();
+    mma64(As, Bs, acc);
+  };
   switch (kind) {
-    case kTrsm: {  // A_ik = A_ik Li^T, i > kb
-      const int i = kb + 1 + b;
-      block_product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{Li, NB, 1}, blk(A, i, kb), D, false);
+    case kPotrf0: {
+      stage(As, BlockOp{blk(A, 0, 0), D, 0});
+      __syncthreads();
+      fac_li = linv(0);
       break;
     }
-    case kSyrk: {  // A_ij -= A_ik A_jk^T, kb < j <= i
-      int r = (int)((sqrt(8.0 * b + 1.0) - 1.0) * 0.5);
-      while (r * (r + 1) / 2 > b) --r;
-      while ((r + 1) * (r + 2) / 2 <= b) ++r;
-      const int c = b - r * (r + 1) / 2;
-      const int i = kb + 1 + r, j = kb + 1 + c;
-      block_product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{blk(A, j, kb), D, 1}, blk(A, i, j), D, true);
+    case kPanel: {
+      const int m = nb - 1 - kb;
+      if (b < m) {
+        const int i = kb + 1 + b;
+        product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{linv(kb), NB, 1});
+        store_block(acc, blk(A, i, kb), D, false);
+      } else {
+        const int j = b - m;
+        product(BlockOp{linv(kb), NB, 0}, BlockOp{blk(X, kb, j), D, 0});
+        if (m == 0) {
+          __syncthreads();
+          for_acc(acc, [&](int r, int c, double v) { Bs[r * LDP + c] = v; });
+          stage(As, BlockOp{linv(kb), NB, 1});
+          __syncthreads();
+          mma64(As, Bs, acc);
+        }
+        store_block(acc, blk(X, kb, j), D, false);
+      }
       break;
     }
-    case kFwdDiag: {  // X_kb,j = Li X_kb,j
-      block_product(BlockOp{Li, NB, 0}, BlockOp{blk(X, kb, b), D, 0}, blk(X, kb, b), D, false);
+    case kUpdate: {
+      const int m = nb - 1 - kb;
+      const int ntri = m * (m + 1) / 2;
+      if (b < ntri) {
+        int r = (int)((sqrt(8.0 * b + 1.0) - 1.0) * 0.5);
+        while (r * (r + 1) / 2 > b) --r;
+        while ((r + 1) * (r + 2) / 2 <= b) ++r;
+        const int c = b - r * (r + 1) / 2;
+        const int i = kb + 1 + r, j = kb + 1 + c;
+        product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{blk(A, j, kb), D, 1});
+        if (b == 0) {  // the next diagonal block: finish it and factor it here
+          __syncthreads();
+          sub_to_lds(acc, blk(A, i, i), D, As);
+          __syncthreads();
+          fac_li = linv(i);
+          fac_base = i * NB;
+        } else {
+          store_block(acc, blk(A, i, j), D, true);
+        }
+      } else {
+        const int q = b - ntri;
+        const int i = kb + 1 + q / nb, j = q % nb;
+        product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{blk(X, kb, j), D, 0});
+        store_block(acc, blk(X, i, j), D, true);
+      }
       break;
     }
-    case kFwdUpd: {  // X_ij -= A_i,kb X_kb,j, i > kb
-      const int i = kb + 1 + b / nb, j = b % nb;
-      block_product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{blk(X, kb, j), D, 0}, blk(X, i, j), D, true);
-      break;
-    }
-    case kBwdDiag: {  // X_kb,j = Li^T X_kb,j
-      block_product(BlockOp{Li, NB, 1}, BlockOp{blk(X, kb, b), D, 0}, blk(X, kb, b), D, false);
-      break;
-    }
-    case kBwdUpd: {  // X_ij -= A_kb,i^T X_kb,j, i < kb
-      const int i = b / nb, j = b % nb;
-      block_product(BlockOp{blk(A, kb, i), D, 1}, BlockOp{blk(X, kb, j), D, 0}, blk(X, i, j), D, true);
+    case kBwd: {
+      const int i = kb - 1 - b / nb, j = b % nb;
+      product(BlockOp{blk(A, kb, i), D, 1}, BlockOp{blk(X, kb, j), D, 0});
+      if (i == kb - 1) {
+        __syncthreads();
+        sub_to_lds(acc, blk(X, i, j), D, Bs);
+        stage(As, BlockOp{linv(i), NB, 1});
+        __syncthreads();
+        mma64(As, Bs, acc);
+        store_block(acc, blk(X, i, j), D, false);
+      } else {
+        store_block(acc, blk(X, i, j), D, true);
+      }
       break;
     }
   }
+  if (fac_li) factor_block(As, Bs, fac_li, info + l, fac_base);
 }
 
 // dW out, W_eff, and per-block partial sums <X, C>, ||X||^2
@@ -312,31 +385,19 @@ ispa_status run_solve(int32_t L, int32_t D, const float* G, const float* C, cons
   const int64_t DD = (int64_t)D * D;
   const unsigned fill_blocks = (unsigned)std::min<int64_t>((DD + 255) / 256, 4096);
   hipLaunchKernelGGL(fill_kernel, dim3(fill_blocks, L), dim3(256), 0, stream, D, G, C, ms, s.lam, s.A, s.X);
+  hipLaunchKernelGGL(solve_step_kernel, dim3(1, L), dim3(256), 0, stream, (int)kPotrf0, D, 0, s.A, s.X, s.Linv,
+                     info);
   for (int kb = 0; kb < nb; ++kb) {
-    hipLaunchKernelGGL(potrf_kernel, dim3(L), dim3(256), 0, stream, D, kb, s.A, s.Linv, info);
     const int m = nb - 1 - kb;
-    if (m > 0) {
-      hipLaunchKernelGGL(block_step_kernel, dim3(m, L), dim3(256), 0, stream, (int)kTrsm, D, kb, s.A, s.X,
-                         s.Linv);
-      hipLaunchKernelGGL(block_step_kernel, dim3(m * (m + 1) / 2, L), dim3(256), 0, stream, (int)kSyrk, D,
-                         kb, s.A, s.X, s.Linv);
-    }
-  }
-  for (int kb = 0; kb < nb; ++kb) {
-    hipLaunchKernelGGL(block_step_kernel, dim3(nb, L), dim3(256), 0, stream, (int)kFwdDiag, D, kb, s.A, s.X,
-                       s.Linv);
-    const int m = nb - 1 - kb;
+    hipLaunchKernelGGL(solve_step_kernel, dim3(m + nb, L), dim3(256), 0, stream, (int)kPanel, D, kb, s.A, s.X,
+                       s.Linv, info);
     if (m > 0)
-      hipLaunchKernelGGL(block_step_kernel, dim3(m * nb, L), dim3(256), 0, stream, (int)kFwdUpd, D, kb, s.A,
-                         s.X, s.Linv);
+      hipLaunchKernelGGL(solve_step_kernel, dim3(m * (m + 1) / 2 + m * nb, L), dim3(256), 0, stream, (int)kUpdate,
+                         D, kb, s.A, s.X, s.Linv, info);
   }
-  for (int kb = nb - 1; kb >= 0; --kb) {
-    hipLaunchKernelGGL(block_step_kernel, dim3(nb, L), dim3(256), 0, stream, (int)kBwdDiag, D, kb, s.A, s.X,
-                       s.Linv);
-    if (kb > 0)
-      hipLaunchKernelGGL(block_step_kernel, dim3(kb * nb, L), dim3(256), 0, stream, (int)kBwdUpd, D, kb, s.A,
-                         s.X, s.Linv);
-  }
+  for (int kb = nb - 1; kb >= 1; --kb)
+    hipLaunchKernelGGL(solve_step_kernel, dim3(kb * nb, L), dim3(256), 0, stream, (int)kBwd, D, kb, s.A, s.X,
+                       s.Linv, info);
   hipLaunchKernelGGL(finalize_kernel, dim3(kEpsBlocks, L), dim3(256), 0, stream, D, s.X, C, ms, info, dW, w,
                      w_dt, w_eff, s.part);
   hipLaunchKernelGGL(eps_kernel, dim3((L + 63) / 64), dim3(64), 0, stream, L, r2, s.lam, info, s.part, eps);
