@@ -162,7 +162,7 @@ size_t ispa_accum_stats_workspace_bytes(ispa_dtype a_dt, int64_t n, int32_t D) {
   const size_t rblocks = (size_t)((D + kNtBM - 1) / kNtBM) * (size_t)((np + 127) / 128);
   const int64_t split = nt_stats_split(D, np);
   const size_t part = split > 1 ? align256((size_t)split * 2 * D * D * 4) : 0;
-  return 2 * align256((size_t)D * D * 2) + 2 * align256((size_t)D * np * 2) + align256(rblocks * 8) + part;
+  return align256((size_t)D * D * 2) + 2 * align256((size_t)D * np * 2) + align256(rblocks * 8) + part;
 }
 
 ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_t D, const void* a_loc,
@@ -186,14 +186,12 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   if (a_dt == ISPA_F32)
     return launch_stats_f32(n, D, (const float*)a_loc, (const float*)delta_a, (const float*)w, G, C, r2, ws,
                             stream);
-  // Workspace: W^T and (if W's type differs) W converted, A_loc^T and R^T with the
+  // Workspace: W^T (in the operand type), A_loc^T and R^T with the
   // token dimension zero-padded to a multiple of the GEMM's K stage, per-workgroup
   // ||R||^2, and (when the token range is split) the partial G and C sums.
   const int64_t np = (n + kNtBK - 1) / kNtBK * kNtBK;
   char* wp = (char*)ws;
   uint16_t* Wt = (uint16_t*)wp;
-  wp += align256((size_t)D * D * 2);
-  uint16_t* Wc = (uint16_t*)wp;
   wp += align256((size_t)D * D * 2);
   uint16_t* At = (uint16_t*)wp;
   wp += align256((size_t)D * np * 2);
@@ -202,13 +200,8 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   double* partials = (double*)wp;
   const size_t rblocks_bytes = (size_t)((D + kNtBM - 1) / kNtBM) * (size_t)((np + 127) / 128) * 8;
   ispa_status st;
-  const void* wsrc = w;
-  if (w_dt != a_dt) {
-    if ((st = launch_convert16(w, (int64_t)D * D, w_dt, Wc, a_dt, stream))) return st;
-    wsrc = Wc;
-  }
-  if ((st = launch_transpose16(wsrc, D, D, D, Wt, D, D, stream))) return st;
-  if ((st = launch_transpose16(a_loc, D, n, D, At, np, np, stream))) return st;
+  if ((st = launch_transpose16(w, D, D, D, Wt, D, D, w_dt, a_dt, stream))) return st;
+  if ((st = launch_transpose16(a_loc, D, n, D, At, np, np, a_dt, a_dt, stream))) return st;
   // R^T = W^T dA^T, stored with zero padding, and per-workgroup ||R||^2
   NtGemmParams r{};
   r.M = D;
@@ -231,7 +224,6 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   r.sq_partials = partials;
   int nblk = 0;
   if ((st = launch_nt_gemm(r, a_dt, stream, &nblk))) return st;
-  if ((st = launch_reduce_add(partials, nblk, r2, stream))) return st;
   // G += A^T A (upper-triangle tiles) and C += A^T R (all tiles) in one launch
   NtGemmParams g{};
   g.M = D;
@@ -256,7 +248,7 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   g.kchunk = (stages + g.ksplit - 1) / g.ksplit * kNtBK;
   g.part = g.ksplit > 1 ? (float*)(wp + align256(rblocks_bytes)) : nullptr;
   if ((st = launch_nt_gemm(g, a_dt, stream, nullptr))) return st;
-  return launch_nt_split_reduce(g, stream);
+  return launch_nt_split_reduce(g, partials, nblk, r2, stream);
 }
 
 // ---------------------------------------------------------------- solve_dw

@@ -219,23 +219,33 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
     __syncthreads();
     frags(0, 0, fa0, fb0);
   }
+  // The last stage is peeled off so that the loop body has no path around
+  // its barrier: the slice-1 MFMAs after the barrier then see their fragments
+  // as complete and do not wait for the next stage's reads.
   int cbuf = 0;
-  for (int s = 0; s < ns; ++s) {
+  for (int s = 0; s + 1 < ns; ++s) {
     if (issued < ns) {
       issue(issued, lbuf);
       lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
       ++issued;
     }
     frags(cbuf, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);  // keep each phase's reads ahead of the MFMAs they overlap
     mfmas(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
     const int nbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;
-    if (s + 1 < ns) {
-      wait_stage(issued - (s + 2));  // stage s + 1 is in LDS
-      __syncthreads();
-      frags(nbuf, 0, fa0, fb0);
-    }
+    wait_stage(issued - (s + 2));  // stage s + 1 is in LDS
+    __syncthreads();
+    frags(nbuf, 0, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
     mfmas(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
     cbuf = nbuf;
+  }
+  if (ns > 0) {  // every stage has been issued by now
+    frags(cbuf, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    mfmas(fa1, fb1);
   }
 
   // ---- epilogues: lane holds out[m][n .. n+3] in acc[i][j][4 g .. 4 g + 3] with
@@ -333,10 +343,17 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
   }
 }
 
-// out[c][r] = in[r][c] for r < rows, 0 for rows <= r < rows_pad (16-bit elements).
+// out[c][r] = in[r][c] for r < rows, 0 for rows <= r < rows_pad (16-bit elements),
+// converted from in_dt to out_dt (bf16 <-> f16, round to nearest even) when they differ
+__device__ __forceinline__ uint16_t conv16(uint32_t v, int in_dt, int out_dt) {
+  if (in_dt == out_dt) return (uint16_t)v;
+  const float f = in_dt == ISPA_BF16 ? bf16_bits_to_f32((uint16_t)v) : f16_bits_to_f32((uint16_t)v);
+  return (uint16_t)(out_dt == ISPA_BF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f));
+}
+
 __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* in, int64_t ld_in, int64_t rows,
                                                           int64_t cols, uint16_t* out, int64_t ld_out,
-                                                          int64_t rows_pad) {
+                                                          int64_t rows_pad, int in_dt, int out_dt) {
   __shared__ uint16_t tile[64][66];
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -346,10 +363,10 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* in, in
     const int64_t r = r0 + rr, c = c0 + tx * 4;
     u32x2 v = {0u, 0u};
     if (r < rows && c < cols) v = *(const u32x2*)(in + r * ld_in + c);
-    tile[rr][tx * 4 + 0] = (uint16_t)(v[0] & 0xffffu);
-    tile[rr][tx * 4 + 1] = (uint16_t)(v[0] >> 16);
-    tile[rr][tx * 4 + 2] = (uint16_t)(v[1] & 0xffffu);
-    tile[rr][tx * 4 + 3] = (uint16_t)(v[1] >> 16);
+    tile[rr][tx * 4 + 0] = conv16(v[0] & 0xffffu, in_dt, out_dt);
+    tile[rr][tx * 4 + 1] = conv16(v[0] >> 16, in_dt, out_dt);
+    tile[rr][tx * 4 + 2] = conv16(v[1] & 0xffffu, in_dt, out_dt);
+    tile[rr][tx * 4 + 3] = conv16(v[1] >> 16, in_dt, out_dt);
   }
   __syncthreads();
 #pragma unroll
@@ -364,18 +381,25 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* in, in
   }
 }
 
-// 16-bit conversion of a matrix (bf16 <-> f16) into a contiguous buffer
-__global__ void convert16_kernel(const uint16_t* in, int64_t n, int in_dt, uint16_t* out, int out_dt) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const float f = in_dt == ISPA_BF16 ? bf16_bits_to_f32(in[i]) : f16_bits_to_f32(in[i]);
-  out[i] = (uint16_t)(out_dt == ISPA_BF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f));
-}
-
 // out[m][n .. n+3] += sum_s part[s][kind][m][n .. n+3]; the first kind keeps the
-// upper triangle (m <= n) only when tri is set
+// upper triangle (m <= n) only when tri is set.  The last workgroup instead adds
+// the n_sq per-workgroup sums of squares to *r2 (fixed order: deterministic).
 __global__ __launch_bounds__(256) void split_reduce_kernel(float* out0, float* out1, const float* part, int64_t M,
-                                                           int64_t N, int64_t ld, int ksplit, int tri, int two) {
+                                                           int64_t N, int64_t ld, int ksplit, int tri, int two,
+                                                           const double* sq, int64_t n_sq, double* r2) {
+  if (blockIdx.x == gridDim.x - 1) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n_sq; i += 256) s += sq[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+      if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) *r2 += red[0];
+    return;
+  }
   const int64_t vecs_per_row = N / 4;
   const int64_t per_kind = M * vecs_per_row;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -424,11 +448,12 @@ ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t strea
   return check_launch("nt_gemm_kernel");
 }
 
-ispa_status launch_nt_split_reduce(const NtGemmParams& p, hipStream_t stream) {
-  if (p.ksplit <= 1) return ISPA_OK;
-  const int64_t items = p.M * (p.N / 4) * (p.two_kinds ? 2 : 1);
-  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream,
-                     (float*)p.out, (float*)p.out2, p.part, p.M, p.N, p.ld_out, p.ksplit, p.tri, p.two_kinds);
+ispa_status launch_nt_split_reduce(const NtGemmParams& p, const double* sq, int64_t n_sq, double* r2,
+                                   hipStream_t stream) {
+  const int64_t items = p.ksplit > 1 ? p.M * (p.N / 4) * (p.two_kinds ? 2 : 1) : 0;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((items + 255) / 256 + 1)), dim3(256), 0, stream,
+                     (float*)p.out, (float*)p.out2, p.part, p.M, p.N, p.ld_out, p.ksplit, p.tri, p.two_kinds, sq,
+                     n_sq, r2);
   return check_launch("split_reduce_kernel");
 }
 
@@ -443,19 +468,12 @@ int64_t nt_stats_split(int32_t D, int64_t np) {
 }
 
 ispa_status launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,
-                               int64_t ld_out, int64_t rows_pad, hipStream_t stream) {
+                               int64_t ld_out, int64_t rows_pad, int in_dt, int out_dt, hipStream_t stream) {
   if (rows_pad == 0 || cols == 0) return ISPA_OK;
   const dim3 grid((unsigned)((rows_pad + 63) / 64), (unsigned)((cols + 63) / 64));
   hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, (const uint16_t*)in, ld_in, rows, cols,
-                     (uint16_t*)out, ld_out, rows_pad);
+                     (uint16_t*)out, ld_out, rows_pad, in_dt, out_dt);
   return check_launch("transpose16_kernel");
-}
-
-ispa_status launch_convert16(const void* in, int64_t n, int in_dt, void* out, int out_dt, hipStream_t stream) {
-  if (n == 0) return ISPA_OK;
-  hipLaunchKernelGGL(convert16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     (const uint16_t*)in, n, in_dt, (uint16_t*)out, out_dt);
-  return check_launch("convert16_kernel");
 }
 
 }  // namespace ispa

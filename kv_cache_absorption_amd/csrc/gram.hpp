@@ -35,13 +35,15 @@ struct NtGemmParams {
 
 ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t stream, int* n_blocks_out);
 // out (and out2) += sum over splits of the partial sums a kNtAccum launch left in p.part
-ispa_status launch_nt_split_reduce(const NtGemmParams& p, hipStream_t stream);
+// (nothing when p.ksplit == 1), and *r2 += the n_sq sums of squares in sq
+ispa_status launch_nt_split_reduce(const NtGemmParams& p, const double* sq, int64_t n_sq, double* r2,
+                                   hipStream_t stream);
 // K split of the statistics GEMM over np tokens at width D (tiles of kNtBM)
 int64_t nt_stats_split(int32_t D, int64_t np);
-// out[c][r] = in[r][c] (r < rows), 0 for rows <= r < rows_pad; rows_pad multiple of 4, cols of 4
+// out[c][r] = in[r][c] (r < rows), 0 for rows <= r < rows_pad; rows_pad multiple of 4, cols of 4;
+// 16-bit elements converted from in_dt to out_dt when they differ
 ispa_status launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,
-                               int64_t ld_out, int64_t rows_pad, hipStream_t stream);
-ispa_status launch_convert16(const void* in, int64_t n, int in_dt, void* out, int out_dt, hipStream_t stream);
+                               int64_t ld_out, int64_t rows_pad, int in_dt, int out_dt, hipStream_t stream);
 
 constexpr int kNtBM = 256, kNtBK = 32;
 
