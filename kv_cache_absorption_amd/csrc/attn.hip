@@ -1014,43 +1014,51 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
   job.lse[qrow * p.H + head] = l > 0.0f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
+// V vectors of 4 elements per thread.  Per row: m = max_k LSE_k, e_k = exp(LSE_k - m)
+// (0 for an empty part), LSE = m + ln sum_k e_k and weight_k = e_k / sum_k e_k, which
+// is exp(LSE_k - LSE); every thread of the row forms the same weights.
+template <int V>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
-  const int tpr = p.d >> 2;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int tpr = p.d / (4 * V);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / tpr;
-  const int c4 = gid - row * tpr;
+  const int c = (int)(gid - row * tpr);
   if (row >= p.n_rows) return;
   float m = -INFINITY;
   for (int k = 0; k < p.n_parts; ++k) m = fmaxf(m, p.lse[k][row]);
-  float L = -INFINITY;
-  if (m != -INFINITY) {
-    float tot = 0.0f;
-    for (int k = 0; k < p.n_parts; ++k) {
-      const float lk = p.lse[k][row];
-      if (lk != -INFINITY) tot += expf(lk - m);
-    }
-    L = m + logf(tot);
-  }
-  const int64_t off = row * p.d + c4 * 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, o0 = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.0f;
+  if (m != -INFINITY)
+    for (int k = 0; k < p.n_parts; ++k) tot += exp2f((p.lse[k][row] - m) * kLog2e);  // exp2(-inf) = 0
+  const float L = m != -INFINITY ? m + log2f(tot) * kLn2 : -INFINITY;
+  const float inv = m != -INFINITY ? 1.0f / tot : 0.0f;
+  const int64_t off = row * p.d + (int64_t)c * 4 * V;
+  f32x4 acc[V], o0[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = o0[v] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < p.n_parts; ++k) {
-    const float lk = p.lse[k][row];
-    const f32x4 ok = *(const f32x4*)(p.o[k] + off);
-    if (k == 0) o0 = ok;
-    if (lk != -INFINITY && L != -INFINITY) acc += expf(lk - L) * ok;
+    const float w = m != -INFINITY ? exp2f((p.lse[k][row] - m) * kLog2e) * inv : 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const f32x4 ok = *(const f32x4*)(p.o[k] + off + 4 * v);
+      if (k == 0) o0[v] = ok;
+      acc[v] += w * ok;
+    }
   }
-  if (p.o_full) *(f32x4*)(p.o_full + off) = acc;
-  if (p.lse_full && c4 == 0) p.lse_full[row] = L;
-  if (p.a0 || p.delta) {
-    const f32x4 dl = acc - o0;
+  if (p.lse_full && c == 0) p.lse_full[row] = L;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int64_t o = off + 4 * v;
+    if (p.o_full) *(f32x4*)(p.o_full + o) = acc[v];
+    const f32x4 dl = acc[v] - o0[v];
     if (p.out_dt == ISPA_F32) {
-      if (p.a0) *(f32x4*)((float*)p.a0 + off) = o0;
-      if (p.delta) *(f32x4*)((float*)p.delta + off) = dl;
+      if (p.a0) *(f32x4*)((float*)p.a0 + o) = o0[v];
+      if (p.delta) *(f32x4*)((float*)p.delta + o) = dl;
     } else {
       const bool bf = p.out_dt == ISPA_BF16;
       auto pk = [&](float x, float y) { return bf ? pack_bf16(x, y) : pack_f16(x, y); };
-      if (p.a0) *(u32x2*)((uint16_t*)p.a0 + off) = (u32x2){pk(o0[0], o0[1]), pk(o0[2], o0[3])};
-      if (p.delta) *(u32x2*)((uint16_t*)p.delta + off) = (u32x2){pk(dl[0], dl[1]), pk(dl[2], dl[3])};
+      if (p.a0) *(u32x2*)((uint16_t*)p.a0 + o) = (u32x2){pk(o0[v][0], o0[v][1]), pk(o0[v][2], o0[v][3])};
+      if (p.delta) *(u32x2*)((uint16_t*)p.delta + o) = (u32x2){pk(dl[0], dl[1]), pk(dl[2], dl[3])};
     }
   }
 }
@@ -1059,9 +1067,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 
 ispa_status launch_merge(const MergeParams& p, hipStream_t stream) {
   if (p.n_rows == 0) return ISPA_OK;
-  const int64_t threads = p.n_rows * (p.d / 4);
+  const int V = p.d % 8 == 0 ? 2 : 1;
+  const int64_t threads = p.n_rows * (p.d / (4 * V));
   const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  if (V == 2)
+    hipLaunchKernelGGL(merge_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return check_launch("merge_kernel");
 }
 
