@@ -15,6 +15,7 @@
 // the identity that holds at the ridge optimum, eps = r2 - <dW, C> -
 // lambda ||dW||^2 (from G dW = C - lambda dW), which is ||A_loc dW - R||^2
 // without the penalty (EN review, Key Design 2).
+#include <algorithm>
 #include <cmath>
 
 #include "common.hpp"
@@ -32,7 +33,7 @@ struct SolveWs {
   double* lam;   // [L]
   double* part;  // [L][kEpsBlocks][2]
 };
-constexpr int kEpsBlocks = 64;
+constexpr int kEpsBlocks = 1024;  // finalize workgroups per layer
 
 size_t ws_layout(int L, int D, SolveWs* w, char* base) {
   size_t off = 0;
@@ -119,13 +120,14 @@ __device__ __forceinline__ void stage(double* dst, BlockOp o) {
 // acc = As * Bs for this wave's 32 x 32 quadrant, as 2 x 2 tiles of
 // v_mfma_f64_16x16x4 (A fragment: lane holds A[l % 16][l / 16]; B fragment:
 // B[l / 16][l % 16]; result element e of lane l: row l / 16 + 4 e, column l % 16)
-__device__ __forceinline__ void mma64(const double* As, const double* Bs, f64x4 (&acc)[2][2]) {
+__device__ __forceinline__ void mma64(const double* As, const double* Bs, f64x4 (&acc)[2][2], bool accumulate = false) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = (wave >> 1) * 32, c0 = (wave & 1) * 32, li = lane & 15, lk = lane >> 4;
+  if (!accumulate)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (f64x4){0.0, 0.0, 0.0, 0.0};
+      for (int j = 0; j < 2; ++j) acc[i][j] = (f64x4){0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int ks = 0; ks < NB / 4; ++ks) {
     const double a0 = As[(r0 + li) * LDP + 4 * ks + lk];
@@ -218,19 +220,29 @@ __device__ __forceinline__ void factor_block(const double* As, double* Bs, doubl
 
 enum { kPotrf0 = 0, kPanel = 1, kUpdate = 2, kBwd = 3 };
 
+// Block ranges of one launch (block indices, half-open): the contraction range
+// [k_lo, k_hi) and, for kUpdate, the A columns [j_lo, j_hi) (every block on or
+// below the diagonal in them) and the X block rows [x_lo, x_hi); for kBwd the X
+// block rows [x_lo, x_hi) and the row diag that is finished in the same launch.
+struct StepArgs {
+  int kind, kb;
+  int k_lo, k_hi, j_lo, j_hi, x_lo, x_hi, diag;
+};
+
 // One launch of the blocked solve, batched over layers (blockIdx.y).
 //   kPotrf0      : inv(L_00)
 //   kPanel  (kb) : L_ik = A_ik inv(L_kk)^T for i > kb, and the forward diagonal
 //                  step X_kb = inv(L_kk) X_kb (for the last kb also the backward
 //                  one, X_kb = inv(L_kk)^T X_kb)
-//   kUpdate (kb) : A_ij -= L_ik L_jk^T for kb < j <= i, X_ij -= L_ik X_kb,j for
-//                  i > kb; the workgroup of the block (kb+1, kb+1) then factors it
-//   kBwd    (kb) : X_ij -= L_kb,i^T X_kb,j for i < kb; for i = kb - 1 then also
-//                  X_ij = inv(L_ii)^T X_ij
+//   kUpdate      : A_ij -= sum_k L_ik L_jk^T for j in [j_lo, j_hi), i >= j, and
+//                  X_ij -= sum_k L_ik X_kj for i in [x_lo, x_hi); the workgroup of
+//                  the block (j_lo, j_lo) then factors it
+//   kBwd         : X_ij -= sum_k L_ki^T X_kj for i in [x_lo, x_hi); for i = diag
+//                  then also X_ij = inv(L_ii)^T X_ij
 // Diagonal blocks keep only inv(L_kk) (in Li); the strictly lower blocks of A
 // become L.  Every launch writes blocks that no other workgroup of it reads.
-__global__ __launch_bounds__(256, 2) void solve_step_kernel(int kind, int D, int kb, double* Aall, double* Xall,
-                                                         double* Liall, int32_t* info) {
+__global__ __launch_bounds__(256, 2) void solve_step_kernel(StepArgs g, int D, double* Aall, double* Xall,
+                                                           double* Liall, int32_t* info) {
   __shared__ double As[NB * LDP], Bs[NB * LDP];
   const int l = blockIdx.y;
   const int nb = D / NB;
@@ -243,13 +255,20 @@ __global__ __launch_bounds__(256, 2) void solve_step_kernel(int kind, int D, int
   f64x4 acc[2][2];
   double* fac_li = nullptr;  // set when this workgroup factors a diagonal block (in As)
   int fac_base = 0;
-  auto product = [&](BlockOp x, BlockOp y) {
+  auto product = [&](BlockOp x, BlockOp y, bool accumulate) {
     stage(As, x);
     stage(Bs, y);
     __syncthreads();
-    mma64(As, Bs, acc);
+    mma64(As, Bs, acc, accumulate);
   };
-  switch (kind) {
+  // acc = sum over the contraction range of x(k) y(k)
+  auto sum_products = [&](auto x, auto y) {
+    for (int k = g.k_lo; k < g.k_hi; ++k) {
+      if (k > g.k_lo) __syncthreads();  // the previous product is done with As and Bs
+      product(x(k), y(k), k > g.k_lo);
+    }
+  };
+  switch (g.kind) {
     case kPotrf0: {
       stage(As, BlockOp{blk(A, 0, 0), D, 0});
       __syncthreads();
@@ -257,14 +276,15 @@ __global__ __launch_bounds__(256, 2) void solve_step_kernel(int kind, int D, int
       break;
     }
     case kPanel: {
+      const int kb = g.kb;
       const int m = nb - 1 - kb;
       if (b < m) {
         const int i = kb + 1 + b;
-        product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{linv(kb), NB, 1});
+        product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{linv(kb), NB, 1}, false);
         store_block(acc, blk(A, i, kb), D, false);
       } else {
         const int j = b - m;
-        product(BlockOp{linv(kb), NB, 0}, BlockOp{blk(X, kb, j), D, 0});
+        product(BlockOp{linv(kb), NB, 0}, BlockOp{blk(X, kb, j), D, 0}, false);
         if (m == 0) {
           __syncthreads();
           for_acc(acc, [&](int r, int c, double v) { Bs[r * LDP + c] = v; });
@@ -277,16 +297,17 @@ __global__ __launch_bounds__(256, 2) void solve_step_kernel(int kind, int D, int
       break;
     }
     case kUpdate: {
-      const int m = nb - 1 - kb;
-      const int ntri = m * (m + 1) / 2;
-      if (b < ntri) {
-        int r = (int)((sqrt(8.0 * b + 1.0) - 1.0) * 0.5);
-        while (r * (r + 1) / 2 > b) --r;
-        while ((r + 1) * (r + 2) / 2 <= b) ++r;
-        const int c = b - r * (r + 1) / 2;
-        const int i = kb + 1 + r, j = kb + 1 + c;
-        product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{blk(A, j, kb), D, 1});
-        if (b == 0) {  // the next diagonal block: finish it and factor it here
+      // A blocks: columns j_lo .. j_hi - 1, rows j .. nb - 1 each, column by column
+      int q = b, j = g.j_lo;
+      while (j < g.j_hi && q >= nb - j) {
+        q -= nb - j;
+        ++j;
+      }
+      if (j < g.j_hi) {
+        const int i = j + q;
+        sum_products([&](int k) { return BlockOp{blk(A, i, k), D, 0}; },
+                     [&](int k) { return BlockOp{blk(A, j, k), D, 1}; });
+        if (i == g.j_lo && j == g.j_lo) {  // the next diagonal block: finish it and factor it here
           __syncthreads();
           sub_to_lds(acc, blk(A, i, i), D, As);
           __syncthreads();
@@ -296,17 +317,19 @@ __global__ __launch_bounds__(256, 2) void solve_step_kernel(int kind, int D, int
           store_block(acc, blk(A, i, j), D, true);
         }
       } else {
-        const int q = b - ntri;
-        const int i = kb + 1 + q / nb, j = q % nb;
-        product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{blk(X, kb, j), D, 0});
-        store_block(acc, blk(X, i, j), D, true);
+        const int i = g.x_lo + q / nb, jx = q % nb;
+        sum_products([&](int k) { return BlockOp{blk(A, i, k), D, 0}; },
+                     [&](int k) { return BlockOp{blk(X, k, jx), D, 0}; });
+        store_block(acc, blk(X, i, jx), D, true);
       }
       break;
     }
     case kBwd: {
-      const int i = kb - 1 - b / nb, j = b % nb;
-      product(BlockOp{blk(A, kb, i), D, 1}, BlockOp{blk(X, kb, j), D, 0});
-      if (i == kb - 1) {
+      // rows diag (if in range) first, then downwards
+      const int i = g.x_hi - 1 - b / nb, j = b % nb;
+      sum_products([&](int k) { return BlockOp{blk(A, k, i), D, 1}; },
+                   [&](int k) { return BlockOp{blk(X, k, j), D, 0}; });
+      if (i == g.diag) {
         __syncthreads();
         sub_to_lds(acc, blk(X, i, j), D, Bs);
         stage(As, BlockOp{linv(i), NB, 1});
@@ -359,21 +382,40 @@ __global__ void finalize_kernel(int D, const double* Xall, const float* C, int64
   }
 }
 
-__global__ void eps_kernel(int L, const double* r2, const double* lam, const int32_t* info,
-                           const double* part, double* eps) {
-  const int l = blockIdx.x * blockDim.x + threadIdx.x;
-  if (l >= L) return;
+// one workgroup per layer: fixed-order sums of the finalize partials
+__global__ __launch_bounds__(256) void eps_kernel(const double* r2, const double* lam, const int32_t* info,
+                                                  const double* part, double* eps) {
+  __shared__ double r1[256], r2s[256];
+  const int l = blockIdx.x;
   double dot = 0.0, nrm = 0.0;
-  for (int b = 0; b < kEpsBlocks; ++b) {
-    dot += part[(l * kEpsBlocks + b) * 2 + 0];
-    nrm += part[(l * kEpsBlocks + b) * 2 + 1];
+  for (int b = threadIdx.x; b < kEpsBlocks; b += 256) {
+    dot += part[((int64_t)l * kEpsBlocks + b) * 2 + 0];
+    nrm += part[((int64_t)l * kEpsBlocks + b) * 2 + 1];
   }
-  eps[l] = info[l] ? NAN : r2[l] - dot - lam[l] * nrm;
+  r1[threadIdx.x] = dot;
+  r2s[threadIdx.x] = nrm;
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if ((int)threadIdx.x < off) {
+      r1[threadIdx.x] += r1[threadIdx.x + off];
+      r2s[threadIdx.x] += r2s[threadIdx.x + off];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) eps[l] = info[l] ? NAN : r2[l] - r1[0] - lam[l] * r2s[0];
 }
 
 }  // namespace
 
 size_t solve_ws_bytes(int32_t n_layers, int32_t D) { return ws_layout(n_layers, D, nullptr, nullptr); }
+
+// Block columns per trailing update: deeper updates cut the read-modify-write of
+// the trailing blocks (which bounds large batched solves) but lengthen each
+// workgroup, which a small solve feels as latency.
+static int solve_group(int L, int D) {
+  const double blocks = (double)L * (D / NB) * (D / NB);
+  return blocks >= 4096.0 ? 4 : 1;
+}
 
 ispa_status run_solve(int32_t L, int32_t D, const float* G, const float* C, const double* r2,
                       int64_t ms, double la, double lr, float* dW, double* eps, int32_t* info,
@@ -385,22 +427,41 @@ ispa_status run_solve(int32_t L, int32_t D, const float* G, const float* C, cons
   const int64_t DD = (int64_t)D * D;
   const unsigned fill_blocks = (unsigned)std::min<int64_t>((DD + 255) / 256, 4096);
   hipLaunchKernelGGL(fill_kernel, dim3(fill_blocks, L), dim3(256), 0, stream, D, G, C, ms, s.lam, s.A, s.X);
-  hipLaunchKernelGGL(solve_step_kernel, dim3(1, L), dim3(256), 0, stream, (int)kPotrf0, D, 0, s.A, s.X, s.Linv,
-                     info);
-  for (int kb = 0; kb < nb; ++kb) {
-    const int m = nb - 1 - kb;
-    hipLaunchKernelGGL(solve_step_kernel, dim3(m + nb, L), dim3(256), 0, stream, (int)kPanel, D, kb, s.A, s.X,
-                       s.Linv, info);
-    if (m > 0)
-      hipLaunchKernelGGL(solve_step_kernel, dim3(m * (m + 1) / 2 + m * nb, L), dim3(256), 0, stream, (int)kUpdate,
-                         D, kb, s.A, s.X, s.Linv, info);
+  // Block columns are taken in groups of P: inside a group the trailing update
+  // covers only the group's own columns (and X block rows), and the blocks right
+  // of (below) the group get the group's P columns in one update of depth P.
+  const int P = solve_group(L, D);
+  auto launch = [&](StepArgs g, int blocks) {
+    if (blocks > 0)
+      hipLaunchKernelGGL(solve_step_kernel, dim3((unsigned)blocks, (unsigned)L), dim3(256), 0, stream, g, D, s.A,
+                         s.X, s.Linv, info);
+  };
+  auto strip = [&](int j_lo, int j_hi) {  // A blocks on or below the diagonal in columns [j_lo, j_hi)
+    int n = 0;
+    for (int j = j_lo; j < j_hi; ++j) n += nb - j;
+    return n;
+  };
+  launch(StepArgs{kPotrf0, 0, 0, 0, 0, 0, 0, 0, -1}, 1);
+  for (int g0 = 0; g0 < nb; g0 += P) {
+    const int g1 = std::min(g0 + P, nb);
+    for (int kb = g0; kb < g1; ++kb) {
+      launch(StepArgs{kPanel, kb, 0, 0, 0, 0, 0, 0, -1}, (nb - 1 - kb) + nb);
+      if (kb + 1 < g1)  // the rest of the group, by column kb
+        launch(StepArgs{kUpdate, kb, kb, kb + 1, kb + 1, g1, kb + 1, g1, -1}, strip(kb + 1, g1) + (g1 - kb - 1) * nb);
+      else if (g1 < nb)  // everything past the group, by the whole group
+        launch(StepArgs{kUpdate, kb, g0, g1, g1, nb, g1, nb, -1}, strip(g1, nb) + (nb - g1) * nb);
+    }
   }
-  for (int kb = nb - 1; kb >= 1; --kb)
-    hipLaunchKernelGGL(solve_step_kernel, dim3(kb * nb, L), dim3(256), 0, stream, (int)kBwd, D, kb, s.A, s.X,
-                       s.Linv, info);
+  for (int g0 = (nb - 1) / P * P; g0 >= 0; g0 -= P) {
+    const int g1 = std::min(g0 + P, nb);
+    for (int kb = g1 - 1; kb > g0; --kb)  // rows of the group, by row kb
+      launch(StepArgs{kBwd, kb, kb, kb + 1, 0, 0, g0, kb, kb - 1}, (kb - g0) * nb);
+    if (g0 > 0)  // rows before the group, by the whole group
+      launch(StepArgs{kBwd, g0, g0, g1, 0, 0, 0, g0, g0 - 1}, g0 * nb);
+  }
   hipLaunchKernelGGL(finalize_kernel, dim3(kEpsBlocks, L), dim3(256), 0, stream, D, s.X, C, ms, info, dW, w,
                      w_dt, w_eff, s.part);
-  hipLaunchKernelGGL(eps_kernel, dim3((L + 63) / 64), dim3(64), 0, stream, L, r2, s.lam, info, s.part, eps);
+  hipLaunchKernelGGL(eps_kernel, dim3(L), dim3(256), 0, stream, r2, s.lam, info, s.part, eps);
   return check_launch("solve kernels");
 }
 

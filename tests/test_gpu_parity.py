@@ -298,6 +298,32 @@ def test_solve_parity(D, L):
             2 ** -7 * weff_ref.float().abs().max()
 
 
+def test_solve_grouped_batch():
+    """A batch large enough for the grouped trailing updates (16 layers at
+    D = 1088: 17 block columns, so the last group is partial), each layer against
+    numpy's fp64 solve of the same symmetrised system."""
+    D, L = 1088, 16
+    print(f"solve_dw grouped D={D} layers={L}", flush=True)
+    rng = np.random.default_rng(77)
+    Gs, Cs = [], []
+    for _ in range(L):
+        a = rng.normal(size=(2 * D, D)).astype(np.float32)
+        Gs.append(a.T @ a)
+        Cs.append(rng.normal(size=(D, D)).astype(np.float32))
+    G = torch.tensor(np.stack(Gs), device=DEV)
+    C = torch.tensor(np.stack(Cs), device=DEV)
+    r2 = torch.ones(L, dtype=torch.float64, device=DEV)
+    dW, eps, info, _ = K().ispa_solve_dw(G, C, r2, 0.0, 1e-3)
+    torch.cuda.synchronize()
+    assert torch.all(info == 0)
+    for l in (0, 7, L - 1):
+        Gl = Gs[l].astype(np.float64)
+        Gsym = np.triu(Gl) + np.triu(Gl, 1).T
+        lam = 1e-3 * np.trace(Gsym) / D
+        ref = np.linalg.solve(Gsym + lam * np.eye(D), Cs[l].astype(np.float64))
+        assert rel(h64(dW[l]), ref) <= 1e-6, l
+
+
 def test_solve_non_spd_reports_pivot():
     print("solve_dw non-SPD", flush=True)
     D = 128
