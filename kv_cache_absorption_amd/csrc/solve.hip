@@ -414,7 +414,7 @@ size_t solve_ws_bytes(int32_t n_layers, int32_t D) { return ws_layout(n_layers, 
 // workgroup, which a small solve feels as latency.
 static int solve_group(int L, int D) {
   const double blocks = (double)L * (D / NB) * (D / NB);
-  return blocks >= 4096.0 ? 4 : 1;
+  return blocks < 4096.0 ? 1 : D / NB >= 48 ? 8 : 4;
 }
 
 ispa_status run_solve(int32_t L, int32_t D, const float* G, const float* C, const double* r2,
