@@ -25,6 +25,10 @@ layers (the chunk's Q, K, V are generated on the GPU before its events):
   wan14b_post    40 post-switch chunks of the same 40 layers (20 L-Layers on
                  sink + current, 20 F-Layers on up to 187200 keys), with the
                  selection and W + dW of an untimed wan14b_warmup pass
+  wan13b_recal   the wan13b_stream layers with warmup re-entered: warmup 0-5,
+                 switch, post-switch 6-11, warmup again at 12-17 (statistics
+                 from zero, every layer over the keys it still holds), switch,
+                 post-switch 18-23
 """
 from __future__ import annotations
 
@@ -107,6 +111,9 @@ STREAMS = {
     "wan13b_stream": dict(N=30, H=12, d=128, chunks=20, warm=6, K=15, wid=3),
     "wan14b_warmup": dict(N=40, H=40, d=128, chunks=19, warm=19, K=20, wid=4),
     "wan14b_post": dict(N=40, H=40, d=128, chunks=40, warm=0, K=20, wid=5),
+    # re-calibration: warmup 0-5, switch, post 6-11, warmup re-entered at 12
+    # (12-17), switch again, post 18-23
+    "wan13b_recal": dict(N=30, H=12, d=128, chunks=24, warm=6, K=15, wid=3, recal=12, warm2=6),
 }
 TOKENS_PER_CHUNK = 4680  # 3 latent frames of 1560 tokens
 
@@ -137,20 +144,29 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
     qbuf = torch.empty((N, T, H, d), dtype=torch.bfloat16, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     recs = []
-    switch_ev = None
+    switch_ev = []
+    selections = []
+    recal, warm2 = spec.get("recal"), spec.get("warm2", 0)
+
+    def switch_now(evict=True):
+        s0, s1 = ev(), ev()
+        s0.record(stream)
+        st.switch(spec["K"], evict=evict)
+        s1.record(stream)
+        switch_ev.append((s0, s1))
+        selections.append([i for i, f in enumerate(st.is_local_host) if f])
+
     for c in range(spec["chunks"]):
-        if c == spec["warm"] and adopt is None:
-            s0, s1 = ev(), ev()
-            s0.record(stream)
-            st.switch(spec["K"])
-            s1.record(stream)
-            switch_ev = (s0, s1)
+        if adopt is None and (c == spec["warm"] or (recal is not None and c == recal + warm2)):
+            switch_now()
+        if recal is not None and c == recal:
+            st.recalibrate(c)
         for layer in range(N):
             k, v = si.kv(layer, c)
             st.write_kv(layer, c, k, v)
             qbuf[layer].copy_(si.q(layer, c))
             del k, v
-        warm = c < spec["warm"]
+        warm = c < spec["warm"] or (recal is not None and recal <= c < recal + warm2)
         marks = []
         e_start = ev()
         e_start.record(stream)
@@ -162,16 +178,13 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
             e = ev()
             e.record(stream)
             marks.append(e)
-        # keys each layer's call attends to: local + history during warmup
-        n_keys = [(c + 1) * T] * N if warm else st.keys_held(c)
-        recs.append(dict(c=c, warm=warm, start=e_start, marks=marks, n_keys=n_keys,
+        # keys each layer's call attends to (local + history during warmup)
+        n_keys = st.keys_held(c)
+        recs.append(dict(c=c, warm=warm, phase=0 if recal is None or c < recal else 1,
+                         start=e_start, marks=marks, n_keys=n_keys,
                          kv_held=st.kv_bytes_held(c), kv_alloc=st.kv_bytes_allocated()))
     if spec["warm"] == spec["chunks"] and adopt is None:  # warmup-only pass ends in the switch
-        s0, s1 = ev(), ev()
-        s0.record(stream)
-        st.switch(spec["K"], evict=False)
-        s1.record(stream)
-        switch_ev = (s0, s1)
+        switch_now(evict=False)
     torch.cuda.synchronize()
     for r in recs:
         t, prev = [], r["start"]
@@ -181,8 +194,9 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
         r["layer_ms"] = t
         r["ms"] = sum(t)
         del r["start"], r["marks"]
-    switch_ms = switch_ev[0].elapsed_time(switch_ev[1]) if switch_ev else None
-    return recs, switch_ms, st
+    switch_ms = [a.elapsed_time(b) for a, b in switch_ev]
+    st.selection_history = selections
+    return recs, (switch_ms[0] if switch_ms else None), st, switch_ms
 
 
 def run_stream(args, name, dev):
@@ -194,7 +208,7 @@ def run_stream(args, name, dev):
     pre = {}
     if name == "wan14b_post":
         t0 = time.perf_counter()
-        _, pre_switch_ms, st4 = _stream_pass(STREAMS["wan14b_warmup"], dev, args.seed)
+        _, pre_switch_ms, st4, _ = _stream_pass(STREAMS["wan14b_warmup"], dev, args.seed)
         adopt = (list(st4.is_local_host), st4.W, st4.w_eff)
         pre = {"switch_source": "untimed wan14b_warmup pass (same seed)",
                "switch_ms": round(pre_switch_ms, 3), "setup_s": round(time.perf_counter() - t0, 1)}
@@ -211,7 +225,7 @@ def run_stream(args, name, dev):
         passes.append(_stream_pass(spec, dev, args.seed, adopt))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    recs, switch_ms, st = passes[-1]
+    recs, switch_ms, st, switches = passes[-1]
     all_recs = [r for p in passes for r in p[0]]
     chunk_ms = [r["ms"] for r in all_recs]
     mean = lambda xs: sum(xs) / len(xs) if xs else None  # noqa: E731
@@ -227,6 +241,15 @@ def run_stream(args, name, dev):
         else:
             proj_flops += N * 2.0 * T * D * D
     pass_ms = sum(r["ms"] for r in recs)
+    if spec.get("recal") is not None:
+        for ph, tag in ((0, "before"), (1, "after")):
+            w = [r["ms"] for r in all_recs if r["phase"] == ph and r["warm"]]
+            p_ = [r["ms"] for r in all_recs if r["phase"] == ph and not r["warm"]]
+            pre[f"warmup ms/chunk {tag} re-entry"] = round(mean(w), 3) if w else None
+            pre[f"post-switch ms/chunk {tag} re-entry"] = round(mean(p_), 3) if p_ else None
+        pre["warmup re-entered at chunk"] = spec["recal"]
+        pre["switch ms (each switch)"] = [round(x, 3) for x in switches]
+        pre["L-Layers (each switch)"] = st.selection_history
     last = recs[-1]
     c_last = last["c"]
     full_bytes = 2 * N * (c_last + 1) * T * D * 2

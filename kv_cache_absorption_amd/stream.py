@@ -22,14 +22,18 @@ import torch
 from . import _lib as B
 
 
-def chunk_segments(k_cache: torch.Tensor, v_cache: torch.Tensor, c: int, T: int):
-    """(local, history) lists of (k, v) row views of one layer's cache at chunk c."""
+def chunk_segments(k_cache: torch.Tensor, v_cache: torch.Tensor, c: int, T: int, slot: int | None = None):
+    """(local, history) lists of (k, v) row views of one layer's cache at chunk
+    c, whose rows sit in cache slot ``slot`` (default c: the layer holds every
+    chunk in order).  History is every slot between the sink and the current
+    chunk."""
     def rows(a, b):
         return (k_cache[a:b], v_cache[a:b])
+    sc = c if slot is None else slot
     if c == 0:
         return [rows(0, T)], []
-    local = [rows(0, T), rows(c * T, (c + 1) * T)]
-    hist = [rows(T, c * T)] if c >= 2 else []
+    local = [rows(0, T), rows(sc * T, (sc + 1) * T)]
+    hist = [rows(T, sc * T)] if sc >= 2 else []
     return local, hist
 
 
@@ -70,15 +74,20 @@ class Workspace:
 class LayerKV:
     """K and V rows of one layer.
 
-    While the layer is full, chunk c lives in slot c (rows [cT, (c+1)T)).
-    After :meth:`evict_history` (an L-Layer) the cache shrinks to two slots:
-    the sink stays in slot 0 and every later chunk is written to slot 1,
-    replacing the previous current chunk."""
+    While the layer is full, slot 0 holds the sink and chunk c >= first lives
+    in slot c - first + 1 (first = 1 from the start, so chunk c is in slot c,
+    rows [cT, (c+1)T)).  After :meth:`evict_history` (an L-Layer) the cache
+    shrinks to two slots: the sink stays in slot 0 and every later chunk is
+    written to slot 1, replacing the previous current chunk.
+    :meth:`keep_from` makes such a layer full again from its last chunk on
+    (re-entering warmup)."""
 
     def __init__(self, capacity_chunks: int, T: int, H: int, d: int, dtype, device):
         self.T, self.H, self.d = T, H, d
         self.dtype, self.device = dtype, device
         self.local_only = False
+        self.first = 1     # first history chunk held while full
+        self.last = -1     # last chunk written
         self._alloc(capacity_chunks)
 
     def _alloc(self, chunks: int):
@@ -87,7 +96,13 @@ class LayerKV:
         self.v = torch.empty_like(self.k)
 
     def slot(self, c: int) -> int:
-        return min(c, 1) if self.local_only else c
+        if self.local_only:
+            return min(c, 1)
+        if c == 0:
+            return 0
+        if c < self.first:
+            raise ValueError(f"chunk {c} precedes the first history chunk held ({self.first})")
+        return c - self.first + 1
 
     def _rows(self, a: int, b: int):
         return (self.k[a * self.T:b * self.T], self.v[a * self.T:b * self.T])
@@ -100,6 +115,7 @@ class LayerKV:
         kk, vv = self._rows(s, s + 1)
         kk.copy_(k)
         vv.copy_(v)
+        self.last = c
 
     def grow(self, chunks: int):
         """Reallocate with room for ``chunks`` slots, keeping the rows held."""
@@ -117,11 +133,24 @@ class LayerKV:
         self.k[:self.T].copy_(sink_k)
         self.v[:self.T].copy_(sink_v)
         self.local_only = True
+        self.last = 0  # nothing but the sink is held until the next chunk
+
+    def keep_from(self, c: int):
+        """Re-enter warmup at chunk c: a full layer keeps everything; an
+        L-Layer becomes full again, holding its sink and its last chunk (if it
+        wrote one since the eviction), and keeps every chunk from then on."""
+        if not self.local_only:
+            return
+        if self.last >= 1 and self.last < c:
+            self.first = self.last          # already in slot 1
+        else:
+            self.first = c                  # only the sink is held
+        self.local_only = False
 
     def warmup_groups(self, c: int):
         """(local, history) segment lists at warmup chunk c (the layer is full)."""
         assert not self.local_only
-        return chunk_segments(self.k, self.v, c, self.T)
+        return chunk_segments(self.k, self.v, c, self.T, self.slot(c))
 
     def attend_all(self, c: int):
         """Segments of every key the layer holds at chunk c: for a full layer
@@ -196,6 +225,7 @@ class IspaStream:
         self.dW = self.eps = self.info = self.w_eff = None
         self.selected = self.is_local = self.status = None
         self.is_local_host = None
+        self.warmups = 1  # warmup phases entered (re-calibration adds one)
 
     # ------------------------------------------------------------------ helpers
     def _ck(self, st):
@@ -299,6 +329,32 @@ class IspaStream:
             if flag:
                 self.kv[layer].evict_history()
         self.G = self.C = None
+
+    def recalibrate(self, c: int):
+        """Re-enter warmup at chunk c (after a scene change, which the caller
+        detects; EN review, Limitations: warmup is re-entered to refresh the
+        layer selection and the weight corrections).  The statistics restart
+        from zero, every layer goes back to dual-stream attention with its
+        original W over the keys it still holds plus the chunks that arrive
+        (an L-Layer holds its sink and last chunk), and the next
+        :meth:`switch` solves, selects and evicts again."""
+        if not self.switched:
+            raise RuntimeError("re-calibration starts from a switched stream")
+        D, dev = self.D, self.device
+        if self.G is None:
+            self.G = torch.empty((self.N, D, D), dtype=torch.float32, device=dev)
+            self.C = torch.empty_like(self.G)
+        if self.r2 is None:
+            self.r2 = torch.empty(self.N, dtype=torch.float64, device=dev)
+        self.G.zero_()
+        self.C.zero_()
+        self.r2.zero_()
+        for kv in self.kv:
+            kv.keep_from(c)
+        self.switched = False
+        self.dW = self.eps = self.info = self.w_eff = None
+        self.selected = self.is_local = self.status = None
+        self.warmups += 1
 
     # ------------------------------------------------------------------ post-switch
     def post(self, layer: int, c: int, q: torch.Tensor):

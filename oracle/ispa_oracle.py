@@ -47,6 +47,7 @@ __all__ = [
     "stream_groups",
     "kv_bytes_retained",
     "remaining_kv_fraction",
+    "stream_groups_kept",
 ]
 
 
@@ -306,6 +307,30 @@ def stream_groups(c: int, chunk_tokens: int):
         return [(0, T)], []
     local = [(0, T), (c * T, (c + 1) * T)]
     hist = [(T, c * T)] if c >= 2 else []
+    return local, hist
+
+
+def stream_groups_kept(c: int, chunk_tokens: int, first_kept: int):
+    """Key groups at chunk step c for a layer that holds its sink and the
+    chunks first_kept .. c, and no history before first_kept.
+
+    This is the state after re-entering warmup (EN review, Limitations: the
+    method re-enters warmup after a major scene change to refresh the
+    selection and the weight corrections; it gives no detector).  Reading
+    taken: a layer re-enters warmup with the keys it still holds.  An F-Layer
+    holds everything, so first_kept = 1 and the groups are those of
+    stream_groups.  An L-Layer holds its sink and its last current chunk, so
+    first_kept is that chunk's index.  Chunks arriving from then on are kept.
+    Local = {sink, chunk c}, history = chunks first_kept .. c-1 (empty when
+    c <= first_kept).  Ranges index the original key sequence, as in
+    stream_groups."""
+    T = chunk_tokens
+    if first_kept < 1:
+        raise ValueError("first_kept counts from chunk 1 (chunk 0 is the sink)")
+    if c == 0:
+        return [(0, T)], []
+    local = [(0, T), (c * T, (c + 1) * T)]
+    hist = [(first_kept * T, c * T)] if c > first_kept else []
     return local, hist
 
 

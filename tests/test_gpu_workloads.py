@@ -210,3 +210,84 @@ def test_wan14b_warmup_switch_then_post_stream():
     frac = check_kv_accounting(st5, chunks - 1)
     print(f"KV held at chunk {chunks - 1}: {frac:.4f} of all-full", flush=True)
     assert abs(frac - (1 - 0.5 * (1 - 2 / 40))) <= 1e-12
+
+
+def test_recalibration_reenters_warmup():
+    """Re-entering warmup after a switch (a small stream: 4 layers of 2 x 128
+    heads, 256-token chunks): warmup 0-3, switch with K = 2, post-switch 4-5,
+    re-entry at chunk 6, warmup 6-8, switch again, post-switch 9-10.
+
+    * the statistics restart from zero: after the first re-entered chunk, G, C
+      and r2 of every layer equal the oracle's statistics of that chunk alone
+      (from the A_loc and dA the GPU produced);
+    * an L-Layer's re-entered dual attention runs over its sink, its last
+      post-switch chunk and the new chunks (oracle groups with first_kept = 5),
+      sampled rows against the oracle;
+    * the second switch obeys the normal equations and sorts eps;
+    * the key accounting after it matches the oracle's groups per layer."""
+    from kv_cache_absorption_amd.stream import IspaStream
+    N, H, d, Tc, K = 4, 2, 128, 256, 2
+    si = synth.StreamInputs(N, H, d, Tc, torch.bfloat16, 21, DEV, workload=3)
+    st = IspaStream(N, H, d, Tc, 4, DEV)
+    for layer in range(N):
+        st.set_w(layer, si.w(layer))
+    for c in range(4):
+        for layer in range(N):
+            st.write_kv(layer, c, *si.kv(layer, c))
+            st.warmup(layer, c, si.q(layer, c))
+    st.switch(K)
+    first_sel = list(st.is_local_host)
+    for c in (4, 5):
+        for layer in range(N):
+            st.write_kv(layer, c, *si.kv(layer, c))
+            st.post(layer, c, si.q(layer, c))
+    st.recalibrate(6)
+    l_old = first_sel.index(1)
+    rows = [0, 1, 200, 255]
+    for c in (6, 7, 8):
+        for layer in range(N):
+            k, v = si.kv(layer, c)
+            st.write_kv(layer, c, k, v)
+            q = si.q(layer, c)
+            outs = st.warmup(layer, c, q)
+            if c == 6:
+                torch.cuda.synchronize()
+                G, C, r2 = O.accumulate_stats(outs[4].cpu(), outs[5].cpu(), st.W[layer].cpu())
+                Gg = np.triu(h64(st.G[layer]))
+                assert rel(Gg, np.triu(G)) <= 5e-4, layer
+                assert rel(h64(st.C[layer]), C) <= 5e-4, layer
+                assert abs(float(st.r2[layer]) - r2) <= 1e-5 * r2, layer
+            if c == 8 and layer == l_old:
+                first = 5  # its last post-switch chunk
+                loc_r, hist_r = O.stream_groups_kept(c, Tc, first)
+                seq_k = {j: si.kv(layer, j)[0].cpu() for j in range(first, c + 1)}
+                seq_v = {j: si.kv(layer, j)[1].cpu() for j in range(first, c + 1)}
+                seq_k[0], seq_v[0] = (t.cpu() for t in si.kv(layer, 0))
+
+                def gather(ranges, src):
+                    parts = [src[r // Tc] for a, b in ranges for r in range(a, b, Tc)]
+                    return torch.cat(parts) if parts else torch.zeros((0, H, d), dtype=torch.bfloat16)
+                ref = O.dual_stream_attention(q[rows].cpu(), gather(loc_r, seq_k), gather(loc_r, seq_v),
+                                              gather(hist_r, seq_k), gather(hist_r, seq_v), st.scale)
+                assert rel(h64(outs[0][rows]), ref["o_loc"]) <= 5e-3
+                assert rel(h64(outs[2][rows]), ref["o_hist"]) <= 5e-3
+                assert np.abs(h64(outs[3][rows]) - ref["lse_hist"]).max() <= 2e-3
+    st.switch(K, evict=False)
+    check_switch(st, K)
+    sel2 = list(st.is_local_host)
+    st.evict()
+    for c in (9, 10):
+        for layer in range(N):
+            st.write_kv(layer, c, *si.kv(layer, c))
+            y = st.post(layer, c, si.q(layer, c))
+            assert bool(torch.isfinite(y).all())
+    held = st.keys_held(10)
+    for layer in range(N):
+        if sel2[layer]:
+            want = 2 * Tc
+        else:
+            first = 5 if first_sel[layer] else 1
+            loc_r, hist_r = O.stream_groups_kept(10, Tc, first)
+            want = sum(b - a for a, b in loc_r + hist_r)
+        assert held[layer] == want, (layer, held[layer], want)
+    print(f"selections {first_sel} -> {sel2}; keys held at chunk 10: {held}", flush=True)

@@ -9,7 +9,7 @@ import pytest
 from oracle import (accumulate_stats, dual_stream_attention, epsilon_from_stats,
                     group_attention, kv_bytes_retained, local_attn_proj,
                     remaining_kv_fraction, ridge_lambda, select_layers, solve_dw,
-                    stream_groups)
+                    stream_groups, stream_groups_kept)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -84,6 +84,43 @@ def test_stream_groups_partition():
         if c >= 1:
             assert loc[1] == (c * T, (c + 1) * T)
         assert (hist == []) == (c <= 1)
+
+
+def test_stream_groups_kept_reduces_to_full_history():
+    """A layer that never dropped history (first_kept = 1) has the groups of
+    the plain stream."""
+    T = 5
+    for c in range(8):
+        assert stream_groups_kept(c, T, 1) == stream_groups(c, T)
+
+
+def test_stream_groups_kept_against_held_chunk_sets():
+    """Brute force on chunk sets: a layer is full through chunk s - 1, becomes
+    an L-Layer at the switch (it then holds the sink and its current chunk
+    only), and re-enters warmup at chunk r (holding the sink and chunk r - 1).
+    From then on every arriving chunk is kept.  At each warmup chunk c >= r the
+    local group must be {sink, c} and the history every other held chunk below
+    c; the oracle's ranges must name exactly those chunks."""
+    T = 3
+
+    def chunks(ranges):
+        out = set()
+        for a, b in ranges:
+            assert a % T == 0 and b % T == 0
+            out |= set(range(a // T, b // T))
+        return out
+
+    for s in range(2, 6):
+        for r in range(s + 1, s + 5):
+            held = set(range(s))            # full through the warmup
+            for c in range(s, r):           # post-switch L-Layer: sink + current
+                held = {0, c}
+            for c in range(r, r + 5):       # re-entered warmup
+                held.add(c)
+                loc, hist = stream_groups_kept(c, T, r - 1)
+                assert chunks(loc) == {0, c}
+                assert chunks(hist) == held - {0, c}
+                assert not (chunks(loc) & chunks(hist))
 
 
 def test_table2_remaining_kv_identity():

@@ -57,3 +57,53 @@ def test_keys_retained_matches_oracle_bytes():
         n_full = n_loc + sum(b - a for a, b in ohist)
         assert n == [n_loc if f else n_full for f in flags]
         assert kv_bytes(n, D) == O.kv_bytes_retained(n, D)
+
+
+def _check_groups(kv, c, T, oloc, ohist):
+    loc, hist = kv.warmup_groups(c)
+    for got, want in ((loc, oloc), (hist, ohist)):
+        got_chunks = [int(x) for k, _ in got for x in k[:, 0, 0].tolist()]
+        want_chunks = [r // T for a, b in want for r in range(a, b)]
+        assert got_chunks == want_chunks
+
+
+def test_reentered_warmup_groups_follow_oracle():
+    """An L-Layer that re-enters warmup holds its sink and last chunk, then
+    keeps every arriving chunk; its groups are the oracle's for that
+    first-kept chunk.  A layer that stayed full keeps the plain groups."""
+    T, H, d = 2, 1, 4
+    for post_chunks in (1, 3):
+        kv_l = LayerKV(6, T, H, d, torch.float32, "cpu")
+        kv_f = LayerKV(6, T, H, d, torch.float32, "cpu")
+        for c in range(5):                      # warmup 0..4
+            _fill(kv_l, c, T, H, d)
+            _fill(kv_f, c, T, H, d)
+        kv_l.evict_history()                    # switch: kv_l is an L-Layer
+        r = 5 + post_chunks
+        for c in range(5, r):                   # post-switch chunks
+            _fill(kv_l, c, T, H, d)
+            _fill(kv_f, c, T, H, d)
+        for kv in (kv_l, kv_f):
+            kv.keep_from(r)                     # re-enter warmup at chunk r
+        assert not kv_l.local_only
+        for c in range(r, r + 4):
+            _fill(kv_l, c, T, H, d)
+            _fill(kv_f, c, T, H, d)
+            _check_groups(kv_l, c, T, *O.stream_groups_kept(c, T, r - 1))
+            _check_groups(kv_f, c, T, *O.stream_groups(c, T))
+            assert kv_l.keys_held(c) == T * (2 + c - (r - 1))
+            assert kv_f.keys_held(c) == T * (c + 1)
+
+
+def test_reentry_right_after_eviction_holds_sink_only():
+    """With no chunk written since the eviction, re-entering at chunk r keeps
+    only the sink: history starts at r."""
+    T, H, d = 2, 1, 4
+    kv = LayerKV(4, T, H, d, torch.float32, "cpu")
+    for c in range(4):
+        _fill(kv, c, T, H, d)
+    kv.evict_history()
+    kv.keep_from(4)
+    for c in range(4, 7):
+        _fill(kv, c, T, H, d)
+        _check_groups(kv, c, T, *O.stream_groups_kept(c, T, 4))
