@@ -114,6 +114,10 @@ STREAMS = {
     # re-calibration: warmup 0-5, switch, post 6-11, warmup re-entered at 12
     # (12-17), switch again, post 18-23
     "wan13b_recal": dict(N=30, H=12, d=128, chunks=24, warm=6, K=15, wid=3, recal=12, warm2=6),
+    # budget / warmup sweep: one 8-chunk (24-frame) warmup, evaluated after
+    # 2, 4, 6 and 8 chunks (6-24 frames) for x = 0.3, 0.4, 0.5, 0.7
+    "wan13b_sweep": dict(N=30, H=12, d=128, chunks=8, warm=8, K=15, wid=3,
+                         evaluate_at=(2, 4, 6, 8), xs=(0.3, 0.4, 0.5, 0.7)),
 }
 TOKENS_PER_CHUNK = 4680  # 3 latent frames of 1560 tokens
 
@@ -146,6 +150,7 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
     recs = []
     switch_ev = []
     selections = []
+    evaluations = []
     recal, warm2 = spec.get("recal"), spec.get("warm2", 0)
 
     def switch_now(evict=True):
@@ -178,6 +183,13 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
             e = ev()
             e.record(stream)
             marks.append(e)
+        if spec.get("evaluate_at") and c + 1 in spec["evaluate_at"]:
+            Ks = [round(x * N) for x in spec["xs"]]
+            v0, v1 = ev(), ev()
+            v0.record(stream)
+            eps_e, sels_e, _, _ = st.evaluate(Ks)
+            v1.record(stream)
+            evaluations.append(dict(chunks=c + 1, eps=eps_e, sels=sels_e, ev=(v0, v1)))
         # keys each layer's call attends to (local + history during warmup)
         n_keys = st.keys_held(c)
         recs.append(dict(c=c, warm=warm, phase=0 if recal is None or c < recal else 1,
@@ -196,6 +208,10 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
         del r["start"], r["marks"]
     switch_ms = [a.elapsed_time(b) for a, b in switch_ev]
     st.selection_history = selections
+    st.evaluations = [dict(chunks=e["chunks"], ms=e["ev"][0].elapsed_time(e["ev"][1]),
+                           eps=[float(x) for x in e["eps"].cpu()],
+                           sels={K: sorted(v.cpu().tolist()) for K, v in e["sels"].items()})
+                      for e in evaluations]
     return recs, (switch_ms[0] if switch_ms else None), st, switch_ms
 
 
@@ -250,6 +266,20 @@ def run_stream(args, name, dev):
         pre["warmup re-entered at chunk"] = spec["recal"]
         pre["switch ms (each switch)"] = [round(x, 3) for x in switches]
         pre["L-Layers (each switch)"] = st.selection_history
+    if spec.get("evaluate_at"):
+        r20 = 2 / 20  # local share of the keys at chunk 19 of a 20-chunk stream
+        sweep = []
+        for e in st.evaluations:
+            eps_sorted = sorted(e["eps"])
+            for x, K in zip(spec["xs"], sorted(e["sels"])):
+                sweep.append({"warmup_frames": 3 * e["chunks"], "x": x, "K": K,
+                              "L-Layers": e["sels"][K],
+                              "eps_sum_selected": sum(eps_sorted[:K]),
+                              "kv_fraction_at_chunk_19": round(1 - x * (1 - r20), 4)})
+        pre["sweep"] = sweep
+        pre["evaluate ms (solve all layers + 4 selections)"] = [round(e["ms"], 3) for e in st.evaluations]
+        pre["selection overlap (x=0.5) with the 24-frame selection"] = [
+            len(set(e["sels"][15]) & set(st.evaluations[-1]["sels"][15])) for e in st.evaluations]
     last = recs[-1]
     c_last = last["c"]
     full_bytes = 2 * N * (c_last + 1) * T * D * 2

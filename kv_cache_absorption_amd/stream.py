@@ -309,6 +309,37 @@ class IspaStream:
             self.evict()
         return self.selected[:K], self.is_local, self.eps
 
+    def evaluate(self, Ks):
+        """Solve every layer on the statistics gathered so far and select the
+        K lowest-eps layers for each K in ``Ks``, without ending the warmup
+        (a budget / warmup-length sweep: the pages' ablation axes x = K / N and
+        the warmup length; EN review, Ablation Study).  The statistics are not
+        modified; warmup may continue afterwards.  Returns (eps [N] fp64,
+        {K: selected int32 [K]}, {K: is_local uint8 [N]}) on the device, plus
+        the solve's info."""
+        if self.switched or self.G is None:
+            raise RuntimeError("evaluate runs during warmup")
+        L, s, N, D, dev = self.L, self._stream(), self.N, self.D, self.device
+        dW = torch.empty((N, D, D), dtype=torch.float32, device=dev)
+        eps = torch.empty(N, dtype=torch.float64, device=dev)
+        info = torch.empty(N, dtype=torch.int32, device=dev)
+        need = L.ispa_solve_dw_workspace_bytes(N, D)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self._ck(L.ispa_solve_dw(N, D, self.G.data_ptr(), self.C.data_ptr(), self.r2.data_ptr(), D * D,
+                                 self.lambda_abs, self.lambda_rel, dW.data_ptr(), eps.data_ptr(),
+                                 info.data_ptr(), None, B.ISPA_BF16, None, ws.data_ptr(), need, s))
+        sels, masks = {}, {}
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+        for K in Ks:
+            if not 0 <= K <= N:
+                raise ValueError("K must lie in 0 .. n_layers")
+            sel = torch.empty(max(K, 1), dtype=torch.int32, device=dev)
+            mask = torch.empty(N, dtype=torch.uint8, device=dev)
+            self._ck(L.ispa_select_layers(N, K, eps.data_ptr(), sel.data_ptr(), mask.data_ptr(),
+                                          status.data_ptr(), s))
+            sels[K], masks[K] = sel[:K], mask
+        return eps, sels, masks, info
+
     def evict(self):
         """Free the history rows of every L-Layer; drop the statistics."""
         for layer, flag in enumerate(self.is_local_host):

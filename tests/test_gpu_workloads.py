@@ -291,3 +291,45 @@ def test_recalibration_reenters_warmup():
             want = sum(b - a for a, b in loc_r + hist_r)
         assert held[layer] == want, (layer, held[layer], want)
     print(f"selections {first_sel} -> {sel2}; keys held at chunk 10: {held}", flush=True)
+
+
+def test_budget_and_warmup_sweep():
+    """evaluate() during warmup (4 layers of 2 x 128 heads, 256-token chunks):
+    after 2 and after 4 warmup chunks, for K = 1..4, every selection is the
+    first K of a stable sort of that eps, the selections are nested in K, the
+    statistics are untouched (warmup goes on), and eps after the last warmup
+    chunk equals the switch's eps on the same statistics."""
+    from kv_cache_absorption_amd.stream import IspaStream
+    N, H, d, Tc = 4, 2, 128, 256
+    si = synth.StreamInputs(N, H, d, Tc, torch.bfloat16, 31, DEV, workload=3)
+    st = IspaStream(N, H, d, Tc, 4, DEV)
+    for layer in range(N):
+        st.set_w(layer, si.w(layer))
+    Ks = [1, 2, 3, 4]
+    evals = {}
+    for c in range(4):
+        for layer in range(N):
+            st.write_kv(layer, c, *si.kv(layer, c))
+            st.warmup(layer, c, si.q(layer, c))
+        if c in (1, 3):
+            G0 = st.G.clone()
+            eps, sels, masks, info = st.evaluate(Ks)
+            torch.cuda.synchronize()
+            assert int(info.abs().max()) == 0
+            assert torch.equal(st.G, G0)
+            e = [float(x) for x in eps.cpu()]
+            order = sorted(range(N), key=lambda i: (e[i], i))
+            prev = set()
+            for K in Ks:
+                got = sels[K].cpu().tolist()
+                assert got == order[:K]
+                assert prev <= set(got)
+                prev = set(got)
+                assert masks[K].cpu().tolist() == [1 if i in got else 0 for i in range(N)]
+            evals[c] = e
+    st.switch(2, evict=False)
+    e_sw = [float(x) for x in st.eps.cpu()]
+    for a, b in zip(evals[3], e_sw):
+        assert abs(a - b) <= 1e-12 * max(abs(b), 1.0)
+    print(f"eps after 2 chunks {['%.4g' % x for x in evals[1]]}, after 4 {['%.4g' % x for x in evals[3]]}",
+          flush=True)
