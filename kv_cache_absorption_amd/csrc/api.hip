@@ -291,8 +291,28 @@ size_t ispa_local_attn_proj_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t 
   if (n_q <= 0 || H < 1 || n_segs < 0 || n_segs > ISPA_MAX_SEGS) return 0;
   HostGroup g[1] = {{segs, n_segs}};
   const SplitPlan plan = plan_splits(attn_block_q(dt, d), n_q, H, g, 1);
-  return align256((size_t)n_q * H * d * 4) + align256((size_t)n_q * H * 4) +
+  const size_t D = (size_t)H * d;
+  // fp32 attention output and LSE, its 16-bit copy and W^T for the projection GEMM, split parts
+  const size_t proj = dt == ISPA_F32 ? 0 : align256((size_t)n_q * D * 2) + align256(D * D * 2);
+  return align256((size_t)n_q * D * 4) + align256((size_t)n_q * H * 4) + proj +
          split_workspace_bytes(n_q, H, d, plan, 1);
+}
+
+// Width of the projection GEMM's tiles: the one whose last wave of workgroups
+// leaves the fewest CU-tiles idle (256 CUs, one workgroup each).
+static int proj_tile_n(int64_t n_q, int32_t D) {
+  const int64_t tm = (n_q + kNtBM - 1) / kNtBM;
+  int best = 128;
+  int64_t best_cost = -1;
+  for (int bn : {256, 128}) {
+    const int64_t tiles = tm * ((D + bn - 1) / bn);
+    const int64_t cost = (tiles + 255) / 256 * bn;  // waves x tile width
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = bn;
+    }
+  }
+  return best;
 }
 
 ispa_status ispa_local_attn_proj(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale, const void* q,
@@ -317,13 +337,46 @@ ispa_status ispa_local_attn_proj(ispa_dtype dt, int64_t n_q, int32_t H, int32_t 
   float* O = (float*)ws;
   float* lse = (float*)((char*)ws + align256((size_t)n_q * D * 4));
   char* rest = (char*)lse + align256((size_t)n_q * H * 4);
+  uint16_t* O16 = nullptr;
+  uint16_t* Wt = nullptr;
+  if (dt != ISPA_F32) {
+    O16 = (uint16_t*)rest;
+    rest += align256((size_t)n_q * D * 2);
+    Wt = (uint16_t*)rest;
+    rest += align256((size_t)D * D * 2);
+  }
+  // The NT GEMM stores 4 consecutive outputs per lane and reads W in 8-byte pieces.
+  const bool nt = dt != ISPA_F32 && aligned(y, y_dt == ISPA_F32 ? 16 : 8) && aligned(w_proj, 8);
   HostGroup g[1] = {{segs, n_segs}};
   float* oo[1] = {O};
   float* ll[1] = {lse};
   st = run_group_attention(dt, n_q, H, d, scale, q, q_stride, g, 1, oo, ll, rest,
-                           ws_bytes - (size_t)(rest - (char*)ws), stream);
+                           ws_bytes - (size_t)(rest - (char*)ws), stream, nt ? O16 : nullptr, ISPA_BF16);
   if (st) return st;
   if (dt == ISPA_F32) return launch_proj_f32(n_q, D, O, (const float*)w_proj, y, y_dt, stream);
+  if (nt) {
+    // y = O W: W^T (bf16) once, then the K-contiguous GEMM over the bf16 attention output
+    if ((st = launch_transpose16(w_proj, D, D, D, Wt, D, D, w_dt, ISPA_BF16, stream))) return st;
+    NtGemmParams p{};
+    p.M = n_q;
+    p.N = D;
+    p.K = D;
+    p.x = O16;
+    p.ldx = D;
+    p.y = Wt;
+    p.ldy = D;
+    p.y_rows = D;
+    p.epi = kNtStore;
+    p.out = y;
+    p.out_dt = y_dt;
+    p.ld_out = D;
+    p.bn = proj_tile_n(n_q, D);
+    p.tiles_m = (int)((n_q + kNtBM - 1) / kNtBM);
+    p.tiles_n = (int)((D + p.bn - 1) / p.bn);
+    p.ksplit = 1;
+    p.kchunk = D;
+    return launch_nt_gemm(p, ISPA_BF16, stream, nullptr);
+  }
   GemmParams p{};
   p.M = n_q;
   p.N = D;

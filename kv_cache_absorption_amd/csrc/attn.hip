@@ -1050,6 +1050,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   for (int v = 0; v < V; ++v) {
     const int64_t o = off + 4 * v;
     if (p.o_full) *(f32x4*)(p.o_full + o) = acc[v];
+    if (p.o16) {
+      const bool bf = p.o16_dt == ISPA_BF16;
+      auto pk = [&](float x, float y) { return bf ? pack_bf16(x, y) : pack_f16(x, y); };
+      *(u32x2*)((uint16_t*)p.o16 + o) = (u32x2){pk(acc[v][0], acc[v][1]), pk(acc[v][2], acc[v][3])};
+    }
     const f32x4 dl = acc[v] - o0[v];
     if (p.out_dt == ISPA_F32) {
       if (p.a0) *(f32x4*)((float*)p.a0 + o) = o0[v];
@@ -1061,6 +1066,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
       if (p.delta) *(u32x2*)((uint16_t*)p.delta + o) = (u32x2){pk(dl[0], dl[1]), pk(dl[2], dl[3])};
     }
   }
+}
+
+// out[i .. i+3] = in[i .. i+3] rounded to 16-bit out_dt (n a multiple of 4)
+__global__ __launch_bounds__(256) void to16_kernel(const float* in, int64_t n, uint16_t* out, int out_dt) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  const f32x4 v = *(const f32x4*)(in + i);
+  const bool bf = out_dt == ISPA_BF16;
+  auto pk = [&](float x, float y) { return bf ? pack_bf16(x, y) : pack_f16(x, y); };
+  *(u32x2*)(out + i) = (u32x2){pk(v[0], v[1]), pk(v[2], v[3])};
 }
 
 }  // namespace
@@ -1138,7 +1153,7 @@ size_t split_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan&
 ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale,
                                 const void* q, int64_t q_stride, const HostGroup* groups,
                                 int n_groups, float* const* o_out, float* const* lse_out,
-                                void* ws, size_t ws_bytes, hipStream_t stream) {
+                                void* ws, size_t ws_bytes, hipStream_t stream, void* o16_g0, int o16_dt) {
   if (n_q == 0) return ISPA_OK;
   AttnParams p{};
   p.q = q;
@@ -1185,6 +1200,11 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
     mp.o_full = o_out[g];
     mp.lse_full = lse_out[g];
     mp.out_dt = ISPA_F32;
+    if (g == 0 && o16_g0) {  // the 16-bit output replaces the fp32 one
+      mp.o16 = o16_g0;
+      mp.o16_dt = o16_dt;
+      mp.o_full = nullptr;
+    }
     for (int s = 0; s < plan.n_splits[g]; ++s) {
       float* po = (float*)wsp;
       wsp += align256((size_t)n_q * H * d * 4);
@@ -1235,6 +1255,12 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
   for (int i = 0; i < n_merges; ++i) {
     st = launch_merge(merges[i], stream);
     if (st != ISPA_OK) return st;
+  }
+  if (o16_g0 && plan.n_splits[0] == 1) {  // unsplit group 0: its fp32 output, rounded
+    const int64_t n = n_q * H * d;       // d is a multiple of 4
+    hipLaunchKernelGGL(to16_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, o_out[0], n,
+                       (uint16_t*)o16_g0, o16_dt);
+    return check_launch("to16_kernel");
   }
   return ISPA_OK;
 }

@@ -69,10 +69,13 @@ size_t split_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan&
 // Run attention for n_groups (1 or 2) groups.  For each group the final
 // normalised o / lse go to o_out[g] / lse_out[g]; split groups use ws for
 // partials and are merged with the LSE rule.
+// With o16_g0 set, group 0's output is (also) written there as 16-bit o16_dt;
+// when group 0 is split into merged parts, that replaces its fp32 output.
 ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale,
                                 const void* q, int64_t q_stride, const HostGroup* groups,
                                 int n_groups, float* const* o_out, float* const* lse_out,
-                                void* ws, size_t ws_bytes, hipStream_t stream);
+                                void* ws, size_t ws_bytes, hipStream_t stream,
+                                void* o16_g0 = nullptr, int o16_dt = ISPA_BF16);
 
 // n-way merge used both by the public call and by split combining.
 struct MergeParams {
@@ -86,6 +89,8 @@ struct MergeParams {
   void* a0;
   void* delta;
   int32_t out_dt;
+  void* o16;       // optional: the merged output again, as 16-bit o16_dt
+  int32_t o16_dt;
 };
 ispa_status launch_merge(const MergeParams& p, hipStream_t stream);
 

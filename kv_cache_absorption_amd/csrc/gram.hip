@@ -287,6 +287,29 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
     if (tid == 0) p.sq_partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
     return;
   }
+  if (p.epi == kNtStore) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 32 + lq;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + wn * WN + j * 32 + g * 8 + hh * 4;  // N is a multiple of 4
+          if (n >= p.N) continue;
+          const f32x4 v = {acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
+          if (p.out_dt == ISPA_F32) {
+            *(f32x4*)((float*)p.out + m * p.ld_out + n) = v;
+          } else {
+            const bool bf = p.out_dt == ISPA_BF16;
+            auto pk = [&](float x, float y) { return bf ? pack_bf16(x, y) : pack_f16(x, y); };
+            *(u32x2*)((uint16_t*)p.out + m * p.ld_out + n) = (u32x2){pk(v[0], v[1]), pk(v[2], v[3])};
+          }
+        }
+    }
+    return;
+  }
   float* outf = (float*)(kind1 ? p.out2 : p.out);
   const bool tri_tile = p.tri && !kind1;
   if (p.ksplit > 1) {

@@ -8,8 +8,9 @@ namespace ispa {
 enum {
   kNtAccum = 0,   // out[m][n] += acc (fp32), upper triangle for first-kind tiles if tri; with a K split the
                   // workgroups store partial sums to part[split][kind] (layout of out) for nt_split_reduce
-  kNtStoreT = 1   // out[m][n] = acc as 16-bit (mfma type) for n < n_valid, 0 for n_valid <= n < N;
+  kNtStoreT = 1,  // out[m][n] = acc as 16-bit (mfma type) for n < n_valid, 0 for n_valid <= n < N;
                   // per-workgroup sum of squares of the stored values
+  kNtStore = 2    // out[m][n] = acc as out_dt (bf16, f16 or fp32)
 };
 
 struct NtGemmParams {
@@ -31,6 +32,7 @@ struct NtGemmParams {
   int64_t kchunk;
   double* sq_partials;
   float* part;        // kNtAccum with ksplit > 1: [ksplit][2][M][ld_out] partial sums
+  int32_t out_dt;     // kNtStore
 };
 
 ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t stream, int* n_blocks_out);

@@ -381,6 +381,7 @@ def test_select_parity():
     (2, 128, 300, [64, 300], torch.float32),        # L-layer: sink + current
     (2, 128, 130, [64, 500, 700, 130], torch.bfloat16),  # F-layer, several segments
     (4, 64, 200, [5000], torch.float32),             # long single segment (split)
+    (12, 128, 600, [4680, 700], torch.bfloat16),     # D = 1536: several GEMM tiles, ragged rows
 ])
 def test_local_attn_proj_parity(H, d, n_q, seg_lens, y_dt):
     print(f"local_attn_proj H={H} d={d} n_q={n_q} segs={seg_lens} {y_dt}", flush=True)
@@ -392,6 +393,20 @@ def test_local_attn_proj_parity(H, d, n_q, seg_lens, y_dt):
     torch.cuda.synchronize()
     ref = O.local_attn_proj(q.cpu(), torch.cat([s[0] for s in segs]).cpu(),
                             torch.cat([s[1] for s in segs]).cpu(), w.cpu(), d ** -0.5)
+    assert rel(h64(y), ref) <= 5e-3
+
+
+def test_local_attn_proj_f16_weight():
+    """W given as fp16: converted to the bf16 GEMM operand on its transpose."""
+    H, d, n_q = 4, 128, 333
+    print(f"local_attn_proj f16 W H={H} n_q={n_q}", flush=True)
+    D = H * d
+    q = _cache(n_q, H, d, 32)
+    k, v = _cache(900, H, d, 41), _cache(900, H, d, 61)
+    w = synth.normal((D, D), 91, DEV, std=D ** -0.5).to(torch.float16)
+    y = K().ispa_local_attn_proj(q, [(k, v)], w, d ** -0.5, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.local_attn_proj(q.cpu(), k.cpu(), v.cpu(), w.cpu(), d ** -0.5)
     assert rel(h64(y), ref) <= 5e-3
 
 
