@@ -271,7 +271,7 @@ def _stats_for_solve(D, n, seed, planted=False):
     return G.astype(np.float32), C.astype(np.float32), r2, w
 
 
-@pytest.mark.parametrize("D,L", [(128, 3), (256, 1), (1536, 1)])
+@pytest.mark.parametrize("D,L", [(64, 2), (128, 3), (256, 1), (1536, 1)])
 def test_solve_parity(D, L):
     print(f"solve_dw D={D} layers={L}", flush=True)
     Gs, Cs, rs, ws = zip(*[_stats_for_solve(D, 3 * D, 50 + l) for l in range(L)])
