@@ -5,14 +5,18 @@ One step is one full cycle of the Wan-1.3B-shaped single-layer workload
 (12 heads x 128 = 1536 wide, 4680 queries per chunk, a 4680-key sink, a
 28080-key history, fresh current chunk each step):
 
-  8 warmup chunk steps, each ispa_dual_attn -> ispa_lse_merge -> ispa_accum_stats
+  8 warmup chunk steps, each ispa_dual_attn_merge (dual-stream attention and
+    the LSE merge into A_loc, A_full - A_loc) -> ispa_accum_stats
   the switch: ispa_solve_dw (dW, eps, W + dW) -> ispa_select_layers (K = 1 of 1)
   one post-switch chunk of the (local) layer: ispa_local_attn_proj with W + dW
 
 All inputs are generated on the GPU before the timed region.  Prints one JSON
 line; the headline value is dual-stream attention + LSE merge TFLOP/s (QK^T
-and PV flops, 4 n_q n_k D per chunk, over the time of the two calls), with
-Gram-statistics TFLOP/s and ms per warmup chunk beside it.
+and PV flops, 4 n_q n_k D per chunk, over the time of the fused call), with
+Gram-statistics TFLOP/s and ms per warmup chunk beside it.  The same chunks
+through the two separate calls (ispa_dual_attn, then ispa_lse_merge) are
+timed after the timed steps and reported beside it; the roofline entry is the
+ispa_dual_attn call.
 
 Other workloads (``--workload``), each one pass of a chunked stream through
 IspaStream, timed per chunk with HIP events around the ISPA calls of all
@@ -409,8 +413,10 @@ def main():
         ls, nl = segs([(g.sink_k, g.sink_v), (kc, vc)])
         hs, nh = segs([(g.hist_k, g.hist_v)])
         seg_tables.append((q, ls, nl, hs, nh))
-    ws_attn_b = L.ispa_dual_attn_workspace_bytes(B.ISPA_BF16, n_q, H, d, seg_tables[0][1], 2,
-                                                 seg_tables[0][3], 1)
+    ws_attn_b = max(L.ispa_dual_attn_workspace_bytes(B.ISPA_BF16, n_q, H, d, seg_tables[0][1], 2,
+                                                     seg_tables[0][3], 1),
+                    L.ispa_dual_attn_merge_workspace_bytes(B.ISPA_BF16, n_q, H, d, seg_tables[0][1], 2,
+                                                           seg_tables[0][3], 1))
     ws_stats_b = L.ispa_accum_stats_workspace_bytes(B.ISPA_F16, n_q, D)
     ws_solve_b = L.ispa_solve_dw_workspace_bytes(1, D)
     post_segs, post_n = segs([(g.sink_k, g.sink_v), (k_post, v_post)])
@@ -436,7 +442,7 @@ def main():
             raise B.IspaError(st, L.ispa_last_error().decode())
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    rec = {"attn": [], "merge": [], "stats": [], "switch": [], "post": []}
+    rec = {"fused": [], "attn": [], "merge": [], "stats": [], "switch": [], "post": []}
 
     def cycle(timed):
         G.zero_()
@@ -444,19 +450,15 @@ def main():
         r2.zero_()
         marks = []
         for (q, ls, nl, hs, nh) in seg_tables:
-            e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+            e0, e1, e2 = ev(), ev(), ev()
             e0.record(stream)
-            ck(L.ispa_dual_attn(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
-                                o_loc.data_ptr(), lse_loc.data_ptr(), o_hist.data_ptr(), lse_hist.data_ptr(),
-                                wsp, wsn, sh))
+            ck(L.ispa_dual_attn_merge(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs,
+                                      nh, a_loc.data_ptr(), delta.data_ptr(), B.ISPA_F16, None, wsp, wsn, sh))
             e1.record(stream)
-            ck(L.ispa_lse_merge(2, op, lp, n_q, H, d, None, None, a_loc.data_ptr(), delta.data_ptr(),
-                                B.ISPA_F16, sh))
-            e2.record(stream)
             ck(L.ispa_accum_stats(B.ISPA_F16, B.ISPA_BF16, n_q, D, a_loc.data_ptr(), delta.data_ptr(),
                                   g.w.data_ptr(), G.data_ptr(), C.data_ptr(), r2.data_ptr(), wsp, wsn, sh))
-            e3.record(stream)
-            marks.append((e0, e1, e2, e3))
+            e2.record(stream)
+            marks.append((e0, e1, e2))
         s0, s1, s2 = ev(), ev(), ev()
         s0.record(stream)
         ck(L.ispa_solve_dw(1, D, G.data_ptr(), C.data_ptr(), r2.data_ptr(), D * D, 0.0, 1e-3, dW.data_ptr(),
@@ -479,11 +481,27 @@ def main():
         cycle(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the same warmup chunks through the two separate calls (after the timed steps)
+    two_call = []
+    for (q, ls, nl, hs, nh) in seg_tables:
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        ck(L.ispa_dual_attn(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
+                            o_loc.data_ptr(), lse_loc.data_ptr(), o_hist.data_ptr(), lse_hist.data_ptr(),
+                            wsp, wsn, sh))
+        e1.record(stream)
+        ck(L.ispa_lse_merge(2, op, lp, n_q, H, d, None, None, a_loc.data_ptr(), delta.data_ptr(),
+                            B.ISPA_F16, sh))
+        e2.record(stream)
+        two_call.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    for e0, e1, e2 in two_call:
+        rec["attn"].append(e0.elapsed_time(e1))
+        rec["merge"].append(e1.elapsed_time(e2))
     for marks, (s0, s1, s2) in rec.pop("_pending", []):
-        for e0, e1, e2, e3 in marks:
-            rec["attn"].append(e0.elapsed_time(e1))
-            rec["merge"].append(e1.elapsed_time(e2))
-            rec["stats"].append(e2.elapsed_time(e3))
+        for e0, e1, e2 in marks:
+            rec["fused"].append(e0.elapsed_time(e1))
+            rec["stats"].append(e1.elapsed_time(e2))
         rec["switch"].append(s0.elapsed_time(s1))
         rec["post"].append(s1.elapsed_time(s2))
     if int(info[0]) != 0 or int(status[0]) != 0 or not torch.isfinite(eps).all():
@@ -493,10 +511,11 @@ def main():
     attn_flops = 4.0 * n_q * (n_loc + n_hist) * D
     stats_flops = 5.0 * n_q * D * D + 3.0 * n_q * D
     merge_bytes = 2 * (4 * n_q * D + 4 * n_q * H) + 2 * 2 * n_q * D
+    t_fused = mean(rec["fused"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
     t_merge = mean(rec["merge"]) * 1e-3
     t_stats = mean(rec["stats"]) * 1e-3
-    value = attn_flops / (t_attn + t_merge) / 1e12
+    value = attn_flops / t_fused / 1e12
     achieved = attn_flops / t_attn / 1e12
     traffic = _traffic("attn_bf16_wan13b_traffic.txt", "attn.hip")
     out = {
@@ -519,7 +538,9 @@ def main():
                    "warmup_chunks": n_warm, "stats_operands": "fp16", "seed": args.seed},
         "also": {
             "Gram-stat TFLOP/s": round(stats_flops / t_stats / 1e12, 2),
-            "ms/chunk (1 GPU)": round((t_attn + t_merge + t_stats) * 1e3, 4),
+            "ms/chunk (1 GPU)": round((t_fused + t_stats) * 1e3, 4),
+            "dual_attn_merge call ms": round(t_fused * 1e3, 4),
+            "two-call path TFLOP/s (ispa_dual_attn + ispa_lse_merge)": round(attn_flops / (t_attn + t_merge) / 1e12, 2),
             "merge GB/s": round(merge_bytes / t_merge / 1e9, 1),
             "switch ms (solve+select)": round(mean(rec["switch"]), 4),
             "post-switch chunk ms (local attn + W+dW)": round(mean(rec["post"]), 4),

@@ -126,6 +126,32 @@ ispa_status ispa_lse_merge(int32_t n_parts, const float* const* o_parts,
                            ispa_dtype out_dt, hipStream_t stream);
 
 /*
+ * ispa_dual_attn_merge -- dual-stream attention followed by the LSE merge in
+ * one call, for the warmup path (EN review, Key Design 1: the local and
+ * history groups are attended separately and their outputs combined by
+ * their log-sum-exp weights; the same review's Key Design 2 regresses
+ * A_full - A_loc on A_loc).
+ * Same inputs and grouping as ispa_dual_attn; the outputs are those that
+ * ispa_lse_merge would give on its (o_loc, o_hist) results:
+ *   a_loc    o_loc converted to out_dt, [n_q, D]   (A_loc)
+ *   delta    o - o_loc in fp32, converted to out_dt, [n_q, D], where o is the
+ *            merge of both groups                     (A_full - A_loc)
+ *   lse_full fp32 [n_q, H] LSE of both groups, or NULL.
+ * The groups' pieces are merged once, without materialising o_loc and o_hist
+ * in fp32.  out_dt: ISPA_F32, ISPA_BF16 or ISPA_F16.  a_loc and delta must be
+ * 16-byte aligned (8-byte for 16-bit out_dt).
+ */
+size_t ispa_dual_attn_merge_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d,
+                                            const ispa_seg* loc, int32_t n_loc,
+                                            const ispa_seg* hist, int32_t n_hist);
+ispa_status ispa_dual_attn_merge(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale,
+                                 const void* q, int64_t q_stride,
+                                 const ispa_seg* loc, int32_t n_loc,
+                                 const ispa_seg* hist, int32_t n_hist,
+                                 void* a_loc, void* delta, ispa_dtype out_dt, float* lse_full,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * ispa_accum_stats -- in-place accumulation of the regression statistics
  * (EN review, Key Design 2: activation outer products and activation-residual
  * cross statistics are accumulated over the warmup forward passes).

@@ -24,6 +24,7 @@ ISPA_MAX_SEGS = 8
 EXPORTED = [
     "ispa_version", "ispa_status_str", "ispa_last_error",
     "ispa_dual_attn_workspace_bytes", "ispa_dual_attn",
+    "ispa_dual_attn_merge_workspace_bytes", "ispa_dual_attn_merge",
     "ispa_lse_merge",
     "ispa_accum_stats_workspace_bytes", "ispa_accum_stats",
     "ispa_solve_dw_workspace_bytes", "ispa_solve_dw",
@@ -66,6 +67,9 @@ def lib() -> ctypes.CDLL:
             "ispa_dual_attn_workspace_bytes": (sz, [i32, i64, i32, i32, segp, i32, segp, i32]),
             "ispa_dual_attn": (i32, [i32, i64, i32, i32, f32, vp, i64, segp, i32, segp, i32,
                                      vp, vp, vp, vp, vp, sz, vp]),
+            "ispa_dual_attn_merge_workspace_bytes": (sz, [i32, i64, i32, i32, segp, i32, segp, i32]),
+            "ispa_dual_attn_merge": (i32, [i32, i64, i32, i32, f32, vp, i64, segp, i32, segp, i32,
+                                           vp, vp, i32, vp, vp, sz, vp]),
             "ispa_lse_merge": (i32, [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, i32,
                                      vp, vp, vp, vp, i32, vp]),
             "ispa_accum_stats_workspace_bytes": (sz, [i32, i64, i32]),
@@ -144,6 +148,29 @@ def ispa_dual_attn(q, loc, hist, scale: float | None = None):
                             o_loc.data_ptr(), lse_loc.data_ptr(), o_hist.data_ptr(),
                             lse_hist.data_ptr(), _ptr(ws), wsb, _stream(dev)))
     return o_loc, lse_loc, o_hist, lse_hist
+
+
+def ispa_dual_attn_merge(q, loc, hist, scale: float | None = None, out_dtype=torch.float16,
+                         want_lse=True):
+    """Dual-stream attention and the LSE merge in one call.  Returns (a_loc,
+    delta, lse_full): a_loc = o_loc and delta = o_full - o_loc as [n_q, D] of
+    out_dtype, lse_full fp32 [n_q, H] (None unless requested)."""
+    n_q, H, d, qs = _q_args(q)
+    dt = _DT[q.dtype]
+    scale = d ** -0.5 if scale is None else scale
+    ls, nl = _segs(loc, H, d)
+    hs, nh = _segs(hist, H, d)
+    dev = q.device
+    a_loc = torch.empty((n_q, H * d), dtype=out_dtype, device=dev)
+    delta = torch.empty_like(a_loc)
+    lse = torch.empty((n_q, H), dtype=torch.float32, device=dev) if want_lse else None
+    L = lib()
+    wsb = L.ispa_dual_attn_merge_workspace_bytes(dt, n_q, H, d, ls, nl, hs, nh)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_dual_attn_merge(dt, n_q, H, d, scale, q.data_ptr(), qs, ls, nl, hs, nh,
+                                  a_loc.data_ptr(), delta.data_ptr(), _DT[out_dtype], _ptr(lse),
+                                  _ptr(ws), wsb, _stream(dev)))
+    return a_loc, delta, lse
 
 
 def ispa_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],

@@ -124,6 +124,43 @@ ispa_status ispa_dual_attn(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, flo
   return run_group_attention(dt, n_q, H, d, scale, q, q_stride, g, 2, o, l, ws, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------- dual_attn_merge
+size_t ispa_dual_attn_merge_workspace_bytes(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d,
+                                            const ispa_seg* loc, int32_t n_loc, const ispa_seg* hist,
+                                            int32_t n_hist) {
+  if (n_q <= 0 || H < 1 || n_loc < 0 || n_hist < 0 || n_loc > ISPA_MAX_SEGS || n_hist > ISPA_MAX_SEGS)
+    return 0;
+  HostGroup g[2] = {{loc, n_loc}, {hist, n_hist}};
+  const SplitPlan plan = plan_splits(attn_block_q(dt, d), n_q, H, g, 2, 16);
+  return merged_workspace_bytes(n_q, H, d, plan, 2);
+}
+
+ispa_status ispa_dual_attn_merge(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale, const void* q,
+                                 int64_t q_stride, const ispa_seg* loc, int32_t n_loc, const ispa_seg* hist,
+                                 int32_t n_hist, void* a_loc, void* delta, ispa_dtype out_dt, float* lse_full,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  ispa_status st = check_attn_common(dt, n_q, H, d, q, q_stride);
+  if (st) return st;
+  if ((st = check_group("loc", dt, H, d, loc, n_loc))) return st;
+  if ((st = check_group("hist", dt, H, d, hist, n_hist))) return st;
+  if (!valid_dtype(out_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad out_dt");
+  if (n_q > 0 && (!a_loc || !delta)) return fail(ISPA_ERR_INVALID_ARG, "null output pointer");
+  const size_t oal = out_dt == ISPA_F32 ? 16 : 8;
+  if (!aligned(a_loc, oal) || !aligned(delta, oal))
+    return fail(ISPA_ERR_INVALID_ARG, "a_loc and delta must be 16-byte (fp32) or 8-byte (16-bit) aligned");
+  if (!std::isfinite(scale)) return fail(ISPA_ERR_INVALID_ARG, "scale must be finite");
+  const size_t need = ispa_dual_attn_merge_workspace_bytes(dt, n_q, H, d, loc, n_loc, hist, n_hist);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(ISPA_ERR_WORKSPACE, "dual_attn_merge workspace too small or misaligned");
+  if (n_q == 0) return ISPA_OK;
+  HostGroup g[2] = {{loc, n_loc}, {hist, n_hist}};
+  float* o[2] = {nullptr, nullptr};
+  float* l[2] = {nullptr, nullptr};
+  const MergeOut mo{a_loc, delta, out_dt, lse_full};
+  return run_group_attention(dt, n_q, H, d, scale, q, q_stride, g, 2, o, l, ws, ws_bytes, stream, nullptr,
+                             ISPA_BF16, &mo);
+}
+
 // ---------------------------------------------------------------- lse_merge
 ispa_status ispa_lse_merge(int32_t n_parts, const float* const* o_parts, const float* const* lse_parts,
                            int64_t n_q, int32_t H, int32_t d, float* o_full, float* lse_full, void* a0_out,

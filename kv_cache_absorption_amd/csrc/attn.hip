@@ -1032,16 +1032,28 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     for (int k = 0; k < p.n_parts; ++k) tot += exp2f((p.lse[k][row] - m) * kLog2e);  // exp2(-inf) = 0
   const float L = m != -INFINITY ? m + log2f(tot) * kLn2 : -INFINITY;
   const float inv = m != -INFINITY ? 1.0f / tot : 0.0f;
+  // the first n_first parts on their own (a0 and delta refer to their merge)
+  const int nf = p.n_first > 1 ? p.n_first : 1;
+  float m0 = -INFINITY;
+  for (int k = 0; k < nf; ++k) m0 = fmaxf(m0, p.lse[k][row]);
+  float tot0 = 0.0f;
+  if (m0 != -INFINITY)
+    for (int k = 0; k < nf; ++k) tot0 += exp2f((p.lse[k][row] - m0) * kLog2e);
+  const float inv0 = m0 != -INFINITY ? 1.0f / tot0 : 0.0f;
   const int64_t off = row * p.d + (int64_t)c * 4 * V;
   f32x4 acc[V], o0[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = o0[v] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < p.n_parts; ++k) {
-    const float w = m != -INFINITY ? exp2f((p.lse[k][row] - m) * kLog2e) * inv : 0.0f;
+    const float lk = p.lse[k][row];
+    const float w = m != -INFINITY ? exp2f((lk - m) * kLog2e) * inv : 0.0f;
+    // weight in the first group's merge (exactly 1 for a single finite first part)
+    const float w0 = k < nf && m0 != -INFINITY ? exp2f((lk - m0) * kLog2e) * inv0 : 0.0f;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const f32x4 ok = *(const f32x4*)(p.o[k] + off + 4 * v);
-      if (k == 0) o0[v] = ok;
+      if (k == 0 && nf == 1) o0[v] = ok;
+      else if (k < nf) o0[v] += w0 * ok;
       acc[v] += w * ok;
     }
   }
@@ -1097,7 +1109,7 @@ int attn_block_q(ispa_dtype dt, int32_t d) {
   return kBQ;
 }
 
-SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, int n_groups) {
+SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, int n_groups, int max_jobs) {
   SplitPlan plan;
   int64_t shortest = 0;
   int nonempty = 0;
@@ -1132,12 +1144,19 @@ SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, i
     const int64_t n = groups[g].n_keys();
     int s = (int)std::max<int64_t>(1, (n + piece - 1) / piece);
     s = std::min(s, 16);
-    if (total - 1 + s > kMaxJobs) s = std::max(1, kMaxJobs - (total - 1));
+    if (total - 1 + s > max_jobs) s = std::max(1, max_jobs - (total - 1));
     total += s - 1;
     plan.n_splits[g] = s;
     plan.split_len[g] = s > 1 ? (((n + s - 1) / s + kBK - 1) / kBK) * kBK : n;
   }
   return plan;
+}
+
+size_t merged_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan& plan, int n_groups) {
+  size_t total = 0;
+  for (int g = 0; g < n_groups; ++g)
+    total += plan.n_splits[g] * (align256((size_t)n_q * H * d * 4) + align256((size_t)n_q * H * 4));
+  return total;
 }
 
 size_t split_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan& plan, int n_groups) {
@@ -1153,7 +1172,8 @@ size_t split_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan&
 ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale,
                                 const void* q, int64_t q_stride, const HostGroup* groups,
                                 int n_groups, float* const* o_out, float* const* lse_out,
-                                void* ws, size_t ws_bytes, hipStream_t stream, void* o16_g0, int o16_dt) {
+                                void* ws, size_t ws_bytes, hipStream_t stream, void* o16_g0, int o16_dt,
+                                const MergeOut* merge_all) {
   if (n_q == 0) return ISPA_OK;
   AttnParams p{};
   p.q = q;
@@ -1170,8 +1190,9 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
       p.segs[g][s] = AttnSeg{sg.k, sg.v, sg.n, sg.k_stride, sg.v_stride};
     }
   }
-  const SplitPlan plan = plan_splits(bq, n_q, H, groups, n_groups);
-  if (split_workspace_bytes(n_q, H, d, plan, n_groups) > ws_bytes) {
+  const SplitPlan plan = plan_splits(bq, n_q, H, groups, n_groups, merge_all ? 16 : kMaxJobs);
+  if ((merge_all ? merged_workspace_bytes(n_q, H, d, plan, n_groups)
+                 : split_workspace_bytes(n_q, H, d, plan, n_groups)) > ws_bytes) {
     set_error("attention workspace too small");
     return ISPA_ERR_WORKSPACE;
   }
@@ -1187,7 +1208,34 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
   char* wsp = (char*)ws;
   MergeParams merges[2];
   int n_merges = 0;
-  for (int g = 0; g < n_groups; ++g) {
+  if (merge_all) {
+    // every group's pieces become parts of one merge
+    MergeParams mp{};
+    mp.d = d;
+    mp.n_rows = n_q * H;
+    mp.a0 = merge_all->a0;
+    mp.delta = merge_all->delta;
+    mp.out_dt = merge_all->out_dt;
+    mp.lse_full = merge_all->lse_full;
+    mp.n_first = plan.n_splits[0];
+    for (int g = 0; g < n_groups; ++g) {
+      const int64_t n = groups[g].n_keys();
+      for (int s = 0; s < plan.n_splits[g]; ++s) {
+        float* po = (float*)wsp;
+        wsp += align256((size_t)n_q * H * d * 4);
+        float* pl = (float*)wsp;
+        wsp += align256((size_t)n_q * H * 4);
+        const int64_t kb = std::min<int64_t>(n, s * plan.split_len[g]);
+        const int64_t ke = std::min<int64_t>(n, (s + 1) * plan.split_len[g]);
+        pend[nj++] = Pending{g, kb, ke, po, pl};
+        mp.o[mp.n_parts] = po;
+        mp.lse[mp.n_parts] = pl;
+        ++mp.n_parts;
+      }
+    }
+    merges[n_merges++] = mp;
+  }
+  for (int g = 0; g < n_groups && !merge_all; ++g) {
     const int64_t n = groups[g].n_keys();
     if (plan.n_splits[g] == 1) {
       pend[nj++] = Pending{g, 0, n, o_out[g], lse_out[g]};

@@ -61,21 +61,26 @@ struct SplitPlan {
 int attn_block_q(ispa_dtype dt, int32_t d);
 
 // Choose splits so the launch has enough equal-sized work units.
-SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, int n_groups);
+SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, int n_groups,
+                      int max_jobs = kMaxJobs);
 
 // Workspace bytes for the partial (o, lse) of the split groups.
 size_t split_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan& plan, int n_groups);
+// Partials of every group, split or not (the merged mode of run_group_attention).
+size_t merged_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan& plan, int n_groups);
 
 // Run attention for n_groups (1 or 2) groups.  For each group the final
 // normalised o / lse go to o_out[g] / lse_out[g]; split groups use ws for
 // partials and are merged with the LSE rule.
+struct MergeOut;
 // With o16_g0 set, group 0's output is (also) written there as 16-bit o16_dt;
 // when group 0 is split into merged parts, that replaces its fp32 output.
 ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, float scale,
                                 const void* q, int64_t q_stride, const HostGroup* groups,
                                 int n_groups, float* const* o_out, float* const* lse_out,
                                 void* ws, size_t ws_bytes, hipStream_t stream,
-                                void* o16_g0 = nullptr, int o16_dt = ISPA_BF16);
+                                void* o16_g0 = nullptr, int o16_dt = ISPA_BF16,
+                                const MergeOut* merge_all = nullptr);
 
 // n-way merge used both by the public call and by split combining.
 struct MergeParams {
@@ -91,6 +96,17 @@ struct MergeParams {
   int32_t out_dt;
   void* o16;       // optional: the merged output again, as 16-bit o16_dt
   int32_t o16_dt;
+  int32_t n_first;  // a0 and delta refer to the merge of parts [0, n_first) (0 means 1)
+};
+
+// All groups' parts merged in one pass (run_group_attention): a0 = the merged
+// first group, delta = merge of everything - a0, both as out_dt; lse_full the
+// merged LSE (optional).
+struct MergeOut {
+  void* a0;
+  void* delta;
+  int32_t out_dt;
+  float* lse_full;
 };
 ispa_status launch_merge(const MergeParams& p, hipStream_t stream);
 

@@ -211,15 +211,10 @@ class IspaStream:
             self.G = torch.zeros((n_layers, D, D), **f32)
             self.C = torch.zeros((n_layers, D, D), **f32)
             self.r2 = torch.zeros(n_layers, dtype=torch.float64, device=dev)
-        self.o_loc = torch.empty((T, H, d), **f32)
-        self.o_hist = torch.empty_like(self.o_loc)
-        self.lse_loc = torch.empty((T, H), **f32)
-        self.lse_hist = torch.empty_like(self.lse_loc)
+        self.lse_full = torch.empty((T, H), **f32)
         self.a_loc = torch.empty((T, D), dtype=stats_dtype, device=dev)
         self.delta = torch.empty_like(self.a_loc)
         self.y = torch.empty((T, D), dtype=dtype, device=dev)
-        self._op = (ctypes.c_void_p * 2)(self.o_loc.data_ptr(), self.o_hist.data_ptr())
-        self._lp = (ctypes.c_void_p * 2)(self.lse_loc.data_ptr(), self.lse_hist.data_ptr())
         self.ws = Workspace(dev)
         self.switched = False
         self.dW = self.eps = self.info = self.w_eff = None
@@ -247,9 +242,9 @@ class IspaStream:
     # ------------------------------------------------------------------ warmup
     def warmup(self, layer: int, c: int, q: torch.Tensor):
         """Chunk c of one layer during warmup: dual-stream attention over the
-        local and history groups, the LSE merge into A_loc and A_full - A_loc,
-        and the statistics update.  Returns (o_loc, lse_loc, o_hist, lse_hist,
-        a_loc, delta) views."""
+        local and history groups merged by their LSE into A_loc and
+        A_full - A_loc (one fused call), and the statistics update.  Returns
+        (a_loc, delta, lse_full) views."""
         if self.switched or self.G is None:
             raise RuntimeError("warmup needs the statistics and must come before the switch")
         if q.shape != (self.T, self.H, self.d) or q.dtype != self.dtype:
@@ -259,22 +254,19 @@ class IspaStream:
         ls, nl = self._segs(loc)
         hs, nh = self._segs(hist)
         n = self.T
-        need = max(L.ispa_dual_attn_workspace_bytes(B.ISPA_BF16, n, self.H, self.d, ls, nl, hs, nh),
+        need = max(L.ispa_dual_attn_merge_workspace_bytes(B.ISPA_BF16, n, self.H, self.d, ls, nl, hs, nh),
                    L.ispa_accum_stats_workspace_bytes(B._DT[self.stats_dtype], n, self.D))
         ws = self.ws.get(need)
         wsp = ws.data_ptr() if ws is not None else None
-        self._ck(L.ispa_dual_attn(B.ISPA_BF16, n, self.H, self.d, self.scale, q.data_ptr(), q.stride(0),
-                                  ls, nl, hs, nh, self.o_loc.data_ptr(), self.lse_loc.data_ptr(),
-                                  self.o_hist.data_ptr(), self.lse_hist.data_ptr(), wsp, need, s))
-        self._ck(L.ispa_lse_merge(2, self._op, self._lp, n, self.H, self.d, None, None,
-                                  self.a_loc.data_ptr(), self.delta.data_ptr(),
-                                  B._DT[self.stats_dtype], s))
+        self._ck(L.ispa_dual_attn_merge(B.ISPA_BF16, n, self.H, self.d, self.scale, q.data_ptr(), q.stride(0),
+                                        ls, nl, hs, nh, self.a_loc.data_ptr(), self.delta.data_ptr(),
+                                        B._DT[self.stats_dtype], self.lse_full.data_ptr(), wsp, need, s))
         self._ck(L.ispa_accum_stats(B._DT[self.stats_dtype], B.ISPA_BF16, n, self.D,
                                     self.a_loc.data_ptr(), self.delta.data_ptr(),
                                     self.W[layer].data_ptr(), self.G[layer].data_ptr(),
                                     self.C[layer].data_ptr(), self.r2[layer:layer + 1].data_ptr(),
                                     wsp, need, s))
-        return self.o_loc, self.lse_loc, self.o_hist, self.lse_hist, self.a_loc, self.delta
+        return self.a_loc, self.delta, self.lse_full
 
     # ------------------------------------------------------------------ switch
     def switch(self, K: int, evict: bool = True):

@@ -67,6 +67,26 @@ def test_dual_attn_rejects_bad_args():
                             FAKE, FAKE, FAKE, FAKE, None, 0, None) == m.ISPA_ERR_INVALID_ARG
 
 
+def test_dual_attn_merge_rejects_bad_args():
+    """The fused attention + merge call validates like ispa_dual_attn, plus
+    its output type and alignment; every error returns before any launch."""
+    m, L = _lib()
+    segs = _segarr(m, [_seg(10, ptr=FAKE)])
+
+    def call(out_dt=m.ISPA_F16, a_loc=FAKE, delta=FAKE, nl=1, ws=None, wsb=0, d=128):
+        return L.ispa_dual_attn_merge(m.ISPA_BF16, 4, 2, d, 0.1, FAKE, 256, segs, nl, segs, 1,
+                                      a_loc, delta, out_dt, None, ws, wsb, None)
+    assert call(d=96) == m.ISPA_ERR_UNSUPPORTED
+    assert call(nl=9) == m.ISPA_ERR_INVALID_ARG
+    assert call(out_dt=7) == m.ISPA_ERR_UNSUPPORTED
+    assert call(a_loc=None) == m.ISPA_ERR_INVALID_ARG
+    assert call(delta=FAKE + 4) == m.ISPA_ERR_INVALID_ARG            # 8-byte alignment for fp16
+    assert call(out_dt=m.ISPA_F32, a_loc=FAKE + 8) == m.ISPA_ERR_INVALID_ARG  # 16 for fp32
+    need = L.ispa_dual_attn_merge_workspace_bytes(m.ISPA_BF16, 4, 2, 128, segs, 1, segs, 1)
+    assert need > 0  # every piece goes through the workspace, split or not
+    assert call(ws=FAKE, wsb=need - 1) == m.ISPA_ERR_WORKSPACE
+
+
 def test_workspace_queries_and_errors():
     m, L = _lib()
     # Wan-1.3B layer: 37 q-tiles x 12 heads x 2 groups is below the split target,

@@ -198,6 +198,47 @@ def test_dual_attn_f32_and_merge_tiny():
     assert rel(h64(dl), ref_delta) <= 1e-4
 
 
+@pytest.mark.parametrize("dt,H,d,n_q,n_sink,n_cur,n_hist,out_dt", [
+    (torch.bfloat16, 2, 128, 300, 256, 300, 1700, torch.float16),   # history in several pieces
+    (torch.bfloat16, 2, 128, 600, 4680, 600, 300, torch.bfloat16),  # local longer: local split
+    (torch.bfloat16, 2, 128, 257, 128, 257, 0, torch.float32),      # empty history
+    (torch.float32, 2, 64, 64, 64, 64, 384, torch.float32),         # fp32 mode, tiny workload
+])
+def test_dual_attn_merge_parity(dt, H, d, n_q, n_sink, n_cur, n_hist, out_dt):
+    """The fused call against the oracle's dual-stream attention + merge, and
+    against the two-call path (ispa_dual_attn then ispa_lse_merge) on the same
+    inputs: A_loc equal, dA within fp32 reassociation of the merge."""
+    print(f"dual_attn_merge {dt} H={H} d={d} n_q={n_q} local={n_sink}+{n_cur} hist={n_hist} -> {out_dt}",
+          flush=True)
+    q = _cache(n_q, H, d, 131, dtype=dt)
+    loc = [(_cache(n_sink, H, d, 132, dtype=dt), _cache(n_sink, H, d, 133, dtype=dt)),
+           (_cache(n_cur, H, d, 134, dtype=dt), _cache(n_cur, H, d, 135, dtype=dt))]
+    hist = [(_cache(n_hist, H, d, 136, dtype=dt), _cache(n_hist, H, d, 137, dtype=dt))] if n_hist else []
+    a_loc, delta, lse = K().ispa_dual_attn_merge(q, loc, hist, out_dtype=out_dt)
+    o_l, l_l, o_h, l_h = K().ispa_dual_attn(q, loc, hist)
+    o_f, l_f, a0, dl = K().ispa_lse_merge([o_l, o_h], [l_l, l_h], out_dtype=out_dt)
+    torch.cuda.synchronize()
+    # the two GPU paths
+    assert torch.equal(a_loc, a0)
+    ulp = {torch.float32: 2.0 ** -23, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -10}[out_dt]
+    scale_full = float(o_f.abs().max())
+    assert float((delta.float() - dl.float()).abs().max()) <= 4 * ulp * scale_full + 1e-6 * scale_full
+    assert float((lse - l_f).abs().max()) <= 1e-5
+    # the oracle
+    cat = lambda pairs, i: torch.cat([p[i] for p in pairs]).cpu() if pairs else \
+        torch.zeros((0, H, d), dtype=dt)  # noqa: E731
+    ref = O.dual_stream_attention(q.cpu(), cat(loc, 0), cat(loc, 1), cat(hist, 0), cat(hist, 1), d ** -0.5)
+    bar = 1e-5 if dt == torch.float32 else 5e-3
+    a_ref = ref["a_loc"].reshape(n_q, -1)
+    full_ref = ref["a_full"].reshape(n_q, -1)
+    assert rel(h64(a_loc), a_ref) <= bar + ulp
+    # dA = A_full - A_loc: its error is bounded by the errors of the two activations
+    err = np.linalg.norm(h64(delta) - ref["delta"].reshape(n_q, -1))
+    assert err <= (bar + ulp) * np.linalg.norm(full_ref) + (bar + ulp) * np.linalg.norm(a_ref)
+    assert np.abs(h64(lse) - ref["lse_full"]).max() <= (1e-5 if dt == torch.float32 else 2e-3)
+
+
+
 # ---------------------------------------------------------------- merge
 def test_merge_parts_from_oracle():
     print("merge: oracle parts, 3-way and empty", flush=True)

@@ -49,19 +49,27 @@ def h64(t):
 ROWS = [0, 1, 1337, 2047, 2048, 4000, 4679]  # first, tile edges, last
 
 
+def check_merged_rows(outs, rows, q_rows, loc, hist, H, d, scale):
+    """Sampled query rows of a warmup call (A_loc, A_full - A_loc and the
+    merged LSE) against the oracle's dual-stream attention and merge over the
+    given key groups."""
+    a_loc, delta, lse = (t[rows].clone() for t in outs)
+    cat = lambda pairs, i: torch.cat([p[i] for p in pairs]).cpu() if pairs else \
+        torch.zeros((0, H, d), dtype=torch.bfloat16)  # noqa: E731
+    ref = O.dual_stream_attention(q_rows, cat(loc, 0), cat(loc, 1), cat(hist, 0), cat(hist, 1), scale)
+    n = len(rows)
+    a_ref, full_ref = ref["a_loc"].reshape(n, -1), ref["a_full"].reshape(n, -1)
+    assert rel(h64(a_loc), a_ref) <= 5e-3
+    err = np.linalg.norm(h64(delta) - ref["delta"].reshape(n, -1))
+    assert err <= 5e-3 * (np.linalg.norm(full_ref) + np.linalg.norm(a_ref))
+    assert np.abs(h64(lse) - ref["lse_full"]).max() <= 2e-3
+
+
 def check_dual_rows(st, layer, c, q, outs):
     """Sampled query rows of a warmup call against the oracle on the layer's
     own cache rows."""
-    o_l, l_l, o_h, l_h = (t[ROWS].clone() for t in outs[:4])
     loc, hist = st.kv[layer].warmup_groups(c)
-    cat = lambda pairs, i: torch.cat([p[i] for p in pairs]).cpu() if pairs else \
-        torch.zeros((0, st.H, st.d), dtype=torch.bfloat16)  # noqa: E731
-    ref = O.dual_stream_attention(q[ROWS].cpu(), cat(loc, 0), cat(loc, 1), cat(hist, 0), cat(hist, 1),
-                                  st.scale)
-    assert rel(h64(o_l), ref["o_loc"]) <= 5e-3
-    assert rel(h64(o_h), ref["o_hist"]) <= 5e-3
-    assert np.abs(h64(l_l) - ref["lse_loc"]).max() <= 2e-3
-    assert np.abs(h64(l_h) - ref["lse_hist"]).max() <= 2e-3
+    check_merged_rows(outs, ROWS, q[ROWS].cpu(), loc, hist, st.H, st.d, st.scale)
 
 
 def check_post_rows(st, layer, c, q, w):
@@ -243,7 +251,6 @@ def test_recalibration_reenters_warmup():
             st.post(layer, c, si.q(layer, c))
     st.recalibrate(6)
     l_old = first_sel.index(1)
-    rows = [0, 1, 200, 255]
     for c in (6, 7, 8):
         for layer in range(N):
             k, v = si.kv(layer, c)
@@ -252,7 +259,7 @@ def test_recalibration_reenters_warmup():
             outs = st.warmup(layer, c, q)
             if c == 6:
                 torch.cuda.synchronize()
-                G, C, r2 = O.accumulate_stats(outs[4].cpu(), outs[5].cpu(), st.W[layer].cpu())
+                G, C, r2 = O.accumulate_stats(outs[0].cpu(), outs[1].cpu(), st.W[layer].cpu())
                 Gg = np.triu(h64(st.G[layer]))
                 assert rel(Gg, np.triu(G)) <= 5e-4, layer
                 assert rel(h64(st.C[layer]), C) <= 5e-4, layer
@@ -260,18 +267,10 @@ def test_recalibration_reenters_warmup():
             if c == 8 and layer == l_old:
                 first = 5  # its last post-switch chunk
                 loc_r, hist_r = O.stream_groups_kept(c, Tc, first)
-                seq_k = {j: si.kv(layer, j)[0].cpu() for j in range(first, c + 1)}
-                seq_v = {j: si.kv(layer, j)[1].cpu() for j in range(first, c + 1)}
-                seq_k[0], seq_v[0] = (t.cpu() for t in si.kv(layer, 0))
-
-                def gather(ranges, src):
-                    parts = [src[r // Tc] for a, b in ranges for r in range(a, b, Tc)]
-                    return torch.cat(parts) if parts else torch.zeros((0, H, d), dtype=torch.bfloat16)
-                ref = O.dual_stream_attention(q[rows].cpu(), gather(loc_r, seq_k), gather(loc_r, seq_v),
-                                              gather(hist_r, seq_k), gather(hist_r, seq_v), st.scale)
-                assert rel(h64(outs[0][rows]), ref["o_loc"]) <= 5e-3
-                assert rel(h64(outs[2][rows]), ref["o_hist"]) <= 5e-3
-                assert np.abs(h64(outs[3][rows]) - ref["lse_hist"]).max() <= 2e-3
+                chunk = {j: tuple(t.cpu() for t in si.kv(layer, j)) for j in [0] + list(range(first, c + 1))}
+                pairs = lambda ranges: [chunk[r // Tc] for a, b in ranges for r in range(a, b, Tc)]  # noqa: E731
+                rows = [0, 1, 200, 255]
+                check_merged_rows(outs, rows, q[rows].cpu(), pairs(loc_r), pairs(hist_r), H, d, st.scale)
     st.switch(K, evict=False)
     check_switch(st, K)
     sel2 = list(st.is_local_host)
