@@ -269,6 +269,20 @@ class IspaStream:
         return self.a_loc, self.delta, self.lse_full
 
     # ------------------------------------------------------------------ switch
+    def reserve_switch(self):
+        """Allocate the switch's outputs (dW, eps, info, W + dW) and the solve's
+        workspace now, so that :meth:`switch` allocates nothing; they are reused
+        by every later switch (re-calibration)."""
+        N, D, dev = self.N, self.D, self.device
+        if self.dW is None:
+            self.dW = torch.empty((N, D, D), dtype=torch.float32, device=dev)
+            self.eps = torch.empty(N, dtype=torch.float64, device=dev)
+            self.info = torch.empty(N, dtype=torch.int32, device=dev)
+            self.w_eff = torch.empty_like(self.W)
+        need = self.L.ispa_solve_dw_workspace_bytes(N, D)
+        if getattr(self, "_solve_ws", None) is None or self._solve_ws.numel() < need:
+            self._solve_ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
     def switch(self, K: int, evict: bool = True):
         """Ridge solve of every layer in one batched call (dW, eps, W + dW),
         selection of the K lowest-eps layers, then (optionally) eviction of the
@@ -276,12 +290,9 @@ class IspaStream:
         which decides the later calls."""
         L, s, N, D = self.L, self._stream(), self.N, self.D
         dev = self.device
-        self.dW = torch.empty((N, D, D), dtype=torch.float32, device=dev)
-        self.eps = torch.empty(N, dtype=torch.float64, device=dev)
-        self.info = torch.empty(N, dtype=torch.int32, device=dev)
-        self.w_eff = torch.empty_like(self.W)
-        need = L.ispa_solve_dw_workspace_bytes(N, D)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.reserve_switch()
+        ws = self._solve_ws
+        need = ws.numel()
         self._ck(L.ispa_solve_dw(N, D, self.G.data_ptr(), self.C.data_ptr(), self.r2.data_ptr(), D * D,
                                  self.lambda_abs, self.lambda_rel, self.dW.data_ptr(), self.eps.data_ptr(),
                                  self.info.data_ptr(), self.W.data_ptr(), B.ISPA_BF16,
@@ -293,8 +304,7 @@ class IspaStream:
                                       self.is_local.data_ptr(), self.status.data_ptr(), s))
         self.K = K
         self.is_local_host = [int(x) for x in self.is_local.cpu()]  # synchronises
-        del ws
-        if int(self.status.cpu()[0]) != 0 or int(self.info.max().cpu()) != 0:
+        if int(self.status.cpu()[0]) != 0 or any(int(x) != 0 for x in self.info.cpu()):
             raise RuntimeError("switch failed: eps is NaN or a Gram matrix is not positive definite")
         self.switched = True
         if evict:
@@ -338,6 +348,7 @@ class IspaStream:
             if flag:
                 self.kv[layer].evict_history()
         self.G = self.C = None
+        self._solve_ws = None
         self.ws.release()
 
     def adopt_switch(self, is_local, w_eff, dW=None, eps=None):
@@ -375,7 +386,6 @@ class IspaStream:
         for kv in self.kv:
             kv.keep_from(c)
         self.switched = False
-        self.dW = self.eps = self.info = self.w_eff = None
         self.selected = self.is_local = self.status = None
         self.warmups += 1
 
