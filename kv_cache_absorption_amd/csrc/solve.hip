@@ -11,7 +11,7 @@
 // The backward substitution is one launch per block row, whose workgroups of
 // block row kb - 1 also apply inv(L)^T of that row right after its last
 // update.  Block products are 64 x 64 x 64 fp64 MFMA tiles from LDS; a
-// diagonal block is turned into inv(L_kk) by one wave (chol_inv64).  eps uses
+// diagonal block is turned into inv(L_kk) by the workgroup (chol_inv64).  eps uses
 // the identity that holds at the ridge optimum, eps = r2 - <dW, C> -
 // lambda ||dW||^2 (from G dW = C - lambda dW), which is ||A_loc dW - R||^2
 // without the penalty (EN review, Key Design 2).
@@ -167,53 +167,71 @@ __device__ __forceinline__ void sub_to_lds(const f64x4 (&acc)[2][2], const doubl
   for_acc(acc, [&](int r, int c, double v) { dst[r * LDP + c] = old[(int64_t)r * ld + c] - v; });
 }
 
-// Inverse of the Cholesky factor of the SPD 64 x 64 block M (LDS), by one wave.
+// Inverse of the Cholesky factor of the SPD 64 x 64 block M (LDS, pitch LDP),
+// by the workgroup's four waves.
 //
-// Lane a holds column a of the block in registers and eliminates below the
-// diagonal one pivot at a time (right-looking, symmetric Schur complements,
-// so the multipliers of step j are row j, which every lane publishes to LDS).
-// When step j reaches its own column, lane j stops updating: its remaining
-// entries are then column j of the inverse unit factor times -pivot_j, and the
-// later steps update them with the same formula as the matrix columns.  Pivot
-// j of the elimination is the squared diagonal of the Cholesky factor, so
-// inv(L)[i][a] = E[i][a] / sqrt(pivot_i) with E the inverse unit factor.
-// rows: 64 x 64 doubles of LDS.  Writes Li (row-major, 64 wide); returns the
-// first non-positive pivot (1-based) or 0.
-__device__ __forceinline__ int chol_inv64(const double* M, double* rows, double* Li) {
+// Lane a of every wave holds column a; wave w holds its rows 16w .. 16w+15.
+// Elimination is right-looking, pivot by pivot, on symmetric Schur
+// complements, so the multipliers of step j are row j.  The wave that holds
+// row j publishes it to LDS twice: as is, for each lane's own multiplier, and
+// with the entries at and above the diagonal zeroed, so that every wave
+// updates all 16 of its rows without a branch.  One barrier per step makes
+// each row visible.  When step j reaches its own column, lane j stops
+// updating: its remaining entries are then column j of the inverse unit
+// factor times -pivot_j, and the later steps update them with the same
+// formula as the matrix columns.  Pivot j is the squared diagonal of the
+// Cholesky factor, so inv(L)[i][a] = E[i][a] / sqrt(pivot_i) with E the
+// inverse unit factor.
+// M is overwritten (it holds the zeroed rows); rows: 64 x 64 doubles of LDS.
+// Writes Li (row-major, 64 wide); returns the first non-positive pivot
+// (1-based) or 0.  Every thread of the workgroup must call it.
+__device__ __forceinline__ int chol_inv64(double* M, double* rows, double* Li) {
   const int a = threadIdx.x & 63;
-  double c[NB];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  double c[16];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) c[i] = M[i * LDP + a];
+  for (int r = 0; r < 16; ++r) c[r] = M[(16 * w + r) * LDP + a];
+  __syncthreads();  // every row is in registers: M becomes the zeroed-row table
+  double* mult = M;
+  double* rowv = rows;
+  auto publish = [&](int j, double v) {
+    rowv[j * NB + a] = v;
+    mult[j * NB + a] = a > j ? v : 0.0;
+  };
+  if (w == 0) publish(0, c[0]);
   int bad = 0;
-  rows[a] = c[0];
-#pragma unroll
+#pragma unroll 1
   for (int j = 0; j < NB; ++j) {
-    const double* rj = rows + j * NB;
-    const double piv = rj[j];
+    __syncthreads();  // row j is published
+    const double piv = rowv[j * NB + j];
     if (!(piv > 0.0) && bad == 0) bad = j + 1;
-    const double s = a == j ? 0.0 : c[j] / piv;
-    if (j + 1 < NB) {
-      // the next pivot row first, so its publication overlaps this step's tail
-      c[j + 1] = fma(-rj[j + 1], s, c[j + 1]);
-      rows[(j + 1) * NB + a] = c[j + 1];
+    const double s = a == j ? 0.0 : rowv[j * NB + a] / piv;
+    const double* mj = mult + j * NB + 16 * w;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = fma(-mj[r], s, c[r]);
+    const int jn = j + 1;
+    if (jn < NB && w == (jn >> 4)) {  // this wave holds row j + 1 (wave-uniform)
+      const int rl = jn & 15;
+      double v = c[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) v = rl == r ? c[r] : v;
+      publish(jn, v);
     }
-#pragma unroll
-    for (int i = j + 2; i < NB; ++i) c[i] = fma(-rj[i], s, c[i]);
   }
-  const double pa = rows[a * NB + a];
-  const double ea = -1.0 / pa;
+  __syncthreads();  // the last row is published
+  const double ea = -1.0 / rowv[a * NB + a];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const double isq = 1.0 / sqrt(rows[i * NB + i]);
-    double v = i < a ? 0.0 : (i == a ? isq : c[i] * ea * isq);
+  for (int r = 0; r < 16; ++r) {
+    const int i = 16 * w + r;
+    const double isq = 1.0 / sqrt(rowv[i * NB + i]);
+    const double v = i < a ? 0.0 : (i == a ? isq : c[r] * ea * isq);
     Li[i * NB + a] = bad ? NAN : v;
   }
   return bad;
 }
 
-// factor the block in As (wave 0 only) and record the first failing pivot
-__device__ __forceinline__ void factor_block(const double* As, double* Bs, double* Li, int32_t* info, int base) {
-  if (threadIdx.x >= 64) return;
+// factor the block in As (all waves) and record the first failing pivot
+__device__ __forceinline__ void factor_block(double* As, double* Bs, double* Li, int32_t* info, int base) {
   const int bad = chol_inv64(As, Bs, Li);
   if (bad && threadIdx.x == 0 && *info == 0) *info = base + bad;
 }
