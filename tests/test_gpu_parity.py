@@ -277,6 +277,7 @@ def test_merge_parts_from_oracle():
     (torch.bfloat16, 300, 256, 2),
     (torch.float16, 777, 128, 3),
     (torch.float16, 4680, 1536, 1),   # one Wan-1.3B warmup step
+    (torch.float16, 4680, 5120, 1),   # one Wan-14B warmup step (no token split)
     (torch.float32, 64, 128, 4),      # tiny fp32 workload
 ])
 def test_accum_stats_parity(dt, n, D, steps):
@@ -363,6 +364,33 @@ def test_solve_grouped_batch():
         lam = 1e-3 * np.trace(Gsym) / D
         ref = np.linalg.solve(Gsym + lam * np.eye(D), Cs[l].astype(np.float64))
         assert rel(h64(dW[l]), ref) <= 1e-6, l
+
+
+def test_solve_wan14b_layer():
+    """One layer at the Wan-14B width (D = 5120: 80 block columns, grouped by
+    8), against LAPACK's fp64 solve of the same symmetrised system; eps against
+    the oracle's evaluation from the statistics."""
+    D, n = 5120, 5376
+    print(f"solve_dw D={D} layers=1", flush=True)
+    rng = np.random.default_rng(78)
+    a = rng.normal(size=(n, D)).astype(np.float32)
+    Gf = a.T @ a
+    Cf = (a.T @ rng.normal(size=(n, D)).astype(np.float32)).astype(np.float32)
+    r2v = float(n * D)
+    G = torch.tensor(Gf[None], device=DEV)
+    C = torch.tensor(Cf[None], device=DEV)
+    r2 = torch.tensor([r2v], dtype=torch.float64, device=DEV)
+    dW, eps, info, _ = K().ispa_solve_dw(G, C, r2, 0.0, 1e-3)
+    torch.cuda.synchronize()
+    assert int(info[0]) == 0
+    Gl = Gf.astype(np.float64)
+    Gsym = np.triu(Gl) + np.triu(Gl, 1).T
+    lam = 1e-3 * np.trace(Gsym) / D
+    Cl = Cf.astype(np.float64)
+    ref = np.linalg.solve(Gsym + lam * np.eye(D), Cl)
+    assert rel(h64(dW[0]), ref) <= 1e-6
+    e_ref = O.epsilon_from_stats(Gsym, Cl, r2v, ref)
+    assert abs(float(eps[0]) - e_ref) <= 1e-6 * r2v
 
 
 def test_solve_non_spd_reports_pivot():
