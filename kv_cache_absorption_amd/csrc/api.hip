@@ -237,8 +237,11 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   double* partials = (double*)wp;
   const size_t rblocks_bytes = (size_t)((D + kNtBM - 1) / kNtBM) * (size_t)((np + 127) / 128) * 8;
   ispa_status st;
-  if ((st = launch_transpose16(w, D, D, D, Wt, D, D, w_dt, a_dt, stream))) return st;
-  if ((st = launch_transpose16(a_loc, D, n, D, At, np, np, a_dt, a_dt, stream))) return st;
+  {
+    // W^T (converted to the operand type) and A_loc^T in one launch
+    const Transpose16 tj[2] = {{w, Wt, D, D, D, D, D, w_dt, a_dt}, {a_loc, At, D, n, D, np, np, a_dt, a_dt}};
+    if ((st = launch_transpose16(tj, 2, stream))) return st;
+  }
   // R^T = W^T dA^T, stored with zero padding, and per-workgroup ||R||^2
   NtGemmParams r{};
   r.M = D;

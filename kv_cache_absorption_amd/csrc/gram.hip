@@ -374,11 +374,29 @@ __device__ __forceinline__ uint16_t conv16(uint32_t v, int in_dt, int out_dt) {
   return (uint16_t)(out_dt == ISPA_BF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f));
 }
 
-__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* in, int64_t ld_in, int64_t rows,
-                                                          int64_t cols, uint16_t* out, int64_t ld_out,
-                                                          int64_t rows_pad, int in_dt, int out_dt) {
+// Up to two transposes in one launch: workgroups [0, j[0].nblk) take job 0,
+// the rest job 1; inside a job the 64 x 64 blocks go row block fastest.
+struct T16Job {
+  const uint16_t* in;
+  uint16_t* out;
+  int64_t ld_in, rows, cols, ld_out, rows_pad;
+  int32_t in_dt, out_dt;
+  int32_t gx, nblk;  // 64-row blocks over rows_pad; all blocks of the job
+};
+struct T16Jobs {
+  T16Job j[2];
+};
+
+__global__ __launch_bounds__(256) void transpose16_kernel(const T16Jobs js) {
   __shared__ uint16_t tile[64][66];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const bool second = (int)blockIdx.x >= js.j[0].nblk;
+  const T16Job t = second ? js.j[1] : js.j[0];
+  const int b = second ? (int)blockIdx.x - js.j[0].nblk : (int)blockIdx.x;
+  const uint16_t* in = t.in;
+  uint16_t* out = t.out;
+  const int64_t ld_in = t.ld_in, rows = t.rows, cols = t.cols, ld_out = t.ld_out, rows_pad = t.rows_pad;
+  const int in_dt = t.in_dt, out_dt = t.out_dt;
+  const int64_t r0 = (int64_t)(b % t.gx) * 64, c0 = (int64_t)(b / t.gx) * 64;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -490,13 +508,47 @@ int64_t nt_stats_split(int32_t D, int64_t np) {
   return (stages + kchunk - 1) / kchunk;
 }
 
+static T16Job t16_job(const Transpose16& t) {
+  T16Job j{};
+  j.in = (const uint16_t*)t.in;
+  j.out = (uint16_t*)t.out;
+  j.ld_in = t.ld_in;
+  j.rows = t.rows;
+  j.cols = t.cols;
+  j.ld_out = t.ld_out;
+  j.rows_pad = t.rows_pad;
+  j.in_dt = t.in_dt;
+  j.out_dt = t.out_dt;
+  j.gx = (int32_t)((t.rows_pad + 63) / 64);
+  j.nblk = t.rows_pad > 0 && t.cols > 0 ? j.gx * (int32_t)((t.cols + 63) / 64) : 0;
+  return j;
+}
+
+ispa_status launch_transpose16(const Transpose16* jobs, int n_jobs, hipStream_t stream) {
+  if (n_jobs < 1 || n_jobs > 2) {
+    set_error("launch_transpose16: 1 or 2 jobs");
+    return ISPA_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < n_jobs; ++i) {
+    const int64_t blocks = (jobs[i].rows_pad + 63) / 64 * ((jobs[i].cols + 63) / 64);
+    if (jobs[i].rows_pad < 0 || jobs[i].cols < 0 || blocks > (int64_t)INT32_MAX / 2) {
+      set_error("launch_transpose16: matrix too large");
+      return ISPA_ERR_INVALID_ARG;
+    }
+  }
+  T16Jobs js{};
+  js.j[0] = t16_job(jobs[0]);
+  if (n_jobs == 2) js.j[1] = t16_job(jobs[1]);
+  const int64_t total = (int64_t)js.j[0].nblk + js.j[1].nblk;
+  if (total == 0) return ISPA_OK;
+  hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)total), dim3(256), 0, stream, js);
+  return check_launch("transpose16_kernel");
+}
+
 ispa_status launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,
                                int64_t ld_out, int64_t rows_pad, int in_dt, int out_dt, hipStream_t stream) {
-  if (rows_pad == 0 || cols == 0) return ISPA_OK;
-  const dim3 grid((unsigned)((rows_pad + 63) / 64), (unsigned)((cols + 63) / 64));
-  hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, (const uint16_t*)in, ld_in, rows, cols,
-                     (uint16_t*)out, ld_out, rows_pad, in_dt, out_dt);
-  return check_launch("transpose16_kernel");
+  const Transpose16 t{in, out, ld_in, rows, cols, ld_out, rows_pad, in_dt, out_dt};
+  return launch_transpose16(&t, 1, stream);
 }
 
 }  // namespace ispa

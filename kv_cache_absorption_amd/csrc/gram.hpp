@@ -46,6 +46,14 @@ int64_t nt_stats_split(int32_t D, int64_t np);
 // 16-bit elements converted from in_dt to out_dt when they differ
 ispa_status launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,
                                int64_t ld_out, int64_t rows_pad, int in_dt, int out_dt, hipStream_t stream);
+// one or two such transposes in a single launch
+struct Transpose16 {
+  const void* in;
+  void* out;
+  int64_t ld_in, rows, cols, ld_out, rows_pad;
+  int in_dt, out_dt;
+};
+ispa_status launch_transpose16(const Transpose16* jobs, int n_jobs, hipStream_t stream);
 
 constexpr int kNtBM = 256, kNtBK = 32;
 
