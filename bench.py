@@ -51,8 +51,8 @@ PEAK_HBM_GBS = 8000.0
 
 
 def _fail_multi(n):
-    print(json.dumps({"error": f"--gpus {n}: this build runs on one GPU only; "
-                      "multi-GPU sharding is described in DESIGN.md, not implemented"}))
+    print(json.dumps({"error": f"--gpus {n}: libispa runs on one GPU; "
+                      "sharding across GPUs is not implemented"}))
     sys.exit(2)
 
 
