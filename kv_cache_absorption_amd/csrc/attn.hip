@@ -1129,10 +1129,21 @@ SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, i
   if (wgs >= kTargetWgs || nonempty == 0) return plan;
   int64_t piece;
   if (nonempty == 1) {
-    // one key set: cut it so the launch reaches the target, pieces >= kMinPiece keys
-    const int64_t want = (kTargetWgs + wgs - 1) / wgs;
-    const int64_t most = std::max<int64_t>(1, shortest / kMinPiece);
-    const int64_t s = std::min<int64_t>(std::min(want, most), 16);
+    // One key set: the piece count s that minimises the launch's estimated time,
+    // (waves of workgroups over the CUs) x (key tiles per piece + a fixed cost of
+    // about kFillTiles tiles per workgroup: pipeline fill, output store and the
+    // extra merge part).  Both constants are MI355X measurements (256 CUs; the
+    // fixed cost fitted to 1-, 2-, 3- and 4-piece timings of a 9360-key group).
+    constexpr int64_t kCUs = 256, kFillTiles = 10, kMinTiles = 4;
+    const int64_t tiles = (shortest + kBK - 1) / kBK;
+    int64_t s = 1, best = INT64_MAX;
+    for (int64_t c = 1; c <= 16 && (c == 1 || tiles / c >= kMinTiles); ++c) {
+      const int64_t cost = (wgs * c + kCUs - 1) / kCUs * ((tiles + c - 1) / c + kFillTiles);
+      if (cost < best) {
+        best = cost;
+        s = c;
+      }
+    }
     piece = (shortest + s - 1) / s;
   } else {
     // several groups: pieces about as long as the shortest group, so every
