@@ -48,6 +48,13 @@ __all__ = [
     "kv_bytes_retained",
     "remaining_kv_fraction",
     "stream_groups_kept",
+    "E4M3_MAX",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize_rows_e4m3",
+    "quantize_weight_e4m3",
+    "w8a8_linear",
+    "local_attn_proj_w8a8",
 ]
 
 
@@ -287,6 +294,106 @@ def local_attn_proj(q, k, v, w_proj, scale: float):
     o, _ = group_attention(q, k, v, scale)
     n_q = o.shape[0]
     return o.reshape(n_q, -1) @ as_f64(w_proj)
+
+
+# ---------------------------------------------------------------------------
+# W8A8 post-switch projection
+#
+# The pages report a 1.86x overall speed-up when ISPA is combined with W8A8
+# post-training quantisation (EN review, Key Findings, the Figure 7 item; DE
+# summary, section 4 "Experimentelle Ergebnisse", the acceleration item), and
+# give no scheme: no format, granularity or scale rule.  The reading taken
+# here is the plainest W8A8 for the one linear layer the method changes, the
+# output projection with W (F-Layers) or W + Delta W (L-Layers): 8-bit
+# floating point (OCP FP8 E4M3) for both operands, one symmetric scale per
+# activation row (token) and per weight output column, fp32 accumulation.
+# Attention itself stays in its own precision.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes: 1 sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits.  Exponent field 0 holds subnormals m * 2^-9; codes 0x7f
+    and 0xff are NaN; there is no infinity, so the largest finite magnitude
+    is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c >> 7, -mag, mag)
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F, dtype=np.uint8))  # codes 0x00..0x7e, increasing
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """E4M3 code of each value with |x| <= 448: the nearest finite magnitude,
+    a tie going to the even code (even mantissa), the sign from the sign of x.
+    A magnitude that rounds to zero is encoded as +0 (0x00), whatever the sign
+    of x: the scheme has a single zero code."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any() or (np.abs(x) > E4M3_MAX).any():
+        raise ValueError("e4m3_encode: values must be finite and within +-448")
+    a = np.abs(x)
+    hi = np.minimum(np.searchsorted(_E4M3_POS, a, side="left"), len(_E4M3_POS) - 1)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where((x < 0) & (code != 0), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def quantize_rows_e4m3(x):
+    """Symmetric per-row E4M3 quantisation (the scheme stated above).
+
+    Row i: amax_i = max_k |x_ik|, scale_i = amax_i / 448 and
+    code_ik = E4M3(clamp(x_ik / scale_i, -448, 448)).  The two divisions are
+    fp32 operations rounded to nearest: the codes are integers decided by
+    floating point, so the oracle takes the decision in the kernel's
+    precision.  Inputs are fp32 or 16-bit values (exact in fp32).  A row of
+    zeros gets scale 0 and zero codes.  Returns (codes uint8, scales fp32)."""
+    x32 = np.asarray(as_f64(x), dtype=np.float32)
+    if x32.ndim != 2:
+        raise ValueError("quantize_rows_e4m3: 2-D input")
+    amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = (x32 / safe[:, None]).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    codes = np.where(scale[:, None] > 0, e4m3_encode(y), 0).astype(np.uint8)
+    return codes, scale
+
+
+def quantize_weight_e4m3(w):
+    """W [D_in, D_out] -> (codes [D_out, D_in], scales [D_out]): one scale per
+    output column, the codes of a column stored as a row (input index
+    contiguous)."""
+    return quantize_rows_e4m3(as_f64(w).T)
+
+
+def w8a8_linear(x, w_codes, w_scales):
+    """y = (x quantised per row) times (W quantised per output column), in
+    fp64 on the dequantised operands: y_ij = sx_i sw_j sum_k dec(qx_ik)
+    dec(qw_jk).  x [n, D_in]; w_codes [D_out, D_in]; returns [n, D_out]."""
+    qx, sx = quantize_rows_e4m3(x)
+    xa = e4m3_decode(qx) * sx.astype(np.float64)[:, None]
+    wb = e4m3_decode(w_codes) * np.asarray(w_scales, dtype=np.float64)[:, None]
+    return xa @ wb.T
+
+
+def local_attn_proj_w8a8(q, k, v, w_proj, scale: float):
+    """Post-switch layer output with the W8A8 projection: attention over the
+    retained keys (fp64, as local_attn_proj), its output rounded to fp32 (the
+    attention's output type) and quantised per token, times W quantised per
+    output column.  Returns [n_q, D_out]."""
+    o, _ = group_attention(q, k, v, scale)
+    o32 = o.reshape(o.shape[0], -1).astype(np.float32)
+    wq, ws = quantize_weight_e4m3(w_proj)
+    return w8a8_linear(o32, wq, ws)
 
 
 # ---------------------------------------------------------------------------
