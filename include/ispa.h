@@ -233,6 +233,62 @@ ispa_status ispa_local_attn_proj(ispa_dtype dt, int64_t n_q, int32_t H, int32_t 
                                  void* y, ispa_dtype y_dt,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * W8A8 post-switch projection.  The pages report a 1.86x overall speed-up of
+ * ISPA combined with W8A8 post-training quantisation (EN review, Key
+ * Findings, the Figure 7 item; DE summary, section 4 "Experimentelle
+ * Ergebnisse") and give no scheme.  The scheme here, our reading: OCP FP8
+ * E4M3 codes for both operands of y = O W, one symmetric scale per activation
+ * row (token) and per weight output column, fp32 accumulation on the fp8
+ * matrix core.  For a row x: scale = max|x| / 448 and
+ * code = E4M3(clamp(x / scale, -448, 448)), both divisions IEEE fp32, round
+ * to nearest even, a zero magnitude stored as code 0x00; a zero row has
+ * scale 0 and zero codes.
+ *
+ * ispa_quantize_w_fp8 -- the weight step, once per switch for each layer.
+ *   w         [d_in, d_out] of w_dt (ISPA_BF16 or ISPA_F16), 8-byte aligned
+ *             (W + dW of an L-Layer, or W of an F-Layer).
+ *   w_codes   uint8 [d_out, d_in]: output column j's codes as row j.
+ *   w_scales  fp32 [d_out].
+ *   d_in, d_out positive multiples of 4.  Needs the workspace below.
+ */
+size_t ispa_quantize_w_fp8_workspace_bytes(int32_t d_in, int32_t d_out);
+ispa_status ispa_quantize_w_fp8(ispa_dtype w_dt, int32_t d_in, int32_t d_out, const void* w,
+                                uint8_t* w_codes, float* w_scales,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ispa_w8a8_linear -- y = Q(x) Q(W): x quantised per row here, W given as
+ * ispa_quantize_w_fp8 left it;  y_ij = sx_i sw_j sum_k dec(qx_ik) dec(qw_jk).
+ *   x         [n, d_in] of x_dt (ISPA_F32, ISPA_BF16 or ISPA_F16), rows ld_x
+ *             elements apart (ld_x >= d_in, a multiple of 4); 16-byte aligned
+ *             for F32, 8-byte for 16-bit types.
+ *   w_codes   uint8 [d_out, d_in], 16-byte aligned; w_scales fp32 [d_out],
+ *             16-byte aligned.
+ *   y         [n, d_out] of y_dt (F32 16-byte aligned, BF16 or F16 8-byte).
+ *   d_in a positive multiple of 64, d_out of 4.
+ */
+size_t ispa_w8a8_linear_workspace_bytes(int64_t n, int32_t d_in);
+ispa_status ispa_w8a8_linear(ispa_dtype x_dt, int64_t n, int32_t d_in, int32_t d_out,
+                             const void* x, int64_t ld_x, const uint8_t* w_codes,
+                             const float* w_scales, void* y, ispa_dtype y_dt,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ispa_local_attn_proj_fp8 -- ispa_local_attn_proj with the W8A8 projection:
+ * bf16 attention over the segments (as ispa_local_attn_proj, fp32 output),
+ * then ispa_w8a8_linear of that output with (w_codes, w_scales) of
+ * [D, D] (D = H d).  Arguments as the two calls it combines.
+ */
+size_t ispa_local_attn_proj_fp8_workspace_bytes(int64_t n_q, int32_t H, int32_t d,
+                                                const ispa_seg* segs, int32_t n_segs);
+ispa_status ispa_local_attn_proj_fp8(int64_t n_q, int32_t H, int32_t d, float scale,
+                                     const void* q, int64_t q_stride,
+                                     const ispa_seg* segs, int32_t n_segs,
+                                     const uint8_t* w_codes, const float* w_scales,
+                                     void* y, ispa_dtype y_dt,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

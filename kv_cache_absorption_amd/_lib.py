@@ -30,6 +30,9 @@ EXPORTED = [
     "ispa_solve_dw_workspace_bytes", "ispa_solve_dw",
     "ispa_select_layers",
     "ispa_local_attn_proj_workspace_bytes", "ispa_local_attn_proj",
+    "ispa_quantize_w_fp8_workspace_bytes", "ispa_quantize_w_fp8",
+    "ispa_w8a8_linear_workspace_bytes", "ispa_w8a8_linear",
+    "ispa_local_attn_proj_fp8_workspace_bytes", "ispa_local_attn_proj_fp8",
 ]
 
 _DT = {torch.float32: ISPA_F32, torch.bfloat16: ISPA_BF16, torch.float16: ISPA_F16}
@@ -81,6 +84,13 @@ def lib() -> ctypes.CDLL:
             "ispa_local_attn_proj_workspace_bytes": (sz, [i32, i64, i32, i32, segp, i32]),
             "ispa_local_attn_proj": (i32, [i32, i64, i32, i32, f32, vp, i64, segp, i32, vp, i32,
                                            vp, i32, vp, sz, vp]),
+            "ispa_quantize_w_fp8_workspace_bytes": (sz, [i32, i32]),
+            "ispa_quantize_w_fp8": (i32, [i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+            "ispa_w8a8_linear_workspace_bytes": (sz, [i64, i32]),
+            "ispa_w8a8_linear": (i32, [i32, i64, i32, i32, vp, i64, vp, vp, vp, i32, vp, sz, vp]),
+            "ispa_local_attn_proj_fp8_workspace_bytes": (sz, [i64, i32, i32, segp, i32]),
+            "ispa_local_attn_proj_fp8": (i32, [i64, i32, i32, f32, vp, i64, segp, i32, vp, vp, vp, i32,
+                                               vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -279,4 +289,63 @@ def ispa_local_attn_proj(q, segs, w_proj, scale: float | None = None, out_dtype=
     _check(L.ispa_local_attn_proj(dt, n_q, H, d, scale, q.data_ptr(), qs, ss, ns,
                                   w_proj.data_ptr(), _DT[w_proj.dtype], y.data_ptr(),
                                   _DT[out_dtype], _ptr(ws), wsb, _stream(dev)))
+    return y
+
+
+def ispa_quantize_w_fp8(w):
+    """W8A8 weight step: w [d_in, d_out] (bf16 or f16) -> (codes uint8
+    [d_out, d_in], scales fp32 [d_out]), one scale per output column."""
+    if not w.is_contiguous() or w.dim() != 2:
+        raise ValueError("w must be a contiguous [d_in, d_out] matrix")
+    d_in, d_out = w.shape
+    dev = w.device
+    codes = torch.empty((d_out, d_in), dtype=torch.uint8, device=dev)
+    scales = torch.empty(d_out, dtype=torch.float32, device=dev)
+    L = lib()
+    wsb = L.ispa_quantize_w_fp8_workspace_bytes(d_in, d_out)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_quantize_w_fp8(_DT[w.dtype], d_in, d_out, w.data_ptr(), codes.data_ptr(),
+                                 scales.data_ptr(), _ptr(ws), wsb, _stream(dev)))
+    return codes, scales
+
+
+def ispa_w8a8_linear(x, w_codes, w_scales, out_dtype=torch.bfloat16):
+    """y = Q(x) Q(W): x [n, d_in] (rows may be strided) quantised per row,
+    (w_codes, w_scales) from ispa_quantize_w_fp8.  Returns y [n, d_out]."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [n, d_in] with contiguous rows")
+    n, d_in = x.shape
+    d_out = w_codes.shape[0]
+    if not w_codes.is_contiguous() or not w_scales.is_contiguous() or w_codes.shape[1] != d_in:
+        raise ValueError("w_codes [d_out, d_in] and w_scales [d_out] must be contiguous")
+    dev = x.device
+    y = torch.empty((n, d_out), dtype=out_dtype, device=dev)
+    L = lib()
+    wsb = L.ispa_w8a8_linear_workspace_bytes(n, d_in)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_w8a8_linear(_DT[x.dtype], n, d_in, d_out, x.data_ptr(), x.stride(0),
+                              w_codes.data_ptr(), w_scales.data_ptr(), y.data_ptr(), _DT[out_dtype],
+                              _ptr(ws), wsb, _stream(dev)))
+    return y
+
+
+def ispa_local_attn_proj_fp8(q, segs, w_codes, w_scales, scale: float | None = None,
+                             out_dtype=torch.bfloat16):
+    """bf16 attention over the segments, then the W8A8 projection with
+    (w_codes, w_scales) from ispa_quantize_w_fp8.  Returns y [n_q, D]."""
+    n_q, H, d, qs = _q_args(q)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the fp8 projection path takes bf16 attention inputs")
+    scale = d ** -0.5 if scale is None else scale
+    ss, ns = _segs(segs, H, d)
+    dev = q.device
+    if not w_codes.is_contiguous() or not w_scales.is_contiguous():
+        raise ValueError("w_codes and w_scales must be contiguous")
+    y = torch.empty((n_q, H * d), dtype=out_dtype, device=dev)
+    L = lib()
+    wsb = L.ispa_local_attn_proj_fp8_workspace_bytes(n_q, H, d, ss, ns)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_local_attn_proj_fp8(n_q, H, d, scale, q.data_ptr(), qs, ss, ns, w_codes.data_ptr(),
+                                      w_scales.data_ptr(), y.data_ptr(), _DT[out_dtype], _ptr(ws), wsb,
+                                      _stream(dev)))
     return y

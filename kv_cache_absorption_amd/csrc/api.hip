@@ -434,4 +434,137 @@ ispa_status ispa_local_attn_proj(ispa_dtype dt, int64_t n_q, int32_t H, int32_t 
   return launch_gemm(p, ISPA_BF16, stream, nullptr);
 }
 
+// ---------------------------------------------------------------- W8A8 projection
+// The fp8 product of quantised rows (codes xq, scales sx) with the quantised
+// weight: the NT GEMM on the fp8 matrix core, dequantised in its store.
+static ispa_status run_w8a8_gemm(int64_t n, int32_t d_in, int32_t d_out, const uint8_t* xq, const float* sx,
+                                 const uint8_t* w_codes, const float* w_scales, void* y, ispa_dtype y_dt,
+                                 hipStream_t stream) {
+  NtGemmParams p{};
+  p.M = n;
+  p.N = d_out;
+  p.K = d_in;
+  p.x = xq;
+  p.ldx = d_in;
+  p.y = w_codes;
+  p.ldy = d_in;
+  p.y_rows = d_out;
+  p.epi = kNtStoreScaled;
+  p.sx = sx;
+  p.sy = w_scales;
+  p.out = y;
+  p.out_dt = y_dt;
+  p.ld_out = d_out;
+  p.bn = proj_tile_n(n, d_out);
+  p.tiles_m = (int)((n + kNtBM - 1) / kNtBM);
+  p.tiles_n = (int)((d_out + p.bn - 1) / p.bn);
+  p.ksplit = 1;
+  p.kchunk = d_in;
+  return launch_nt_gemm(p, kMtE4M3, stream, nullptr);
+}
+
+size_t ispa_quantize_w_fp8_workspace_bytes(int32_t d_in, int32_t d_out) {
+  if (d_in <= 0 || d_out <= 0) return 0;
+  return align256((size_t)d_in * d_out * 2);  // W^T in its 16-bit type
+}
+
+ispa_status ispa_quantize_w_fp8(ispa_dtype w_dt, int32_t d_in, int32_t d_out, const void* w, uint8_t* w_codes,
+                                float* w_scales, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (w_dt != ISPA_BF16 && w_dt != ISPA_F16) return fail(ISPA_ERR_UNSUPPORTED, "W must be BF16 or F16");
+  if (d_in <= 0 || d_out <= 0 || d_in % 4 || d_out % 4)
+    return fail(ISPA_ERR_INVALID_ARG, "d_in and d_out must be positive multiples of 4");
+  if (!w || !w_codes || !w_scales) return fail(ISPA_ERR_INVALID_ARG, "null w, w_codes or w_scales");
+  if (!aligned(w, 8) || !aligned(w_codes, 4) || !aligned(w_scales, 4))
+    return fail(ISPA_ERR_INVALID_ARG, "misaligned w, w_codes or w_scales");
+  const size_t need = ispa_quantize_w_fp8_workspace_bytes(d_in, d_out);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "quantize_w_fp8 workspace too small or misaligned");
+  // W^T [d_out][d_in] (an output column per row), then per-row codes
+  const Transpose16 t{w, ws, d_out, d_in, d_out, d_in, d_in, w_dt, w_dt};
+  ispa_status st = launch_transpose16(&t, 1, stream);
+  if (st) return st;
+  return launch_quant_rows_e4m3(ws, w_dt, d_in, d_out, d_in, w_codes, d_in, w_scales, stream);
+}
+
+size_t ispa_w8a8_linear_workspace_bytes(int64_t n, int32_t d_in) {
+  if (n <= 0 || d_in <= 0) return 0;
+  return align256((size_t)n * d_in) + align256((size_t)n * 4);  // activation codes and scales
+}
+
+static ispa_status check_w8a8(int32_t d_in, int32_t d_out, const uint8_t* w_codes, const float* w_scales, void* y,
+                              ispa_dtype y_dt, bool any_rows) {
+  if (!valid_dtype(y_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad y_dt");
+  if (d_in <= 0 || d_in % 64 || d_out <= 0 || d_out % 4)
+    return fail(ISPA_ERR_INVALID_ARG, "d_in must be a positive multiple of 64 and d_out of 4");
+  if (!w_codes || !w_scales || (any_rows && !y)) return fail(ISPA_ERR_INVALID_ARG, "null w_codes, w_scales or y");
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(y, y_dt == ISPA_F32 ? 16 : 8))
+    return fail(ISPA_ERR_INVALID_ARG, "misaligned w_codes, w_scales or y");
+  return ISPA_OK;
+}
+
+ispa_status ispa_w8a8_linear(ispa_dtype x_dt, int64_t n, int32_t d_in, int32_t d_out, const void* x, int64_t ld_x,
+                             const uint8_t* w_codes, const float* w_scales, void* y, ispa_dtype y_dt, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad x_dt");
+  if (n < 0) return fail(ISPA_ERR_INVALID_ARG, "n must be >= 0");
+  ispa_status st = check_w8a8(d_in, d_out, w_codes, w_scales, y, y_dt, n > 0);
+  if (st) return st;
+  if (ld_x < d_in || ld_x % 4) return fail(ISPA_ERR_INVALID_ARG, "ld_x must be >= d_in and a multiple of 4");
+  if (n > 0 && !x) return fail(ISPA_ERR_INVALID_ARG, "null x");
+  if (!aligned(x, x_dt == ISPA_F32 ? 16 : 8)) return fail(ISPA_ERR_INVALID_ARG, "misaligned x");
+  if (n == 0) return ISPA_OK;
+  const size_t need = ispa_w8a8_linear_workspace_bytes(n, d_in);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "w8a8_linear workspace too small or misaligned");
+  uint8_t* xq = (uint8_t*)ws;
+  float* sx = (float*)((char*)ws + align256((size_t)n * d_in));
+  if ((st = launch_quant_rows_e4m3(x, x_dt, ld_x, n, d_in, xq, d_in, sx, stream))) return st;
+  return run_w8a8_gemm(n, d_in, d_out, xq, sx, w_codes, w_scales, y, y_dt, stream);
+}
+
+size_t ispa_local_attn_proj_fp8_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const ispa_seg* segs,
+                                                int32_t n_segs) {
+  if (n_q <= 0 || H < 1 || n_segs < 0 || n_segs > ISPA_MAX_SEGS) return 0;
+  HostGroup g[1] = {{segs, n_segs}};
+  const SplitPlan plan = plan_splits(attn_block_q(ISPA_BF16, d), n_q, H, g, 1);
+  const size_t D = (size_t)H * d;
+  // fp32 attention output and LSE, its codes and row scales, split parts
+  return align256((size_t)n_q * D * 4) + align256((size_t)n_q * H * 4) + align256((size_t)n_q * D) +
+         align256((size_t)n_q * 4) + split_workspace_bytes(n_q, H, d, plan, 1);
+}
+
+ispa_status ispa_local_attn_proj_fp8(int64_t n_q, int32_t H, int32_t d, float scale, const void* q,
+                                     int64_t q_stride, const ispa_seg* segs, int32_t n_segs,
+                                     const uint8_t* w_codes, const float* w_scales, void* y, ispa_dtype y_dt,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  ispa_status st = check_attn_common(ISPA_BF16, n_q, H, d, q, q_stride);
+  if (st) return st;
+  if (n_segs < 1) return fail(ISPA_ERR_INVALID_ARG, "n_segs must be >= 1");
+  if ((st = check_group("segs", ISPA_BF16, H, d, segs, n_segs))) return st;
+  const int32_t D = H * d;
+  if ((st = check_w8a8(D, D, w_codes, w_scales, y, y_dt, n_q > 0))) return st;
+  if (!std::isfinite(scale)) return fail(ISPA_ERR_INVALID_ARG, "scale must be finite");
+  if (n_q == 0) return ISPA_OK;
+  const size_t need = ispa_local_attn_proj_fp8_workspace_bytes(n_q, H, d, segs, n_segs);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "local_attn_proj_fp8 workspace too small or misaligned");
+  char* wp = (char*)ws;
+  float* O = (float*)wp;
+  wp += align256((size_t)n_q * D * 4);
+  float* lse = (float*)wp;
+  wp += align256((size_t)n_q * H * 4);
+  uint8_t* xq = (uint8_t*)wp;
+  wp += align256((size_t)n_q * D);
+  float* sx = (float*)wp;
+  wp += align256((size_t)n_q * 4);
+  HostGroup g[1] = {{segs, n_segs}};
+  float* oo[1] = {O};
+  float* ll[1] = {lse};
+  st = run_group_attention(ISPA_BF16, n_q, H, d, scale, q, q_stride, g, 1, oo, ll, wp,
+                           ws_bytes - (size_t)(wp - (char*)ws), stream);
+  if (st) return st;
+  if ((st = launch_quant_rows_e4m3(O, ISPA_F32, D, n_q, D, xq, D, sx, stream))) return st;
+  return run_w8a8_gemm(n_q, D, D, xq, sx, w_codes, w_scales, y, y_dt, stream);
+}
+
 }  // extern "C"

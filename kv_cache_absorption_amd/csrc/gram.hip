@@ -47,6 +47,18 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds
                : "memory", "m0");
 }
 
+// fp8 product over a whole 64-byte K stage: each operand's two 16-byte
+// fragments (k slices 0 and 1 of the stage) form the 32 bytes a lane supplies.
+// Both operands take their bytes from the same row offsets, so the pairing of
+// k indices is the same on both sides and the sum runs over the stage's 64 k.
+__device__ __forceinline__ f32x16 mfma_e4m3(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  // format 0 (E4M3) for both operands; block scale exponent 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 template <int MT>
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
   if constexpr (MT == ISPA_BF16)
@@ -90,6 +102,9 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, bo
 
 template <int MT, int WN>
 __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
+  constexpr bool F8 = MT == kMtE4M3;
+  constexpr int ES = F8 ? 1 : 2;     // bytes per element
+  constexpr int BKE = ROWB / ES;     // elements per K stage (32, or 64 for fp8)
   constexpr int BN = 2 * WN;
   constexpr int NJ = WN / 32;                 // 32-column blocks per wave
   constexpr int XB = BM * ROWB, YB = BN * ROWB;  // bytes per stage of each operand
@@ -121,30 +136,30 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kb = (int64_t)split * p.kchunk;
   const int64_t ke = min(p.K, kb + p.kchunk);
-  const int ns = ke > kb ? (int)((ke - kb) / BK) : 0;  // K is a multiple of BK
+  const int ns = ke > kb ? (int)((ke - kb) / BKE) : 0;  // K is a multiple of BKE
 
   // ---- operand sources: rows of 2*ld bytes; rows past the end reload the last one
   const int64_t xrows = p.M, yrows = p.y_rows;
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)p.x + m0 * p.ldx * 2), 0, (int)(min<int64_t>(BM, xrows - m0) * p.ldx * 2), 0x00020000);
+      (void*)((const char*)p.x + m0 * p.ldx * ES), 0, (int)(min<int64_t>(BM, xrows - m0) * p.ldx * ES), 0x00020000);
   const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(yp + n0 * p.ldy * 2), 0, (int)(min<int64_t>(BN, yrows - n0) * p.ldy * 2), 0x00020000);
+      (void*)(yp + n0 * p.ldy * ES), 0, (int)(min<int64_t>(BN, yrows - n0) * p.ldy * ES), 0x00020000);
   int xo[XL], yo[YL];
 #pragma unroll
   for (int i = 0; i < XL; ++i) {
     const int row = (wave * XL + i) * RPI + lane / (ROWB / 16);  // RPI rows per 1 KB instruction
     const int xr = (int)min<int64_t>(row, xrows - m0 - 1);
-    xo[i] = xr * (int)(p.ldx * 2) + gswz(row, lane % (ROWB / 16)) * 16;
+    xo[i] = xr * (int)(p.ldx * ES) + gswz(row, lane % (ROWB / 16)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < YL; ++i) {
     const int row = (wave * YL + i) * RPI + lane / (ROWB / 16);
     const int yr = (int)min<int64_t>(row, yrows - n0 - 1);
-    yo[i] = yr * (int)(p.ldy * 2) + gswz(row, lane % (ROWB / 16)) * 16;
+    yo[i] = yr * (int)(p.ldy * ES) + gswz(row, lane % (ROWB / 16)) * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
   auto issue = [&](int s, int buf) {
-    const int soff = (int)((kb + (int64_t)s * BK) * 2);
+    const int soff = (int)((kb + (int64_t)s * BKE) * ES);
     const uint32_t xb = lds0 + buf * (XB + YB), yb = xb + XB;
 #pragma unroll
     for (int i = 0; i < XL; ++i) lds_dma16(rx, xb + (wave * XL + i) * 1024, xo[i], soff);
@@ -202,6 +217,13 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = mfma<MT>(b[j], a[i], acc[i][j]);
   };
+  // fp8: one MFMA per output block over both slices of a stage
+  auto mfmas8 = [&](const u32x4 (&a0)[4], const u32x4 (&b0)[NJ], const u32x4 (&a1)[4], const u32x4 (&b1)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_e4m3(b0[j], b1[j], a0[i], a1[i], acc[i][j]);
+  };
 
   int issued = 0, lbuf = 0;
   for (; issued < PD && issued < ns; ++issued) {
@@ -231,21 +253,28 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
     }
     frags(cbuf, 1, fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);  // keep each phase's reads ahead of the MFMAs they overlap
-    mfmas(fa0, fb0);
+    if constexpr (F8)
+      mfmas8(fa0, fb0, fa1, fb1);  // the whole stage, before the barrier: both slices are in registers
+    else
+      mfmas(fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
     const int nbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;
     wait_stage(issued - (s + 2));  // stage s + 1 is in LDS
     __syncthreads();
     frags(nbuf, 0, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa1, fb1);
+    if constexpr (!F8) mfmas(fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
     cbuf = nbuf;
   }
   if (ns > 0) {  // every stage has been issued by now
     frags(cbuf, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    mfmas(fa1, fb1);
+    if constexpr (F8) {
+      mfmas8(fa0, fb0, fa1, fb1);
+    } else {
+      mfmas(fa0, fb0);
+      mfmas(fa1, fb1);
+    }
   }
 
   // ---- epilogues: lane holds out[m][n .. n+3] in acc[i][j][4 g .. 4 g + 3] with
@@ -285,6 +314,34 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     if (tid == 0) p.sq_partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+    return;
+  }
+  if (p.epi == kNtStoreScaled) {
+    // dequantising store: acc * sx[m] * sy[n], in out_dt
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 32 + lq;
+      if (m >= p.M) continue;
+      const float sxm = p.sx[m];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + wn * WN + j * 32 + g * 8 + hh * 4;  // N is a multiple of 4
+          if (n >= p.N) continue;
+          const f32x4 sy = *(const f32x4*)(p.sy + n);
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][g * 4 + e] * sxm * sy[e];
+          if (p.out_dt == ISPA_F32) {
+            *(f32x4*)((float*)p.out + m * p.ld_out + n) = v;
+          } else {
+            const bool bf = p.out_dt == ISPA_BF16;
+            auto pk = [&](float x, float y) { return bf ? pack_bf16(x, y) : pack_f16(x, y); };
+            *(u32x2*)((uint16_t*)p.out + m * p.ld_out + n) = (u32x2){pk(v[0], v[1]), pk(v[2], v[3])};
+          }
+        }
+    }
     return;
   }
   if (p.epi == kNtStore) {
@@ -422,6 +479,64 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const T16Jobs js) {
   }
 }
 
+// Symmetric per-row FP8 E4M3 quantisation, one workgroup per row: the row's
+// absolute maximum, then its codes four at a time (the second pass re-reads the
+// row from cache).  Both divisions are the compiler's IEEE fp32 division
+// (correctly rounded: no fast-math flags), so the codes are those of the same
+// arithmetic done in any IEEE fp32 implementation.  v_cvt_pk_fp8_f32 rounds to
+// nearest even and does not saturate (480 and above become NaN), hence the
+// clamp to +-448; a magnitude that rounds to zero is stored as code 0.
+template <typename InT>
+__global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const InT* in, int in_dt, int64_t ld_in, int64_t cols,
+                                                              uint8_t* codes, int64_t ld_codes, float* scales) {
+  const int64_t r = blockIdx.x;
+  const InT* row = in + r * ld_in;
+  auto to_f32 = [&](uint32_t b) { return in_dt == ISPA_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b); };
+  auto load4 = [&](int64_t c) {
+    f32x4 v;
+    if constexpr (sizeof(InT) == 4) {
+      v = *(const f32x4*)(row + c);
+    } else {
+      const u32x2 w = *(const u32x2*)(row + c);
+      v[0] = to_f32(w[0] & 0xffffu);
+      v[1] = to_f32(w[0] >> 16);
+      v[2] = to_f32(w[1] & 0xffffu);
+      v[3] = to_f32(w[1] >> 16);
+    }
+    return v;
+  };
+  float amax = 0.0f;
+  for (int64_t c = 4 * (int64_t)threadIdx.x; c < cols; c += 1024) {
+    const f32x4 v = load4(c);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float scale = amax / 448.0f;
+  if (threadIdx.x == 0) scales[r] = scale;
+  uint8_t* out = codes + r * ld_codes;
+  for (int64_t c = 4 * (int64_t)threadIdx.x; c < cols; c += 1024) {
+    uint32_t w = 0u;
+    if (scale > 0.0f) {
+      const f32x4 v = load4(c);
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(v[e] / scale, -448.0f), 448.0f);
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], pk, true);
+      w = (uint32_t)pk;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (((w >> (8 * b)) & 0x7fu) == 0u) w &= ~(0xffu << (8 * b));
+    }
+    *(uint32_t*)(out + c) = w;
+  }
+}
+
 // out[m][n .. n+3] += sum_s part[s][kind][m][n .. n+3]; the first kind keeps the
 // upper triangle (m <= n) only when tri is set.  The last workgroup instead adds
 // the n_sq per-workgroup sums of squares to *r2 (fixed order: deterministic).
@@ -467,15 +582,23 @@ ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t strea
   const int64_t n0 = p.tri ? (int64_t)p.tiles_m * (p.tiles_m + 1) / 2 : (int64_t)p.tiles_m * p.tiles_n;
   const int64_t blocks = (n0 + (p.two_kinds ? (int64_t)p.tiles_m * p.tiles_n : 0)) * p.ksplit;
   if (n_blocks_out) *n_blocks_out = (int)blocks;
-  if (p.K % BK || p.kchunk % BK || p.ksplit < 1 || (int64_t)p.ksplit * p.kchunk < p.K || p.ldx % 8 || p.ldy % 8 ||
-      (p.bn != 256 && p.bn != 128) || (p.tri && p.bn != BM) || p.N % 4 || p.ld_out % 4 ||
-      (p.epi == kNtAccum && p.ksplit > 1 && !p.part)) {
+  const bool f8 = mfma_dt == kMtE4M3;
+  const int64_t bke = f8 ? 2 * BK : BK, lda = f8 ? 16 : 8;
+  if (p.K % bke || p.kchunk % bke || p.ksplit < 1 || (int64_t)p.ksplit * p.kchunk < p.K || p.ldx % lda ||
+      p.ldy % lda || (p.bn != 256 && p.bn != 128) || (p.tri && p.bn != BM) || p.N % 4 || p.ld_out % 4 ||
+      (p.epi == kNtAccum && p.ksplit > 1 && !p.part) || (p.epi == kNtStoreScaled && (!p.sx || !p.sy)) ||
+      (f8 && p.epi != kNtStore && p.epi != kNtStoreScaled)) {
     set_error("nt_gemm: K, split, tile or leading dimensions not aligned");
     return ISPA_ERR_INVALID_ARG;
   }
   if (blocks == 0) return ISPA_OK;
   const dim3 grid((unsigned)blocks), block(256);
-  if (mfma_dt == ISPA_BF16) {
+  if (f8) {
+    if (p.bn == 256)
+      hipLaunchKernelGGL((nt_gemm_kernel<kMtE4M3, 128>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((nt_gemm_kernel<kMtE4M3, 64>), grid, block, 0, stream, p);
+  } else if (mfma_dt == ISPA_BF16) {
     if (p.bn == 256)
       hipLaunchKernelGGL((nt_gemm_kernel<ISPA_BF16, 128>), grid, block, 0, stream, p);
     else
@@ -487,6 +610,22 @@ ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t strea
       hipLaunchKernelGGL((nt_gemm_kernel<ISPA_F16, 64>), grid, block, 0, stream, p);
   }
   return check_launch("nt_gemm_kernel");
+}
+
+ispa_status launch_quant_rows_e4m3(const void* in, int in_dt, int64_t ld_in, int64_t rows, int64_t cols,
+                                   uint8_t* codes, int64_t ld_codes, float* scales, hipStream_t stream) {
+  if (rows <= 0) return ISPA_OK;
+  if (cols < 0 || cols % 4 || ld_in % 4 || ld_codes % 4 || ld_in < cols || ld_codes < cols || rows > INT32_MAX) {
+    set_error("quant_rows_e4m3: cols, ld_in and ld_codes must be multiples of 4 (ld >= cols)");
+    return ISPA_ERR_INVALID_ARG;
+  }
+  if (in_dt == ISPA_F32)
+    hipLaunchKernelGGL(quant_rows_e4m3_kernel<float>, dim3((unsigned)rows), dim3(256), 0, stream,
+                       (const float*)in, in_dt, ld_in, cols, codes, ld_codes, scales);
+  else
+    hipLaunchKernelGGL(quant_rows_e4m3_kernel<uint16_t>, dim3((unsigned)rows), dim3(256), 0, stream,
+                       (const uint16_t*)in, in_dt, ld_in, cols, codes, ld_codes, scales);
+  return check_launch("quant_rows_e4m3_kernel");
 }
 
 ispa_status launch_nt_split_reduce(const NtGemmParams& p, const double* sq, int64_t n_sq, double* r2,

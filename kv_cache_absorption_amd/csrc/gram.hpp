@@ -10,8 +10,14 @@ enum {
                   // workgroups store partial sums to part[split][kind] (layout of out) for nt_split_reduce
   kNtStoreT = 1,  // out[m][n] = acc as 16-bit (mfma type) for n < n_valid, 0 for n_valid <= n < N;
                   // per-workgroup sum of squares of the stored values
-  kNtStore = 2    // out[m][n] = acc as out_dt (bf16, f16 or fp32)
+  kNtStore = 2,   // out[m][n] = acc as out_dt (bf16, f16 or fp32)
+  kNtStoreScaled = 3  // out[m][n] = acc * sx[m] * sy[n] as out_dt (the dequantising store of the fp8 product)
 };
+
+// Operand type of an NT GEMM with OCP FP8 E4M3 operands (1-byte elements, 64
+// per K stage, v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales).  Not
+// an ispa_dtype: only the W8A8 projection uses it.
+constexpr int kMtE4M3 = 0x38;
 
 struct NtGemmParams {
   int64_t M, N, K;   // acc[m][n] = sum_k X[m][k] Y[n][k]; K a multiple of kNtBK
@@ -32,10 +38,22 @@ struct NtGemmParams {
   int64_t kchunk;
   double* sq_partials;
   float* part;        // kNtAccum with ksplit > 1: [ksplit][2][M][ld_out] partial sums
-  int32_t out_dt;     // kNtStore
+  int32_t out_dt;     // kNtStore, kNtStoreScaled
+  const float* sx;    // kNtStoreScaled: per-row (m) and per-column (n) scales
+  const float* sy;
 };
 
+// mfma_dt: ISPA_BF16, ISPA_F16 or kMtE4M3; x, y element size follows it (ldx,
+// ldy in elements: multiples of 8, and of 16 for kMtE4M3); K a multiple of the
+// K stage (32 elements, 64 for kMtE4M3)
 ispa_status launch_nt_gemm(const NtGemmParams& p, int mfma_dt, hipStream_t stream, int* n_blocks_out);
+// Symmetric per-row FP8 E4M3 quantisation: for each of `rows` rows of `cols`
+// elements (in_dt fp32, bf16 or f16; cols a multiple of 4, ld_in of 4),
+// scale = amax / 448 and code = E4M3(clamp(x / scale, -448, 448)) with both
+// divisions correctly rounded in fp32, ties to even, and a zero magnitude as
+// code 0; a zero row gets scale 0 and zero codes.  codes: rows x ld_codes bytes.
+ispa_status launch_quant_rows_e4m3(const void* in, int in_dt, int64_t ld_in, int64_t rows, int64_t cols,
+                                   uint8_t* codes, int64_t ld_codes, float* scales, hipStream_t stream);
 // out (and out2) += sum over splits of the partial sums a kNtAccum launch left in p.part
 // (nothing when p.ksplit == 1), and *r2 += the n_sq sums of squares in sq
 ispa_status launch_nt_split_reduce(const NtGemmParams& p, const double* sq, int64_t n_sq, double* r2,

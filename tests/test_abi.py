@@ -22,7 +22,7 @@ def _lib():
 def test_exports_match_header():
     m, L = _lib()
     hdr = open(os.path.join(ROOT, "include", "ispa.h")).read()
-    declared = set(re.findall(r"\b(ispa_[a-z_]+)\s*\(", hdr))
+    declared = set(re.findall(r"\b(ispa_[a-z0-9_]+)\s*\(", hdr))
     assert declared == set(m.EXPORTED)
     for name in declared:
         assert hasattr(L, name), name
@@ -155,3 +155,42 @@ def test_stream_layout_matches_oracle_grouping():
     for c in (0, 1, 7):
         n = keys_retained(c, T, flags)
         assert kv_bytes(n, 1536) == kv_bytes_retained(n, 1536)
+
+
+def test_w8a8_calls_reject_bad_args():
+    m, L = _lib()
+    F = FAKE
+    big = 1 << 30
+    # weight quantisation: 16-bit W only, dims multiples of 4, workspace checked
+    assert L.ispa_quantize_w_fp8_workspace_bytes(1536, 1536) >= 1536 * 1536 * 2
+    assert L.ispa_quantize_w_fp8(m.ISPA_F32, 128, 128, F, F, F, F, big, None) == m.ISPA_ERR_UNSUPPORTED
+    assert L.ispa_quantize_w_fp8(m.ISPA_BF16, 130, 128, F, F, F, F, big, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_quantize_w_fp8(m.ISPA_BF16, 128, 128, None, F, F, F, big, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_quantize_w_fp8(m.ISPA_BF16, 128, 128, F, F, F, F, 10, None) == m.ISPA_ERR_WORKSPACE
+    # the W8A8 product: d_in a multiple of 64, ld_x >= d_in, 16-byte aligned codes and scales
+    assert L.ispa_w8a8_linear_workspace_bytes(4680, 1536) >= 4680 * 1536 + 4680 * 4
+    assert L.ispa_w8a8_linear(m.ISPA_F32, 8, 96, 64, F, 96, F, F, F, m.ISPA_F32, F, big, None) \
+        == m.ISPA_ERR_INVALID_ARG  # d_in not a multiple of 64
+    assert L.ispa_w8a8_linear(m.ISPA_F32, 8, 128, 64, F, 64, F, F, F, m.ISPA_F32, F, big, None) \
+        == m.ISPA_ERR_INVALID_ARG  # ld_x < d_in
+    assert L.ispa_w8a8_linear(m.ISPA_F32, 8, 128, 64, F, 128, F + 4, F, F, m.ISPA_F32, F, big, None) \
+        == m.ISPA_ERR_INVALID_ARG  # misaligned codes
+    assert L.ispa_w8a8_linear(9, 8, 128, 64, F, 128, F, F, F, m.ISPA_F32, F, big, None) \
+        == m.ISPA_ERR_UNSUPPORTED
+    assert L.ispa_w8a8_linear(m.ISPA_F32, 8, 128, 64, F, 128, F, F, F, m.ISPA_F32, F, 10, None) \
+        == m.ISPA_ERR_WORKSPACE
+    assert L.ispa_w8a8_linear(m.ISPA_F32, 0, 128, 64, None, 128, F, F, None, m.ISPA_F32, None, 0, None) \
+        == m.ISPA_OK  # no rows: nothing launched
+    # attention + W8A8 projection: bf16 attention arguments, D = H d
+    segs = _segarr(m, [_seg(10, ptr=F)])
+    assert L.ispa_local_attn_proj_fp8_workspace_bytes(4, 2, 128, segs, 1) > 4 * 256 * 4
+    assert L.ispa_local_attn_proj_fp8(4, 2, 96, 0.1, F, 256, segs, 1, F, F, F, m.ISPA_BF16, F, big,
+                                      None) == m.ISPA_ERR_UNSUPPORTED  # head_dim
+    assert L.ispa_local_attn_proj_fp8(4, 2, 128, 0.1, F, 256, segs, 0, F, F, F, m.ISPA_BF16, F, big,
+                                      None) == m.ISPA_ERR_INVALID_ARG  # no segments
+    assert L.ispa_local_attn_proj_fp8(4, 2, 128, 0.1, F, 256, segs, 1, None, F, F, m.ISPA_BF16, F, big,
+                                      None) == m.ISPA_ERR_INVALID_ARG  # no weight codes
+    assert L.ispa_local_attn_proj_fp8(4, 2, 128, float("nan"), F, 256, segs, 1, F, F, F, m.ISPA_BF16, F,
+                                      big, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_local_attn_proj_fp8(4, 2, 128, 0.1, F, 256, segs, 1, F, F, F, m.ISPA_BF16, F, 10,
+                                      None) == m.ISPA_ERR_WORKSPACE

@@ -529,3 +529,135 @@ def test_end_to_end_tiny_fp32():
     y_ref = O.local_attn_proj(q.cpu(), torch.cat([g.sink_k, kc]).cpu(), torch.cat([g.sink_v, vc]).cpu(),
                               g.w.cpu().double().numpy() + dW_ref, 64 ** -0.5)
     assert rel(h64(y), y_ref) <= 1e-4
+
+
+# ---------------------------------------------------------------- W8A8 projection
+# The quantisation scheme is the oracle's (its docstrings state it): codes are
+# integers decided in fp32 on both sides, so they must agree exactly.
+@pytest.mark.parametrize("w_dt,d_in,d_out", [
+    (torch.bfloat16, 1536, 1536),   # Wan-1.3B W_eff
+    (torch.float16, 320, 196),      # ragged widths
+])
+def test_quantize_w_fp8_codes_exact(w_dt, d_in, d_out):
+    print(f"quantize_w_fp8 {w_dt} {d_in}x{d_out}", flush=True)
+    w = synth.normal((d_in, d_out), 91, DEV, std=d_in ** -0.5, dtype=w_dt)
+    w[:, 5] = 0  # a zero output column: scale 0, zero codes
+    codes, scales = K().ispa_quantize_w_fp8(w)
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_weight_e4m3(w.cpu())
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+# The fp8 matrix core (v_mfma_scale_f32_32x32x64_f8f6f4) does not sum its
+# products exactly: a GPU probe of known dot products shows each aligned group
+# of 8 consecutive k added with about 12 bits below the group's largest
+# product (smaller parts truncated; 448 + 2^-9 in one group gives 448, in two
+# groups 448.001953125), the group sums then added in fp32.  So an output
+# differs from the exact sum of the dequantised products by at most
+# 7 * 2^-12 < 2^-9 of each group's largest |product|, summed over the groups,
+# plus fp32 roundings.
+def _w8a8_group_bound(x, w, rows, cols):
+    """Per-output bound on |y_gpu - y_exact| for the sampled rows and columns:
+    2^-9 * sum over 8-wide k groups of the largest |product| + 2^-20 * sum |product|."""
+    qx, sx = O.quantize_rows_e4m3(x)
+    qw, sw = O.quantize_weight_e4m3(w)
+    xa = O.e4m3_decode(qx[rows]) * sx[rows].astype(np.float64)[:, None]
+    wb = O.e4m3_decode(qw[cols]) * sw[cols].astype(np.float64)[:, None]
+    prod = np.abs(xa[:, None, :] * wb[None, :, :])  # [rows, cols, d_in]
+    gmax = prod.reshape(len(rows), len(cols), -1, 8).max(axis=3).sum(axis=2)
+    return 2.0 ** -9 * gmax + 2.0 ** -20 * prod.sum(axis=2)
+
+
+@pytest.mark.parametrize("x_dt,n,d_in,d_out,y_dt", [
+    (torch.float32, 300, 320, 196, torch.float32),      # ragged: partial row and column tiles
+    (torch.bfloat16, 4680, 1536, 1536, torch.float32),  # Wan-1.3B projection
+    (torch.float32, 4680, 5120, 5120, torch.bfloat16),  # Wan-14B projection, bf16 output
+])
+def test_w8a8_linear_parity(x_dt, n, d_in, d_out, y_dt):
+    print(f"w8a8_linear {x_dt} n={n} {d_in}x{d_out} -> {y_dt}", flush=True)
+    x = synth.normal((n, d_in), 92, DEV, dtype=x_dt)
+    x[7] = 0  # a zero row
+    w = synth.normal((d_in, d_out), 93, DEV, std=d_in ** -0.5, dtype=torch.bfloat16)
+    codes, scales = K().ispa_quantize_w_fp8(w)
+    y = K().ispa_w8a8_linear(x, codes, scales, out_dtype=y_dt)
+    torch.cuda.synchronize()
+    xc, wc = x.cpu(), w.cpu()
+    ref = O.w8a8_linear(xc, *O.quantize_weight_e4m3(wc))
+    yg = h64(y)
+    assert not yg[7].any()
+    # whole output: the group truncation measured at 1.4e-5 rel-L2 (K = 320);
+    # 1e-4 stays far below the ~3% the quantisation itself costs
+    bf = y_dt == torch.bfloat16
+    assert rel(yg, ref) <= (1e-4 + 2.0 ** -9 if bf else 1e-4)
+    # sampled outputs against the elementwise bound (bf16 output: one more
+    # rounding, 2^-9 of |y|)
+    rows = np.unique(np.linspace(0, n - 1, 24).astype(int))
+    cols = np.unique(np.linspace(0, d_out - 1, 40).astype(int))
+    bound = _w8a8_group_bound(xc, wc, rows, cols)
+    err = np.abs(yg[np.ix_(rows, cols)] - ref[np.ix_(rows, cols)])
+    if bf:
+        bound = bound + 2.0 ** -9 * np.abs(ref[np.ix_(rows, cols)])
+    assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def test_local_attn_proj_fp8_exact_when_attention_is():
+    """Degenerate case: every key of a head has the same value row, so the
+    attention output is that row whatever the scores (to fp32 rounding).  The
+    rows hold values on the E4M3 grid times 2^-5 with a row maximum of 14, so
+    the activation scale is 2^-5 and every code is a grid point, far from a
+    rounding tie: the attention -> quantisation -> fp8 product wiring is then
+    checked at the fp8 matrix core's own accuracy."""
+    H, d, n_q, n_k = 12, 128, 300, 2000
+    D = H * d
+    print(f"local_attn_proj_fp8 degenerate H={H} n_q={n_q} keys={n_k}", flush=True)
+    q = _cache(n_q, H, d, 95)
+    k = _cache(n_k, H, d, 96)
+    c = torch.arange(D, dtype=torch.float32)
+    u = ((8 + (c * 5) % 8) / 8) * torch.exp2((c % 6) - 4) * torch.where(c % 3 == 0, -1.0, 1.0)
+    u[17] = 14.0  # the row maximum: 1.75 * 2^3
+    v = u.to(torch.bfloat16).reshape(1, H, d).expand(n_k, H, d).contiguous().to(DEV)
+    w = synth.normal((D, D), 97, DEV, std=D ** -0.5, dtype=torch.bfloat16)
+    codes, scales = K().ispa_quantize_w_fp8(w)
+    y = K().ispa_local_attn_proj_fp8(q, [(k, v)], codes, scales, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.local_attn_proj_w8a8(q.cpu(), k.cpu(), v.cpu(), w.cpu(), d ** -0.5)
+    # the fp8 matrix core's group truncation (see above) is the only error
+    # left: 1e-4, as for the plain product, far below any wiring mistake
+    assert rel(h64(y), ref) <= 1e-4
+    o = u.double().numpy()[None, :].repeat(n_q, axis=0)
+    cols = np.arange(0, D, 37)
+    bound = _w8a8_group_bound(o.astype(np.float32), w.cpu(), np.arange(3), cols)
+    assert np.all(np.abs(h64(y)[:3][:, cols] - ref[:3][:, cols]) <= bound + 1e-6 * np.abs(ref[:3][:, cols]))
+
+
+def test_local_attn_proj_fp8_wan13b_shape():
+    """Sink + current chunk of a Wan-1.3B layer (300 of the 4680 queries),
+    against the oracle's W8A8 result and against the unquantised projection.
+
+    Bar against the oracle's W8A8: the GPU attention differs from the fp64
+    one by up to 5e-3 relative; an activation whose x / scale lies that close
+    to a rounding midpoint gets the neighbouring code on one side, one E4M3
+    step (2^-4 .. 2^-3 relative) apart.  About 5e-3 / 2^-4 = 8% of the codes
+    can flip, an rms activation difference of sqrt(0.08) * 2^-3.5 ~ 2.5%,
+    which carries into y; 4e-2 leaves margin.  The quantisation itself costs
+    a few percent against the unquantised projection (oracle pin: 1e-3 to
+    6e-2 on Gaussian operands)."""
+    H, d, n_q, n_sink, n_cur = 12, 128, 300, 1560, 300
+    D = H * d
+    print(f"local_attn_proj_fp8 H={H} n_q={n_q} keys={n_sink + n_cur}", flush=True)
+    g = synth.GroupInputs(n_q, H, d, n_sink, 0, torch.bfloat16, 98, DEV, workload=2)
+    q, kc, vc = g.step(0)
+    w = synth.normal((D, D), 99, DEV, std=D ** -0.5, dtype=torch.bfloat16)
+    codes, scales = K().ispa_quantize_w_fp8(w)
+    segs = [(g.sink_k, g.sink_v), (kc, vc)]
+    y = K().ispa_local_attn_proj_fp8(q, segs, codes, scales, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kk = torch.cat([g.sink_k, kc]).cpu()
+    vv = torch.cat([g.sink_v, vc]).cpu()
+    ref = O.local_attn_proj_w8a8(q.cpu(), kk, vv, w.cpu(), d ** -0.5)
+    ref_full = O.local_attn_proj(q.cpu(), kk, vv, w.cpu(), d ** -0.5)
+    e8, ef = rel(h64(y), ref), rel(h64(y), ref_full)
+    print(f"rel-L2 vs oracle W8A8 {e8:.3e}, vs unquantised {ef:.3e}", flush=True)
+    assert e8 <= 4e-2
+    assert ef <= 6e-2
