@@ -29,6 +29,9 @@ layers (the chunk's Q, K, V are generated on the GPU before its events):
   wan14b_post    40 post-switch chunks of the same 40 layers (20 L-Layers on
                  sink + current, 20 F-Layers on up to 187200 keys), with the
                  selection and W + dW of an untimed wan14b_warmup pass
+  wan14b_post_w8a8  wan14b_post with the W8A8 projections: W and W + dW
+                 quantised once (untimed, at the switch) to FP8 E4M3, the
+                 attention output per token, the products on the fp8 matrix core
   wan13b_recal   the wan13b_stream layers with warmup re-entered: warmup 0-5,
                  switch, post-switch 6-11, warmup again at 12-17 (statistics
                  from zero, every layer over the keys it still holds), switch,
@@ -115,6 +118,7 @@ STREAMS = {
     "wan13b_stream": dict(N=30, H=12, d=128, chunks=20, warm=6, K=15, wid=3),
     "wan14b_warmup": dict(N=40, H=40, d=128, chunks=19, warm=19, K=20, wid=4),
     "wan14b_post": dict(N=40, H=40, d=128, chunks=40, warm=0, K=20, wid=5),
+    "wan14b_post_w8a8": dict(N=40, H=40, d=128, chunks=40, warm=0, K=20, wid=5, w8a8=True),
     # re-calibration: warmup 0-5, switch, post 6-11, warmup re-entered at 12
     # (12-17), switch again, post 18-23
     "wan13b_recal": dict(N=30, H=12, d=128, chunks=24, warm=6, K=15, wid=3, recal=12, warm2=6),
@@ -149,6 +153,8 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
         st = IspaStream(N, H, d, T, caps, dev, with_stats=False)
         st.W = W
         st.adopt_switch(is_local, w_eff)
+        if spec.get("w8a8"):
+            st.quantize_projections()  # once per switch, before the timed chunks
     stream = torch.cuda.current_stream(dev)
     qbuf = torch.empty((N, T, H, d), dtype=torch.bfloat16, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -255,7 +261,7 @@ def run_stream(args, name, dev):
     D = H * d
     adopt = None
     pre = {}
-    if name == "wan14b_post":
+    if name in ("wan14b_post", "wan14b_post_w8a8"):
         t0 = time.perf_counter()
         _, pre_switch_ms, st4, _ = _stream_pass(STREAMS["wan14b_warmup"], dev, args.seed)
         adopt = (list(st4.is_local_host), st4.W, st4.w_eff)

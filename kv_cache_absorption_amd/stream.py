@@ -218,6 +218,7 @@ class IspaStream:
         self.ws = Workspace(dev)
         self.switched = False
         self.dW = self.eps = self.info = self.w_eff = None
+        self.wq = self.wq_scale = None  # W8A8 projection codes and scales, when quantised
         self.selected = self.is_local = self.status = None
         self.is_local_host = None
         self.warmups = 1  # warmup phases entered (re-calibration adds one)
@@ -364,6 +365,25 @@ class IspaStream:
                 self.kv[layer].evict_history()
         self.G = self.C = None
 
+    def quantize_projections(self):
+        """W8A8 post-switch projections (the pages report ISPA combined with
+        W8A8 quantisation; EN review, Key Findings): quantise each layer's
+        projection once, W + dW for an L-Layer and W for an F-Layer, to FP8
+        E4M3 codes with one scale per output column.  Later :meth:`post` calls
+        then quantise the attention output per token and project on the fp8
+        matrix core.  Call after the switch; a re-calibration drops the codes."""
+        if not self.switched:
+            raise RuntimeError("projections are quantised after the switch")
+        L, s, N, D, dev = self.L, self._stream(), self.N, self.D, self.device
+        self.wq = torch.empty((N, D, D), dtype=torch.uint8, device=dev)
+        self.wq_scale = torch.empty((N, D), dtype=torch.float32, device=dev)
+        need = L.ispa_quantize_w_fp8_workspace_bytes(D, D)
+        ws = self.ws.get(need)
+        for layer in range(N):
+            w = self.w_eff[layer] if self.is_local_host[layer] else self.W[layer]
+            self._ck(L.ispa_quantize_w_fp8(B.ISPA_BF16, D, D, w.data_ptr(), self.wq[layer].data_ptr(),
+                                           self.wq_scale[layer].data_ptr(), ws.data_ptr(), need, s))
+
     def recalibrate(self, c: int):
         """Re-enter warmup at chunk c (after a scene change, which the caller
         detects; EN review, Limitations: warmup is re-entered to refresh the
@@ -387,6 +407,7 @@ class IspaStream:
             kv.keep_from(c)
         self.switched = False
         self.selected = self.is_local = self.status = None
+        self.wq = self.wq_scale = None
         self.warmups += 1
 
     # ------------------------------------------------------------------ post-switch
@@ -399,6 +420,15 @@ class IspaStream:
         L, s = self.L, self._stream()
         local = bool(self.is_local_host[layer])
         segs, ns = self._segs(self.kv[layer].attend_all(c))
+        if self.wq is not None:  # W8A8 projection
+            need = L.ispa_local_attn_proj_fp8_workspace_bytes(self.T, self.H, self.d, segs, ns)
+            ws = self.ws.get(need)
+            self._ck(L.ispa_local_attn_proj_fp8(self.T, self.H, self.d, self.scale, q.data_ptr(), q.stride(0),
+                                                segs, ns, self.wq[layer].data_ptr(),
+                                                self.wq_scale[layer].data_ptr(), self.y.data_ptr(),
+                                                B.ISPA_BF16, ws.data_ptr() if ws is not None else None,
+                                                need, s))
+            return self.y
         w = self.w_eff[layer] if local else self.W[layer]
         need = L.ispa_local_attn_proj_workspace_bytes(B.ISPA_BF16, self.T, self.H, self.d, segs, ns)
         ws = self.ws.get(need)

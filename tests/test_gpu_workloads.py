@@ -332,3 +332,43 @@ def test_budget_and_warmup_sweep():
         assert abs(a - b) <= 1e-12 * max(abs(b), 1.0)
     print(f"eps after 2 chunks {['%.4g' % x for x in evals[1]]}, after 4 {['%.4g' % x for x in evals[3]]}",
           flush=True)
+
+
+def test_stream_w8a8_projection():
+    """A short Wan-1.3B-shaped stream (4 layers, warmup chunks 0-2, switch
+    with K = 2, W8A8 projections quantised once, post-switch chunks 3-4): an
+    F-Layer's output rows at the last chunk against the oracle's attention +
+    W8A8 projection with its seeded W (bar 4e-2, derived in the parity tests
+    from code flips caused by the bf16 attention's error), and every output
+    finite."""
+    from kv_cache_absorption_amd.stream import IspaStream
+    N, H, d, K, warm, chunks = 4, 12, 128, 2, 3, 5
+    print(f"W8A8 stream: {N} layers, warmup {warm}, K={K}, {chunks} chunks", flush=True)
+    si = synth.StreamInputs(N, H, d, T, torch.bfloat16, 13, DEV, workload=3)
+    st = IspaStream(N, H, d, T, chunks, DEV)
+    for layer in range(N):
+        st.set_w(layer, si.w(layer))
+    for c in range(warm):
+        for layer in range(N):
+            k, v = si.kv(layer, c)
+            st.write_kv(layer, c, k, v)
+            st.warmup(layer, c, si.q(layer, c))
+    st.switch(K)
+    st.quantize_projections()
+    assert st.wq.shape == (N, H * d, H * d) and bool(torch.isfinite(st.wq_scale).all())
+    f_layer = st.is_local_host.index(0)
+    for c in range(warm, chunks):
+        for layer in range(N):
+            k, v = si.kv(layer, c)
+            st.write_kv(layer, c, k, v)
+            q = si.q(layer, c)
+            y = st.post(layer, c, q)
+            assert bool(torch.isfinite(y).all())
+            if layer == f_layer and c == chunks - 1:
+                segs = st.kv[layer].attend_all(c)
+                kk = torch.cat([s[0] for s in segs]).cpu()
+                vv = torch.cat([s[1] for s in segs]).cpu()
+                ref = O.local_attn_proj_w8a8(q[ROWS].cpu(), kk, vv, si.w(layer).cpu(), st.scale)
+                e = rel(h64(y[ROWS]), ref)
+                print(f"F-Layer {layer} chunk {c}: {kk.shape[0]} keys, rel-L2 vs oracle W8A8 {e:.3e}", flush=True)
+                assert e <= 4e-2
