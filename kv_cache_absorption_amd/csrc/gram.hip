@@ -26,6 +26,11 @@
 //   * operand rows past the matrix reload the last valid row (results there
 //     are discarded); the token dimension is zero-padded to a multiple of 32 so
 //     no K masking is needed.
+// The same kernel takes FP8 E4M3 operands for the W8A8 post-switch projection:
+// 1-byte elements in the same 64-byte LDS rows (64 k per stage), one
+// v_mfma_scale_f32_32x32x64_f8f6f4 per output block and stage over both
+// fragments of the stage, and a store that multiplies by the row and column
+// scales.
 #include "gram.hpp"
 
 #include <algorithm>
