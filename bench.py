@@ -364,6 +364,42 @@ def run_stream(args, name, dev):
     print(json.dumps(out), flush=True)
 
 
+def proj_compare(n_calls, dev):
+    """Post-switch attention + projection of one chunk (4680 queries over the
+    sink and current chunk, 9360 keys) with the bf16 projection and with the
+    W8A8 one, and the W8A8 product alone on fp32 activations, at D = 1536
+    (12 heads) and D = 5120 (40 heads).  Mean ms per call with HIP events on
+    the current stream."""
+    import torch
+    import synth
+    import kv_cache_absorption_amd as K
+    out = {"calls": n_calls}
+    for H in (12, 40):
+        D = H * 128
+        g = synth.GroupInputs(TOKENS_PER_CHUNK, H, 128, TOKENS_PER_CHUNK, 0, torch.bfloat16, 1, dev, workload=2)
+        q, kc, vc = g.step(0)
+        w = synth.normal((D, D), 5, dev, std=D ** -0.5, dtype=torch.bfloat16)
+        segs = [(g.sink_k, g.sink_v), (kc, vc)]
+        codes, scales = K.ispa_quantize_w_fp8(w)
+        x = synth.normal((TOKENS_PER_CHUNK, D), 6, dev, dtype=torch.float32)
+        for name, f in (("bf16 attention + projection", lambda: K.ispa_local_attn_proj(q, segs, w)),
+                        ("attention + W8A8 projection", lambda: K.ispa_local_attn_proj_fp8(q, segs, codes, scales)),
+                        ("W8A8 product", lambda: K.ispa_w8a8_linear(x, codes, scales)),
+                        ("weight quantisation", lambda: K.ispa_quantize_w_fp8(w))):
+            for _ in range(2):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n_calls):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            out[f"D={D} {name} ms"] = round(e0.elapsed_time(e1) / n_calls, 4)
+        del g, q, kc, vc, w, codes, scales, x
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +412,9 @@ def main():
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only run this many dual-attention calls of the workload (counter runs)")
+    ap.add_argument("--proj-compare", type=int, default=0,
+                    help="only time the post-switch projection paths (bf16 and W8A8) at the Wan-1.3B "
+                         "and Wan-14B widths, this many calls each")
     args = ap.parse_args()
     is_stream = args.workload != "wan13b_layer"
     if args.steps is None:
@@ -405,6 +444,9 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes}))
         return
     L = B.lib()  # raises if libispa.so is missing: no fallback path exists
+    if args.proj_compare:
+        print(json.dumps(proj_compare(args.proj_compare, dev)))
+        return
     if args.workload != "wan13b_layer":
         run_stream(args, args.workload, dev)
         return
