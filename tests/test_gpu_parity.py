@@ -661,3 +661,18 @@ def test_local_attn_proj_fp8_wan13b_shape():
     print(f"rel-L2 vs oracle W8A8 {e8:.3e}, vs unquantised {ef:.3e}", flush=True)
     assert e8 <= 4e-2
     assert ef <= 6e-2
+
+
+def test_local_attn_proj_fp8_empty_keys():
+    """An empty key set: attention gives 0, the activation rows are all zero
+    (scale 0, zero codes), so y = 0 exactly, as on the bf16 path."""
+    H, d, n_q = 2, 128, 70
+    print("local_attn_proj_fp8 empty key set", flush=True)
+    q = _cache(n_q, H, d, 101)
+    k = _cache(1, H, d, 102)[:0]
+    w = synth.normal((H * d, H * d), 103, DEV, std=(H * d) ** -0.5, dtype=torch.bfloat16)
+    codes, scales = K().ispa_quantize_w_fp8(w)
+    y = K().ispa_local_attn_proj_fp8(q, [(k, k)], codes, scales, out_dtype=torch.float32)
+    y16 = K().ispa_local_attn_proj(q, [(k, k)], w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert not h64(y).any() and not h64(y16).any()
