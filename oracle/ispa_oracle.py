@@ -35,6 +35,8 @@ __all__ = [
     "dual_stream_attention",
     "residual_target",
     "accumulate_stats",
+    "accumulate_gram",
+    "stats_from_gram",
     "ridge_lambda",
     "cholesky_lower",
     "forward_substitution",
@@ -166,6 +168,34 @@ def accumulate_stats(a_loc, delta_a, w):
     a = as_f64(a_loc)
     r = as_f64(delta_a) @ as_f64(w)
     return a.T @ a, a.T @ r, float(np.sum(r * r))
+
+
+def accumulate_gram(a_loc, delta_a):
+    """One step's contribution to the statistics in the grouping of the
+    printed closed form.
+
+    DE summary, Methodik: Delta W = (A_loc^T A_loc + lambda I)^-1
+    A_loc^T (A_full - A_loc) W.  The factor A_loc^T (A_full - A_loc) does
+    not involve W, so it can be summed over the warmup rows on its own and
+    multiplied by W once at the switch; the same holds for the residual
+    energy, ||(A_full - A_loc) W||_F^2 = <dA^T dA, W W^T>.  With rows a_i of
+    A_loc and d_i of A_full - A_loc:
+        G = sum_i a_i a_i^T = A_loc^T A_loc      (D x D)
+        M = sum_i a_i d_i^T = A_loc^T dA         (D x D)
+        H = sum_i d_i d_i^T = dA^T dA            (D x D)
+    Sums over rows; the warmup total is the sum of the per-step
+    contributions.  Returns (G, M, H)."""
+    a, dl = as_f64(a_loc), as_f64(delta_a)
+    return a.T @ a, a.T @ dl, dl.T @ dl
+
+
+def stats_from_gram(G, M, H, w):
+    """The statistics the solve takes, from the grouped sums of
+    accumulate_gram: G unchanged, C = M W (= A_loc^T R) and
+    r2 = <H, W W^T> = trace(W^T H W) (= ||R||_F^2), with R = dA W the
+    residual target (EN review, Key Design 2).  Returns (G, C, r2)."""
+    G, M, H, w = as_f64(G), as_f64(M), as_f64(H), as_f64(w)
+    return G, M @ w, float(np.sum(H * (w @ w.T)))
 
 
 # ---------------------------------------------------------------------------

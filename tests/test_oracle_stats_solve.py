@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import scipy.linalg
 
-from oracle import (accumulate_stats, backward_substitution, cholesky_lower,
+from oracle import (accumulate_gram, accumulate_stats, backward_substitution, cholesky_lower, stats_from_gram,
                     epsilon_direct, epsilon_from_stats, forward_substitution,
                     residual_target, ridge_lambda, solve_dw)
 
@@ -47,6 +47,55 @@ def test_stats_additive_over_steps(rng):
     np.testing.assert_allclose(Gs, Ga, rtol=1e-13)
     np.testing.assert_allclose(Cs, Ca, rtol=1e-12, atol=1e-13)
     assert abs(rs - ra) < 1e-11 * ra
+
+
+def test_gram_brute_force(rng):
+    """The grouped sums as explicit outer products over rows (tiny shape,
+    non-square-symmetric data: a swapped operand or a transpose fails)."""
+    n, D = 5, 3
+    a, dl = rng.normal(size=(n, D)), rng.normal(size=(n, D))
+    G, M, H = accumulate_gram(a, dl)
+    for i in range(D):
+        for j in range(D):
+            assert abs(G[i, j] - sum(a[r][i] * a[r][j] for r in range(n))) < 1e-12
+            assert abs(M[i, j] - sum(a[r][i] * dl[r][j] for r in range(n))) < 1e-12
+            assert abs(H[i, j] - sum(dl[r][i] * dl[r][j] for r in range(n))) < 1e-12
+    assert abs(M[0, 1] - M[1, 0]) > 1e-3  # M is not symmetric on this data
+
+
+def test_gram_regrouping_equals_stats(rng):
+    """C = (A_loc^T dA) W and r2 = <dA^T dA, W W^T> equal A_loc^T (dA W) and
+    ||dA W||^2 (associativity; the printed closed form groups the product
+    this way), for a non-symmetric W and over several steps."""
+    D = 7
+    w = rng.normal(size=(D, D))
+    Gs, Ms, Hs = np.zeros((D, D)), np.zeros((D, D)), np.zeros((D, D))
+    Gr, Cr, rr = np.zeros((D, D)), np.zeros((D, D)), 0.0
+    for _ in range(3):
+        a, dl = rng.normal(size=(11, D)), rng.normal(size=(11, D))
+        G, M, H = accumulate_gram(a, dl)
+        Gs, Ms, Hs = Gs + G, Ms + M, Hs + H
+        g, c, r = accumulate_stats(a, dl, w)
+        Gr, Cr, rr = Gr + g, Cr + c, rr + r
+    G2, C2, r2 = stats_from_gram(Gs, Ms, Hs, w)
+    np.testing.assert_allclose(G2, Gr, rtol=1e-13)
+    np.testing.assert_allclose(C2, Cr, rtol=1e-11, atol=1e-12)
+    assert abs(r2 - rr) <= 1e-12 * rr
+    # the transposed products give different numbers on this data
+    assert abs(float(np.sum(Hs * (w.T @ w))) - rr) > 1e-6 * rr
+    assert np.abs(Ms.T @ w - Cr).max() > 1e-6
+
+
+def test_gram_invariants(rng):
+    a, dl = rng.normal(size=(40, 6)), rng.normal(size=(40, 6))
+    G, M, H = accumulate_gram(a, dl)
+    np.testing.assert_allclose(H, H.T, rtol=0, atol=0)
+    assert np.linalg.eigvalsh(H).min() > -1e-10
+    assert abs(np.trace(H) - np.sum(dl * dl)) < 1e-11
+    # no history: dA = 0 gives M = 0, H = 0, hence C = 0 and r2 = 0
+    _, M0, H0 = accumulate_gram(a, np.zeros_like(dl))
+    _, C0, r0 = stats_from_gram(G, M0, H0, rng.normal(size=(6, 6)))
+    assert not M0.any() and not H0.any() and not C0.any() and r0 == 0.0
 
 
 def _spd(rng, D, n=None):
