@@ -203,7 +203,7 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
             Ks = [round(x * N) for x in spec["xs"]]
             v0, v1 = ev(), ev()
             v0.record(stream)
-            eps_e, sels_e, _, _ = st.evaluate(Ks)
+            eps_e, sels_e, _, _, _ = st.evaluate(Ks)
             v1.record(stream)
             evaluations.append(dict(chunks=c + 1, eps=eps_e, sels=sels_e, ev=(v0, v1)))
         # keys each layer's call attends to (local + history during warmup)

@@ -318,8 +318,8 @@ class IspaStream:
         (a budget / warmup-length sweep: the pages' ablation axes x = K / N and
         the warmup length; EN review, Ablation Study).  The statistics are not
         modified; warmup may continue afterwards.  Returns (eps [N] fp64,
-        {K: selected int32 [K]}, {K: is_local uint8 [N]}) on the device, plus
-        the solve's info."""
+        {K: selected int32 [K]}, {K: is_local uint8 [N]}, info [N] int32,
+        dW [N, D, D] fp32), all on the device."""
         if self.switched or self.G is None:
             raise RuntimeError("evaluate runs during warmup")
         L, s, N, D, dev = self.L, self._stream(), self.N, self.D, self.device
@@ -341,7 +341,7 @@ class IspaStream:
             self._ck(L.ispa_select_layers(N, K, eps.data_ptr(), sel.data_ptr(), mask.data_ptr(),
                                           status.data_ptr(), s))
             sels[K], masks[K] = sel[:K], mask
-        return eps, sels, masks, info
+        return eps, sels, masks, info, dW
 
     def evict(self):
         """Free the history rows of every L-Layer; drop the statistics."""

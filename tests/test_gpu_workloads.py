@@ -84,42 +84,118 @@ def check_post_rows(st, layer, c, q, w):
     return segs[0][0].shape[0]
 
 
-def check_switch(st, K):
-    """Properties of the batched solve, eps and the selection on the GPU's
-    own statistics (fp64 arithmetic in torch, independent of libispa)."""
+def check_stream_output(st, layer, c, q, y):
+    """Sampled rows of the y that IspaStream.post returned for one layer
+    against the oracle's attention + projection over the keys that layer
+    holds, with the projection it must use: W + dW (its bf16 rounding, as
+    stored by the switch) for an L-Layer, W for an F-Layer.  Bar: the
+    attention's 5e-3 plus the bf16 rounding of y (2^-9 relative)."""
+    local = bool(st.is_local_host[layer])
+    w = st.w_eff[layer] if local else st.W[layer]
+    segs = st.kv[layer].attend_all(c)
+    ref = O.local_attn_proj(q[ROWS].cpu(), torch.cat([s_[0] for s_ in segs]).cpu(),
+                            torch.cat([s_[1] for s_ in segs]).cpu(), w.cpu(), st.scale)
+    e = rel(h64(y[ROWS]), ref)
+    assert e <= 5e-3 + 2.0 ** -9, (layer, c, e)
+    return e
+
+
+def selection_gap_rule(sel, eps_ref, K, band=1e-4):
+    """The selection bar on the oracle's eps: with e_(K), e_(K+1) the oracle's
+    sorted values, the GPU's set must equal the oracle's when their relative
+    gap exceeds ``band``; otherwise every layer outside the band around the
+    boundary must agree.  Returns the gap."""
+    N = len(eps_ref)
+    order = sorted(range(N), key=lambda i: (eps_ref[i], i))
+    if K in (0, N):
+        assert set(sel) == set(order[:K])
+        return float("inf")
+    lo, hi = eps_ref[order[K - 1]], eps_ref[order[K]]
+    gap = (hi - lo) / hi if hi > 0 else 0.0
+    if gap > band:
+        assert set(sel) == set(order[:K]), (sorted(sel), sorted(order[:K]), gap)
+    else:
+        b = 0.5 * (lo + hi)
+        for i in range(N):
+            if eps_ref[i] < b * (1 - band):
+                assert i in sel, (i, eps_ref[i], b)
+            elif eps_ref[i] > b * (1 + band):
+                assert i not in sel, (i, eps_ref[i], b)
+    return gap
+
+
+def check_switch(st, K, n_oracle_solves=2, n_window=None):
+    """The batched solve, eps and the selection on the GPU's own statistics.
+
+    Against the oracle on identical inputs (the GPU's G, C and r2 copied to
+    the host): dW against an fp64 solve of the same symmetrised G and C
+    (LAPACK Cholesky, which the oracle's own solve is pinned to; the
+    oracle's hand-written solve_dw itself for the ``n_oracle_solves`` layers
+    nearest the selection boundary), rel-Frobenius <= 1e-3 (the north-star
+    bar; fp32 storage of the fp64 solution sits near 1e-7); eps against the
+    oracle's epsilon_from_stats at that fp64 solution, within 1e-6 of r2;
+    the selection against the oracle's eps by the gap rule.
+
+    ``n_window`` (None: every layer) limits the fp64 solves to the
+    ``n_window`` layers nearest the boundary in the GPU's eps order, every
+    layer within 2e-3 (relative) of the boundary, and the first and the last
+    layer.  Every other layer keeps its GPU eps in the selection check: it
+    lies more than 1e-3 from the boundary, far beyond the 1e-6 * r2 eps
+    error measured on the solved layers, so its side of the boundary is the
+    oracle's too.
+
+    Properties on the GPU side: 0 <= eps <= r2, the selection a stable sort
+    of its own eps, W + dW rounded once to bf16."""
+    import scipy.linalg
     N, D = st.N, st.D
     assert int(st.info.abs().max()) == 0
-    eps = st.eps.double()
-    worst = 0.0
+    eps_gpu = [float(x) for x in st.eps.cpu()]
+    r2s = [float(x) for x in st.r2.cpu()]
+    order_gpu = sorted(range(N), key=lambda i: (eps_gpu[i], i))
+    near = order_gpu[max(0, K - n_oracle_solves // 2):K + (n_oracle_solves + 1) // 2]
+    if n_window is None or not 0 < K < N:
+        solved = list(range(N))
+    else:  # the boundary layers, every layer within 2e-3 of the boundary, the first and the last
+        b = 0.5 * (eps_gpu[order_gpu[K - 1]] + eps_gpu[order_gpu[K]])
+        solved = set(order_gpu[max(0, K - n_window // 2):K + (n_window + 1) // 2]) | {0, N - 1}
+        solved = sorted(solved | {i for i in range(N) if abs(eps_gpu[i] - b) <= 2e-3 * b})
+    eps_ref, worst_dw, worst_eps = list(eps_gpu), 0.0, 0.0
+    for layer in solved:
+        Gu = np.triu(h64(st.G[layer]))
+        Gs = Gu + np.triu(Gu, 1).T  # the solve reads the upper triangle
+        C = h64(st.C[layer])
+        lam = O.ridge_lambda(Gs, 0.0, 1e-3)
+        if layer in near:
+            X, info = O.solve_dw(Gs, C, lam)
+            assert info == 0
+        else:
+            X = scipy.linalg.cho_solve(scipy.linalg.cho_factor(Gs + lam * np.eye(D), lower=True), C)
+        e_dw = rel(h64(st.dW[layer]), X)
+        assert e_dw <= 1e-3, (layer, e_dw)
+        worst_dw = max(worst_dw, e_dw)
+        e_ref = O.epsilon_from_stats(Gs, C, r2s[layer], X)
+        eps_ref[layer] = e_ref
+        assert abs(eps_gpu[layer] - e_ref) <= 1e-6 * r2s[layer], (layer, eps_gpu[layer], e_ref)
+        worst_eps = max(worst_eps, abs(eps_gpu[layer] - e_ref) / r2s[layer])
     for layer in range(N):
-        G = st.G[layer].double()
-        Gs = torch.triu(G) + torch.triu(G, 1).T  # the solve reads the upper triangle
-        C = st.C[layer].double()
-        dW = st.dW[layer].double()
-        r2 = float(st.r2[layer])
-        lam = 1e-3 * float(torch.trace(Gs)) / D
-        GdW = Gs @ dW
-        res = (GdW + lam * dW - C).norm() / C.norm()
-        # dW is the fp64 solution rounded to fp32: residual ~ cond * 2^-24
-        assert float(res) <= 1e-4, (layer, float(res))
-        worst = max(worst, float(res))
-        full = r2 - 2.0 * float((dW * C).sum()) + float((dW * GdW).sum())
-        e = float(eps[layer])
-        assert abs(e - full) <= 1e-6 * r2, (layer, e, full)
-        assert -1e-9 * r2 <= e <= r2
+        assert -1e-9 * r2s[layer] <= eps_gpu[layer] <= r2s[layer]
         w_eff_ref = (st.W[layer].float() + st.dW[layer]).to(torch.bfloat16)
         assert torch.equal(st.w_eff[layer], w_eff_ref)
-    e_host = [float(x) for x in eps.cpu()]
-    order = sorted(range(N), key=lambda i: (e_host[i], i))
-    assert st.selected[:K].cpu().tolist() == order[:K]
+    if len(solved) < N and 0 < K < N:
+        b = 0.5 * (eps_gpu[order_gpu[K - 1]] + eps_gpu[order_gpu[K]])
+        for layer in set(range(N)) - set(solved):
+            assert abs(eps_gpu[layer] - b) > 1e-3 * b, (layer, eps_gpu[layer], b)
+    sel = st.selected[:K].cpu().tolist()
+    assert sel == order_gpu[:K]
     mask = [0] * N
-    for i in order[:K]:
+    for i in order_gpu[:K]:
         mask[i] = 1
     assert st.is_local.cpu().tolist() == mask == st.is_local_host
-    srt = sorted(e_host)
-    gap = (srt[K] - srt[K - 1]) / srt[K]
-    print(f"eps/r2 range {min(e_host) / float(st.r2.max()):.3g}..{max(e_host) / float(st.r2.min()):.3g}, "
-          f"boundary gap {gap:.3g}, worst normal-equation residual {worst:.3g}", flush=True)
+    gap = selection_gap_rule(sel, eps_ref, K)
+    print(f"eps/r2 range {min(eps_gpu) / max(r2s):.3g}..{max(eps_gpu) / min(r2s):.3g}; oracle boundary gap "
+          f"{gap:.3g}; {len(solved)} fp64 solves: worst dW rel-Frobenius {worst_dw:.3g}, worst "
+          f"|eps - eps_oracle|/r2 {worst_eps:.3g}", flush=True)
+    return eps_ref
 
 
 def check_kv_accounting(st, c):
@@ -172,9 +248,10 @@ def test_wan13b_stream_30_layers():
             y = st.post(layer, c, q)
             assert bool(torch.isfinite(y).all())
             if c == chunks - 1 and layer in (l_layer, f_layer):
+                e = check_stream_output(st, layer, c, q, y)
                 n = check_post_rows(st, layer, c, q, si.w(layer))
-                print(f"post-switch rows: layer {layer} ({'L' if layer == l_layer else 'F'}), {n} keys",
-                      flush=True)
+                print(f"post-switch rows: layer {layer} ({'L' if layer == l_layer else 'F'}), {n} keys; "
+                      f"stream output rel-L2 {e:.3g}", flush=True)
     frac = check_kv_accounting(st, chunks - 1)
     print(f"KV held at chunk {chunks - 1}: {frac:.4f} of all-full", flush=True)
     assert abs(frac - 0.55) <= 1e-12
@@ -191,7 +268,7 @@ def test_wan14b_warmup_switch_then_post_stream():
         st.set_w(layer, si.w(layer))
     run_warmup(st, si, warm, probe_layer=N - 1, probe_chunk=warm - 1)
     st.switch(K, evict=False)
-    check_switch(st, K)
+    check_switch(st, K, n_oracle_solves=0, n_window=6)
     is_local, W, w_eff = list(st.is_local_host), st.W, st.w_eff
     del st
     torch.cuda.empty_cache()
@@ -212,9 +289,11 @@ def test_wan14b_warmup_switch_then_post_stream():
             y = st5.post(layer, c, q)
             if c in (1, chunks - 1) and layer in (l_layer, f_layer):
                 assert bool(torch.isfinite(y).all())
+                e = check_stream_output(st5, layer, c, q, y)
                 n = check_post_rows(st5, layer, c, q, W[layer])
                 print(f"post-switch rows: chunk {c} layer {layer} "
-                      f"({'L' if layer == l_layer else 'F'}), {n} keys", flush=True)
+                      f"({'L' if layer == l_layer else 'F'}), {n} keys; stream output rel-L2 {e:.3g}",
+                      flush=True)
     frac = check_kv_accounting(st5, chunks - 1)
     print(f"KV held at chunk {chunks - 1}: {frac:.4f} of all-full", flush=True)
     assert abs(frac - (1 - 0.5 * (1 - 2 / 40))) <= 1e-12
@@ -292,46 +371,117 @@ def test_recalibration_reenters_warmup():
     print(f"selections {first_sel} -> {sel2}; keys held at chunk 10: {held}", flush=True)
 
 
+def _gather_chunks(kv, ranges, Tc, i, H, d):
+    parts = [kv[r // Tc][i] for a, b in ranges for r in range(a, b, Tc)]
+    return torch.cat(parts) if parts else torch.zeros((0, H, d), dtype=torch.bfloat16)
+
+
 def test_budget_and_warmup_sweep():
-    """evaluate() during warmup (4 layers of 2 x 128 heads, 256-token chunks):
-    after 2 and after 4 warmup chunks, for K = 1..4, every selection is the
-    first K of a stable sort of that eps, the selections are nested in K, the
-    statistics are untouched (warmup goes on), and eps after the last warmup
-    chunk equals the switch's eps on the same statistics."""
+    """evaluate() during warmup (10 layers of 2 x 128 heads, 256-token
+    chunks), after 2, 3 and 4 warmup chunks (6, 9 and 12 frames; the pages'
+    default warmup is 12 frames) for the pages' budgets x = 0.3, 0.4, 0.5,
+    0.7 (K = 3, 4, 5, 7):
+
+    * on the GPU's own statistics (identical inputs): dW against the
+      oracle's solve_dw (rel-Frobenius <= 1e-3), eps against the oracle's
+      epsilon_from_stats (1e-6 of r2), every selection against the oracle's
+      eps by the gap rule;
+    * end to end from the seeded inputs: the oracle's own chain (its
+      dual-stream attention, statistics, solve and eps) against the GPU's,
+      with the bars derived in the test body, and the selections wherever
+      the oracle's boundary gap exceeds the eps bar;
+    * on the GPU side: each selection is the first K of a stable sort of its
+      eps, the selections are nested in K, the statistics are untouched
+      (warmup goes on), and eps after the last warmup chunk equals the
+      switch's eps on the same statistics."""
     from kv_cache_absorption_amd.stream import IspaStream
-    N, H, d, Tc = 4, 2, 128, 256
+    N, H, d, Tc = 10, 2, 128, 256
+    D = H * d
     si = synth.StreamInputs(N, H, d, Tc, torch.bfloat16, 31, DEV, workload=3)
     st = IspaStream(N, H, d, Tc, 4, DEV)
+    W = [si.w(layer) for layer in range(N)]
     for layer in range(N):
-        st.set_w(layer, si.w(layer))
-    Ks = [1, 2, 3, 4]
+        st.set_w(layer, W[layer])
+    xs = [0.3, 0.4, 0.5, 0.7]
+    Ks = [round(x * N) for x in xs]
+    kv = [[] for _ in range(N)]
+    Go = [np.zeros((D, D)) for _ in range(N)]
+    Co = [np.zeros((D, D)) for _ in range(N)]
+    ro = [0.0] * N
     evals = {}
     for c in range(4):
         for layer in range(N):
-            st.write_kv(layer, c, *si.kv(layer, c))
-            st.warmup(layer, c, si.q(layer, c))
-        if c in (1, 3):
-            G0 = st.G.clone()
-            eps, sels, masks, info = st.evaluate(Ks)
-            torch.cuda.synchronize()
-            assert int(info.abs().max()) == 0
-            assert torch.equal(st.G, G0)
-            e = [float(x) for x in eps.cpu()]
-            order = sorted(range(N), key=lambda i: (e[i], i))
-            prev = set()
-            for K in Ks:
-                got = sels[K].cpu().tolist()
-                assert got == order[:K]
-                assert prev <= set(got)
-                prev = set(got)
-                assert masks[K].cpu().tolist() == [1 if i in got else 0 for i in range(N)]
-            evals[c] = e
-    st.switch(2, evict=False)
+            k, v = si.kv(layer, c)
+            st.write_kv(layer, c, k, v)
+            q = si.q(layer, c)
+            st.warmup(layer, c, q)
+            # the oracle's chain on the same seeded chunk
+            kv[layer].append((k.cpu(), v.cpu()))
+            loc_r, hist_r = O.stream_groups(c, Tc)
+            ref = O.dual_stream_attention(q.cpu(), *(_gather_chunks(kv[layer], loc_r, Tc, i, H, d) for i in (0, 1)),
+                                          *(_gather_chunks(kv[layer], hist_r, Tc, i, H, d) for i in (0, 1)), st.scale)
+            g, cc, r = O.accumulate_stats(ref["a_loc"].reshape(Tc, D), ref["delta"].reshape(Tc, D), W[layer].cpu())
+            Go[layer] += g
+            Co[layer] += cc
+            ro[layer] += r
+        if c == 0:
+            continue
+        G0 = st.G.clone()
+        eps, sels, masks, info, dW = st.evaluate(Ks)
+        torch.cuda.synchronize()
+        assert int(info.abs().max()) == 0
+        assert torch.equal(st.G, G0)
+        e = [float(x) for x in eps.cpu()]
+        order = sorted(range(N), key=lambda i: (e[i], i))
+        prev = set()
+        for K in Ks:
+            got = sels[K].cpu().tolist()
+            assert got == order[:K]
+            assert prev <= set(got)
+            prev = set(got)
+            assert masks[K].cpu().tolist() == [1 if i in got else 0 for i in range(N)]
+        # identical inputs: the oracle's solve, eps and selection on the GPU's statistics
+        e_pc, e_oc, dev_dw, dev_eps = [], [], 0.0, 0.0
+        for layer in range(N):
+            Gu = np.triu(h64(st.G[layer]))
+            Gs = Gu + np.triu(Gu, 1).T
+            Cg, r2g = h64(st.C[layer]), float(st.r2[layer])
+            X, inf = O.solve_dw(Gs, Cg, O.ridge_lambda(Gs, 0.0, 1e-3))
+            assert inf == 0 and rel(h64(dW[layer]), X) <= 1e-3
+            e_pc.append(O.epsilon_from_stats(Gs, Cg, r2g, X))
+            assert abs(e[layer] - e_pc[-1]) <= 1e-6 * max(r2g, 1e-300)
+            # end to end: the oracle's chain from the seeded inputs
+            Xo, inf = O.solve_dw(Go[layer], Co[layer], O.ridge_lambda(Go[layer], 0.0, 1e-3))
+            assert inf == 0
+            e_oc.append(O.epsilon_from_stats(Go[layer], Co[layer], ro[layer], Xo))
+            if ro[layer] > 0:
+                dev_dw = max(dev_dw, rel(h64(dW[layer]), Xo))
+                dev_eps = max(dev_eps, abs(e[layer] - e_oc[-1]) / e_oc[-1])
+            else:  # no history yet: R = 0 on both sides, so dW = 0 and eps = 0 exactly
+                assert not h64(dW[layer]).any() and e[layer] == 0.0 and e_oc[-1] == 0.0
+        gaps = [selection_gap_rule(sels[K].cpu().tolist(), e_pc, K) for K in Ks]
+        # End-to-end bars.  The GPU chain rounds P to bf16 in P V and hands
+        # A_loc, dA, R and W to the statistics as fp16: each activation
+        # carries a relative error of a few 1e-3 (the attention bar is
+        # 5e-3).  eps is the residual of the ridge fit, so
+        # d eps ~ 2 <A dW - R, dA dW - dR>, i.e. |d eps| / eps up to
+        # 2 delta sqrt(r2 / eps); with eps / r2 near 0.1 here that is ~6 delta:
+        # bar 3e-2.  dW = (G + lambda I)^-1 C inherits delta times the
+        # conditioning of the fit: bar 2e-2.
+        assert dev_eps <= 3e-2 and dev_dw <= 2e-2, (dev_eps, dev_dw)
+        for K in Ks:
+            if 0 < K < N:
+                so = sorted(e_oc)
+                if so[K] > 0 and (so[K] - so[K - 1]) / so[K] > 2 * 3e-2:
+                    assert set(sels[K].cpu().tolist()) == set(sorted(range(N), key=lambda i: (e_oc[i], i))[:K])
+        evals[c] = e
+        print(f"after {c + 1} chunks: eps {['%.4g' % x for x in e]}; oracle gaps at K={Ks}: "
+              f"{['%.3g' % gp for gp in gaps]}; end-to-end deviation eps {dev_eps:.3g}, dW {dev_dw:.3g}",
+              flush=True)
+    st.switch(Ks[2], evict=False)
     e_sw = [float(x) for x in st.eps.cpu()]
     for a, b in zip(evals[3], e_sw):
         assert abs(a - b) <= 1e-12 * max(abs(b), 1.0)
-    print(f"eps after 2 chunks {['%.4g' % x for x in evals[1]]}, after 4 {['%.4g' % x for x in evals[3]]}",
-          flush=True)
 
 
 def test_stream_w8a8_projection():
@@ -341,6 +491,7 @@ def test_stream_w8a8_projection():
     W8A8 projection with its seeded W (bar 4e-2, derived in the parity tests
     from code flips caused by the bf16 attention's error), and every output
     finite."""
+    import kv_cache_absorption_amd as KA
     from kv_cache_absorption_amd.stream import IspaStream
     N, H, d, K, warm, chunks = 4, 12, 128, 2, 3, 5
     print(f"W8A8 stream: {N} layers, warmup {warm}, K={K}, {chunks} chunks", flush=True)
@@ -370,5 +521,83 @@ def test_stream_w8a8_projection():
                 vv = torch.cat([s[1] for s in segs]).cpu()
                 ref = O.local_attn_proj_w8a8(q[ROWS].cpu(), kk, vv, si.w(layer).cpu(), st.scale)
                 e = rel(h64(y[ROWS]), ref)
-                print(f"F-Layer {layer} chunk {c}: {kk.shape[0]} keys, rel-L2 vs oracle W8A8 {e:.3e}", flush=True)
+                # the W8A8 stage at the matrix core's accuracy: the same call's
+                # attention output through ispa_w8a8_linear gives y bit for bit,
+                # and the oracle's w8a8_linear of those fp32 activations with
+                # the stream's codes matches it (bf16 y: 2^-9 more)
+                y_rows = y[ROWS].clone()
+                o_gpu = KA.ispa_dual_attn(q, segs, [], st.scale)[0].reshape(T, -1)
+                y_comp = KA.ispa_w8a8_linear(o_gpu, st.wq[layer], st.wq_scale[layer], out_dtype=torch.bfloat16)
+                assert torch.equal(y_rows, y_comp[ROWS])
+                ref_g = O.w8a8_linear(o_gpu[ROWS].cpu(), st.wq[layer].cpu().numpy(), st.wq_scale[layer].cpu().numpy())
+                eg = rel(h64(y_rows), ref_g)
+                print(f"F-Layer {layer} chunk {c}: {kk.shape[0]} keys, rel-L2 vs the oracle's W8A8 chain {e:.3e}, "
+                      f"vs its W8A8 product of the GPU attention output {eg:.3e}", flush=True)
+                assert eg <= 1e-4 + 2.0 ** -9
                 assert e <= 4e-2
+
+
+@pytest.mark.parametrize("H,T_,chunks", [
+    (12, 1024, 5),   # Wan-1.3B width (D = 1536), 1024-token chunks, 5120 warmup rows
+    (40, 1024, 6),   # Wan-14B width (D = 5120), 6144 warmup rows
+])
+def test_end_to_end_dw_deviation(H, T_, chunks):
+    """The warmup -> switch chain from seeded inputs on both sides, at the
+    Wan widths with shorter chunks (1024 tokens instead of 4680, so that the
+    fp64 oracle finishes in seconds): the stream's warmup calls (bf16
+    attention, fp16 statistics operands) and solve on the GPU; the oracle's
+    dual-stream attention, statistics, solve and eps on the host from the
+    same Q, K, V and W (at D = 5120 the ridge solve is LAPACK's fp64
+    Cholesky, to which the oracle's solve is pinned).  This is the deviation
+    of the whole chain, which the per-call bars do not cover; bars:
+
+    * dW: the chain rounds P to bf16 in P V (attention rel-L2 ~2e-3) and
+      hands the statistics 16-bit activations; dW = (G + lambda I)^-1 C
+      carries that error times the fit's conditioning.  A scaled-down numpy
+      probe of this rounding gave 5e-4 (bf16 P) and 2e-4 (fp16 operands) at
+      a conditioning of ~300; these fits sit at 1e3-1e4 (printed), where the
+      GPU measured 2.7e-3 at D = 1536.  Bar 1e-2.
+    * eps: eps is stationary at the ridge optimum up to the penalty, so the
+      dW error enters at second order and the activation errors at first
+      order through r2 and <dW, C>: measured below 1e-5; bar 1e-3.
+    The measured deviations are printed."""
+    import scipy.linalg
+    from kv_cache_absorption_amd.stream import IspaStream
+    d = 128
+    D = H * d
+    print(f"end-to-end chain: H={H} (D={D}), {chunks} warmup chunks of {T_} tokens", flush=True)
+    si = synth.StreamInputs(1, H, d, T_, torch.bfloat16, 41 + H, DEV, workload=3)
+    st = IspaStream(1, H, d, T_, chunks, DEV)
+    w = si.w(0)
+    st.set_w(0, w)
+    Go, Co, ro = np.zeros((D, D)), np.zeros((D, D)), 0.0
+    kv = []
+    for c in range(chunks):
+        k, v = si.kv(0, c)
+        st.write_kv(0, c, k, v)
+        q = si.q(0, c)
+        st.warmup(0, c, q)
+        kv.append((k.cpu(), v.cpu()))
+        loc_r, hist_r = O.stream_groups(c, T_)
+        ref = O.dual_stream_attention(q.cpu(), *(_gather_chunks(kv, loc_r, T_, i, H, d) for i in (0, 1)),
+                                      *(_gather_chunks(kv, hist_r, T_, i, H, d) for i in (0, 1)), st.scale)
+        g, cc, r = O.accumulate_stats(ref["a_loc"].reshape(T_, D), ref["delta"].reshape(T_, D), w.cpu())
+        Go, Co, ro = Go + g, Co + cc, ro + r
+    st.switch(1, evict=False)
+    lam = O.ridge_lambda(Go, 0.0, 1e-3)
+    if D <= 2048:
+        Xo, info = O.solve_dw(Go, Co, lam)
+        assert info == 0
+    else:
+        Xo = scipy.linalg.cho_solve(scipy.linalg.cho_factor(Go + lam * np.eye(D), lower=True), Co)
+    eo = O.epsilon_from_stats(Go, Co, ro, Xo)
+    dev_dw = rel(h64(st.dW[0]), Xo)
+    dev_eps = abs(float(st.eps[0]) - eo) / eo
+    dev_r2 = abs(float(st.r2[0]) - ro) / ro
+    Gu = np.triu(h64(st.G[0]))
+    dev_g = rel(Gu + np.triu(Gu, 1).T, Go)
+    ev = np.linalg.eigvalsh(Go)
+    print(f"D={D}: end-to-end deviation dW {dev_dw:.3g}, eps {dev_eps:.3g} (eps/r2 {eo / ro:.3g}), r2 {dev_r2:.3g}, "
+          f"G {dev_g:.3g}; cond(G + lambda I) {(ev[-1] + lam) / (ev[0] + lam):.3g}", flush=True)
+    assert dev_dw <= 1e-2
+    assert dev_eps <= 1e-3
