@@ -31,7 +31,9 @@
  *    of at least the size returned by the matching *_workspace_bytes query
  *    with the same shape arguments, aligned to 256 bytes.  Calls sharing a
  *    workspace must not overlap in time.
- *  - Stateless and thread-safe: no global flags, no hidden caches.
+ *  - Stateless and thread-safe: no global flags, no hidden caches.  The one
+ *    exception is ispa_w8a8_linear_noalloc, which keeps a fixed scratch
+ *    array per device (see there).
  */
 #ifndef ISPA_H
 #define ISPA_H
@@ -273,6 +275,27 @@ ispa_status ispa_w8a8_linear(ispa_dtype x_dt, int64_t n, int32_t d_in, int32_t d
                              const void* x, int64_t ld_x, const uint8_t* w_codes,
                              const float* w_scales, void* y, ispa_dtype y_dt,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ispa_w8a8_linear_noalloc -- ispa_w8a8_linear for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * layouts, results and kernels as ispa_w8a8_linear, without (ws, ws_bytes):
+ * the activation codes and row scales go to a fixed scratch array of
+ * ISPA_NOALLOC_SCRATCH_BYTES in the library, one per device, held until the
+ * process ends.  Its device address is looked up on the first call on each
+ * device.  Limit: ispa_w8a8_linear_workspace_bytes(n, d_in) must not exceed
+ * ISPA_NOALLOC_SCRATCH_BYTES (n <= 6548 rows at d_in = 5120); larger
+ * calls return ISPA_ERR_INVALID_ARG before anything is launched.  The call
+ * allocates nothing.  Every call on one device shares that device's
+ * scratch: calls that overlap in time on one device (different streams or
+ * threads without ordering) race and give wrong results; calls ordered on
+ * one stream are safe.
+ */
+#define ISPA_NOALLOC_SCRATCH_BYTES (32u << 20)
+ispa_status ispa_w8a8_linear_noalloc(ispa_dtype x_dt, int64_t n, int32_t d_in, int32_t d_out, const void* x,
+                                     int64_t ld_x, const uint8_t* w_codes, const float* w_scales, void* y,
+                                     ispa_dtype y_dt, hipStream_t stream);
 
 /*
  * ispa_local_attn_proj_fp8 -- ispa_local_attn_proj with the W8A8 projection:

@@ -7,5 +7,5 @@ library with ``python -m kv_cache_absorption_amd.build``.
 from ._lib import (ISPA_BF16, ISPA_F16, ISPA_F32, IspaError, ispa_accum_stats,  # noqa: F401
                    ispa_dual_attn, ispa_dual_attn_merge, ispa_local_attn_proj,
                    ispa_local_attn_proj_fp8, ispa_lse_merge, ispa_quantize_w_fp8, ispa_select_layers,
-                   ispa_solve_dw, ispa_w8a8_linear, lib)
+                   ispa_solve_dw, ispa_w8a8_linear, ispa_w8a8_linear_noalloc, lib)
 from .stream import Workspace, chunk_segments, kv_bytes  # noqa: F401

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libispa.so")
 ISPA_OK, ISPA_ERR_INVALID_ARG, ISPA_ERR_UNSUPPORTED, ISPA_ERR_WORKSPACE, ISPA_ERR_HIP = range(5)
 ISPA_F32, ISPA_BF16, ISPA_F16 = 0, 1, 2
 ISPA_MAX_SEGS = 8
+ISPA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = [
     "ispa_version", "ispa_status_str", "ispa_last_error",
@@ -31,7 +32,7 @@ EXPORTED = [
     "ispa_select_layers",
     "ispa_local_attn_proj_workspace_bytes", "ispa_local_attn_proj",
     "ispa_quantize_w_fp8_workspace_bytes", "ispa_quantize_w_fp8",
-    "ispa_w8a8_linear_workspace_bytes", "ispa_w8a8_linear",
+    "ispa_w8a8_linear_workspace_bytes", "ispa_w8a8_linear", "ispa_w8a8_linear_noalloc",
     "ispa_local_attn_proj_fp8_workspace_bytes", "ispa_local_attn_proj_fp8",
 ]
 
@@ -88,6 +89,7 @@ def lib() -> ctypes.CDLL:
             "ispa_quantize_w_fp8": (i32, [i32, i32, i32, vp, vp, vp, vp, sz, vp]),
             "ispa_w8a8_linear_workspace_bytes": (sz, [i64, i32]),
             "ispa_w8a8_linear": (i32, [i32, i64, i32, i32, vp, i64, vp, vp, vp, i32, vp, sz, vp]),
+            "ispa_w8a8_linear_noalloc": (i32, [i32, i64, i32, i32, vp, i64, vp, vp, vp, i32, vp]),
             "ispa_local_attn_proj_fp8_workspace_bytes": (sz, [i64, i32, i32, segp, i32]),
             "ispa_local_attn_proj_fp8": (i32, [i64, i32, i32, f32, vp, i64, segp, i32, vp, vp, vp, i32,
                                                vp, sz, vp]),
@@ -326,6 +328,24 @@ def ispa_w8a8_linear(x, w_codes, w_scales, out_dtype=torch.bfloat16):
     _check(L.ispa_w8a8_linear(_DT[x.dtype], n, d_in, d_out, x.data_ptr(), x.stride(0),
                               w_codes.data_ptr(), w_scales.data_ptr(), y.data_ptr(), _DT[out_dtype],
                               _ptr(ws), wsb, _stream(dev)))
+    return y
+
+
+def ispa_w8a8_linear_noalloc(x, w_codes, w_scales, y):
+    """ispa_w8a8_linear into a caller-allocated y [n, d_out] (bf16, f16 or
+    fp32), with the library's fixed per-device scratch instead of a
+    workspace: the call allocates nothing on the device."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [n, d_in] with contiguous rows")
+    n, d_in = x.shape
+    d_out = w_codes.shape[0]
+    if not w_codes.is_contiguous() or not w_scales.is_contiguous() or w_codes.shape[1] != d_in:
+        raise ValueError("w_codes [d_out, d_in] and w_scales [d_out] must be contiguous")
+    if not y.is_contiguous() or tuple(y.shape) != (n, d_out):
+        raise ValueError("y must be a contiguous [n, d_out] tensor")
+    _check(lib().ispa_w8a8_linear_noalloc(_DT[x.dtype], n, d_in, d_out, x.data_ptr(), x.stride(0),
+                                          w_codes.data_ptr(), w_scales.data_ptr(), y.data_ptr(),
+                                          _DT[y.dtype], _stream(x.device)))
     return y
 
 

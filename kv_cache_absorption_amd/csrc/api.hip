@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "attn.hpp"
@@ -69,6 +70,39 @@ ispa_status check_attn_common(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, 
   return ISPA_OK;
 }
 
+
+}  // namespace
+
+// ---------------------------------------------------------------- W8A8 product without allocation
+// Scratch for ispa_w8a8_linear_noalloc: the activation codes and row scales
+// of one call, in a fixed device array instead of a caller workspace.  Host
+// code never uses the array's name as an address: the per-device address
+// comes from hipGetSymbolAddress on the first call on that device.
+static __device__ __align__(256) unsigned char scratch[ISPA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of this device's copy of `scratch` (looked up once per device).
+ispa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ISPA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(ISPA_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ISPA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ISPA_OK;
+}
 
 }  // namespace
 }  // namespace ispa
@@ -516,6 +550,29 @@ ispa_status ispa_w8a8_linear(ispa_dtype x_dt, int64_t n, int32_t d_in, int32_t d
   const size_t need = ispa_w8a8_linear_workspace_bytes(n, d_in);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(ISPA_ERR_WORKSPACE, "w8a8_linear workspace too small or misaligned");
+  uint8_t* xq = (uint8_t*)ws;
+  float* sx = (float*)((char*)ws + align256((size_t)n * d_in));
+  if ((st = launch_quant_rows_e4m3(x, x_dt, ld_x, n, d_in, xq, d_in, sx, stream))) return st;
+  return run_w8a8_gemm(n, d_in, d_out, xq, sx, w_codes, w_scales, y, y_dt, stream);
+}
+
+ispa_status ispa_w8a8_linear_noalloc(ispa_dtype x_dt, int64_t n, int32_t d_in, int32_t d_out, const void* x,
+                                     int64_t ld_x, const uint8_t* w_codes, const float* w_scales, void* y,
+                                     ispa_dtype y_dt, hipStream_t stream) {
+  if (!valid_dtype(x_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad x_dt");
+  if (n < 0) return fail(ISPA_ERR_INVALID_ARG, "n must be >= 0");
+  ispa_status st = check_w8a8(d_in, d_out, w_codes, w_scales, y, y_dt, n > 0);
+  if (st) return st;
+  if (ld_x < d_in || ld_x % 4) return fail(ISPA_ERR_INVALID_ARG, "ld_x must be >= d_in and a multiple of 4");
+  if (n > 0 && !x) return fail(ISPA_ERR_INVALID_ARG, "null x");
+  if (!aligned(x, x_dt == ISPA_F32 ? 16 : 8)) return fail(ISPA_ERR_INVALID_ARG, "misaligned x");
+  if (n == 0) return ISPA_OK;
+  if (ispa_w8a8_linear_workspace_bytes(n, d_in) > (size_t)ISPA_NOALLOC_SCRATCH_BYTES)
+    return fail(ISPA_ERR_INVALID_ARG, "n * d_in + 4 n (each rounded up to 256) exceeds the fixed scratch of "
+                                      "ISPA_NOALLOC_SCRATCH_BYTES");
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  // the quantiser writes every code and scale the product reads: nothing to clear
   uint8_t* xq = (uint8_t*)ws;
   float* sx = (float*)((char*)ws + align256((size_t)n * d_in));
   if ((st = launch_quant_rows_e4m3(x, x_dt, ld_x, n, d_in, xq, d_in, sx, stream))) return st;

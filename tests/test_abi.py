@@ -194,3 +194,30 @@ def test_w8a8_calls_reject_bad_args():
                                       big, None) == m.ISPA_ERR_INVALID_ARG
     assert L.ispa_local_attn_proj_fp8(4, 2, 128, 0.1, F, 256, segs, 1, F, F, F, m.ISPA_BF16, F, 10,
                                       None) == m.ISPA_ERR_WORKSPACE
+
+
+def test_w8a8_noalloc_rejects_bad_args():
+    """The allocation-free W8A8 product validates on the host: a scratch need
+    above the fixed array is an argument error returned before any device
+    work, as are the usual shape, alignment and pointer errors."""
+    m, L = _lib()
+    lim = m.ISPA_NOALLOC_SCRATCH_BYTES
+
+    def call(n=64, d_in=1536, d_out=1536, x=FAKE, ld=1536, wc=FAKE, ws=FAKE, y=FAKE, xdt=m.ISPA_F32,
+             ydt=m.ISPA_BF16):
+        return L.ispa_w8a8_linear_noalloc(xdt, n, d_in, d_out, x, ld, wc, ws, y, ydt, None)
+
+    def need(n, d_in):
+        return L.ispa_w8a8_linear_workspace_bytes(n, d_in)
+
+    assert call(n=0) == m.ISPA_OK                        # nothing to do
+    assert need(6548, 5120) <= lim < need(6549, 5120)      # the documented limit
+    assert call(n=6560, d_in=5120, d_out=5120, ld=5120) == m.ISPA_ERR_INVALID_ARG
+    assert b"scratch" in L.ispa_last_error()
+    assert call(n=-1) == m.ISPA_ERR_INVALID_ARG
+    assert call(d_in=100, ld=100) == m.ISPA_ERR_INVALID_ARG  # not a multiple of 64
+    assert call(ld=1000) == m.ISPA_ERR_INVALID_ARG
+    assert call(x=None) == m.ISPA_ERR_INVALID_ARG
+    assert call(wc=None) == m.ISPA_ERR_INVALID_ARG
+    assert call(y=FAKE + 4) == m.ISPA_ERR_INVALID_ARG      # bf16 y must be 8-byte aligned
+    assert call(xdt=7) == m.ISPA_ERR_UNSUPPORTED
