@@ -6,17 +6,19 @@ One step is one full cycle of the Wan-1.3B-shaped single-layer workload
 28080-key history, fresh current chunk each step):
 
   8 warmup chunk steps, each ispa_dual_attn_merge (dual-stream attention and
-    the LSE merge into A_loc, A_full - A_loc) -> ispa_accum_stats
-  the switch: ispa_solve_dw (dW, eps, W + dW) -> ispa_select_layers (K = 1 of 1)
+    the LSE merge into A_loc, A_full - A_loc) -> ispa_accum_gram (one rank-k
+    update of [A_loc | A_full - A_loc] into the layer's statistics state)
+  the switch: ispa_gram_finalize (G, C = M W, r2) -> ispa_solve_dw (dW, eps,
+    W + dW) -> ispa_select_layers (K = 1 of 1)
   one post-switch chunk of the (local) layer: ispa_local_attn_proj with W + dW
 
 All inputs are generated on the GPU before the timed region.  Prints one JSON
 line; the headline value is dual-stream attention + LSE merge TFLOP/s (QK^T
 and PV flops, 4 n_q n_k D per chunk, over the time of the fused call), with
 Gram-statistics TFLOP/s and ms per warmup chunk beside it.  The same chunks
-through the two separate calls (ispa_dual_attn, then ispa_lse_merge) are
-timed after the timed steps and reported beside it; the roofline entry is the
-ispa_dual_attn call.
+through the two separate calls (ispa_dual_attn, then ispa_lse_merge), and
+through ispa_accum_stats (G, C and r2 every chunk), are timed after the timed
+steps and reported beside it; the roofline entry is the ispa_dual_attn call.
 
 Other workloads (``--workload``), each one pass of a chunked stream through
 IspaStream, timed per chunk with HIP events around the ISPA calls of all
@@ -246,6 +248,9 @@ def _preload_kernels(dev):
     C = torch.zeros_like(G)
     r2 = torch.zeros(1, dtype=torch.float64, device=dev)
     K.ispa_accum_stats(a_loc, delta, w, G, C, r2)
+    state = K.gram_state(H * d, device=dev)
+    K.ispa_accum_gram(a_loc, delta, state)
+    K.ispa_gram_finalize(state, w)
     G += torch.eye(H * d, device=dev)
     _, eps, _, _ = K.ispa_solve_dw(G, C, r2, 0.0, 1e-3, w=w)
     K.ispa_select_layers(eps, 1)
@@ -292,7 +297,7 @@ def run_stream(args, name, dev):
         for nk in r["n_keys"]:
             attn_flops += 4.0 * T * nk * D
         if r["warm"]:
-            stats_flops += N * (5.0 * T * D * D + 3.0 * T * D)
+            stats_flops += N * (4.0 * T * D * D + 2.0 * T * D)
         else:
             proj_flops += N * 2.0 * T * D * D
     pass_ms = sum(r["ms"] for r in recs)
@@ -339,7 +344,7 @@ def run_stream(args, name, dev):
         "data": "synthetic",
         "config": {"workload": name, "layers": N, "heads": H, "head_dim": d, "tokens_per_chunk": T,
                    "chunks": spec["chunks"], "warmup_chunks": spec["warm"], "K": spec["K"],
-                   "stats_operands": "fp16", "seed": args.seed,
+                   "stats_operands": "fp16", "statistics": "grouped (accum_gram)", "seed": args.seed,
                    "timing": "HIP events around each chunk's ISPA calls of all layers; the chunk's "
                              "synthetic Q/K/V generation sits outside them (ms_per_step is the wall "
                              "time of the whole pass including that generation)"},
@@ -473,6 +478,7 @@ def main():
     G = torch.zeros((D, D), **f32)
     C = torch.zeros((D, D), **f32)
     r2 = torch.zeros(1, dtype=torch.float64, device=dev)
+    state = K.gram_state(D, device=dev)
     dW = torch.empty((D, D), **f32)
     eps = torch.empty(1, dtype=torch.float64, device=dev)
     info = torch.empty(1, dtype=torch.int32, device=dev)
@@ -494,7 +500,7 @@ def main():
                                                      seg_tables[0][3], 1),
                     L.ispa_dual_attn_merge_workspace_bytes(B.ISPA_BF16, n_q, H, d, seg_tables[0][1], 2,
                                                            seg_tables[0][3], 1))
-    ws_stats_b = L.ispa_accum_stats_workspace_bytes(B.ISPA_F16, n_q, D)
+    ws_stats_b = max(L.ispa_accum_stats_workspace_bytes(B.ISPA_F16, n_q, D), L.ispa_gram_finalize_workspace_bytes(D))
     ws_solve_b = L.ispa_solve_dw_workspace_bytes(1, D)
     post_segs, post_n = segs([(g.sink_k, g.sink_v), (k_post, v_post)])
     ws_post_b = L.ispa_local_attn_proj_workspace_bytes(B.ISPA_BF16, n_q, H, d, post_segs, post_n)
@@ -519,12 +525,10 @@ def main():
             raise B.IspaError(st, L.ispa_last_error().decode())
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    rec = {"fused": [], "attn": [], "merge": [], "stats": [], "switch": [], "post": []}
+    rec = {"fused": [], "attn": [], "merge": [], "stats": [], "stats_direct": [], "switch": [], "post": []}
 
     def cycle(timed):
-        G.zero_()
-        C.zero_()
-        r2.zero_()
+        state.zero_()
         marks = []
         for (q, ls, nl, hs, nh) in seg_tables:
             e0, e1, e2 = ev(), ev(), ev()
@@ -532,12 +536,13 @@ def main():
             ck(L.ispa_dual_attn_merge(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs,
                                       nh, a_loc.data_ptr(), delta.data_ptr(), B.ISPA_F16, None, wsp, wsn, sh))
             e1.record(stream)
-            ck(L.ispa_accum_stats(B.ISPA_F16, B.ISPA_BF16, n_q, D, a_loc.data_ptr(), delta.data_ptr(),
-                                  g.w.data_ptr(), G.data_ptr(), C.data_ptr(), r2.data_ptr(), wsp, wsn, sh))
+            ck(L.ispa_accum_gram(B.ISPA_F16, n_q, D, a_loc.data_ptr(), delta.data_ptr(), state.data_ptr(), sh))
             e2.record(stream)
             marks.append((e0, e1, e2))
         s0, s1, s2 = ev(), ev(), ev()
         s0.record(stream)
+        ck(L.ispa_gram_finalize(1, D, state.data_ptr(), state.numel(), g.w.data_ptr(), B.ISPA_BF16, D * D,
+                                G.data_ptr(), C.data_ptr(), r2.data_ptr(), D * D, wsp, wsn, sh))
         ck(L.ispa_solve_dw(1, D, G.data_ptr(), C.data_ptr(), r2.data_ptr(), D * D, 0.0, 1e-3, dW.data_ptr(),
                            eps.data_ptr(), info.data_ptr(), g.w.data_ptr(), B.ISPA_BF16, w_eff.data_ptr(),
                            wsp, wsn, sh))
@@ -558,10 +563,14 @@ def main():
         cycle(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the same warmup chunks through the two separate calls (after the timed steps)
+    # the same warmup chunks through the two separate calls, and the statistics
+    # through ispa_accum_stats (after the timed steps)
     two_call = []
+    G2 = torch.zeros((D, D), **f32)
+    C2 = torch.zeros((D, D), **f32)
+    r22 = torch.zeros(1, dtype=torch.float64, device=dev)
     for (q, ls, nl, hs, nh) in seg_tables:
-        e0, e1, e2 = ev(), ev(), ev()
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record(stream)
         ck(L.ispa_dual_attn(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
                             o_loc.data_ptr(), lse_loc.data_ptr(), o_hist.data_ptr(), lse_hist.data_ptr(),
@@ -570,11 +579,15 @@ def main():
         ck(L.ispa_lse_merge(2, op, lp, n_q, H, d, None, None, a_loc.data_ptr(), delta.data_ptr(),
                             B.ISPA_F16, sh))
         e2.record(stream)
-        two_call.append((e0, e1, e2))
+        ck(L.ispa_accum_stats(B.ISPA_F16, B.ISPA_BF16, n_q, D, a_loc.data_ptr(), delta.data_ptr(),
+                              g.w.data_ptr(), G2.data_ptr(), C2.data_ptr(), r22.data_ptr(), wsp, wsn, sh))
+        e3.record(stream)
+        two_call.append((e0, e1, e2, e3))
     torch.cuda.synchronize()
-    for e0, e1, e2 in two_call:
+    for e0, e1, e2, e3 in two_call:
         rec["attn"].append(e0.elapsed_time(e1))
         rec["merge"].append(e1.elapsed_time(e2))
+        rec["stats_direct"].append(e2.elapsed_time(e3))
     for marks, (s0, s1, s2) in rec.pop("_pending", []):
         for e0, e1, e2 in marks:
             rec["fused"].append(e0.elapsed_time(e1))
@@ -586,12 +599,14 @@ def main():
 
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     attn_flops = 4.0 * n_q * (n_loc + n_hist) * D
-    stats_flops = 5.0 * n_q * D * D + 3.0 * n_q * D
+    stats_flops = 4.0 * n_q * D * D + 2.0 * n_q * D   # G and H as triangles, M = A_loc^T dA
+    direct_flops = 5.0 * n_q * D * D + 3.0 * n_q * D  # R = dA W, C = A_loc^T R, G as a triangle, ||R||^2
     merge_bytes = 2 * (4 * n_q * D + 4 * n_q * H) + 2 * 2 * n_q * D
     t_fused = mean(rec["fused"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
     t_merge = mean(rec["merge"]) * 1e-3
     t_stats = mean(rec["stats"]) * 1e-3
+    t_direct = mean(rec["stats_direct"]) * 1e-3
     value = attn_flops / t_fused / 1e12
     achieved = attn_flops / t_attn / 1e12
     traffic = _traffic("attn_bf16_wan13b_traffic.txt", "attn.hip")
@@ -615,15 +630,18 @@ def main():
                    "warmup_chunks": n_warm, "stats_operands": "fp16", "seed": args.seed},
         "also": {
             "Gram-stat TFLOP/s": round(stats_flops / t_stats / 1e12, 2),
+            "Gram-stat TFLOP/s counted as the direct form (5nD^2 + 3nD per chunk)": round(direct_flops / t_stats / 1e12, 2),
+            "accum_stats (direct form) call ms": round(t_direct * 1e3, 4),
+            "accum_stats (direct form) TFLOP/s": round(direct_flops / t_direct / 1e12, 2),
             "ms/chunk (1 GPU)": round((t_fused + t_stats) * 1e3, 4),
             "dual_attn_merge call ms": round(t_fused * 1e3, 4),
             "two-call path TFLOP/s (ispa_dual_attn + ispa_lse_merge)": round(attn_flops / (t_attn + t_merge) / 1e12, 2),
             "merge GB/s": round(merge_bytes / t_merge / 1e9, 1),
-            "switch ms (solve+select)": round(mean(rec["switch"]), 4),
+            "switch ms (finalize statistics + solve + select)": round(mean(rec["switch"]), 4),
             "post-switch chunk ms (local attn + W+dW)": round(mean(rec["post"]), 4),
             "dual_attn call ms": round(t_attn * 1e3, 4),
             "merge call ms": round(t_merge * 1e3, 4),
-            "stats call ms": round(t_stats * 1e3, 4),
+            "accum_gram call ms": round(t_stats * 1e3, 4),
             "eps": float(eps[0]),
         },
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -633,7 +651,7 @@ def main():
         "roofline_other": [
             {"kernel": "ispa_lse_merge", "bound": "hbm", "achieved": round(merge_bytes / t_merge / 1e9, 1),
              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_bytes / t_merge / 1e9 / PEAK_HBM_GBS, 4)},
-            {"kernel": "ispa_accum_stats", "bound": "mfma",
+            {"kernel": "ispa_accum_gram (flops performed: 4nD^2 + 2nD)", "bound": "mfma",
              "achieved": round(stats_flops / t_stats / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
              "frac": round(stats_flops / t_stats / 1e12 / PEAK_BF16_TFLOPS, 4)},
         ],

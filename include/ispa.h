@@ -176,6 +176,47 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Statistics in the grouping of the printed closed form (DE summary,
+ * Methodik: dW = (A_loc^T A_loc + lambda I)^-1 A_loc^T (A_full - A_loc) W;
+ * EN review, Key Design 2: the statistics are accumulated over the warmup
+ * forward passes).  The factor A_loc^T dA (dA = A_full - A_loc) does not
+ * involve W, and ||dA W||^2 = <dA^T dA, W W^T>, so each warmup chunk adds
+ * one symmetric rank-k update of X = [A_loc | dA]:
+ *   G += A_loc^T A_loc,  M += A_loc^T dA,  H += dA^T dA
+ * (4 n D^2 multiply-adds counted as flops, against 5 n D^2 for
+ * ispa_accum_stats, and no R = dA W), and the switch forms C = M W and
+ * r2 = <H, W W^T> once.  The accumulator is a per-layer state whose layout
+ * is private to the library: ispa_gram_state_bytes(D) bytes, 16-byte
+ * aligned, all-zero bytes meaning "no rows yet" (the caller zeroes it when
+ * a warmup starts).
+ *
+ * ispa_accum_gram -- one chunk's rows into the state.
+ *   a_dt     ISPA_F16 or ISPA_BF16 (the products run on MFMA in that type,
+ *            exact, with fp32 sums).
+ *   a_loc, delta_a  [n, D] row-major (D elements per row), 16-byte aligned.
+ *   D a positive multiple of 64; n >= 0 (n = 0 is a no-op).
+ * ispa_gram_finalize -- G, C and r2 of n_layers states (layer l at
+ *   state + l*state_stride floats, its W at w + l*w_stride elements, its G
+ *   and C at + l*mat_stride floats, its r2 at r2[l]), for ispa_solve_dw:
+ *   G   the upper triangle of sum A_loc^T A_loc (entries below the diagonal
+ *       are not touched), fp32 [D, D];
+ *   C   M W, fp32 [D, D] (M split into three bf16 planes, so the product
+ *       runs on the bf16 matrix core to fp32 accuracy);
+ *   r2  <H, W W^T> summed in fp64.
+ *   Written, not accumulated; the state is left as it was.  W: ISPA_BF16
+ *   [D, D] (y = a W).  Needs ispa_gram_finalize_workspace_bytes(D) of
+ *   workspace (reused layer by layer).
+ */
+size_t ispa_gram_state_bytes(int32_t D);
+ispa_status ispa_accum_gram(ispa_dtype a_dt, int64_t n, int32_t D, const void* a_loc, const void* delta_a,
+                            void* state, hipStream_t stream);
+size_t ispa_gram_finalize_workspace_bytes(int32_t D);
+ispa_status ispa_gram_finalize(int32_t n_layers, int32_t D, const void* state, int64_t state_stride,
+                               const void* w, ispa_dtype w_dt, int64_t w_stride, float* G, float* C,
+                               double* r2, int64_t mat_stride, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/*
  * ispa_solve_dw -- closed-form ridge absorption and reconstruction error,
  * batched over layers (DE summary, Methodik: Delta W minimises
  * ||A_loc (W + dW) - A_full W||^2 + lambda ||dW||^2, closed form

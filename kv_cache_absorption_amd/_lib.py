@@ -28,6 +28,7 @@ EXPORTED = [
     "ispa_dual_attn_merge_workspace_bytes", "ispa_dual_attn_merge",
     "ispa_lse_merge",
     "ispa_accum_stats_workspace_bytes", "ispa_accum_stats",
+    "ispa_gram_state_bytes", "ispa_accum_gram", "ispa_gram_finalize_workspace_bytes", "ispa_gram_finalize",
     "ispa_solve_dw_workspace_bytes", "ispa_solve_dw",
     "ispa_select_layers",
     "ispa_local_attn_proj_workspace_bytes", "ispa_local_attn_proj",
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
                                      vp, vp, vp, vp, i32, vp]),
             "ispa_accum_stats_workspace_bytes": (sz, [i32, i64, i32]),
             "ispa_accum_stats": (i32, [i32, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ispa_gram_state_bytes": (sz, [i32]),
+            "ispa_accum_gram": (i32, [i32, i64, i32, vp, vp, vp, vp]),
+            "ispa_gram_finalize_workspace_bytes": (sz, [i32]),
+            "ispa_gram_finalize": (i32, [i32, i32, vp, i64, vp, i32, i64, vp, vp, vp, i64, vp, sz, vp]),
             "ispa_solve_dw_workspace_bytes": (sz, [i32, i32]),
             "ispa_solve_dw": (i32, [i32, i32, vp, vp, vp, i64, f64, f64, vp, vp, vp, vp, i32, vp,
                                     vp, sz, vp]),
@@ -223,6 +228,54 @@ def ispa_accum_stats(a_loc, delta_a, w, G, C, r2):
     _check(L.ispa_accum_stats(adt, _DT[w.dtype], n, D, a_loc.data_ptr(), delta_a.data_ptr(),
                               w.data_ptr(), G.data_ptr(), C.data_ptr(), r2.data_ptr(), _ptr(ws), wsb,
                               _stream(dev)))
+
+
+def gram_state(D: int, n_layers: int | None = None, device="cuda"):
+    """A zeroed statistics state (fp32 words, opaque layout) for one layer, or
+    [n_layers, ...] for several."""
+    nb = lib().ispa_gram_state_bytes(D)
+    if nb == 0:
+        raise ValueError("D must be a positive multiple of 64")
+    shape = (nb // 4,) if n_layers is None else (n_layers, nb // 4)
+    return torch.zeros(shape, dtype=torch.float32, device=device)
+
+
+def ispa_accum_gram(a_loc, delta_a, state):
+    """In place: the layer's statistics state += this chunk's rows
+    (G += a^T a, M += a^T delta, H += delta^T delta)."""
+    n, D = a_loc.shape
+    for t in (a_loc, delta_a, state):
+        if not t.is_contiguous():
+            raise ValueError("accum_gram operands must be contiguous")
+    if delta_a.shape != a_loc.shape or delta_a.dtype != a_loc.dtype:
+        raise ValueError("a_loc and delta_a must match")
+    if state.dtype != torch.float32 or state.numel() * 4 < lib().ispa_gram_state_bytes(D):
+        raise ValueError("state too small (see gram_state)")
+    _check(lib().ispa_accum_gram(_DT[a_loc.dtype], n, D, a_loc.data_ptr(), delta_a.data_ptr(),
+                                 state.data_ptr(), _stream(a_loc.device)))
+
+
+def ispa_gram_finalize(state, w, G=None, C=None, r2=None):
+    """G (upper triangle), C = M W and r2 = <H, W W^T> of one state ([S]) and
+    W ([D, D]) or of a batch ([L, S] and [L, D, D]).  Returns (G, C, r2)."""
+    squeeze = state.dim() == 1
+    if squeeze:
+        state, w = state.unsqueeze(0), w.unsqueeze(0)
+    nl, D = w.shape[0], w.shape[1]
+    dev = w.device
+    if not state.is_contiguous() or not w.is_contiguous() or w.dtype != torch.bfloat16:
+        raise ValueError("state and w (bf16) must be contiguous")
+    G = torch.zeros((nl, D, D), dtype=torch.float32, device=dev) if G is None else G
+    C = torch.empty((nl, D, D), dtype=torch.float32, device=dev) if C is None else C
+    r2 = torch.empty(nl, dtype=torch.float64, device=dev) if r2 is None else r2
+    L = lib()
+    wsb = L.ispa_gram_finalize_workspace_bytes(D)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_gram_finalize(nl, D, state.data_ptr(), state.shape[1], w.data_ptr(), ISPA_BF16, D * D,
+                                G.data_ptr(), C.data_ptr(), r2.data_ptr(), D * D, _ptr(ws), wsb, _stream(dev)))
+    if squeeze:
+        return G[0], C[0], r2
+    return G, C, r2
 
 
 def ispa_solve_dw(G, C, r2, lambda_abs=0.0, lambda_rel=1e-3, w=None, w_eff_dtype=None):

@@ -325,6 +325,74 @@ ispa_status ispa_accum_stats(ispa_dtype a_dt, ispa_dtype w_dt, int64_t n, int32_
   return launch_nt_split_reduce(g, partials, nblk, r2, stream);
 }
 
+// ---------------------------------------------------------------- grouped statistics
+size_t ispa_gram_state_bytes(int32_t D) {
+  if (D <= 0 || D % 64) return 0;
+  return (size_t)gram_splits(D) * 3 * (size_t)D * D * 4;
+}
+
+ispa_status ispa_accum_gram(ispa_dtype a_dt, int64_t n, int32_t D, const void* a_loc, const void* delta_a,
+                            void* state, hipStream_t stream) {
+  if (a_dt != ISPA_BF16 && a_dt != ISPA_F16) return fail(ISPA_ERR_UNSUPPORTED, "activations must be BF16 or F16");
+  if (D <= 0 || D % 64) return fail(ISPA_ERR_INVALID_ARG, "D must be a positive multiple of 64");
+  if (n < 0) return fail(ISPA_ERR_INVALID_ARG, "n must be >= 0");
+  if (!state) return fail(ISPA_ERR_INVALID_ARG, "null state");
+  if (n > 0 && (!a_loc || !delta_a)) return fail(ISPA_ERR_INVALID_ARG, "null activations");
+  if (!aligned(a_loc, 16) || !aligned(delta_a, 16) || !aligned(state, 16))
+    return fail(ISPA_ERR_INVALID_ARG, "activations and state must be 16-byte aligned");
+  if (n == 0) return ISPA_OK;
+  const int S = gram_splits(D);
+  const int64_t stages = (n + 31) / 32;
+  const int64_t kchunk = (stages + S - 1) / S * 32;
+  if (kchunk * D * 2 >= ((int64_t)1 << 31))
+    return fail(ISPA_ERR_UNSUPPORTED, "too many token rows in one call for this width: split the call");
+  SyrkParams p{};
+  p.a = a_loc;
+  p.b = delta_a;
+  p.n = n;
+  p.lda = D;
+  p.D = D;
+  p.nbh = (D + 255) / 256;
+  p.n_tiles = p.nbh * (2 * p.nbh + 1);  // upper triangle of the 2 nbh x 2 nbh block grid
+  p.ksplit = S;
+  p.kchunk = kchunk;
+  p.state = (float*)state;
+  p.split_stride = 3 * (int64_t)D * D;
+  return launch_syrk(p, a_dt, stream);
+}
+
+size_t ispa_gram_finalize_workspace_bytes(int32_t D) {
+  if (D <= 0 || D % 64) return 0;
+  return gram_finalize_ws_bytes(D);
+}
+
+ispa_status ispa_gram_finalize(int32_t n_layers, int32_t D, const void* state, int64_t state_stride, const void* w,
+                               ispa_dtype w_dt, int64_t w_stride, float* G, float* C, double* r2,
+                               int64_t mat_stride, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n_layers < 1) return fail(ISPA_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (D <= 0 || D % 64) return fail(ISPA_ERR_INVALID_ARG, "D must be a positive multiple of 64");
+  if (w_dt != ISPA_BF16) return fail(ISPA_ERR_UNSUPPORTED, "W must be BF16");
+  if (!state || !w || !G || !C || !r2) return fail(ISPA_ERR_INVALID_ARG, "null pointer");
+  const int64_t dd = (int64_t)D * D;
+  const int64_t st_floats = (int64_t)(ispa_gram_state_bytes(D) / 4);
+  if (state_stride < st_floats || w_stride < dd || mat_stride < dd)
+    return fail(ISPA_ERR_INVALID_ARG, "state_stride, w_stride or mat_stride too small");
+  if (!aligned(state, 16) || !aligned(G, 16) || !aligned(C, 16) || !aligned(w, 16) || state_stride % 4 ||
+      w_stride % 8 || mat_stride % 4)
+    return fail(ISPA_ERR_INVALID_ARG, "state, W, G and C (and their layer strides) must be 16-byte aligned");
+  const size_t need = ispa_gram_finalize_workspace_bytes(D);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "gram_finalize workspace too small or misaligned");
+  const int S = gram_splits(D);
+  for (int l = 0; l < n_layers; ++l) {
+    const ispa_status st = launch_gram_finalize(D, (const float*)state + l * state_stride, 3 * dd, S,
+                                                (const uint16_t*)w + l * w_stride, G + l * mat_stride,
+                                                C + l * mat_stride, r2 + l, ws, stream);
+    if (st) return st;
+  }
+  return ISPA_OK;
+}
+
 // ---------------------------------------------------------------- solve_dw
 size_t ispa_solve_dw_workspace_bytes(int32_t n_layers, int32_t D) {
   if (n_layers <= 0 || D <= 0) return 0;

@@ -40,6 +40,8 @@ namespace ispa {
 namespace {
 
 constexpr int BM = kNtBM, BK = kNtBK;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define ISPA_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 constexpr int ROWB = BK * 2;              // bytes per tile row (64)
 constexpr int RPI = 1024 / ROWB;          // rows per 1 KB load instruction (16)
 
@@ -428,6 +430,306 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
   }
 }
 
+// ---- symmetric rank-k update of X = [A_loc | dA] (the grouped statistics) ----
+//
+// X^T X over a chunk's token rows, upper block triangle only, 256 x 256 tiles
+// of the 2 nbh x 2 nbh block grid (nbh = 256-column blocks per half): tile
+// (I, J), I <= J, is G = A_loc^T A_loc for I, J < nbh, M = A_loc^T dA for
+// I < nbh <= J and H = dA^T dA for nbh <= I.  The operands are read as the
+// merge left them, row-major [n, D] 16-bit with the token index as k:
+//   * a K stage is 32 token rows x 256 columns (512 contiguous bytes per row)
+//     of each operand, moved from global memory straight into an LDS ring by
+//     buffer loads with the LDS flag (16 bytes per lane), 3 stages ahead in
+//     5 slots of 32 KB; the 16-byte chunks of row r are XOR-permuted by
+//     4 (r mod 8) so the transposing fragment reads below spread over the banks;
+//   * fragments come from ds_read_b64_tr_b16: a 16-lane group reads 4 token
+//     rows x 16 columns and each lane receives one column's 4 tokens; two
+//     such reads (tokens +0..3 and +8..11 of a 16-token slice, per wave half
+//     +4) form the 8 k values of a v_mfma_f32_32x32x16 operand, in the same
+//     k order on both sides of the product;
+//   * 4 waves as 2 x 2, each 128 x 128 (16 accumulators of 32 x 32), with the
+//     operands swapped so a lane holds 4 consecutive output columns;
+//   * a diagonal tile (I == J) loads one operand and reads both fragments
+//     from it;
+//   * the token range is split S ways (S fixed by D so that the launch fills
+//     the chip); split s adds into its own copy of G, M and H in the per-layer
+//     state, so no partial sums travel and no reduction runs per chunk; the
+//     copies are added at the switch.  Token rows past n read as zero (buffer
+//     range), columns past D repeat the last valid chunk (their outputs are
+//     not stored).
+constexpr int SY_BM = 256, SY_BK = 32;
+constexpr int SY_ROWB = SY_BM * 2;         // bytes per LDS row of one operand
+constexpr int SY_OPB = SY_BK * SY_ROWB;    // 16 KB per operand and stage
+constexpr int SY_PD = 3, SY_NBUF = 5;      // stages in flight, ring slots
+static_assert(SY_NBUF * 2 * SY_OPB <= 160 * 1024, "LDS budget");
+
+template <int MT, bool DIAG>
+__device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm, int tn, int split) {
+  constexpr int LOADS = DIAG ? 4 : 8;  // 1 KB loads per wave and stage
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hh = lane >> 5, lq = lane & 31, g16 = lane >> 4, s16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nbh = p.nbh;
+  // operand halves and column offsets of the two blocks
+  const bool xb = tm >= nbh, yb = tn >= nbh;
+  const int64_t cx = (int64_t)(xb ? tm - nbh : tm) * SY_BM, cy = (int64_t)(yb ? tn - nbh : tn) * SY_BM;
+  const int64_t kb = (int64_t)split * p.kchunk;
+  const int64_t ke = min(p.n, kb + p.kchunk);
+  const int ns = ke > kb ? (int)((ke - kb + SY_BK - 1) / SY_BK) : 0;
+  const int64_t ldb = p.lda * 2;  // row pitch in bytes
+  // buffer descriptors over this split's rows of each block: rows past ke are
+  // out of range (read as zero)
+  auto rsrc = [&](bool half_b, int64_t col0) {
+    const char* base = (const char*)(half_b ? p.b : p.a) + kb * ldb + col0 * 2;
+    const int64_t rows = ke - kb;
+    const int64_t bytes = rows > 0 ? (rows - 1) * ldb + (p.D - col0) * 2 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t rx = rsrc(xb, cx), ry = rsrc(yb, cy);
+  // this lane's part of load instruction i (0..3) of its wave: LDS row
+  // 2 q + hh (q = 4 wave + i), physical chunk lq holding logical chunk lq ^ 4 (row mod 8)
+  int xo[4], yo[4];
+  {
+    const int lastx = (int)((p.D - cx) / 8) - 1, lasty = (int)((p.D - cy) / 8) - 1;  // last valid chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 2 * (wave * 4 + i) + hh;
+      const int lch = lq ^ ((row & 7) << 2);
+      xo[i] = row * (int)ldb + min(lch, lastx) * 16;
+      yo[i] = row * (int)ldb + min(lch, lasty) * 16;
+    }
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
+  // the stage's row offset goes into the per-lane offset (not the scalar
+  // one) so that the buffer range check sees it: rows past the split's end
+  // then read as zero
+  auto issue = [&](int s, int buf) {
+    const int so = (int)((int64_t)s * SY_BK * ldb);
+    const uint32_t xd = lds0 + buf * 2 * SY_OPB, yd = xd + SY_OPB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(rx, xd + (wave * 4 + i) * 1024, xo[i] + so, 0);
+    if constexpr (!DIAG) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_dma16(ry, yd + (wave * 4 + i) * 1024, yo[i] + so, 0);
+    }
+  };
+  // wait until at most `newer` stages of loads are outstanding (0 <= newer < SY_PD)
+  auto wait_stage = [&](int newer) {
+    constexpr int v1 = LOADS, v2 = 2 * LOADS;
+    if (newer <= 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (newer == 1)
+      __builtin_amdgcn_s_waitcnt((v1 & 15) | ((v1 >> 4) << 14) | 0x0F70);
+    else
+      __builtin_amdgcn_s_waitcnt((v2 & 15) | ((v2 >> 4) << 14) | 0x0F70);
+  };
+  // per-lane fragment offsets inside a stage: LDS row 4 hh + (s16 >> 2) (+8 for the
+  // second read, +16 per k slice), column block c0 + 32 b: chunk
+  // (c0 / 8 + 4 b) ^ 4 (row mod 8), plus (g16 & 1) * 2 + (s16 & 3) / 2 and a
+  // half-chunk (s16 & 1) * 8
+  int fx[4], fy[4];
+  {
+    const int r = 4 * hh + (s16 >> 2);
+    const int fl = r & 7;
+    const int low = ((g16 & 1) * 2 + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      fx[b] = r * SY_ROWB + ((((wm * 4 + b) ^ fl) << 2) << 4) + low;
+      fy[b] = r * SY_ROWB + ((((wn * 4 + b) ^ fl) << 2) << 4) + low;
+    }
+  }
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  auto read8 = [&](const char* base, int off) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, base + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS_PTR(s16x4, base + off + 8 * SY_ROWB));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(u32x4, v);
+  };
+  auto frags = [&](int buf, int ks, u32x4 (&a)[4], u32x4 (&b)[4]) {
+    const char* xs = lds + buf * 2 * SY_OPB + ks * 16 * SY_ROWB;
+    const char* ys = DIAG ? xs : xs + SY_OPB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = read8(xs, fx[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = read8(ys, fy[j]);
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+  auto mfmas = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma<MT>(b[j], a[i], acc[i][j]);
+  };
+
+  int issued = 0, lbuf = 0;
+  for (; issued < SY_PD && issued < ns; ++issued) {
+    issue(issued, lbuf);
+    lbuf = lbuf + 1 == SY_NBUF ? 0 : lbuf + 1;
+  }
+  u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  if (ns > 0) {
+    wait_stage(issued - 1);
+    __syncthreads();
+    frags(0, 0, fa0, fb0);
+  }
+  // Per stage s: slice 1's fragments are read while slice 0's MFMAs run; the
+  // wait and barrier for stage s + 1; then stage s + 1's slice 0 is read while
+  // slice 1's MFMAs run.  A slot refilled in iteration s held stage s - 2,
+  // last read before iteration s - 1's barrier.
+  int cbuf = 0;
+  for (int s = 0; s + 1 < ns; ++s) {
+    if (issued < ns) {
+      issue(issued, lbuf);
+      lbuf = lbuf + 1 == SY_NBUF ? 0 : lbuf + 1;
+      ++issued;
+    }
+    frags(cbuf, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nbuf = cbuf + 1 == SY_NBUF ? 0 : cbuf + 1;
+    wait_stage(issued - (s + 2));  // stage s + 1 is in LDS
+    __syncthreads();
+    frags(nbuf, 0, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    cbuf = nbuf;
+  }
+  if (ns > 0) {
+    frags(cbuf, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    mfmas(fa1, fb1);
+  }
+
+  // ---- epilogue: this split's copy of the output block += acc.  Lane holds
+  // out[m][n .. n+3] in acc[i][j][4 g .. 4 g + 3], m = wm*128 + 32 i + lq and
+  // n = wn*128 + 32 j + 8 g + 4 hh inside the tile.
+  const int which = !xb && !yb ? 0 : (!xb ? 1 : 2);  // G, M or H
+  float* out = p.state + (int64_t)split * p.split_stride + (int64_t)which * p.D * p.D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = cx + wm * 128 + i * 32 + lq;
+    if (m >= p.D) continue;
+    float* row = out + m * p.D;
+    f32x4 cur[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = cy + wn * 128 + j * 32 + g * 8 + hh * 4;  // D is a multiple of 64
+        cur[j][g] = n < p.D ? *(const f32x4*)(row + n) : (f32x4){};
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = cy + wn * 128 + j * 32 + g * 8 + hh * 4;
+        if (n >= p.D) continue;
+        f32x4 v = cur[j][g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += acc[i][j][g * 4 + e];
+        *(f32x4*)(row + n) = v;
+      }
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(256, 1) void syrk_kernel(const SyrkParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[SY_NBUF * 2 * SY_OPB];
+  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = (int)(bid / (uint32_t)p.n_tiles);
+  const int t = (int)(bid - (uint32_t)split * (uint32_t)p.n_tiles);
+  int tm, tn;
+  grouped_tile(t, 2 * p.nbh, 2 * p.nbh, true, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  if (tm == tn)
+    syrk_tile<MT, true>(p, lds, tm, tn, split);
+  else
+    syrk_tile<MT, false>(p, lds, tm, tn, split);
+}
+
+// ---- the statistics at the switch, from the per-layer state ----
+// One thread per 4 consecutive columns of one row: the S split copies added;
+// G's upper triangle stored (entries below the diagonal untouched); M split
+// into three bf16 planes whose sum is M to fp32 accuracy (each plane the
+// rounding of what the previous ones left), stored side by side as
+// [D][3 D] for the C = M W product; and this row's share of
+// r2 = <H, W W^T> = sum_i H_ii P_ii + 2 sum_{i<j} H_ij P_ij (P = W W^T) in
+// fp64, one partial per workgroup.
+__global__ __launch_bounds__(256) void gram_sum_kernel(const float* state, int64_t split_stride, int S, int32_t D,
+                                                       float* G, const float* P, uint16_t* planes, double* partials) {
+  const int64_t vpr = D / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t DD = (int64_t)D * D;
+  double part = 0.0;
+  if (gid < (int64_t)D * vpr) {
+    const int64_t i = gid / vpr, j = (gid % vpr) * 4;
+    const int64_t o = i * D + j;
+    f32x4 g = {}, m = {}, h = {};
+    for (int sp = 0; sp < S; ++sp) {
+      const float* st = state + sp * split_stride;
+      g += *(const f32x4*)(st + o);
+      m += *(const f32x4*)(st + DD + o);
+      h += *(const f32x4*)(st + 2 * DD + o);
+    }
+    if (j + 3 >= i) {
+      if (j >= i) {
+        *(f32x4*)(G + o) = g;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e >= i) G[o + e] = g[e];
+      }
+    }
+    uint32_t w[3][2];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      float r0 = m[e], r1 = m[e + 1];
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        const uint32_t pk = pack_bf16(r0, r1);
+        w[pl][e / 2] = pk;
+        r0 -= bf16_bits_to_f32(pk & 0xffffu);
+        r1 -= bf16_bits_to_f32(pk >> 16);
+      }
+    }
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) *(u32x2*)(planes + i * 3 * D + pl * D + j) = (u32x2){w[pl][0], w[pl][1]};
+    const f32x4 pv = *(const f32x4*)(P + o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j + e >= i) part += (j + e == i ? 1.0 : 2.0) * (double)h[e] * (double)pv[e];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+  __shared__ double red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// *out = sum of n partials (one workgroup, fixed order: deterministic)
+__global__ __launch_bounds__(256) void sum_set_kernel(const double* partials, int64_t n, double* out) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) s += partials[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
 // out[c][r] = in[r][c] for r < rows, 0 for rows <= r < rows_pad (16-bit elements),
 // converted from in_dt to out_dt (bf16 <-> f16, round to nearest even) when they differ
 __device__ __forceinline__ uint16_t conv16(uint32_t v, int in_dt, int out_dt) {
@@ -640,6 +942,100 @@ ispa_status launch_nt_split_reduce(const NtGemmParams& p, const double* sq, int6
                      (float*)p.out, (float*)p.out2, p.part, p.M, p.N, p.ld_out, p.ksplit, p.tri, p.two_kinds, sq,
                      n_sq, r2);
   return check_launch("split_reduce_kernel");
+}
+
+int gram_splits(int32_t D) {
+  const int64_t nb = 2 * ((D + 255) / 256);
+  const int64_t tiles = nb * (nb + 1) / 2;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(4, 256 / tiles));
+}
+
+ispa_status launch_syrk(const SyrkParams& p, int mfma_dt, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.n_tiles * p.ksplit;
+  if (p.D % 64 || p.lda % 8 || p.kchunk % 32 || p.kchunk * p.lda * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)p.ksplit * p.kchunk < p.n || blocks > INT32_MAX) {
+    set_error("syrk: width, leading dimension or token split out of range");
+    return ISPA_ERR_INVALID_ARG;
+  }
+  if (blocks == 0 || p.n == 0) return ISPA_OK;
+  if (mfma_dt == ISPA_BF16)
+    hipLaunchKernelGGL(syrk_kernel<ISPA_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(syrk_kernel<ISPA_F16>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return check_launch("syrk_kernel");
+}
+
+size_t gram_finalize_ws_bytes(int32_t D) {
+  const size_t d = (size_t)D;
+  const size_t blocks = (d * (d / 4) + 255) / 256;
+  return 2 * align256(d * 3 * d * 2) + align256(d * d * 4) + align256(blocks * 8);
+}
+
+ispa_status launch_gram_finalize(int32_t D, const float* state, int64_t split_stride, int S, const uint16_t* w,
+                                 float* G, float* C, double* r2, void* ws, hipStream_t stream) {
+  const size_t d = (size_t)D;
+  char* wp = (char*)ws;
+  uint16_t* planes = (uint16_t*)wp;  // M as three bf16 planes, [D][3 D]
+  wp += align256(d * 3 * d * 2);
+  uint16_t* wt3 = (uint16_t*)wp;  // W^T three times side by side, [D][3 D]
+  wp += align256(d * 3 * d * 2);
+  float* P = (float*)wp;  // W W^T
+  wp += align256(d * d * 4);
+  double* partials = (double*)wp;
+  ispa_status st;
+  {
+    const Transpose16 t[2] = {{w, wt3, D, D, D, 3 * (int64_t)D, D, ISPA_BF16, ISPA_BF16},
+                              {w, wt3 + D, D, D, D, 3 * (int64_t)D, D, ISPA_BF16, ISPA_BF16}};
+    if ((st = launch_transpose16(t, 2, stream))) return st;
+    const Transpose16 t3{w, wt3 + 2 * (int64_t)D, D, D, D, 3 * (int64_t)D, D, ISPA_BF16, ISPA_BF16};
+    if ((st = launch_transpose16(&t3, 1, stream))) return st;
+  }
+  // P = W W^T: rows of W are k-contiguous on both sides
+  NtGemmParams pp{};
+  pp.M = D;
+  pp.N = D;
+  pp.K = D;
+  pp.x = w;
+  pp.ldx = D;
+  pp.y = w;
+  pp.ldy = D;
+  pp.y_rows = D;
+  pp.epi = kNtStore;
+  pp.out = P;
+  pp.out_dt = ISPA_F32;
+  pp.ld_out = D;
+  pp.bn = 128;
+  pp.tiles_m = (D + kNtBM - 1) / kNtBM;
+  pp.tiles_n = (D + 127) / 128;
+  pp.ksplit = 1;
+  pp.kchunk = D;
+  if ((st = launch_nt_gemm(pp, ISPA_BF16, stream, nullptr))) return st;
+  const int64_t blocks = ((int64_t)D * (D / 4) + 255) / 256;
+  hipLaunchKernelGGL(gram_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, state, split_stride, S, D, G,
+                     (const float*)P, planes, partials);
+  if ((st = check_launch("gram_sum_kernel"))) return st;
+  // C = M W as sum over the planes: K = 3 D with W^T repeated
+  NtGemmParams cp{};
+  cp.M = D;
+  cp.N = D;
+  cp.K = 3 * (int64_t)D;
+  cp.x = planes;
+  cp.ldx = 3 * (int64_t)D;
+  cp.y = wt3;
+  cp.ldy = 3 * (int64_t)D;
+  cp.y_rows = D;
+  cp.epi = kNtStore;
+  cp.out = C;
+  cp.out_dt = ISPA_F32;
+  cp.ld_out = D;
+  cp.bn = 128;
+  cp.tiles_m = (D + kNtBM - 1) / kNtBM;
+  cp.tiles_n = (D + 127) / 128;
+  cp.ksplit = 1;
+  cp.kchunk = 3 * (int64_t)D;
+  if ((st = launch_nt_gemm(cp, ISPA_BF16, stream, nullptr))) return st;
+  hipLaunchKernelGGL(sum_set_kernel, dim3(1), dim3(256), 0, stream, (const double*)partials, blocks, r2);
+  return check_launch("sum_set_kernel");
 }
 
 int64_t nt_stats_split(int32_t D, int64_t np) {

@@ -75,4 +75,30 @@ ispa_status launch_transpose16(const Transpose16* jobs, int n_jobs, hipStream_t 
 
 constexpr int kNtBM = 256, kNtBK = 32;
 
+// Symmetric rank-k update of X = [A_loc | dA] into a per-layer statistics
+// state: S copies (one per token split) of G = A_loc^T A_loc, M = A_loc^T dA
+// and H = dA^T dA, each D x D fp32 (G and H: upper block triangle
+// maintained), copy s at state + s * split_stride floats, G, M, H in order.
+struct SyrkParams {
+  const void* a;      // A_loc [n][lda] 16-bit
+  const void* b;      // dA    [n][lda]
+  int64_t n, lda;
+  int32_t D, nbh;     // width (multiple of 64), 256-column blocks per half
+  int32_t n_tiles;    // upper-triangle tiles of the 2 nbh x 2 nbh block grid
+  int32_t ksplit;     // S
+  int64_t kchunk;     // token rows per split, multiple of 32
+  float* state;
+  int64_t split_stride;  // 3 D^2
+};
+// Splits of the state for width D (fixed per D so that the state layout does
+// not depend on the chunk size).
+int gram_splits(int32_t D);
+ispa_status launch_syrk(const SyrkParams& p, int mfma_dt, hipStream_t stream);
+// The switch-time statistics of one layer from its state: G (upper triangle,
+// entries below the diagonal untouched), C = M W and r2 = <H, W W^T>, all
+// written (not accumulated).  w: bf16 [D][D].  Workspace: gram_finalize_ws_bytes.
+size_t gram_finalize_ws_bytes(int32_t D);
+ispa_status launch_gram_finalize(int32_t D, const float* state, int64_t split_stride, int S, const uint16_t* w,
+                                 float* G, float* C, double* r2, void* ws, hipStream_t stream);
+
 }  // namespace ispa

@@ -181,16 +181,21 @@ class IspaStream:
     :meth:`post` per layer and chunk.  Results of a call live in buffers that
     the next call on the stream overwrites (views are returned).
 
-    Device state per layer: the KV cache, W (bf16 [D, D], y = a W), the
-    statistics G, C (fp32 [D, D], batched as [N, D, D] so the switch solves all
-    layers in one call) and r2 (fp64).  After the switch: dW (fp32), eps
-    (fp64), W + dW (bf16), the selection and the L/F mask.
+    Device state per layer: the KV cache, W (bf16 [D, D], y = a W) and the
+    warmup statistics.  ``stats="gram"`` (the default) accumulates them in the
+    grouping of the printed closed form: one rank-k update of [A_loc | dA]
+    per chunk into a per-layer state (ispa_accum_gram), and G, C = M W and r2
+    formed once at the switch (ispa_gram_finalize).  ``stats="direct"``
+    accumulates G, C = A_loc^T (dA W) and r2 every chunk (ispa_accum_stats).
+    For the switch, G, C (fp32 [N, D, D], so that one call solves every
+    layer) and r2 (fp64 [N]); after it dW (fp32), eps (fp64), W + dW (bf16),
+    the selection and the L/F mask.
     """
 
     def __init__(self, n_layers: int, H: int, d: int, T: int, capacity,
                  device, dtype=torch.bfloat16, stats_dtype=torch.float16,
                  lambda_abs: float = 0.0, lambda_rel: float = 1e-3, scale: float | None = None,
-                 with_stats: bool = True):
+                 with_stats: bool = True, stats: str = "gram"):
         if dtype != torch.bfloat16:
             raise ValueError("streams run on bf16 Q/K/V")
         self.N, self.H, self.d, self.T = n_layers, H, d, T
@@ -206,8 +211,14 @@ class IspaStream:
             raise ValueError("one capacity per layer")
         self.kv = [LayerKV(cap, T, H, d, dtype, dev) for cap in caps]
         self.W = torch.empty((n_layers, D, D), dtype=dtype, device=dev)
-        self.G = self.C = self.r2 = None
-        if with_stats:
+        if stats not in ("gram", "direct"):
+            raise ValueError("stats is 'gram' or 'direct'")
+        self.stats = stats
+        self.has_stats = with_stats
+        self.G = self.C = self.r2 = self.state = None
+        if with_stats and stats == "gram":
+            self.state = B.gram_state(D, n_layers, dev)
+        elif with_stats:
             self.G = torch.zeros((n_layers, D, D), **f32)
             self.C = torch.zeros((n_layers, D, D), **f32)
             self.r2 = torch.zeros(n_layers, dtype=torch.float64, device=dev)
@@ -246,7 +257,7 @@ class IspaStream:
         local and history groups merged by their LSE into A_loc and
         A_full - A_loc (one fused call), and the statistics update.  Returns
         (a_loc, delta, lse_full) views."""
-        if self.switched or self.G is None:
+        if self.switched or not self.has_stats:
             raise RuntimeError("warmup needs the statistics and must come before the switch")
         if q.shape != (self.T, self.H, self.d) or q.dtype != self.dtype:
             raise ValueError("q must be [T, H, d] bf16")
@@ -254,20 +265,50 @@ class IspaStream:
         loc, hist = self.kv[layer].warmup_groups(c)
         ls, nl = self._segs(loc)
         hs, nh = self._segs(hist)
-        n = self.T
-        need = max(L.ispa_dual_attn_merge_workspace_bytes(B.ISPA_BF16, n, self.H, self.d, ls, nl, hs, nh),
-                   L.ispa_accum_stats_workspace_bytes(B._DT[self.stats_dtype], n, self.D))
+        n, sdt = self.T, B._DT[self.stats_dtype]
+        need = L.ispa_dual_attn_merge_workspace_bytes(B.ISPA_BF16, n, self.H, self.d, ls, nl, hs, nh)
+        if self.stats == "direct":
+            need = max(need, L.ispa_accum_stats_workspace_bytes(sdt, n, self.D))
         ws = self.ws.get(need)
         wsp = ws.data_ptr() if ws is not None else None
         self._ck(L.ispa_dual_attn_merge(B.ISPA_BF16, n, self.H, self.d, self.scale, q.data_ptr(), q.stride(0),
                                         ls, nl, hs, nh, self.a_loc.data_ptr(), self.delta.data_ptr(),
-                                        B._DT[self.stats_dtype], self.lse_full.data_ptr(), wsp, need, s))
-        self._ck(L.ispa_accum_stats(B._DT[self.stats_dtype], B.ISPA_BF16, n, self.D,
-                                    self.a_loc.data_ptr(), self.delta.data_ptr(),
-                                    self.W[layer].data_ptr(), self.G[layer].data_ptr(),
-                                    self.C[layer].data_ptr(), self.r2[layer:layer + 1].data_ptr(),
-                                    wsp, need, s))
+                                        sdt, self.lse_full.data_ptr(), wsp, need, s))
+        if self.stats == "gram":
+            self._ck(L.ispa_accum_gram(sdt, n, self.D, self.a_loc.data_ptr(), self.delta.data_ptr(),
+                                       self.state[layer].data_ptr(), s))
+        else:
+            self._ck(L.ispa_accum_stats(sdt, B.ISPA_BF16, n, self.D,
+                                        self.a_loc.data_ptr(), self.delta.data_ptr(),
+                                        self.W[layer].data_ptr(), self.G[layer].data_ptr(),
+                                        self.C[layer].data_ptr(), self.r2[layer:layer + 1].data_ptr(),
+                                        wsp, need, s))
         return self.a_loc, self.delta, self.lse_full
+
+    def statistics(self):
+        """G (upper triangle), C and r2 of every layer from the warmup so far
+        (with the grouped statistics: formed from the states now, which stay
+        as they are).  Returns the (G, C, r2) buffers the solve reads."""
+        if not self.has_stats:
+            raise RuntimeError("this stream keeps no statistics")
+        if self.stats == "gram":
+            self._reserve_stats_out()
+            L, N, D = self.L, self.N, self.D
+            need = L.ispa_gram_finalize_workspace_bytes(D)
+            if getattr(self, "_fin_ws", None) is None or self._fin_ws.numel() < need:
+                self._fin_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self._ck(L.ispa_gram_finalize(N, D, self.state.data_ptr(), self.state.shape[1], self.W.data_ptr(),
+                                          B.ISPA_BF16, D * D, self.G.data_ptr(), self.C.data_ptr(),
+                                          self.r2.data_ptr(), D * D, self._fin_ws.data_ptr(), need,
+                                          self._stream()))
+        return self.G, self.C, self.r2
+
+    def _reserve_stats_out(self):
+        if self.G is None:
+            N, D, dev = self.N, self.D, self.device
+            self.G = torch.zeros((N, D, D), dtype=torch.float32, device=dev)
+            self.C = torch.empty((N, D, D), dtype=torch.float32, device=dev)
+            self.r2 = torch.empty(N, dtype=torch.float64, device=dev)
 
     # ------------------------------------------------------------------ switch
     def reserve_switch(self):
@@ -275,6 +316,11 @@ class IspaStream:
         workspace now, so that :meth:`switch` allocates nothing; they are reused
         by every later switch (re-calibration)."""
         N, D, dev = self.N, self.D, self.device
+        if self.stats == "gram" and self.has_stats:
+            self._reserve_stats_out()
+            need = self.L.ispa_gram_finalize_workspace_bytes(D)
+            if getattr(self, "_fin_ws", None) is None or self._fin_ws.numel() < need:
+                self._fin_ws = torch.empty(need, dtype=torch.uint8, device=dev)
         if self.dW is None:
             self.dW = torch.empty((N, D, D), dtype=torch.float32, device=dev)
             self.eps = torch.empty(N, dtype=torch.float64, device=dev)
@@ -292,6 +338,7 @@ class IspaStream:
         L, s, N, D = self.L, self._stream(), self.N, self.D
         dev = self.device
         self.reserve_switch()
+        self.statistics()
         ws = self._solve_ws
         need = ws.numel()
         self._ck(L.ispa_solve_dw(N, D, self.G.data_ptr(), self.C.data_ptr(), self.r2.data_ptr(), D * D,
@@ -320,9 +367,10 @@ class IspaStream:
         modified; warmup may continue afterwards.  Returns (eps [N] fp64,
         {K: selected int32 [K]}, {K: is_local uint8 [N]}, info [N] int32,
         dW [N, D, D] fp32), all on the device."""
-        if self.switched or self.G is None:
+        if self.switched or not self.has_stats:
             raise RuntimeError("evaluate runs during warmup")
         L, s, N, D, dev = self.L, self._stream(), self.N, self.D, self.device
+        self.statistics()
         dW = torch.empty((N, D, D), dtype=torch.float32, device=dev)
         eps = torch.empty(N, dtype=torch.float64, device=dev)
         info = torch.empty(N, dtype=torch.int32, device=dev)
@@ -348,8 +396,8 @@ class IspaStream:
         for layer, flag in enumerate(self.is_local_host):
             if flag:
                 self.kv[layer].evict_history()
-        self.G = self.C = None
-        self._solve_ws = None
+        self.G = self.C = self.state = None
+        self._solve_ws = self._fin_ws = None
         self.ws.release()
 
     def adopt_switch(self, is_local, w_eff, dW=None, eps=None):
@@ -363,7 +411,8 @@ class IspaStream:
         for layer, flag in enumerate(self.is_local_host):
             if flag:
                 self.kv[layer].evict_history()
-        self.G = self.C = None
+        self.G = self.C = self.state = None
+        self.has_stats = False
 
     def quantize_projections(self):
         """W8A8 post-switch projections (the pages report ISPA combined with
@@ -395,14 +444,21 @@ class IspaStream:
         if not self.switched:
             raise RuntimeError("re-calibration starts from a switched stream")
         D, dev = self.D, self.device
-        if self.G is None:
-            self.G = torch.empty((self.N, D, D), dtype=torch.float32, device=dev)
-            self.C = torch.empty_like(self.G)
-        if self.r2 is None:
-            self.r2 = torch.empty(self.N, dtype=torch.float64, device=dev)
-        self.G.zero_()
-        self.C.zero_()
-        self.r2.zero_()
+        self.has_stats = True
+        if self.stats == "gram":
+            if self.state is None:
+                self.state = B.gram_state(D, self.N, dev)
+            else:
+                self.state.zero_()
+        else:
+            if self.G is None:
+                self.G = torch.empty((self.N, D, D), dtype=torch.float32, device=dev)
+                self.C = torch.empty_like(self.G)
+            if self.r2 is None:
+                self.r2 = torch.empty(self.N, dtype=torch.float64, device=dev)
+            self.G.zero_()
+            self.C.zero_()
+            self.r2.zero_()
         for kv in self.kv:
             kv.keep_from(c)
         self.switched = False

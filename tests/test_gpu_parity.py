@@ -303,6 +303,45 @@ def test_accum_stats_parity(dt, n, D, steps):
     assert abs(float(r2.item()) - rr) <= 1e-5 * rr
 
 
+@pytest.mark.parametrize("dt,n,D,steps", [
+    (torch.float16, 4680, 1536, 2),   # two Wan-1.3B warmup chunks
+    (torch.bfloat16, 300, 320, 3),    # ragged rows, a width that is not a multiple of 256
+    (torch.float16, 33, 64, 2),       # one 64-wide block, a 1-row last stage
+    (torch.float16, 4680, 5120, 1),   # one Wan-14B warmup chunk (no token split)
+])
+def test_accum_gram_parity(dt, n, D, steps):
+    """The grouped statistics (one rank-k update of [A_loc | dA] per chunk,
+    C = M W and r2 = <H, W W^T> at the switch) against the oracle's
+    accumulate_gram and stats_from_gram on the same 16-bit operands.  The
+    products are exact and summed in fp32 on both sides of the fp64 oracle,
+    and M W runs on three bf16 planes of M (fp32 accuracy): bar 1e-5 for G,
+    C and r2 (no operand is rounded on the way, unlike ispa_accum_stats's R)."""
+    print(f"accum_gram {dt} n={n} D={D} steps={steps}", flush=True)
+    state = K().gram_state(D, device=DEV)
+    w = synth.normal((D, D), 77, DEV, std=D ** -0.5, dtype=torch.bfloat16)
+    Gr = np.zeros((D, D)); Mr = np.zeros((D, D)); Hr = np.zeros((D, D))
+    for s in range(steps):
+        a = synth.normal((n, D), 100 + s, DEV, std=0.3, dtype=dt)
+        dl = synth.normal((n, D), 200 + s, DEV, std=0.1, dtype=dt)
+        K().ispa_accum_gram(a, dl, state)
+        g, m, hh = O.accumulate_gram(a.cpu(), dl.cpu())
+        Gr += g; Mr += m; Hr += hh
+    st0 = state.clone()
+    G, C, r2 = K().ispa_gram_finalize(state, w)
+    torch.cuda.synchronize()
+    assert torch.equal(state, st0)  # the finalize leaves the state as it was
+    Gref, Cref, rref = O.stats_from_gram(Gr, Mr, Hr, w.cpu())
+    Gg = h64(G)
+    eg, ec, er = rel_fro_upper(Gg, Gref), rel(h64(C), Cref), abs(float(r2.item()) - rref) / rref
+    print(f"G {eg:.2e}  C {ec:.2e}  r2 {er:.2e}", flush=True)
+    assert eg <= 1e-5 and ec <= 1e-5 and er <= 1e-5
+    assert np.all(np.tril(Gg, -1) == 0)  # below the diagonal untouched (zeros from gram_finalize's G)
+    # n = 0 is a no-op
+    K().ispa_accum_gram(a[:0], dl[:0], state)
+    torch.cuda.synchronize()
+    assert torch.equal(state, st0)
+
+
 # ---------------------------------------------------------------- solve
 def _stats_for_solve(D, n, seed, planted=False):
     rng = np.random.default_rng(seed)

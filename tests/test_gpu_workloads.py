@@ -339,6 +339,7 @@ def test_recalibration_reenters_warmup():
             if c == 6:
                 torch.cuda.synchronize()
                 G, C, r2 = O.accumulate_stats(outs[0].cpu(), outs[1].cpu(), st.W[layer].cpu())
+                st.statistics()
                 Gg = np.triu(h64(st.G[layer]))
                 assert rel(Gg, np.triu(G)) <= 5e-4, layer
                 assert rel(h64(st.C[layer]), C) <= 5e-4, layer
@@ -426,11 +427,11 @@ def test_budget_and_warmup_sweep():
             ro[layer] += r
         if c == 0:
             continue
-        G0 = st.G.clone()
+        acc0 = st.state.clone()  # the warmup's accumulator
         eps, sels, masks, info, dW = st.evaluate(Ks)
         torch.cuda.synchronize()
         assert int(info.abs().max()) == 0
-        assert torch.equal(st.G, G0)
+        assert torch.equal(st.state, acc0)
         e = [float(x) for x in eps.cpu()]
         order = sorted(range(N), key=lambda i: (e[i], i))
         prev = set()
