@@ -84,35 +84,74 @@ def _traffic(kernel_file, src):
     return rec["bytes"]
 
 
-def cpu_baseline(g, q, kc, vc, rows_target_s=15.0):
-    """The oracle timed on host cores on a bounded sample: dual-stream
-    attention + merge for a subset of query rows of one warmup chunk."""
+def _host_info():
+    import platform
+    import subprocess
+    model = platform.processor() or ""
+    try:
+        for line in subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:  # lscpu missing
+        pass
+    return {"nproc": os.cpu_count(), "cpu": model, "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_baseline(g, q, kc, vc, budget_s=8.0):
+    """The oracle timed on the host cores on bounded samples of the same
+    workload, all threads and one thread: dual-stream attention + merge for a
+    subset of query rows of one warmup chunk (the headline's unit), the
+    grouped statistics for a subset of rows, and one ridge solve at D = 1536."""
     import numpy as np
     import torch
     sys.path.insert(0, ROOT)
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing
-        cores = os.cpu_count()
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     k_loc = torch.cat([g.sink_k, kc]).cpu()
     v_loc = torch.cat([g.sink_v, vc]).cpu()
     k_h, v_h = g.hist_k.cpu(), g.hist_v.cpu()
     qh = q.cpu()
     n_k = k_loc.shape[0] + k_h.shape[0]
     D = g.D
-    rows_done, t_tot, chunk = 0, 0.0, 64
-    while t_tot < rows_target_s and rows_done + chunk <= qh.shape[0]:
+
+    def attention(limit_s):
+        rows, t, chunk = 0, 0.0, 64
+        while t < limit_s and rows + chunk <= qh.shape[0]:
+            t0 = time.perf_counter()
+            O.dual_stream_attention(qh[rows:rows + chunk], k_loc, v_loc, k_h, v_h, g.d ** -0.5)
+            t += time.perf_counter() - t0
+            rows += chunk
+        return rows, t
+
+    rng = np.random.default_rng(0)
+    a = (0.3 * rng.standard_normal((1024, D))).astype(np.float16)
+    dl = (0.1 * rng.standard_normal((1024, D))).astype(np.float16)
+    w = (rng.standard_normal((D, D)) / np.sqrt(D)).astype(np.float32)
+
+    def legs():
+        rows, ta = attention(budget_s)
         t0 = time.perf_counter()
-        O.dual_stream_attention(qh[rows_done:rows_done + chunk], k_loc, v_loc, k_h, v_h, g.d ** -0.5)
-        t_tot += time.perf_counter() - t0
-        rows_done += chunk
-    flops = 4.0 * rows_done * n_k * D
-    return {"value": flops / t_tot / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, dual-stream attention + LSE merge of {rows_done} of 4680 "
-                      f"query rows (all 12 heads, {n_k} keys) of one warmup chunk; {t_tot:.1f} s",
-            "seconds": t_tot}
+        G, M, H = O.accumulate_gram(a, dl)
+        O.stats_from_gram(G, M, H, w)
+        ts = time.perf_counter() - t0
+        Gs = G + 1e-3 * np.trace(G) / D * np.eye(D)
+        t0 = time.perf_counter()
+        O.solve_dw(Gs, M @ w, 0.0)
+        tv = time.perf_counter() - t0
+        return {"attention": {"TFLOP/s": 4.0 * rows * n_k * D / ta / 1e12, "rows": rows, "s": round(ta, 2)},
+                "statistics": {"TFLOP/s": (4.0 * 1024 * D * D) / ts / 1e12, "rows": 1024, "s": round(ts, 2)},
+                "solve": {"TFLOP/s": (7.0 / 3.0) * D ** 3 / tv / 1e12, "D": D, "s": round(tv, 2)}}
+
+    all_t = legs()
+    with threadpool_limits(limits=1):
+        one_t = legs()
+    return {"value": all_t["attention"]["TFLOP/s"], "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy oracle on host cores: dual-stream attention + LSE merge of "
+                      f"{all_t['attention']['rows']} of 4680 query rows (12 heads, {n_k} keys) of one warmup chunk "
+                      f"(value, all threads); legs below: the grouped statistics of 1024 rows at D = {D} and one "
+                      f"ridge solve at D = {D} (hand-written Cholesky), all threads and one thread",
+            "legs_all_threads": all_t, "legs_one_thread": one_t, "host": _host_info()}
 
 
 STREAMS = {
@@ -256,6 +295,47 @@ def _preload_kernels(dev):
     K.ispa_select_layers(eps, 1)
     K.ispa_local_attn_proj(q, [(k, v)], w)
     torch.cuda.synchronize()
+
+
+def _pass_figures(recs, spec):
+    """ms per chunk and TFLOP/s (attention + statistics + projection flops over
+    the ISPA time) of one stream pass."""
+    N, H, d, T = spec["N"], spec["H"], spec["d"], TOKENS_PER_CHUNK
+    D = H * d
+    flops = 0.0
+    for r in recs:
+        for nk in r["n_keys"]:
+            flops += 4.0 * T * nk * D
+        flops += N * ((4.0 * T * D * D + 2.0 * T * D) if r["warm"] else 2.0 * T * D * D)
+    ms = sum(r["ms"] for r in recs)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms/chunk (mean)": round(ms / len(recs), 3), "last chunk ms": round(recs[-1]["ms"], 3),
+            "pass TFLOP/s": round(tf, 1), "pass roofline frac (bf16 2.5 PFLOP/s)": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def wan14b_figures(seed, dev):
+    """One Wan-14B warmup pass (40 layers x 40 heads, 19 warmup chunks, switch
+    with K = 20) and one 40-chunk post-switch pass with its selection, each
+    timed per chunk with HIP events around the ISPA calls."""
+    import torch
+    _preload_kernels(dev)
+    t0 = time.perf_counter()
+    recs_w, switch_ms, st4, _ = _stream_pass(STREAMS["wan14b_warmup"], dev, seed)
+    out = {"wan14b_warmup": {**_pass_figures(recs_w, STREAMS["wan14b_warmup"]),
+                             "switch ms (finalize + 40 solves at D = 5120 + select)": round(switch_ms, 3)}}
+    adopt = (list(st4.is_local_host), st4.W, st4.w_eff)
+    st4.kv = []
+    st4.G = st4.C = st4.dW = st4.state = None
+    torch.cuda.empty_cache()
+    recs_p, _, st5, _ = _stream_pass(STREAMS["wan14b_post"], dev, seed, adopt)
+    last = recs_p[-1]
+    full = 2 * STREAMS["wan14b_post"]["N"] * (last["c"] + 1) * TOKENS_PER_CHUNK * 5120 * 2
+    out["wan14b_post"] = {**_pass_figures(recs_p, STREAMS["wan14b_post"]),
+                          "kv_held_fraction_last_chunk": round(last["kv_held"] / full, 4)}
+    out["wan14b wall s (both passes, input generation included)"] = round(time.perf_counter() - t0, 1)
+    del st4, st5
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_stream(args, name, dev):
@@ -413,10 +493,17 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--workload", default="wan13b_layer", choices=["wan13b_layer"] + sorted(STREAMS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-14b", action="store_true", help="skip the Wan-14B stream passes of the default run")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only run this many dual-attention calls of the workload (counter runs)")
+    ap.add_argument("--fused-only", type=int, default=0,
+                    help="only run this many fused dual-attention + merge calls of the workload (counter runs)")
+    ap.add_argument("--gram-only", type=int, default=0,
+                    help="only run this many statistics updates (ispa_accum_gram) of the workload (counter runs)")
+    ap.add_argument("--merge-only", type=int, default=0,
+                    help="only run this many two-part LSE merges of the workload (counter runs)")
     ap.add_argument("--proj-compare", type=int, default=0,
                     help="only time the post-switch projection paths (bf16 and W8A8) at the Wan-1.3B "
                          "and Wan-14B widths, this many calls each")
@@ -506,6 +593,32 @@ def main():
     ws_post_b = L.ispa_local_attn_proj_workspace_bytes(B.ISPA_BF16, n_q, H, d, post_segs, post_n)
     ws = torch.empty(max(ws_attn_b, ws_stats_b, ws_solve_b, ws_post_b, 256), dtype=torch.uint8, device=dev)
     wsp, wsn = ws.data_ptr(), ws.numel()
+    if args.fused_only or args.gram_only or args.merge_only:
+        q, ls, nl, hs, nh = seg_tables[0]
+        fo = (ctypes.c_void_p * 2)(o_loc.data_ptr(), o_hist.data_ptr())
+        fl = (ctypes.c_void_p * 2)(lse_loc.data_ptr(), lse_hist.data_ptr())
+        if args.gram_only or args.merge_only:  # inputs of one chunk
+            L.ispa_dual_attn(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
+                             o_loc.data_ptr(), lse_loc.data_ptr(), o_hist.data_ptr(), lse_hist.data_ptr(), wsp, wsn, sh)
+            L.ispa_lse_merge(2, fo, fl, n_q, H, d, None, None, a_loc.data_ptr(), delta.data_ptr(), B.ISPA_F16, sh)
+        for _ in range(args.fused_only):
+            st = L.ispa_dual_attn_merge(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
+                                        a_loc.data_ptr(), delta.data_ptr(), B.ISPA_F16, None, wsp, wsn, sh)
+            if st:
+                raise B.IspaError(st, L.ispa_last_error().decode())
+        for _ in range(args.gram_only):
+            st = L.ispa_accum_gram(B.ISPA_F16, n_q, D, a_loc.data_ptr(), delta.data_ptr(), state.data_ptr(), sh)
+            if st:
+                raise B.IspaError(st, L.ispa_last_error().decode())
+        for _ in range(args.merge_only):
+            st = L.ispa_lse_merge(2, fo, fl, n_q, H, d, None, None, a_loc.data_ptr(), delta.data_ptr(),
+                                  B.ISPA_F16, sh)
+            if st:
+                raise B.IspaError(st, L.ispa_last_error().decode())
+        torch.cuda.synchronize()
+        print(json.dumps({"fused_only_calls": args.fused_only, "gram_only_calls": args.gram_only,
+                          "merge_only_calls": args.merge_only}))
+        return
     if args.attn_only:
         q, ls, nl, hs, nh = seg_tables[0]
         for _ in range(args.attn_only):
@@ -656,8 +769,12 @@ def main():
              "frac": round(stats_flops / t_stats / 1e12 / PEAK_BF16_TFLOPS, 4)},
         ],
     }
+    if not args.no_14b:
+        del steps_in, seg_tables, ws
+        torch.cuda.empty_cache()
+        out["also"]["Wan-14B streams"] = wan14b_figures(args.seed, dev)
     if not args.no_cpu_baseline:
-        q, kc, vc = steps_in[0]
+        q, kc, vc = g.step(0)
         out["cpu_baseline"] = cpu_baseline(g, q, kc, vc)
     else:
         out["cpu_baseline"] = None

@@ -188,6 +188,8 @@ ispa_status ispa_dual_attn_merge(ispa_dtype dt, int64_t n_q, int32_t H, int32_t 
     return fail(ISPA_ERR_WORKSPACE, "dual_attn_merge workspace too small or misaligned");
   if (n_q == 0) return ISPA_OK;
   HostGroup g[2] = {{loc, n_loc}, {hist, n_hist}};
+  if (dual_single_pass(dt, n_q, H, d, g, out_dt))
+    return run_dual_single_pass(n_q, H, scale, q, q_stride, g, a_loc, delta, out_dt, lse_full, ws, stream);
   float* o[2] = {nullptr, nullptr};
   float* l[2] = {nullptr, nullptr};
   const MergeOut mo{a_loc, delta, out_dt, lse_full};

@@ -439,7 +439,14 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // kRuns: every job covers at most two runs of consecutive rows (one run per
 // segment it overlaps); tile addresses are then computed from the tile index.
-template <bool kRuns>
+// kDual (with kRuns): one workgroup per (query tile, head) attends to the
+// local group and then to the history group, each by the whole tile pipeline
+// below (one pass per group).  Between the passes the local output goes to
+// o_stash unnormalised, straight from the accumulators, and the running
+// maximum and sum restart; the epilogue reads it back, merges the two groups
+// by their log-sum-exp and writes A_loc, A_full - A_loc and the merged LSE,
+// so no partial result is written per key piece and no merge kernel runs.
+template <bool kRuns, bool kDual = false>
 __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const AttnParams p) {
   using namespace a5;
   __shared__ __attribute__((aligned(1024))) char lds[2 * NSLOT * TILEB];
@@ -458,7 +465,6 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   const int head = rest % p.H;
   const int jidx = rest / p.H;
   const AttnJob job = p.jobs[jidx];
-  const int g = job.group;
   const float c = p.c;
 
   // this lane's queries (B operand of S^T = K Q^T): block qb, slices of 16 d
@@ -476,13 +482,60 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     }
   }
 
+  f32x16 o[QB][DH / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int i = 0; i < DH / 32; ++i) o[qb][i] = (f32x16){};
+  float m[QB], l_part[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l_part[qb] = 0.0f;
+  }
+  float l_loc[QB], m_loc[QB];  // kDual: the local group's row sum (total) and maximum
+  constexpr int kPasses = kDual ? 2 : 1;
+#pragma unroll 1
+  for (int pass = 0; pass < kPasses; ++pass) {
+  const int g = kDual ? pass : job.group;
+  int64_t kbeg = job.kbeg, kend = job.kend;
+  if constexpr (kDual) {
+    kbeg = 0;
+    kend = 0;
+    for (int s = 0; s < p.n_segs[g]; ++s) kend += p.segs[g][s].n;
+    if (pass == 1) {
+      // the local group is complete: keep its output, row sum and maximum and
+      // restart for the history group
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[qb]), __float_as_uint(l_part[qb]), false,
+                                                  false);
+        l_loc[qb] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        m_loc[qb] = m[qb];
+        m[qb] = -INFINITY;
+        l_part[qb] = 0.0f;
+        const int64_t qrow = qrow0 + qb * 32;
+        float* sp = p.o_stash + (qrow * p.H + head) * (int64_t)DH + hh * 4;
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) {
+          if (qrow < p.n_q) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+              *(f32x4*)(sp + dt * 32 + g4 * 8) = (f32x4){o[qb][dt][g4 * 4], o[qb][dt][g4 * 4 + 1],
+                                                         o[qb][dt][g4 * 4 + 2], o[qb][dt][g4 * 4 + 3]};
+          }
+          o[qb][dt] = (f32x16){};
+        }
+      }
+    }
+  }
   int n_tiles = 0;
   {
     int64_t st = 0;
     for (int s = 0; s < p.n_segs[g]; ++s) {
       const int64_t n = p.segs[g][s].n;
-      const int64_t a = job.kbeg > st ? job.kbeg : st;
-      const int64_t b = job.kend < st + n ? job.kend : st + n;
+      const int64_t a = kbeg > st ? kbeg : st;
+      const int64_t b = kend < st + n ? kend : st + n;
       if (a < b) n_tiles += (int)((b - a + BK - 1) / BK);
       st += n;
     }
@@ -569,7 +622,7 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
       st.c.row += BK;
       if (--st.full == 0 && st.c.row >= st.c.end) {
         asm volatile("" ::: "memory");  // the segment ends on a tile boundary: next segment
-        if (segc_seek(p, g, head, st.c.seg + 1, job.kbeg, job.kend, st.c)) stream_init(st, is_v);
+        if (segc_seek(p, g, head, st.c.seg + 1, kbeg, kend, st.c)) stream_init(st, is_v);
       }
       return ld;
     }
@@ -583,7 +636,7 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
       ld.voff[i] = (int)(row * st.sb) + swz(lrow, s16) * 16;
     }
     st.c.row += BK;
-    if (segc_seek(p, g, head, st.c.seg + 1, job.kbeg, job.kend, st.c)) stream_init(st, is_v);
+    if (segc_seek(p, g, head, st.c.seg + 1, kbeg, kend, st.c)) stream_init(st, is_v);
     return ld;
   };
   auto issue_load = [&](const Load& ld, const int i) __attribute__((always_inline)) {
@@ -592,7 +645,7 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   Stream ks_, vs_;
   SegCursor ccur;
   int cfull = 0;  // full tiles left from ccur.row in its segment
-  segc_seek(p, g, head, 0, job.kbeg, job.kend, ccur);
+  segc_seek(p, g, head, 0, kbeg, kend, ccur);
   ks_.c = vs_.c = ccur;
   stream_init(ks_, false);
   stream_init(vs_, true);
@@ -603,14 +656,14 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
       ccur.row += BK;
       if (--cfull == 0 && ccur.row >= ccur.end) {
         asm volatile("" ::: "memory");
-        if (segc_seek(p, g, head, ccur.seg + 1, job.kbeg, job.kend, ccur)) cfull = (int)((ccur.end - ccur.row) / BK);
+        if (segc_seek(p, g, head, ccur.seg + 1, kbeg, kend, ccur)) cfull = (int)((ccur.end - ccur.row) / BK);
       }
       return BK;
     }
     asm volatile("" ::: "memory");
     const int nv = (int)(ccur.end - ccur.row);
     ccur.row += BK;
-    if (segc_seek(p, g, head, ccur.seg + 1, job.kbeg, job.kend, ccur)) cfull = (int)((ccur.end - ccur.row) / BK);
+    if (segc_seek(p, g, head, ccur.seg + 1, kbeg, kend, ccur)) cfull = (int)((ccur.end - ccur.row) / BK);
     return nv;
   };
 
@@ -629,8 +682,8 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     int nr = 0;
     for (int s = 0; s < p.n_segs[g]; ++s) {
       const AttnSeg sg = p.segs[g][s];
-      const int64_t a = job.kbeg > st ? job.kbeg : st;
-      const int64_t b = job.kend < st + sg.n ? job.kend : st + sg.n;
+      const int64_t a = kbeg > st ? kbeg : st;
+      const int64_t b = kend < st + sg.n ? kend : st + sg.n;
       if (a < b) {
         Run r;
         r.ksb = (int)(sg.ks * 2);
@@ -695,11 +748,6 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   };
   auto wait_iter = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW)); };
 
-  f32x16 o[QB][DH / 32];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int i = 0; i < DH / 32; ++i) o[qb][i] = (f32x16){};
   f32x16 S[QB][2];  // [query block][key block]: S_t, then S_{t+1}
   // P as packed bf16 pairs [buffer][query block][pair]; pairs 4g .. 4g+3 form
   // the MFMA operand of key group g (32-bit words: the row sums read them one
@@ -709,13 +757,6 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     return __builtin_bit_cast(bf16x8, (u32x4){P[b][qb][4 * gp], P[b][qb][4 * gp + 1], P[b][qb][4 * gp + 2],
                                               P[b][qb][4 * gp + 3]});
   };
-  float m[QB], l_part[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l_part[qb] = 0.0f;
-  }
-
   // P pair k of query block qb into P[b] (uses m)
   auto exp_pair = [&](const int b, const int qb, const int k) __attribute__((always_inline)) {
     const int blk = k >> 3, i = (k & 7) * 2;
@@ -936,9 +977,61 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
       run_iter(t, 3, 1);
       if (++t > n_tiles) break;
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS write in flight when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS write in flight when the pass ends
   }
+  }  // pass
 
+  if constexpr (kDual) {
+    // merge: A_full = (1 - sigma) A_loc + sigma O_hist with sigma the history
+    // group's share of the softmax mass (from the two LSEs), so
+    // A_full - A_loc = sigma (O_hist - A_loc), all in fp32
+    const bool out_bf = p.out_dt == ISPA_BF16;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[qb]), __float_as_uint(l_part[qb]), false,
+                                                false);
+      const float l_h = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      const int64_t qrow = qrow0 + qb * 32;
+      if (qrow >= p.n_q) continue;
+      const float lse0 = l_loc[qb] > 0.0f ? m_loc[qb] + log2f(l_loc[qb]) : -INFINITY;  // log2 units
+      const float lse1 = l_h > 0.0f ? m[qb] + log2f(l_h) : -INFINITY;
+      const float mm = fmaxf(lse0, lse1);
+      float sigma = 0.0f, lse = -INFINITY;
+      if (mm != -INFINITY) {
+        const float e0 = exp2f(lse0 - mm), e1 = exp2f(lse1 - mm);
+        sigma = e1 / (e0 + e1);
+        lse = (mm + log2f(e0 + e1)) * kLn2;
+      }
+      const float inv_h = l_h > 0.0f ? 1.0f / l_h : 0.0f;
+      const float inv_l = l_loc[qb] > 0.0f ? 1.0f / l_loc[qb] : 0.0f;
+      const int64_t base = (qrow * p.H + head) * (int64_t)DH;
+      // this lane's own stores between the passes (complete: the first pass
+      // ended with vmcnt(0)), read back
+      const float* sp = p.o_stash + base + hh * 4;
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = dt * 32 + g4 * 8 + hh * 4;
+          const f32x4 ol = *(const f32x4*)(sp + dt * 32 + g4 * 8);
+          float a[4], dl[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = ol[e] * inv_l;
+            dl[e] = sigma * (o[qb][dt][g4 * 4 + e] * inv_h - a[e]);
+          }
+          *(u32x2*)((uint16_t*)p.a_loc + base + d0) =
+              out_bf ? (u32x2){pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])}
+                     : (u32x2){pack_f16(a[0], a[1]), pack_f16(a[2], a[3])};
+          *(u32x2*)((uint16_t*)p.delta + base + d0) =
+              out_bf ? (u32x2){pack_bf16(dl[0], dl[1]), pack_bf16(dl[2], dl[3])}
+                     : (u32x2){pack_f16(dl[0], dl[1]), pack_f16(dl[2], dl[3])};
+        }
+      }
+      if (hh == 0 && p.lse_full) p.lse_full[qrow * p.H + head] = lse;
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[qb]), __float_as_uint(l_part[qb]), false, false);
@@ -1161,6 +1254,49 @@ SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, i
     plan.split_len[g] = s > 1 ? (((n + s - 1) / s + kBK - 1) / kBK) * kBK : n;
   }
   return plan;
+}
+
+bool dual_single_pass(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, const HostGroup* groups, int out_dt) {
+  if (dt != ISPA_BF16 || d != 128 || (out_dt != ISPA_BF16 && out_dt != ISPA_F16) || n_q <= 0) return false;
+  for (int g = 0; g < 2; ++g) {
+    int runs = 0;  // the two-run tile addressing, per group
+    for (int s = 0; s < groups[g].n_segs; ++s) runs += groups[g].segs[s].n > 0;
+    if (runs > 2) return false;
+  }
+  // one workgroup per (query tile, head): use it when that fills most of the
+  // 256 CUs; fewer pairs are better served by splitting the keys
+  const int64_t units = (n_q + a5::BQ - 1) / a5::BQ * H;
+  return units >= 192;
+}
+
+ispa_status run_dual_single_pass(int64_t n_q, int32_t H, float scale, const void* q, int64_t q_stride,
+                                 const HostGroup* groups, void* a_loc, void* delta, int out_dt, float* lse_full,
+                                 void* ws, hipStream_t stream) {
+  AttnParams p{};
+  p.q = q;
+  p.q_stride = q_stride;
+  p.n_q = n_q;
+  p.H = H;
+  p.n_qtiles = (int)((n_q + a5::BQ - 1) / a5::BQ);
+  p.c = scale * kLog2e;
+  for (int g = 0; g < 2; ++g) {
+    p.n_segs[g] = groups[g].n_segs;
+    for (int s = 0; s < groups[g].n_segs; ++s) {
+      const ispa_seg& sg = groups[g].segs[s];
+      p.segs[g][s] = AttnSeg{sg.k, sg.v, sg.n, sg.k_stride, sg.v_stride};
+    }
+  }
+  p.n_jobs = 1;
+  p.jobs[0] = AttnJob{0, 0, 0, groups[0].n_keys(), nullptr, nullptr};
+  p.a_loc = a_loc;
+  p.delta = delta;
+  p.lse_full = lse_full;
+  p.out_dt = out_dt;
+  p.o_stash = (float*)ws;
+  const int64_t blocks = (int64_t)p.n_qtiles * H;
+  hipLaunchKernelGGL((attn_bf16_d128_kernel<true, true>), dim3((unsigned)blocks), dim3(a5::WAVES * 64), 0, stream,
+                     p);
+  return check_launch("attention kernel (single-pass dual form)");
 }
 
 size_t merged_workspace_bytes(int64_t n_q, int32_t H, int32_t d, const SplitPlan& plan, int n_groups) {

@@ -38,6 +38,13 @@ struct AttnParams {
   int32_t n_segs[2];
   AttnSeg segs[2][ISPA_MAX_SEGS];
   AttnJob jobs[kMaxJobs];
+  // single-pass dual form (one workgroup per query tile and head over both
+  // groups, merged in its epilogue): 16-bit outputs
+  void* a_loc;     // [n_q, H, d] of out_dt: the local group's output
+  void* delta;     // [n_q, H, d] of out_dt: merged - a_loc
+  float* lse_full; // [n_q, H] or null
+  int32_t out_dt;  // ISPA_BF16 or ISPA_F16
+  float* o_stash;  // fp32 [n_q, H, d]: the local group's unnormalised output, from the boundary to the epilogue
 };
 
 // A group description on the host.
@@ -81,6 +88,15 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
                                 void* ws, size_t ws_bytes, hipStream_t stream,
                                 void* o16_g0 = nullptr, int o16_dt = ISPA_BF16,
                                 const MergeOut* merge_all = nullptr);
+
+// The single-pass dual form applies (bf16 inputs, d = 128, 16-bit outputs,
+// at most 4 runs of rows over both groups, enough (query tile, head) pairs
+// to fill the chip): ispa_dual_attn_merge then needs no workspace.
+bool dual_single_pass(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, const HostGroup* groups, int out_dt);
+// ws: n_q * H * d fp32 (the local output between the group boundary and the epilogue)
+ispa_status run_dual_single_pass(int64_t n_q, int32_t H, float scale, const void* q, int64_t q_stride,
+                                 const HostGroup* groups, void* a_loc, void* delta, int out_dt, float* lse_full,
+                                 void* ws, hipStream_t stream);
 
 // n-way merge used both by the public call and by split combining.
 struct MergeParams {

@@ -238,6 +238,59 @@ def test_dual_attn_merge_parity(dt, H, d, n_q, n_sink, n_cur, n_hist, out_dt):
     assert np.abs(h64(lse) - ref["lse_full"]).max() <= (1e-5 if dt == torch.float32 else 2e-3)
 
 
+@pytest.mark.parametrize("H,n_q,loc_lens,hist_lens,out_dt", [
+    (12, 4680, (4680, 4680), (9360,), torch.float16),        # Wan-1.3B layout, chunk 3 of a stream
+    (12, 4680, (4680, 4680), (), torch.float16),             # chunk 1: no history yet
+    (8, 6000, (700, 6000), (3000, 1500), torch.bfloat16),    # four ragged runs, ragged query tile
+    (12, 4680, (), (3000,), torch.float16),                  # no local keys
+    (12, 4680, (), (), torch.float16),                       # no keys at all
+])
+def test_dual_attn_merge_single_pass(H, n_q, loc_lens, hist_lens, out_dt):
+    """The single-pass form of the fused call (one workgroup per query tile
+    and head over both groups, at least 192 of them, 16-bit outputs).
+
+    Sampled rows against the oracle (the attention bars; dA's own bound as
+    in the split-path test), and every output against the split path on the
+    same inputs (ispa_dual_attn + ispa_lse_merge).  The single pass holds the
+    local output rounded to out_dt and forms dA = A_full - A_loc from that
+    rounded A_loc, so dA may differ from the split path's by the rounding of
+    A_loc (one unit in its last place) besides the attention's own error."""
+    d, dt = 128, torch.bfloat16
+    print(f"dual_attn_merge single pass H={H} n_q={n_q} local={loc_lens} hist={hist_lens} -> {out_dt}", flush=True)
+    q = _cache(n_q, H, d, 141)
+    loc = [(_cache(n, H, d, 142 + 2 * i), _cache(n, H, d, 143 + 2 * i)) for i, n in enumerate(loc_lens)]
+    hist = [(_cache(n, H, d, 152 + 2 * i) + 0.5, _cache(n, H, d, 153 + 2 * i)) for i, n in enumerate(hist_lens)]
+    a_loc, delta, lse = K().ispa_dual_attn_merge(q, loc, hist, out_dtype=out_dt)
+    o_l, l_l, o_h, l_h = K().ispa_dual_attn(q, loc, hist)
+    o_f, l_f, a0, dl = K().ispa_lse_merge([o_l, o_h], [l_l, l_h], out_dtype=out_dt)
+    torch.cuda.synchronize()
+    ulp = 2.0 ** -8 if out_dt == torch.bfloat16 else 2.0 ** -10
+    # against the split path: A_loc within a rounding and the attention's own
+    # difference (both from bf16 P), LSE, dA
+    assert bool(torch.isfinite(a_loc.float()).all() and torch.isfinite(delta.float()).all())
+    ea = rel(h64(a_loc), h64(a0)) if a0.abs().max() > 0 else float(a_loc.abs().max())
+    ed = float((delta.float() - dl.float()).norm() / max(float(o_f.norm()), 1e-30))
+    el = float((lse - l_f).abs().max()) if bool(torch.isfinite(l_f).any()) else 0.0
+    print(f"vs split path: A_loc rel {ea:.2e}, dA rel (to |A_full|) {ed:.2e}, lse {el:.2e}", flush=True)
+    assert ea <= 5e-3 and ed <= 5e-3
+    assert torch.equal(torch.isinf(lse), torch.isinf(l_f))
+    if not loc_lens and not hist_lens:
+        assert not a_loc.float().any() and not delta.float().any() and bool(torch.isneginf(lse).all())
+        return
+    assert el <= 2e-3
+    # sampled rows against the oracle
+    rows = [0, 1, 255, 256, 2047, n_q // 2, n_q - 1]
+    cat = lambda pairs, i: torch.cat([p[i] for p in pairs]).cpu() if pairs else \
+        torch.zeros((0, H, d), dtype=dt)  # noqa: E731
+    ref = O.dual_stream_attention(q[rows].cpu(), cat(loc, 0), cat(loc, 1), cat(hist, 0), cat(hist, 1), d ** -0.5)
+    n = len(rows)
+    a_ref, full_ref = ref["a_loc"].reshape(n, -1), ref["a_full"].reshape(n, -1)
+    ar = h64(a_loc[rows])
+    assert np.linalg.norm(ar - a_ref) <= (5e-3 + ulp) * max(np.linalg.norm(a_ref), 1e-30) + 1e-30
+    err = np.linalg.norm(h64(delta[rows]) - ref["delta"].reshape(n, -1))
+    assert err <= (5e-3 + 2 * ulp) * (np.linalg.norm(full_ref) + np.linalg.norm(a_ref))
+    assert np.nanmax(np.abs(np.where(np.isinf(ref["lse_full"]), 0, h64(lse[rows]) - ref["lse_full"]))) <= 2e-3
+
 
 # ---------------------------------------------------------------- merge
 def test_merge_parts_from_oracle():
