@@ -57,6 +57,9 @@ __all__ = [
     "quantize_weight_e4m3",
     "w8a8_linear",
     "local_attn_proj_w8a8",
+    "quantize_chunk_e4m3",
+    "quantize_heads_e4m3",
+    "attention_fp8",
 ]
 
 
@@ -424,6 +427,58 @@ def local_attn_proj_w8a8(q, k, v, w_proj, scale: float):
     o32 = o.reshape(o.shape[0], -1).astype(np.float32)
     wq, ws = quantize_weight_e4m3(w_proj)
     return w8a8_linear(o32, wq, ws)
+
+
+# ---------------------------------------------------------------------------
+# Quantised local attention (the post-switch L-Layer on the fp8 matrix core)
+#
+# The pages name W8A8 quantisation beside ISPA and nothing more (EN review,
+# Key Findings, the Figure 7 item).  The reading here for the attention
+# itself: its three operands in OCP FP8 E4M3 with symmetric scales, K and V
+# once per cache chunk and head (a chunk's rows are written once and then
+# only read, so they are quantised when written), Q per query row and head;
+# the attention is then the exact softmax attention of the dequantised
+# operands.  Each scale is amax / 448 in fp32 and each code the E4M3 rounding
+# of x / scale, as in quantize_rows_e4m3.
+# ---------------------------------------------------------------------------
+
+def quantize_chunk_e4m3(x):
+    """One cache chunk [n, H, d] -> (codes uint8 [n, H, d], scales fp32 [H]):
+    one symmetric scale per head over all n x d values of the chunk."""
+    x32 = np.asarray(as_f64(x), dtype=np.float32)
+    n, H, d = x32.shape
+    per_head = x32.transpose(1, 0, 2).reshape(H, n * d)
+    codes, scales = quantize_rows_e4m3(per_head)
+    return codes.reshape(H, n, d).transpose(1, 0, 2).copy(), scales
+
+
+def quantize_heads_e4m3(q):
+    """Queries [n, H, d] -> (codes uint8 [n, H, d], scales fp32 [n, H]): one
+    scale per query row and head."""
+    q32 = np.asarray(as_f64(q), dtype=np.float32)
+    n, H, d = q32.shape
+    codes, scales = quantize_rows_e4m3(q32.reshape(n * H, d))
+    return codes.reshape(n, H, d), scales.reshape(n, H)
+
+
+def attention_fp8(q, k_chunks, v_chunks, scale: float):
+    """Attention of every query over the keys of the given chunks with the
+    operands quantised as stated above: Q per (row, head), each chunk's K
+    and V per head; the softmax attention of the dequantised values in fp64.
+    k_chunks, v_chunks: lists of [n_c, H, d].  Returns (o [n_q, H, d],
+    lse [n_q, H])."""
+    qc, sq = quantize_heads_e4m3(q)
+    q_hat = e4m3_decode(qc) * sq.astype(np.float64)[:, :, None]
+    ks, vs = [], []
+    for k, v in zip(k_chunks, v_chunks):
+        kc, sk = quantize_chunk_e4m3(k)
+        vc, sv = quantize_chunk_e4m3(v)
+        ks.append(e4m3_decode(kc) * sk.astype(np.float64)[None, :, None])
+        vs.append(e4m3_decode(vc) * sv.astype(np.float64)[None, :, None])
+    H, d = q_hat.shape[1], q_hat.shape[2]
+    k_hat = np.concatenate(ks) if ks else np.zeros((0, H, d))
+    v_hat = np.concatenate(vs) if vs else np.zeros((0, H, d))
+    return group_attention(q_hat, k_hat, v_hat, scale)
 
 
 # ---------------------------------------------------------------------------

@@ -165,3 +165,94 @@ def test_local_attn_proj_w8a8_reduces_to_parts():
     o, _ = O.group_attention(q, k, v, 0.25)
     wq, ws = O.quantize_weight_e4m3(w)
     assert np.array_equal(y, O.w8a8_linear(o.reshape(5, -1).astype(np.float32), wq, ws))
+
+
+# ---------------------------------------------------------------- quantised attention
+def test_quantize_chunk_scales_and_codes():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((50, 3, 16)).astype(np.float32)
+    x[:, 1, :] *= 100.0      # heads of very different ranges
+    x[:, 2, :] = 0.0         # an all-zero head
+    codes, scales = O.quantize_chunk_e4m3(x)
+    assert codes.shape == x.shape and scales.shape == (3,)
+    for h in range(3):
+        assert scales[h] == np.float32(np.abs(x[:, h, :]).max() / np.float32(448.0))
+    assert not codes[:, 2, :].any() and scales[2] == 0.0
+    # codes are torch's E4M3 rounding of the fp32 quotient, per head
+    for h in (0, 1):
+        y = (x[:, h, :] / scales[h]).astype(np.float32)
+        assert np.array_equal(codes[:, h, :], torch_encode(np.clip(y, -448, 448)))
+    # queries: one scale per (row, head)
+    qc, sq = O.quantize_heads_e4m3(x[:7])
+    assert sq.shape == (7, 3)
+    for i in range(7):
+        for h in (0, 1):
+            assert sq[i, h] == np.float32(np.abs(x[i, h, :]).max() / np.float32(448.0))
+
+
+def test_attention_fp8_exact_on_the_grid():
+    """Operands on the E4M3 grid with a power-of-two scale per quantisation
+    group (each group reaching 448 * 2^k) are quantised exactly, so the
+    quantised attention equals plain attention on them."""
+    rng = np.random.default_rng(4)
+    pos = O.e4m3_decode(np.arange(1, 0x7F, dtype=np.uint8))
+
+    def grid(shape, groups_axes, k):
+        x = rng.choice(pos, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        # force the maximum 448 once in every group
+        it = np.ndindex(*[shape[a] for a in range(len(shape)) if a not in groups_axes])
+        for idx in it:
+            sl = [slice(None)] * len(shape)
+            j = 0
+            for a in range(len(shape)):
+                if a not in groups_axes:
+                    sl[a] = idx[j]
+                    j += 1
+            g = x[tuple(sl)]
+            g.flat[rng.integers(g.size)] = 448.0
+        return x * 2.0 ** k
+
+    n_q, H, d = 5, 2, 8
+    q = grid((n_q, H, d), (2,), -7)                 # per (row, head)
+    k1, v1 = grid((6, H, d), (0, 2), -6), grid((6, H, d), (0, 2), -3)  # per head over the chunk
+    k2, v2 = grid((9, H, d), (0, 2), -8), grid((9, H, d), (0, 2), -5)
+    o8, l8 = O.attention_fp8(q, [k1, k2], [v1, v2], 0.3)
+    o, l = O.group_attention(q, np.concatenate([k1, k2]), np.concatenate([v1, v2]), 0.3)
+    np.testing.assert_allclose(o8, o, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(l8, l, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_fp8_scales_per_chunk():
+    """The scale is per chunk: a chunk of small values next to a chunk of
+    large ones keeps its own resolution, so the quantised attention stays
+    near the exact one; one shared scale for both chunks would flush the
+    small chunk's values (a pinned difference)."""
+    rng = np.random.default_rng(5)
+    n_q, H, d = 4, 1, 16
+    q = rng.standard_normal((n_q, H, d))
+    k1, k2 = rng.standard_normal((20, H, d)), rng.standard_normal((20, H, d))
+    v1, v2 = 1e-3 * rng.standard_normal((20, H, d)), 1e3 * rng.standard_normal((20, H, d))
+    # queries attend (almost) only to the first chunk
+    k2 = k2 - 10.0 * np.sign(q.mean(axis=0, keepdims=True))
+    o8, _ = O.attention_fp8(q, [k1, k2], [v1, v2], 1.0)
+    o, _ = O.group_attention(q, np.concatenate([k1, k2]), np.concatenate([v1, v2]), 1.0)
+    e_chunk = np.linalg.norm(o8 - o) / np.linalg.norm(o)
+    # one scale shared by both chunks' V
+    vv = np.concatenate([v1, v2])
+    vc, sv = O.quantize_chunk_e4m3(vv)
+    v_shared = O.e4m3_decode(vc) * sv[None, :, None]
+    o_sh, _ = O.attention_fp8(q, [np.concatenate([k1, k2])], [v_shared], 1.0)
+    e_shared = np.linalg.norm(o_sh - o) / np.linalg.norm(o)
+    assert e_chunk < 0.1 and e_shared > 10 * e_chunk, (e_chunk, e_shared)
+
+
+def test_attention_fp8_error_is_the_quantisation():
+    """On Gaussian operands the quantised attention departs from the exact
+    one by the E4M3 step (a few percent), neither zero nor more."""
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((32, 2, 64)) for _ in range(3))
+    o8, l8 = O.attention_fp8(q, [k], [v], 64 ** -0.5)
+    o, l = O.group_attention(q, k, v, 64 ** -0.5)
+    e = np.linalg.norm(o8 - o) / np.linalg.norm(o)
+    assert 1e-3 < e < 8e-2, e
+    assert np.abs(l8 - l).max() < 0.05
