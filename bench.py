@@ -18,7 +18,10 @@ and PV flops, 4 n_q n_k D per chunk, over the time of the fused call), with
 Gram-statistics TFLOP/s and ms per warmup chunk beside it.  The same chunks
 through the two separate calls (ispa_dual_attn, then ispa_lse_merge), and
 through ispa_accum_stats (G, C and r2 every chunk), are timed after the timed
-steps and reported beside it; the roofline entry is the ispa_dual_attn call.
+steps and reported beside it.  The roofline entry is the fused call's single
+kernel (attention of both groups and the merge in one pass per query tile and
+head), priced against the bf16 MFMA peak, with its HBM bytes from the counter
+summary in profiles/ when that was taken on the current attention source.
 
 Other workloads (``--workload``), each one pass of a chunked stream through
 IspaStream, timed per chunk with HIP events around the ISPA calls of all
@@ -78,7 +81,7 @@ def _traffic(kernel_file, src):
             if line.startswith("traffic_bytes_per_launch:"):
                 rec["bytes"] = float(line.split(":", 1)[1])
             if line.startswith("source_sha256_16:"):
-                rec["sha"] = line.split(":", 1)[1].strip()
+                rec["sha"] = line.split(":", 1)[1].split()[0]
     if rec.get("sha") != _src_hash(src) or "bytes" not in rec:
         return None
     return rec["bytes"]
@@ -721,8 +724,8 @@ def main():
     t_stats = mean(rec["stats"]) * 1e-3
     t_direct = mean(rec["stats_direct"]) * 1e-3
     value = attn_flops / t_fused / 1e12
-    achieved = attn_flops / t_attn / 1e12
-    traffic = _traffic("attn_bf16_wan13b_traffic.txt", "attn.hip")
+    achieved = attn_flops / t_fused / 1e12
+    traffic = _traffic("attn_dual_single_pass_wan13b_counters.txt", "attn.hip")
     out = {
         "metric": "dual-stream attn+LSE-merge TFLOP/s",
         "value": round(value, 2),
@@ -760,13 +763,19 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "ispa_dual_attn call (attn_bf16_d128_kernel + history-split combine)"},
+                     "kernel": "ispa_dual_attn_merge (single-pass attn_bf16_d128_kernel: both groups and the merge)"},
         "roofline_other": [
+            {"kernel": "ispa_dual_attn (split pieces + history combine; the two-call path's attention)",
+             "bound": "mfma", "achieved": round(attn_flops / t_attn / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(attn_flops / t_attn / 1e12 / PEAK_BF16_TFLOPS, 4),
+             "traffic": _traffic("attn_split_wan13b_traffic.txt", "attn.hip")},
             {"kernel": "ispa_lse_merge", "bound": "hbm", "achieved": round(merge_bytes / t_merge / 1e9, 1),
-             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_bytes / t_merge / 1e9 / PEAK_HBM_GBS, 4)},
+             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_bytes / t_merge / 1e9 / PEAK_HBM_GBS, 4),
+             "traffic": _traffic("merge_wan13b_traffic.txt", "attn.hip")},
             {"kernel": "ispa_accum_gram (flops performed: 4nD^2 + 2nD)", "bound": "mfma",
              "achieved": round(stats_flops / t_stats / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-             "frac": round(stats_flops / t_stats / 1e12 / PEAK_BF16_TFLOPS, 4)},
+             "frac": round(stats_flops / t_stats / 1e12 / PEAK_BF16_TFLOPS, 4),
+             "traffic": _traffic("syrk_wan13b_counters.txt", "gram.hip")},
         ],
     }
     if not args.no_14b:
