@@ -57,6 +57,8 @@ __all__ = [
     "quantize_weight_e4m3",
     "w8a8_linear",
     "local_attn_proj_w8a8",
+    "pow2_scale",
+    "quantize_rows_e4m3_pow2",
     "quantize_chunk_e4m3",
     "quantize_heads_e4m3",
     "attention_fp8",
@@ -438,9 +440,41 @@ def local_attn_proj_w8a8(q, k, v, w_proj, scale: float):
 # once per cache chunk and head (a chunk's rows are written once and then
 # only read, so they are quantised when written), Q per query row and head;
 # the attention is then the exact softmax attention of the dequantised
-# operands.  Each scale is amax / 448 in fp32 and each code the E4M3 rounding
-# of x / scale, as in quantize_rows_e4m3.
+# operands.  Each scale is a power of two, the smallest 2^e with
+# amax <= 448 * 2^e (the shared-exponent convention of the OCP microscaling
+# formats, whose E8M0 block scales the fp8 matrix core applies itself), so
+# x / scale is exact and each code is the E4M3 rounding of it; a group of
+# zeros takes scale 1 and zero codes.
 # ---------------------------------------------------------------------------
+
+def pow2_scale(amax):
+    """The smallest power of two 2^e with amax <= 448 * 2^e, per element of
+    amax (fp32 magnitudes); 1.0 where amax is 0.  Decided by exact
+    comparisons in fp64 (448 * 2^e and every fp32 value are exact there)."""
+    a = np.asarray(amax, dtype=np.float64)
+    out = np.ones(a.shape, dtype=np.float64)
+    nz = a > 0
+    if nz.any():
+        e = np.ceil(np.log2(a[nz] / E4M3_MAX)).astype(np.int64)
+        # log2 is rounded: step to the exact smallest e
+        e = np.where(a[nz] <= E4M3_MAX * np.ldexp(1.0, e - 1), e - 1, e)
+        e = np.where(a[nz] > E4M3_MAX * np.ldexp(1.0, e), e + 1, e)
+        out[nz] = np.ldexp(1.0, e)
+    return out.astype(np.float32)
+
+
+def quantize_rows_e4m3_pow2(x):
+    """Per-row E4M3 quantisation with power-of-two scales: scale_i =
+    pow2_scale(max_k |x_ik|), code_ik = E4M3(x_ik / scale_i) (the quotient is
+    exact and within +-448).  Returns (codes uint8, scales fp32)."""
+    x32 = np.asarray(as_f64(x), dtype=np.float32)
+    if x32.ndim != 2:
+        raise ValueError("quantize_rows_e4m3_pow2: 2-D input")
+    amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
+    scale = pow2_scale(amax)
+    y = x32.astype(np.float64) / scale.astype(np.float64)[:, None]
+    return e4m3_encode(y), scale
+
 
 def quantize_chunk_e4m3(x):
     """One cache chunk [n, H, d] -> (codes uint8 [n, H, d], scales fp32 [H]):
@@ -448,7 +482,7 @@ def quantize_chunk_e4m3(x):
     x32 = np.asarray(as_f64(x), dtype=np.float32)
     n, H, d = x32.shape
     per_head = x32.transpose(1, 0, 2).reshape(H, n * d)
-    codes, scales = quantize_rows_e4m3(per_head)
+    codes, scales = quantize_rows_e4m3_pow2(per_head)
     return codes.reshape(H, n, d).transpose(1, 0, 2).copy(), scales
 
 
@@ -457,7 +491,7 @@ def quantize_heads_e4m3(q):
     scale per query row and head."""
     q32 = np.asarray(as_f64(q), dtype=np.float32)
     n, H, d = q32.shape
-    codes, scales = quantize_rows_e4m3(q32.reshape(n * H, d))
+    codes, scales = quantize_rows_e4m3_pow2(q32.reshape(n * H, d))
     return codes.reshape(n, H, d), scales.reshape(n, H)
 
 

@@ -168,6 +168,23 @@ def test_local_attn_proj_w8a8_reduces_to_parts():
 
 
 # ---------------------------------------------------------------- quantised attention
+def test_pow2_scale_is_the_smallest_power_of_two():
+    """Brute force over exponents in exact arithmetic: the scale is the least
+    2^e with amax <= 448 * 2^e (the boundary cases 448 * 2^k and the next
+    fp32 value above it included), 1 for a zero group."""
+    from fractions import Fraction
+    rng = np.random.default_rng(2)
+    vals = [np.float32(448.0 * 2.0 ** k) for k in (-20, -3, 0, 5)]
+    vals += [np.nextafter(v, np.float32(np.inf)) for v in vals] + [np.nextafter(v, np.float32(0)) for v in vals]
+    vals += list(rng.lognormal(0, 8, 200).astype(np.float32)) + [np.float32(1e-40), np.float32(3e38)]
+    amax = np.array(vals, dtype=np.float32)
+    got = O.pow2_scale(amax)
+    for a, s in zip(amax, got):
+        e = next(e for e in range(-160, 140) if Fraction(float(a)) <= 448 * Fraction(2) ** e)
+        assert Fraction(float(s)) == Fraction(2) ** e, (a, s, e)
+    assert O.pow2_scale(np.zeros(3, np.float32)).tolist() == [1.0, 1.0, 1.0]
+
+
 def test_quantize_chunk_scales_and_codes():
     rng = np.random.default_rng(3)
     x = rng.standard_normal((50, 3, 16)).astype(np.float32)
@@ -175,19 +192,26 @@ def test_quantize_chunk_scales_and_codes():
     x[:, 2, :] = 0.0         # an all-zero head
     codes, scales = O.quantize_chunk_e4m3(x)
     assert codes.shape == x.shape and scales.shape == (3,)
-    for h in range(3):
-        assert scales[h] == np.float32(np.abs(x[:, h, :]).max() / np.float32(448.0))
-    assert not codes[:, 2, :].any() and scales[2] == 0.0
-    # codes are torch's E4M3 rounding of the fp32 quotient, per head
+    for h in (0, 1):
+        amax = np.abs(x[:, h, :]).max()
+        # a power of two that takes the head's maximum into (224, 448]
+        assert math.frexp(float(scales[h]))[0] == 0.5
+        assert 224.0 < amax / scales[h] <= 448.0
+    assert not codes[:, 2, :].any() and scales[2] == 1.0
+    # codes are torch's E4M3 rounding of the (exact) quotient, per head
     for h in (0, 1):
         y = (x[:, h, :] / scales[h]).astype(np.float32)
-        assert np.array_equal(codes[:, h, :], torch_encode(np.clip(y, -448, 448)))
+        assert np.array_equal(codes[:, h, :], torch_encode(y))
+        assert np.array_equal(y.astype(np.float64) * 1.0, x[:, h, :].astype(np.float64) / float(scales[h]))
     # queries: one scale per (row, head)
     qc, sq = O.quantize_heads_e4m3(x[:7])
     assert sq.shape == (7, 3)
     for i in range(7):
         for h in (0, 1):
-            assert sq[i, h] == np.float32(np.abs(x[i, h, :]).max() / np.float32(448.0))
+            amax = np.abs(x[i, h, :]).max()
+            assert math.frexp(float(sq[i, h]))[0] == 0.5 and 224.0 < amax / sq[i, h] <= 448.0
+            assert np.array_equal(qc[i, h], torch_encode((x[i, h] / sq[i, h]).astype(np.float32)))
+        assert sq[i, 2] == 1.0 and not qc[i, 2].any()
 
 
 def test_attention_fp8_exact_on_the_grid():
