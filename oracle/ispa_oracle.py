@@ -448,9 +448,11 @@ def local_attn_proj_w8a8(q, k, v, w_proj, scale: float):
 # ---------------------------------------------------------------------------
 
 def pow2_scale(amax):
-    """The smallest power of two 2^e with amax <= 448 * 2^e, per element of
-    amax (fp32 magnitudes); 1.0 where amax is 0.  Decided by exact
-    comparisons in fp64 (448 * 2^e and every fp32 value are exact there)."""
+    """The smallest power of two 2^e with amax <= 448 * 2^e and e >= -126
+    (the least normal fp32 power of two, so that every scale is a normal
+    fp32 number), per element of amax (fp32 magnitudes); 1.0 where amax is
+    0.  Decided by exact comparisons in fp64 (448 * 2^e and every fp32 value
+    are exact there)."""
     a = np.asarray(amax, dtype=np.float64)
     out = np.ones(a.shape, dtype=np.float64)
     nz = a > 0
@@ -459,7 +461,7 @@ def pow2_scale(amax):
         # log2 is rounded: step to the exact smallest e
         e = np.where(a[nz] <= E4M3_MAX * np.ldexp(1.0, e - 1), e - 1, e)
         e = np.where(a[nz] > E4M3_MAX * np.ldexp(1.0, e), e + 1, e)
-        out[nz] = np.ldexp(1.0, e)
+        out[nz] = np.ldexp(1.0, np.maximum(e, -126))
     return out.astype(np.float32)
 
 

@@ -170,17 +170,19 @@ def test_local_attn_proj_w8a8_reduces_to_parts():
 # ---------------------------------------------------------------- quantised attention
 def test_pow2_scale_is_the_smallest_power_of_two():
     """Brute force over exponents in exact arithmetic: the scale is the least
-    2^e with amax <= 448 * 2^e (the boundary cases 448 * 2^k and the next
-    fp32 value above it included), 1 for a zero group."""
+    2^e >= 2^-126 with amax <= 448 * 2^e (the boundary cases 448 * 2^k and
+    the fp32 values on either side included, and magnitudes so small that
+    the floor decides), 1 for a zero group."""
     from fractions import Fraction
     rng = np.random.default_rng(2)
     vals = [np.float32(448.0 * 2.0 ** k) for k in (-20, -3, 0, 5)]
     vals += [np.nextafter(v, np.float32(np.inf)) for v in vals] + [np.nextafter(v, np.float32(0)) for v in vals]
-    vals += list(rng.lognormal(0, 8, 200).astype(np.float32)) + [np.float32(1e-40), np.float32(3e38)]
+    vals += list(rng.lognormal(0, 8, 200).astype(np.float32))
+    vals += [np.float32(1e-40), np.float32(2e-38), np.float32(448.0 * 2.0 ** -126), np.float32(3e38)]
     amax = np.array(vals, dtype=np.float32)
     got = O.pow2_scale(amax)
     for a, s in zip(amax, got):
-        e = next(e for e in range(-160, 140) if Fraction(float(a)) <= 448 * Fraction(2) ** e)
+        e = next(e for e in range(-126, 140) if Fraction(float(a)) <= 448 * Fraction(2) ** e)
         assert Fraction(float(s)) == Fraction(2) ** e, (a, s, e)
     assert O.pow2_scale(np.zeros(3, np.float32)).tolist() == [1.0, 1.0, 1.0]
 
