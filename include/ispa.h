@@ -353,6 +353,75 @@ ispa_status ispa_local_attn_proj_fp8(int64_t n_q, int32_t H, int32_t d, float sc
                                      void* y, ispa_dtype y_dt,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Quantised local attention: the post-switch L-Layer's attention on the fp8
+ * matrix core.  The pages report the W8A8 speed-up of ISPA (EN review, Key
+ * Findings, the Figure 7 item; DE summary, section 4) and give no scheme;
+ * the scheme here, our reading: the three operands as OCP FP8 E4M3 codes
+ * with power-of-two scales, K and V once per cache chunk and head (when the
+ * chunk is written), Q per query row and head.  A group's scale is the least
+ * 2^e (e >= -126) with max|x| <= 448 * 2^e (1 for a group of zeros); a code is
+ * the round-to-nearest-even E4M3 value of x / scale (exact division), a
+ * magnitude that rounds to zero stored as 0x00.  The attention is then the
+ * softmax attention of the dequantised operands; the kernel rounds its
+ * probabilities to E4M3 as well (relative step 2^-4) and accumulates in fp32.
+ * Head dimension 128 only.
+ *
+ * fp8 cache of one chunk of n keys: T = ceil(n / 64) tiles per head, each an
+ * 8 KB block of K codes (64 keys x 128) and one of V codes (V transposed,
+ * 128 x 64 key positions), both in the kernel's own row order and swizzle;
+ * keys past n are zero codes.  k_codes and v_codes are each
+ * ispa_kv_fp8_bytes(n, H, 128) bytes, 16-byte aligned; the scales are fp32 [H].
+ *
+ * ispa_quantize_kv_fp8 -- a chunk's K and V ([n, H, 128] rows k_stride /
+ *   v_stride elements apart, dt ISPA_F32, ISPA_BF16 or ISPA_F16; 16-bit rows
+ *   8-byte aligned, fp32 rows 16-byte aligned, strides multiples of 4) into the
+ *   cache format.  Workspace: ispa_quantize_kv_fp8_workspace_bytes.
+ * ispa_quantize_q_fp8 -- queries [n_q, H, 128] (rows q_stride elements apart,
+ *   same dtypes and alignment) -> q_codes uint8 [n_q, H, 128] (4-byte aligned)
+ *   and q_scales fp32 [n_q, H].
+ * ispa_local_attn_fp8 -- for every query row and head, attention over the
+ *   keys of the n_segs (0..ISPA_MAX_SEGS) chunks in order:
+ *     o = sum_j softmax_j(scale <q^, k^_j>) v^_j,  lse = ln sum_j exp(s_j)
+ *   (^ = dequantised).  q_codes 16-byte aligned; scale > 0 and finite;
+ *   o [n_q, H, 128] of o_dt (fp32 16-byte, 16-bit types 8-byte aligned); lse
+ *   fp32 [n_q, H] or NULL.  No keys at all: o = 0, lse = -inf.
+ * ispa_local_attn_fp8_proj -- the post-switch L-Layer output with both stages
+ *   quantised: q (q_dt) quantised as ispa_quantize_q_fp8, ispa_local_attn_fp8
+ *   into an fp32 workspace, then ispa_w8a8_linear of that output with
+ *   (w_codes, w_scales) of [D, D], D = 128 H.  y [n_q, D] of y_dt.
+ */
+#define ISPA_FP8_TILE_KEYS 64
+size_t ispa_kv_fp8_bytes(int64_t n, int32_t H, int32_t d);
+size_t ispa_quantize_kv_fp8_workspace_bytes(int64_t n, int32_t H, int32_t d);
+ispa_status ispa_quantize_kv_fp8(ispa_dtype dt, int64_t n, int32_t H, int32_t d,
+                                 const void* k, int64_t k_stride, const void* v, int64_t v_stride,
+                                 uint8_t* k_codes, uint8_t* v_codes, float* k_scales, float* v_scales,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+ispa_status ispa_quantize_q_fp8(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, const void* q,
+                                int64_t q_stride, uint8_t* q_codes, float* q_scales, hipStream_t stream);
+
+/* One chunk of the fp8 cache as ispa_quantize_kv_fp8 wrote it. */
+typedef struct {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* k_scales;
+  const float* v_scales;
+  int64_t n;
+} ispa_seg_fp8;
+
+ispa_status ispa_local_attn_fp8(int64_t n_q, int32_t H, int32_t d, float scale,
+                                const uint8_t* q_codes, const float* q_scales,
+                                const ispa_seg_fp8* segs, int32_t n_segs,
+                                void* o, ispa_dtype o_dt, float* lse, hipStream_t stream);
+size_t ispa_local_attn_fp8_proj_workspace_bytes(int64_t n_q, int32_t H, int32_t d);
+ispa_status ispa_local_attn_fp8_proj(int64_t n_q, int32_t H, int32_t d, float scale,
+                                     ispa_dtype q_dt, const void* q, int64_t q_stride,
+                                     const ispa_seg_fp8* segs, int32_t n_segs,
+                                     const uint8_t* w_codes, const float* w_scales,
+                                     void* y, ispa_dtype y_dt,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,5 +8,7 @@ from ._lib import (ISPA_BF16, ISPA_F16, ISPA_F32, IspaError, gram_state, ispa_ac
                    ispa_accum_stats, ispa_gram_finalize,
                    ispa_dual_attn, ispa_dual_attn_merge, ispa_local_attn_proj,
                    ispa_local_attn_proj_fp8, ispa_lse_merge, ispa_quantize_w_fp8, ispa_select_layers,
-                   ispa_solve_dw, ispa_w8a8_linear, ispa_w8a8_linear_noalloc, lib)
+                   ispa_solve_dw, ispa_w8a8_linear, ispa_w8a8_linear_noalloc, lib,
+                   Fp8Chunk, ispa_local_attn_fp8, ispa_local_attn_fp8_proj, ispa_quantize_kv_fp8,
+                   ispa_quantize_q_fp8)
 from .stream import Workspace, chunk_segments, kv_bytes  # noqa: F401

@@ -35,7 +35,11 @@ EXPORTED = [
     "ispa_quantize_w_fp8_workspace_bytes", "ispa_quantize_w_fp8",
     "ispa_w8a8_linear_workspace_bytes", "ispa_w8a8_linear", "ispa_w8a8_linear_noalloc",
     "ispa_local_attn_proj_fp8_workspace_bytes", "ispa_local_attn_proj_fp8",
+    "ispa_kv_fp8_bytes", "ispa_quantize_kv_fp8_workspace_bytes", "ispa_quantize_kv_fp8",
+    "ispa_quantize_q_fp8", "ispa_local_attn_fp8",
+    "ispa_local_attn_fp8_proj_workspace_bytes", "ispa_local_attn_fp8_proj",
 ]
+ISPA_FP8_TILE_KEYS = 64
 
 _DT = {torch.float32: ISPA_F32, torch.bfloat16: ISPA_BF16, torch.float16: ISPA_F16}
 _TORCH_DT = {v: k for k, v in _DT.items()}
@@ -52,6 +56,11 @@ class Seg(ctypes.Structure):
                 ("k_stride", ctypes.c_int64), ("v_stride", ctypes.c_int64)]
 
 
+class SegFp8(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -65,6 +74,7 @@ def lib() -> ctypes.CDLL:
         i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
         f32, f64 = ctypes.c_float, ctypes.c_double
         segp = ctypes.POINTER(Seg)
+        seg8p = ctypes.POINTER(SegFp8)
         sig = {
             "ispa_version": (i32, []),
             "ispa_status_str": (ctypes.c_char_p, [i32]),
@@ -97,6 +107,14 @@ def lib() -> ctypes.CDLL:
             "ispa_w8a8_linear_noalloc": (i32, [i32, i64, i32, i32, vp, i64, vp, vp, vp, i32, vp]),
             "ispa_local_attn_proj_fp8_workspace_bytes": (sz, [i64, i32, i32, segp, i32]),
             "ispa_local_attn_proj_fp8": (i32, [i64, i32, i32, f32, vp, i64, segp, i32, vp, vp, vp, i32,
+                                               vp, sz, vp]),
+            "ispa_kv_fp8_bytes": (sz, [i64, i32, i32]),
+            "ispa_quantize_kv_fp8_workspace_bytes": (sz, [i64, i32, i32]),
+            "ispa_quantize_kv_fp8": (i32, [i32, i64, i32, i32, vp, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp]),
+            "ispa_quantize_q_fp8": (i32, [i32, i64, i32, i32, vp, i64, vp, vp, vp]),
+            "ispa_local_attn_fp8": (i32, [i64, i32, i32, f32, vp, vp, seg8p, i32, vp, i32, vp, vp]),
+            "ispa_local_attn_fp8_proj_workspace_bytes": (sz, [i64, i32, i32]),
+            "ispa_local_attn_fp8_proj": (i32, [i64, i32, i32, f32, i32, vp, i64, seg8p, i32, vp, vp, vp, i32,
                                                vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
@@ -419,6 +437,97 @@ def ispa_local_attn_proj_fp8(q, segs, w_codes, w_scales, scale: float | None = N
     wsb = L.ispa_local_attn_proj_fp8_workspace_bytes(n_q, H, d, ss, ns)
     ws = _workspace(wsb, dev)
     _check(L.ispa_local_attn_proj_fp8(n_q, H, d, scale, q.data_ptr(), qs, ss, ns, w_codes.data_ptr(),
+                                      w_scales.data_ptr(), y.data_ptr(), _DT[out_dtype], _ptr(ws), wsb,
+                                      _stream(dev)))
+    return y
+
+
+# ---------------------------------------------------------------- quantised local attention
+class Fp8Chunk:
+    """One chunk of the fp8 key/value cache as ispa_quantize_kv_fp8 wrote it:
+    k_codes and v_codes (uint8, the library's tiled layout), k_scales and
+    v_scales (fp32 [H], powers of two), n keys."""
+
+    def __init__(self, k_codes, v_codes, k_scales, v_scales, n: int, H: int):
+        self.k_codes, self.v_codes, self.k_scales, self.v_scales = k_codes, v_codes, k_scales, v_scales
+        self.n, self.H = int(n), int(H)
+
+
+def ispa_quantize_kv_fp8(k, v) -> Fp8Chunk:
+    """A chunk's k, v ([n, H, 128] with contiguous [H, 128] rows, fp32, bf16
+    or f16) into the fp8 cache format."""
+    n, H, d = k.shape
+    for t in (k, v):
+        if t.dim() != 3 or t.shape != k.shape or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError("k and v must be [n, H, d] with contiguous [H, d] rows")
+    if v.dtype != k.dtype:
+        raise ValueError("k and v must have one dtype")
+    dev = k.device
+    L = lib()
+    nb = L.ispa_kv_fp8_bytes(n, H, d)
+    kc = torch.empty(nb, dtype=torch.uint8, device=dev)
+    vc = torch.empty(nb, dtype=torch.uint8, device=dev)
+    ks = torch.empty(H, dtype=torch.float32, device=dev)
+    vs = torch.empty(H, dtype=torch.float32, device=dev)
+    wsb = L.ispa_quantize_kv_fp8_workspace_bytes(n, H, d)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_quantize_kv_fp8(_DT[k.dtype], n, H, d, k.data_ptr(), k.stride(0), v.data_ptr(), v.stride(0),
+                                  kc.data_ptr(), vc.data_ptr(), ks.data_ptr(), vs.data_ptr(), _ptr(ws), wsb,
+                                  _stream(dev)))
+    return Fp8Chunk(kc, vc, ks, vs, n, H)
+
+
+def ispa_quantize_q_fp8(q):
+    """Queries [n_q, H, 128] -> (codes uint8 [n_q, H, 128], scales fp32 [n_q, H])."""
+    n_q, H, d, qs = _q_args(q)
+    dev = q.device
+    qc = torch.empty((n_q, H, d), dtype=torch.uint8, device=dev)
+    sc = torch.empty((n_q, H), dtype=torch.float32, device=dev)
+    _check(lib().ispa_quantize_q_fp8(_DT[q.dtype], n_q, H, d, q.data_ptr(), qs, qc.data_ptr(), sc.data_ptr(),
+                                     _stream(dev)))
+    return qc, sc
+
+
+def _segs_fp8(chunks):
+    arr = (SegFp8 * max(1, len(chunks)))()
+    for i, c in enumerate(chunks):
+        arr[i] = SegFp8(c.k_codes.data_ptr(), c.v_codes.data_ptr(), c.k_scales.data_ptr(), c.v_scales.data_ptr(),
+                        c.n)
+    return arr, len(chunks)
+
+
+def ispa_local_attn_fp8(q_codes, q_scales, chunks, scale: float | None = None, out_dtype=torch.float32,
+                        want_lse=False):
+    """Attention of the quantised queries over the keys of the fp8 chunks.
+    Returns (o [n_q, H, 128] of out_dtype, lse fp32 [n_q, H] or None)."""
+    n_q, H, d = q_codes.shape
+    if not q_codes.is_contiguous() or not q_scales.is_contiguous() or q_codes.dtype != torch.uint8:
+        raise ValueError("q_codes (uint8) and q_scales must be contiguous")
+    scale = d ** -0.5 if scale is None else scale
+    ss, ns = _segs_fp8(chunks)
+    dev = q_codes.device
+    o = torch.empty((n_q, H, d), dtype=out_dtype, device=dev)
+    lse = torch.empty((n_q, H), dtype=torch.float32, device=dev) if want_lse else None
+    _check(lib().ispa_local_attn_fp8(n_q, H, d, scale, q_codes.data_ptr(), q_scales.data_ptr(), ss, ns,
+                                     o.data_ptr(), _DT[out_dtype], _ptr(lse), _stream(dev)))
+    return o, lse
+
+
+def ispa_local_attn_fp8_proj(q, chunks, w_codes, w_scales, scale: float | None = None, out_dtype=torch.bfloat16):
+    """The post-switch layer output with fp8 attention over the chunks and the
+    W8A8 projection with (w_codes, w_scales) from ispa_quantize_w_fp8.
+    q [n_q, H, 128].  Returns y [n_q, D]."""
+    n_q, H, d, qs = _q_args(q)
+    scale = d ** -0.5 if scale is None else scale
+    ss, ns = _segs_fp8(chunks)
+    dev = q.device
+    if not w_codes.is_contiguous() or not w_scales.is_contiguous():
+        raise ValueError("w_codes and w_scales must be contiguous")
+    y = torch.empty((n_q, H * d), dtype=out_dtype, device=dev)
+    L = lib()
+    wsb = L.ispa_local_attn_fp8_proj_workspace_bytes(n_q, H, d)
+    ws = _workspace(wsb, dev)
+    _check(L.ispa_local_attn_fp8_proj(n_q, H, d, scale, _DT[q.dtype], q.data_ptr(), qs, ss, ns, w_codes.data_ptr(),
                                       w_scales.data_ptr(), y.data_ptr(), _DT[out_dtype], _ptr(ws), wsb,
                                       _stream(dev)))
     return y

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "attn.hpp"
+#include "attn8.hpp"
 #include "gemm.hpp"
 #include "gram.hpp"
 #include "internal.hpp"
@@ -690,6 +691,132 @@ ispa_status ispa_local_attn_proj_fp8(int64_t n_q, int32_t H, int32_t d, float sc
   st = run_group_attention(ISPA_BF16, n_q, H, d, scale, q, q_stride, g, 1, oo, ll, wp,
                            ws_bytes - (size_t)(wp - (char*)ws), stream);
   if (st) return st;
+  if ((st = launch_quant_rows_e4m3(O, ISPA_F32, D, n_q, D, xq, D, sx, stream))) return st;
+  return run_w8a8_gemm(n_q, D, D, xq, sx, w_codes, w_scales, y, y_dt, stream);
+}
+
+// ---------------------------------------------------------------- quantised local attention
+static ispa_status check_rows_in(ispa_dtype dt, const void* x, int64_t stride, int64_t min_stride, bool any,
+                                 const char* what) {
+  if (!valid_dtype(dt)) return fail(ISPA_ERR_UNSUPPORTED, std::string(what) + ": dtype must be F32, BF16 or F16");
+  if (stride < min_stride || stride % 4)
+    return fail(ISPA_ERR_INVALID_ARG, std::string(what) + ": row stride must be >= H*d and a multiple of 4");
+  if (any && !x) return fail(ISPA_ERR_INVALID_ARG, std::string(what) + ": null pointer");
+  if (!aligned(x, dt == ISPA_F32 ? 16 : 8)) return fail(ISPA_ERR_INVALID_ARG, std::string(what) + ": misaligned rows");
+  return ISPA_OK;
+}
+
+size_t ispa_kv_fp8_bytes(int64_t n, int32_t H, int32_t d) {
+  if (n <= 0 || H < 1 || d != kF8D) return 0;
+  return (size_t)H * f8_tiles(n) * kF8TileBytes;
+}
+
+size_t ispa_quantize_kv_fp8_workspace_bytes(int64_t n, int32_t H, int32_t d) {
+  if (d != kF8D) return 0;
+  return quant_kv_ws_bytes(n, H);
+}
+
+ispa_status ispa_quantize_kv_fp8(ispa_dtype dt, int64_t n, int32_t H, int32_t d, const void* k, int64_t k_stride,
+                                 const void* v, int64_t v_stride, uint8_t* k_codes, uint8_t* v_codes,
+                                 float* k_scales, float* v_scales, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (d != kF8D) return fail(ISPA_ERR_UNSUPPORTED, "the fp8 path takes head_dim 128");
+  if (n < 0 || H < 1) return fail(ISPA_ERR_INVALID_ARG, "n must be >= 0 and H >= 1");
+  const int64_t row = (int64_t)H * d;
+  ispa_status st;
+  if ((st = check_rows_in(dt, k, k_stride, row, n > 0, "k"))) return st;
+  if ((st = check_rows_in(dt, v, v_stride, row, n > 0, "v"))) return st;
+  if (n == 0) return ISPA_OK;
+  if (!k_codes || !v_codes || !k_scales || !v_scales)
+    return fail(ISPA_ERR_INVALID_ARG, "null k_codes, v_codes, k_scales or v_scales");
+  if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return fail(ISPA_ERR_INVALID_ARG, "misaligned codes or scales");
+  if (!ws || ws_bytes < quant_kv_ws_bytes(n, H) || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "quantize_kv_fp8 workspace too small or misaligned");
+  return launch_quant_kv_fp8(dt, n, H, k, k_stride, v, v_stride, k_codes, v_codes, k_scales, v_scales, ws, stream);
+}
+
+ispa_status ispa_quantize_q_fp8(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d, const void* q, int64_t q_stride,
+                                uint8_t* q_codes, float* q_scales, hipStream_t stream) {
+  if (d != kF8D) return fail(ISPA_ERR_UNSUPPORTED, "the fp8 path takes head_dim 128");
+  if (n_q < 0 || H < 1) return fail(ISPA_ERR_INVALID_ARG, "n_q must be >= 0 and H >= 1");
+  ispa_status st;
+  if ((st = check_rows_in(dt, q, q_stride, (int64_t)H * d, n_q > 0, "q"))) return st;
+  if (n_q == 0) return ISPA_OK;
+  if (!q_codes || !q_scales) return fail(ISPA_ERR_INVALID_ARG, "null q_codes or q_scales");
+  if (!aligned(q_codes, 4) || !aligned(q_scales, 4)) return fail(ISPA_ERR_INVALID_ARG, "misaligned q_codes or q_scales");
+  return launch_quant_q_fp8(dt, n_q, H, q, q_stride, q_codes, q_scales, stream);
+}
+
+static ispa_status check_attn_fp8(int64_t n_q, int32_t H, int32_t d, float scale, const uint8_t* q_codes,
+                                  const float* q_scales, const ispa_seg_fp8* segs, int32_t n_segs,
+                                  Attn8Seg* out, bool check_q = true) {
+  if (d != kF8D) return fail(ISPA_ERR_UNSUPPORTED, "the fp8 path takes head_dim 128");
+  if (n_q < 0 || H < 1) return fail(ISPA_ERR_INVALID_ARG, "n_q must be >= 0 and H >= 1");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(ISPA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (n_segs < 0 || n_segs > ISPA_MAX_SEGS) return fail(ISPA_ERR_INVALID_ARG, "segment count out of range");
+  if (n_segs > 0 && !segs) return fail(ISPA_ERR_INVALID_ARG, "null segment table");
+  for (int i = 0; i < n_segs; ++i) {
+    const ispa_seg_fp8& s = segs[i];
+    if (s.n < 0) return fail(ISPA_ERR_INVALID_ARG, "negative segment length");
+    if (s.n > 0 && (!s.k_codes || !s.v_codes || !s.k_scales || !s.v_scales))
+      return fail(ISPA_ERR_INVALID_ARG, "null codes or scales in a segment");
+    if (!aligned(s.k_codes, 16) || !aligned(s.v_codes, 16) || !aligned(s.k_scales, 4) || !aligned(s.v_scales, 4))
+      return fail(ISPA_ERR_INVALID_ARG, "misaligned codes or scales in a segment");
+    out[i] = Attn8Seg{s.k_codes, s.v_codes, s.k_scales, s.v_scales, s.n};
+  }
+  if (!check_q) return ISPA_OK;
+  if (n_q > 0 && (!q_codes || !q_scales)) return fail(ISPA_ERR_INVALID_ARG, "null q_codes or q_scales");
+  if (!aligned(q_codes, 16) || !aligned(q_scales, 4)) return fail(ISPA_ERR_INVALID_ARG, "misaligned q_codes or q_scales");
+  return ISPA_OK;
+}
+
+ispa_status ispa_local_attn_fp8(int64_t n_q, int32_t H, int32_t d, float scale, const uint8_t* q_codes,
+                                const float* q_scales, const ispa_seg_fp8* segs, int32_t n_segs, void* o,
+                                ispa_dtype o_dt, float* lse, hipStream_t stream) {
+  Attn8Seg s8[ISPA_MAX_SEGS];
+  ispa_status st = check_attn_fp8(n_q, H, d, scale, q_codes, q_scales, segs, n_segs, s8);
+  if (st) return st;
+  if (!valid_dtype(o_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad o_dt");
+  if (n_q > 0 && !o) return fail(ISPA_ERR_INVALID_ARG, "null o");
+  if (!aligned(o, o_dt == ISPA_F32 ? 16 : 8) || !aligned(lse, 4)) return fail(ISPA_ERR_INVALID_ARG, "misaligned o or lse");
+  if (n_q == 0) return ISPA_OK;
+  return launch_attn_fp8(n_q, H, scale, q_codes, q_scales, s8, n_segs, o, o_dt, lse, stream);
+}
+
+size_t ispa_local_attn_fp8_proj_workspace_bytes(int64_t n_q, int32_t H, int32_t d) {
+  if (n_q <= 0 || H < 1 || d != kF8D) return 0;
+  const size_t D = (size_t)H * d;
+  // Q codes and scales, the fp32 attention output, its codes and row scales
+  return align256((size_t)n_q * D) + align256((size_t)n_q * H * 4) + align256((size_t)n_q * D * 4) +
+         align256((size_t)n_q * D) + align256((size_t)n_q * 4);
+}
+
+ispa_status ispa_local_attn_fp8_proj(int64_t n_q, int32_t H, int32_t d, float scale, ispa_dtype q_dt, const void* q,
+                                     int64_t q_stride, const ispa_seg_fp8* segs, int32_t n_segs,
+                                     const uint8_t* w_codes, const float* w_scales, void* y, ispa_dtype y_dt,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  Attn8Seg s8[ISPA_MAX_SEGS];
+  ispa_status st = check_attn_fp8(n_q, H, d, scale, nullptr, nullptr, segs, n_segs, s8, false);
+  if (st) return st;
+  if ((st = check_rows_in(q_dt, q, q_stride, (int64_t)H * d, n_q > 0, "q"))) return st;
+  const int32_t D = H * d;
+  if ((st = check_w8a8(D, D, w_codes, w_scales, y, y_dt, n_q > 0))) return st;
+  if (n_q == 0) return ISPA_OK;
+  const size_t need = ispa_local_attn_fp8_proj_workspace_bytes(n_q, H, d);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(ISPA_ERR_WORKSPACE, "local_attn_fp8_proj workspace too small or misaligned");
+  char* wp = (char*)ws;
+  uint8_t* qc = (uint8_t*)wp;
+  wp += align256((size_t)n_q * D);
+  float* qsc = (float*)wp;
+  wp += align256((size_t)n_q * H * 4);
+  float* O = (float*)wp;
+  wp += align256((size_t)n_q * D * 4);
+  uint8_t* xq = (uint8_t*)wp;
+  wp += align256((size_t)n_q * D);
+  float* sx = (float*)wp;
+  if ((st = launch_quant_q_fp8(q_dt, n_q, H, q, q_stride, qc, qsc, stream))) return st;
+  if ((st = launch_attn_fp8(n_q, H, scale, qc, qsc, s8, n_segs, O, ISPA_F32, nullptr, stream))) return st;
   if ((st = launch_quant_rows_e4m3(O, ISPA_F32, D, n_q, D, xq, D, sx, stream))) return st;
   return run_w8a8_gemm(n_q, D, D, xq, sx, w_codes, w_scales, y, y_dt, stream);
 }

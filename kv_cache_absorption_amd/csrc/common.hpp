@@ -66,10 +66,13 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, float x, int 
 }
 
 // ---- wave helpers ----------------------------------------------------------
-// Exchange a value with lane l ^ 32 (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) {
+// The larger of the values of lane l and lane l ^ 32, in every lane.  After
+// v_permlane32_swap of a register with a copy of itself, one result holds the
+// lane's own value and the other its partner's (which is which depends on the
+// half), so the maximum of the two results is the pair's maximum.
+__device__ __forceinline__ float pair_max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Map a linear workgroup id so that the workgroups the hardware places on

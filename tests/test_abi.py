@@ -221,3 +221,64 @@ def test_w8a8_noalloc_rejects_bad_args():
     assert call(wc=None) == m.ISPA_ERR_INVALID_ARG
     assert call(y=FAKE + 4) == m.ISPA_ERR_INVALID_ARG      # bf16 y must be 8-byte aligned
     assert call(xdt=7) == m.ISPA_ERR_UNSUPPORTED
+
+
+def test_fp8_attention_calls_reject_bad_args():
+    """The quantised local attention path validates on the host: head_dim 128
+    only, positive finite scale, segment table limits, alignment of codes and
+    scales, workspace size; empty work returns at once."""
+    m, L = _lib()
+    F = FAKE
+    big = 1 << 30
+    assert L.ispa_kv_fp8_bytes(4680, 12, 128) == 12 * 74 * 64 * 128
+    assert L.ispa_kv_fp8_bytes(4680, 12, 64) == 0
+    assert L.ispa_quantize_kv_fp8_workspace_bytes(4680, 12, 128) >= 2 * 12 * 74 * 4
+    # quantize_kv: dtype, head_dim, strides, alignment, workspace
+    kv = lambda **a: L.ispa_quantize_kv_fp8(a.get("dt", m.ISPA_BF16), a.get("n", 100), a.get("H", 2),  # noqa: E731
+                                            a.get("d", 128), a.get("k", F), a.get("ks", 256), F, 256,
+                                            a.get("kc", F), F, F, F, F, a.get("ws", big), None)
+    assert kv(d=64) == m.ISPA_ERR_UNSUPPORTED
+    assert kv(dt=9) == m.ISPA_ERR_UNSUPPORTED
+    assert kv(ks=200) == m.ISPA_ERR_INVALID_ARG      # stride < H * d
+    assert kv(ks=258) == m.ISPA_ERR_INVALID_ARG      # stride not a multiple of 4
+    assert kv(k=F + 2) == m.ISPA_ERR_INVALID_ARG     # 16-bit rows 8-byte aligned
+    assert kv(kc=F + 8) == m.ISPA_ERR_INVALID_ARG    # codes 16-byte aligned
+    assert kv(k=None) == m.ISPA_ERR_INVALID_ARG
+    assert kv(ws=10) == m.ISPA_ERR_WORKSPACE
+    assert kv(n=0, k=None, kc=None) == m.ISPA_OK
+    # quantize_q
+    assert L.ispa_quantize_q_fp8(m.ISPA_BF16, 10, 2, 96, F, 256, F, F, None) == m.ISPA_ERR_UNSUPPORTED
+    assert L.ispa_quantize_q_fp8(m.ISPA_F32, 10, 2, 128, F + 4, 256, F, F, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_quantize_q_fp8(m.ISPA_BF16, 10, 2, 128, F, 256, None, F, None) == m.ISPA_ERR_INVALID_ARG
+    assert L.ispa_quantize_q_fp8(m.ISPA_BF16, 0, 2, 128, None, 256, None, None, None) == m.ISPA_OK
+    # attention
+    arr = (m.SegFp8 * 9)()
+    for i in range(9):
+        arr[i] = m.SegFp8(F, F, F, F, 100)
+
+    def att(n_q=10, d=128, scale=0.1, qc=F, segs=arr, ns=1, o=F, odt=m.ISPA_F32, lse=None):
+        return L.ispa_local_attn_fp8(n_q, 2, d, scale, qc, F, segs, ns, o, odt, lse, None)
+
+    assert att(d=64) == m.ISPA_ERR_UNSUPPORTED
+    assert att(scale=0.0) == m.ISPA_ERR_INVALID_ARG
+    assert att(scale=float("inf")) == m.ISPA_ERR_INVALID_ARG
+    assert att(ns=9) == m.ISPA_ERR_INVALID_ARG
+    assert att(ns=-1) == m.ISPA_ERR_INVALID_ARG
+    assert att(qc=F + 4) == m.ISPA_ERR_INVALID_ARG
+    assert att(o=F + 4) == m.ISPA_ERR_INVALID_ARG
+    assert att(lse=F + 2) == m.ISPA_ERR_INVALID_ARG
+    assert att(odt=7) == m.ISPA_ERR_UNSUPPORTED
+    bad = (m.SegFp8 * 1)()
+    bad[0] = m.SegFp8(F + 8, F, F, F, 100)
+    assert att(segs=bad) == m.ISPA_ERR_INVALID_ARG
+    bad[0] = m.SegFp8(None, F, F, F, 100)
+    assert att(segs=bad) == m.ISPA_ERR_INVALID_ARG
+    bad[0] = m.SegFp8(F, F, F, F, -1)
+    assert att(segs=bad) == m.ISPA_ERR_INVALID_ARG
+    assert att(n_q=0, qc=None, o=None) == m.ISPA_OK
+    # attention + W8A8 projection
+    assert L.ispa_local_attn_fp8_proj_workspace_bytes(4680, 12, 128) >= 4680 * 1536 * 6
+    proj = lambda **a: L.ispa_local_attn_fp8_proj(a.get("n_q", 10), 2, 128, 0.1, m.ISPA_BF16, F, 256, arr, 1,  # noqa: E731
+                                                 a.get("wc", F), F, F, m.ISPA_BF16, F, a.get("ws", big), None)
+    assert proj(wc=None) == m.ISPA_ERR_INVALID_ARG
+    assert proj(ws=10) == m.ISPA_ERR_WORKSPACE
