@@ -34,6 +34,10 @@ layers (the chunk's Q, K, V are generated on the GPU before its events):
   wan14b_post    40 post-switch chunks of the same 40 layers (20 L-Layers on
                  sink + current, 20 F-Layers on up to 187200 keys), with the
                  selection and W + dW of an untimed wan14b_warmup pass
+  wan14b_post_fp8  wan14b_post_w8a8 with the L-Layers' attention quantised
+                 too: sinks to the fp8 cache once at the switch, each current
+                 chunk quantised in its post-switch call, attention on the
+                 fp8 matrix core (F-Layers: bf16 attention, W8A8 projection)
   wan14b_post_w8a8  wan14b_post with the W8A8 projections: W and W + dW
                  quantised once (untimed, at the switch) to FP8 E4M3, the
                  attention output per token, the products on the fp8 matrix core
@@ -55,6 +59,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
 
@@ -163,6 +168,7 @@ STREAMS = {
     "wan14b_warmup": dict(N=40, H=40, d=128, chunks=19, warm=19, K=20, wid=4),
     "wan14b_post": dict(N=40, H=40, d=128, chunks=40, warm=0, K=20, wid=5),
     "wan14b_post_w8a8": dict(N=40, H=40, d=128, chunks=40, warm=0, K=20, wid=5, w8a8=True),
+    "wan14b_post_fp8": dict(N=40, H=40, d=128, chunks=40, warm=0, K=20, wid=5, w8a8=True, fp8attn=True),
     # re-calibration: warmup 0-5, switch, post 6-11, warmup re-entered at 12
     # (12-17), switch again, post 18-23
     "wan13b_recal": dict(N=30, H=12, d=128, chunks=24, warm=6, K=15, wid=3, recal=12, warm2=6),
@@ -199,6 +205,14 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
         st.adopt_switch(is_local, w_eff)
         if spec.get("w8a8"):
             st.quantize_projections()  # once per switch, before the timed chunks
+        if spec.get("fp8attn"):
+            # the L-Layers' sinks to the fp8 cache (once per switch); each later
+            # current chunk is quantised inside the timed post() call
+            for layer, flag in enumerate(is_local):
+                if flag:
+                    k, v = si.kv(layer, 0)
+                    st.write_kv(layer, 0, k, v)
+            st.quantize_local_attention()
     stream = torch.cuda.current_stream(dev)
     qbuf = torch.empty((N, T, H, d), dtype=torch.bfloat16, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -297,6 +311,12 @@ def _preload_kernels(dev):
     _, eps, _, _ = K.ispa_solve_dw(G, C, r2, 0.0, 1e-3, w=w)
     K.ispa_select_layers(eps, 1)
     K.ispa_local_attn_proj(q, [(k, v)], w)
+    c8 = K.ispa_quantize_kv_fp8(k, v)
+    qc8, qs8 = K.ispa_quantize_q_fp8(q)
+    K.ispa_local_attn_fp8(qc8, qs8, [c8])
+    wc, wsc = K.ispa_quantize_w_fp8(w)
+    K.ispa_local_attn_fp8_proj(q, [c8], wc, wsc)
+    K.ispa_local_attn_proj_fp8(q, [(k, v)], wc, wsc)
     torch.cuda.synchronize()
 
 
@@ -318,7 +338,8 @@ def _pass_figures(recs, spec):
 
 def wan14b_figures(seed, dev):
     """One Wan-14B warmup pass (40 layers x 40 heads, 19 warmup chunks, switch
-    with K = 20) and one 40-chunk post-switch pass with its selection, each
+    with K = 20) and two 40-chunk post-switch passes with its selection (bf16,
+    and quantised: fp8 attention for the L-Layers and W8A8 projections), each
     timed per chunk with HIP events around the ISPA calls."""
     import torch
     _preload_kernels(dev)
@@ -335,8 +356,14 @@ def wan14b_figures(seed, dev):
     full = 2 * STREAMS["wan14b_post"]["N"] * (last["c"] + 1) * TOKENS_PER_CHUNK * 5120 * 2
     out["wan14b_post"] = {**_pass_figures(recs_p, STREAMS["wan14b_post"]),
                           "kv_held_fraction_last_chunk": round(last["kv_held"] / full, 4)}
-    out["wan14b wall s (both passes, input generation included)"] = round(time.perf_counter() - t0, 1)
-    del st4, st5
+    del st5
+    torch.cuda.empty_cache()
+    recs_8, _, st6, _ = _stream_pass(STREAMS["wan14b_post_fp8"], dev, seed, adopt)
+    out["wan14b_post_fp8"] = {**_pass_figures(recs_8, STREAMS["wan14b_post_fp8"]),
+                              "note": "L-Layers: current chunk to the fp8 cache, fp8 attention, W8A8 projection; "
+                                      "F-Layers: bf16 attention, W8A8 projection; flops counted as for wan14b_post"}
+    out["wan14b wall s (three passes, input generation included)"] = round(time.perf_counter() - t0, 1)
+    del st4, st6
     torch.cuda.empty_cache()
     return out
 
@@ -349,7 +376,7 @@ def run_stream(args, name, dev):
     D = H * d
     adopt = None
     pre = {}
-    if name in ("wan14b_post", "wan14b_post_w8a8"):
+    if name in ("wan14b_post", "wan14b_post_w8a8", "wan14b_post_fp8"):
         t0 = time.perf_counter()
         _, pre_switch_ms, st4, _ = _stream_pass(STREAMS["wan14b_warmup"], dev, args.seed)
         adopt = (list(st4.is_local_host), st4.W, st4.w_eff)
@@ -505,6 +532,9 @@ def main():
                     help="only run this many fused dual-attention + merge calls of the workload (counter runs)")
     ap.add_argument("--gram-only", type=int, default=0,
                     help="only run this many statistics updates (ispa_accum_gram) of the workload (counter runs)")
+    ap.add_argument("--attn8-only", type=int, default=0,
+                    help="only run this many fp8 local-attention calls (post-switch L-Layer) of the workload "
+                         "(counter runs)")
     ap.add_argument("--merge-only", type=int, default=0,
                     help="only run this many two-part LSE merges of the workload (counter runs)")
     ap.add_argument("--proj-compare", type=int, default=0,
@@ -622,6 +652,20 @@ def main():
         print(json.dumps({"fused_only_calls": args.fused_only, "gram_only_calls": args.gram_only,
                           "merge_only_calls": args.merge_only}))
         return
+    if args.attn8_only:
+        sink8 = K.ispa_quantize_kv_fp8(g.sink_k, g.sink_v)
+        cur8 = K.ispa_quantize_kv_fp8(k_post, v_post)
+        qc8, qs8 = K.ispa_quantize_q_fp8(q_post)
+        o8 = torch.empty((n_q, H, d), dtype=torch.float32, device=dev)
+        segs8, ns8 = B._segs_fp8([sink8, cur8])
+        for _ in range(args.attn8_only):
+            st = L.ispa_local_attn_fp8(n_q, H, d, scale, qc8.data_ptr(), qs8.data_ptr(), segs8, ns8, o8.data_ptr(),
+                                       B.ISPA_F32, None, sh)
+            if st:
+                raise B.IspaError(st, L.ispa_last_error().decode())
+        torch.cuda.synchronize()
+        print(json.dumps({"attn8_only_calls": args.attn8_only}))
+        return
     if args.attn_only:
         q, ls, nl, hs, nh = seg_tables[0]
         for _ in range(args.attn_only):
@@ -699,7 +743,38 @@ def main():
                               g.w.data_ptr(), G2.data_ptr(), C2.data_ptr(), r22.data_ptr(), wsp, wsn, sh))
         e3.record(stream)
         two_call.append((e0, e1, e2, e3))
+    # the post-switch chunk with the L-Layer's attention quantised: the sink in
+    # the fp8 cache and W + dW's codes once per switch (untimed), then per call
+    # the current chunk's quantisation and ispa_local_attn_fp8_proj; and the
+    # fp8 attention kernel alone on quantised queries
+    wq, wqs = K.ispa_quantize_w_fp8(w_eff)
+    sink8 = K.ispa_quantize_kv_fp8(g.sink_k, g.sink_v)
+    cur8 = K.ispa_quantize_kv_fp8(k_post, v_post)
+    qc8, qs8 = K.ispa_quantize_q_fp8(q_post)
+    o8 = torch.empty((n_q, H, d), **f32)
+    segs8, ns8 = B._segs_fp8([sink8, cur8])
+    ws8_b = max(L.ispa_local_attn_fp8_proj_workspace_bytes(n_q, H, d), L.ispa_quantize_kv_fp8_workspace_bytes(n_q, H, d))
+    ws8 = torch.empty(ws8_b, dtype=torch.uint8, device=dev)
+    kv8_b = L.ispa_quantize_kv_fp8_workspace_bytes(n_q, H, d)
+    fp8_marks = []
+    for _ in range(args.steps):
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record(stream)
+        ck(L.ispa_quantize_kv_fp8(B.ISPA_BF16, n_q, H, d, k_post.data_ptr(), k_post.stride(0), v_post.data_ptr(),
+                                  v_post.stride(0), cur8.k_codes.data_ptr(), cur8.v_codes.data_ptr(),
+                                  cur8.k_scales.data_ptr(), cur8.v_scales.data_ptr(), ws8.data_ptr(), kv8_b, sh))
+        ck(L.ispa_local_attn_fp8_proj(n_q, H, d, scale, B.ISPA_BF16, q_post.data_ptr(), q_post.stride(0), segs8, ns8,
+                                      wq.data_ptr(), wqs.data_ptr(), y_post.data_ptr(), B.ISPA_BF16, ws8.data_ptr(),
+                                      ws8_b, sh))
+        e1.record(stream)
+        e2.record(stream)
+        ck(L.ispa_local_attn_fp8(n_q, H, d, scale, qc8.data_ptr(), qs8.data_ptr(), segs8, ns8, o8.data_ptr(),
+                                 B.ISPA_F32, None, sh))
+        e3.record(stream)
+        fp8_marks.append((e0, e1, e2, e3))
     torch.cuda.synchronize()
+    rec["post_fp8"] = [e0.elapsed_time(e1) for e0, e1, _, _ in fp8_marks]
+    rec["attn8"] = [e2.elapsed_time(e3) for _, _, e2, e3 in fp8_marks]
     for e0, e1, e2, e3 in two_call:
         rec["attn"].append(e0.elapsed_time(e1))
         rec["merge"].append(e1.elapsed_time(e2))
@@ -718,6 +793,8 @@ def main():
     stats_flops = 4.0 * n_q * D * D + 2.0 * n_q * D   # G and H as triangles, M = A_loc^T dA
     direct_flops = 5.0 * n_q * D * D + 3.0 * n_q * D  # R = dA W, C = A_loc^T R, G as a triangle, ||R||^2
     merge_bytes = 2 * (4 * n_q * D + 4 * n_q * H) + 2 * 2 * n_q * D
+    attn8_flops = 4.0 * n_q * n_loc * D
+    t_attn8 = mean(rec["attn8"]) * 1e-3
     t_fused = mean(rec["fused"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
     t_merge = mean(rec["merge"]) * 1e-3
@@ -755,6 +832,9 @@ def main():
             "merge GB/s": round(merge_bytes / t_merge / 1e9, 1),
             "switch ms (finalize statistics + solve + select)": round(mean(rec["switch"]), 4),
             "post-switch chunk ms (local attn + W+dW)": round(mean(rec["post"]), 4),
+            "post-switch chunk ms, quantised (current chunk to fp8, fp8 attention, W8A8 projection)":
+                round(mean(rec["post_fp8"]), 4),
+            "fp8 local attention call ms (sink + current, 9360 keys)": round(mean(rec["attn8"]), 4),
             "dual_attn call ms": round(t_attn * 1e3, 4),
             "merge call ms": round(t_merge * 1e3, 4),
             "accum_gram call ms": round(t_stats * 1e3, 4),
@@ -769,6 +849,10 @@ def main():
              "bound": "mfma", "achieved": round(attn_flops / t_attn / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
              "unit": "TFLOP/s", "frac": round(attn_flops / t_attn / 1e12 / PEAK_BF16_TFLOPS, 4),
              "traffic": _traffic("attn_split_wan13b_traffic.txt", "attn.hip")},
+            {"kernel": "ispa_local_attn_fp8 (attn_fp8_d128_kernel, post-switch L-Layer: 4680 queries x 9360 keys)",
+             "bound": "mfma", "achieved": round(attn8_flops / t_attn8 / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(attn8_flops / t_attn8 / 1e12 / PEAK_FP8_TFLOPS, 4),
+             "traffic": _traffic("attn_fp8_wan13b_traffic.txt", "attn8.hip")},
             {"kernel": "ispa_lse_merge", "bound": "hbm", "achieved": round(merge_bytes / t_merge / 1e9, 1),
              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_bytes / t_merge / 1e9 / PEAK_HBM_GBS, 4),
              "traffic": _traffic("merge_wan13b_traffic.txt", "attn.hip")},

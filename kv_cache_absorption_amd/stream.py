@@ -230,6 +230,8 @@ class IspaStream:
         self.switched = False
         self.dW = self.eps = self.info = self.w_eff = None
         self.wq = self.wq_scale = None  # W8A8 projection codes and scales, when quantised
+        self.sink8 = None  # fp8 caches of the L-Layers' sinks, when their attention is quantised
+        self.cur8 = None   # fp8 cache buffers of the current chunk (reused for every layer)
         self.selected = self.is_local = self.status = None
         self.is_local_host = None
         self.warmups = 1  # warmup phases entered (re-calibration adds one)
@@ -433,6 +435,43 @@ class IspaStream:
             self._ck(L.ispa_quantize_w_fp8(B.ISPA_BF16, D, D, w.data_ptr(), self.wq[layer].data_ptr(),
                                            self.wq_scale[layer].data_ptr(), ws.data_ptr(), need, s))
 
+    def quantize_local_attention(self):
+        """Quantised attention for the L-Layers after the switch: each
+        L-Layer's sink chunk is quantised once here to the fp8 cache format
+        (E4M3 codes, a power-of-two scale per chunk and head), each later
+        current chunk in :meth:`post`; their attention then runs on the fp8
+        matrix core and feeds the W8A8 projection (ispa_local_attn_fp8_proj).
+        F-Layers keep bf16 attention over all their keys.  Needs
+        :meth:`quantize_projections` first and the L-Layers' sinks written
+        (chunk 0); a re-calibration drops the caches."""
+        if self.wq is None:
+            raise RuntimeError("quantize the projections first")
+        L, s, T, H, d = self.L, self._stream(), self.T, self.H, self.d
+        nb = L.ispa_kv_fp8_bytes(T, H, d)
+        need = L.ispa_quantize_kv_fp8_workspace_bytes(T, H, d)
+        dev = self.device
+
+        def chunk_bufs():
+            return B.Fp8Chunk(torch.empty(nb, dtype=torch.uint8, device=dev),
+                              torch.empty(nb, dtype=torch.uint8, device=dev),
+                              torch.empty(H, dtype=torch.float32, device=dev),
+                              torch.empty(H, dtype=torch.float32, device=dev), T, H)
+
+        self.sink8 = {}
+        for layer, flag in enumerate(self.is_local_host):
+            if flag:
+                k, v = self.kv[layer]._rows(0, 1)
+                self.sink8[layer] = chunk_bufs()
+                self._quantize_chunk(k, v, self.sink8[layer], need, s)
+        self.cur8 = chunk_bufs()
+
+    def _quantize_chunk(self, k, v, c8, need, s):
+        ws = self.ws.get(need)
+        self._ck(self.L.ispa_quantize_kv_fp8(B.ISPA_BF16, self.T, self.H, self.d, k.data_ptr(), k.stride(0),
+                                             v.data_ptr(), v.stride(0), c8.k_codes.data_ptr(),
+                                             c8.v_codes.data_ptr(), c8.k_scales.data_ptr(),
+                                             c8.v_scales.data_ptr(), ws.data_ptr(), need, s))
+
     def recalibrate(self, c: int):
         """Re-enter warmup at chunk c (after a scene change, which the caller
         detects; EN review, Limitations: warmup is re-entered to refresh the
@@ -464,6 +503,7 @@ class IspaStream:
         self.switched = False
         self.selected = self.is_local = self.status = None
         self.wq = self.wq_scale = None
+        self.sink8 = self.cur8 = None
         self.warmups += 1
 
     # ------------------------------------------------------------------ post-switch
@@ -475,6 +515,21 @@ class IspaStream:
             raise RuntimeError("post-switch call before the switch")
         L, s = self.L, self._stream()
         local = bool(self.is_local_host[layer])
+        if local and self.sink8 is not None:  # fp8 attention over sink + current, W8A8 projection
+            chunks8 = [self.sink8[layer]]
+            if self.kv[layer].slot(c) == 1:  # a current chunk besides the sink
+                k, v = self.kv[layer]._rows(1, 2)
+                self._quantize_chunk(k, v, self.cur8, L.ispa_quantize_kv_fp8_workspace_bytes(self.T, self.H, self.d),
+                                     s)
+                chunks8.append(self.cur8)
+            segs8, ns8 = B._segs_fp8(chunks8)
+            need = L.ispa_local_attn_fp8_proj_workspace_bytes(self.T, self.H, self.d)
+            ws = self.ws.get(need)
+            self._ck(L.ispa_local_attn_fp8_proj(self.T, self.H, self.d, self.scale, B.ISPA_BF16, q.data_ptr(),
+                                                q.stride(0), segs8, ns8, self.wq[layer].data_ptr(),
+                                                self.wq_scale[layer].data_ptr(), self.y.data_ptr(), B.ISPA_BF16,
+                                                ws.data_ptr(), need, s))
+            return self.y
         segs, ns = self._segs(self.kv[layer].attend_all(c))
         if self.wq is not None:  # W8A8 projection
             need = L.ispa_local_attn_proj_fp8_workspace_bytes(self.T, self.H, self.d, segs, ns)

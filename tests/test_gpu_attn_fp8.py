@@ -287,3 +287,41 @@ def test_local_attn_fp8_proj_matches_its_parts():
     y2 = k8.ispa_w8a8_linear(o.reshape(n_q, D), wc, ws, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+
+
+def test_stream_post_uses_fp8_attention_for_l_layers():
+    """IspaStream after quantize_local_attention: an L-Layer's post-switch
+    output equals, bit for bit, ispa_local_attn_fp8_proj over its sink and
+    current chunk with its W + dW codes; an F-Layer keeps bf16 attention with
+    the W8A8 projection (ispa_local_attn_proj_fp8 over all its keys)."""
+    from kv_cache_absorption_amd.stream import IspaStream
+    k8 = K()
+    H, d, T, N = 4, 128, 300, 2
+    D = H * d
+    print(f"stream fp8 post H={H} T={T}", flush=True)
+    st = IspaStream(N, H, d, T, [2, 4], DEV, with_stats=False)
+    W = synth.normal((N, D, D), 350, DEV, std=D ** -0.5, dtype=torch.bfloat16)
+    w_eff = W + synth.normal((N, D, D), 351, DEV, std=1e-3, dtype=torch.bfloat16)
+    st.W = W
+    kv = {c: (synth.normal((T, H, d), 360 + c, DEV, dtype=torch.bfloat16),
+              synth.normal((T, H, d), 370 + c, DEV, dtype=torch.bfloat16)) for c in range(4)}
+    st.adopt_switch([1, 0], w_eff)
+    for layer in range(N):
+        for c in range(3):
+            if layer == 1 or c == 0:
+                st.write_kv(layer, c, *kv[c])
+    st.quantize_projections()
+    st.quantize_local_attention()
+    q = synth.normal((T, H, d), 380, DEV, dtype=torch.bfloat16)
+    for layer in range(N):
+        st.write_kv(layer, 3, *kv[3])
+    y0 = st.post(0, 3, q).clone()
+    y1 = st.post(1, 3, q).clone()
+    chunks = [k8.ispa_quantize_kv_fp8(*kv[0]), k8.ispa_quantize_kv_fp8(*kv[3])]
+    ref0 = k8.ispa_local_attn_fp8_proj(q, chunks, st.wq[0], st.wq_scale[0], out_dtype=torch.bfloat16)
+    ref1 = k8.ispa_local_attn_proj_fp8(q, [(torch.cat([kv[c][0] for c in range(4)]),
+                                            torch.cat([kv[c][1] for c in range(4)]))],
+                                       st.wq[1], st.wq_scale[1], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, ref0)
+    assert torch.equal(y1, ref1)
