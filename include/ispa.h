@@ -381,7 +381,7 @@ ispa_status ispa_local_attn_proj_fp8(int64_t n_q, int32_t H, int32_t d, float sc
  *   same dtypes and alignment) -> q_codes uint8 [n_q, H, 128] (4-byte aligned)
  *   and q_scales fp32 [n_q, H].
  * ispa_local_attn_fp8 -- for every query row and head, attention over the
- *   keys of the n_segs (0..ISPA_MAX_SEGS) chunks in order:
+ *   keys of the n_segs (0..ISPA_MAX_SEGS_FP8) chunks in order:
  *     o = sum_j softmax_j(scale <q^, k^_j>) v^_j,  lse = ln sum_j exp(s_j)
  *   (^ = dequantised).  q_codes 16-byte aligned; scale > 0 and finite;
  *   o [n_q, H, 128] of o_dt (fp32 16-byte, 16-bit types 8-byte aligned); lse
@@ -392,6 +392,8 @@ ispa_status ispa_local_attn_proj_fp8(int64_t n_q, int32_t H, int32_t d, float sc
  *   (w_codes, w_scales) of [D, D], D = 128 H.  y [n_q, D] of y_dt.
  */
 #define ISPA_FP8_TILE_KEYS 64
+/* Maximum chunks (segments) in one quantised attention call. */
+#define ISPA_MAX_SEGS_FP8 64
 size_t ispa_kv_fp8_bytes(int64_t n, int32_t H, int32_t d);
 size_t ispa_quantize_kv_fp8_workspace_bytes(int64_t n, int32_t H, int32_t d);
 ispa_status ispa_quantize_kv_fp8(ispa_dtype dt, int64_t n, int32_t H, int32_t d,

@@ -40,6 +40,7 @@ EXPORTED = [
     "ispa_local_attn_fp8_proj_workspace_bytes", "ispa_local_attn_fp8_proj",
 ]
 ISPA_FP8_TILE_KEYS = 64
+ISPA_MAX_SEGS_FP8 = 64
 
 _DT = {torch.float32: ISPA_F32, torch.bfloat16: ISPA_BF16, torch.float16: ISPA_F16}
 _TORCH_DT = {v: k for k, v in _DT.items()}
@@ -489,6 +490,8 @@ def ispa_quantize_q_fp8(q):
 
 
 def _segs_fp8(chunks):
+    if len(chunks) > ISPA_MAX_SEGS_FP8:
+        raise ValueError(f"at most {ISPA_MAX_SEGS_FP8} chunks")
     arr = (SegFp8 * max(1, len(chunks)))()
     for i, c in enumerate(chunks):
         arr[i] = SegFp8(c.k_codes.data_ptr(), c.v_codes.data_ptr(), c.k_scales.data_ptr(), c.v_scales.data_ptr(),

@@ -753,7 +753,7 @@ static ispa_status check_attn_fp8(int64_t n_q, int32_t H, int32_t d, float scale
   if (d != kF8D) return fail(ISPA_ERR_UNSUPPORTED, "the fp8 path takes head_dim 128");
   if (n_q < 0 || H < 1) return fail(ISPA_ERR_INVALID_ARG, "n_q must be >= 0 and H >= 1");
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(ISPA_ERR_INVALID_ARG, "scale must be positive and finite");
-  if (n_segs < 0 || n_segs > ISPA_MAX_SEGS) return fail(ISPA_ERR_INVALID_ARG, "segment count out of range");
+  if (n_segs < 0 || n_segs > ISPA_MAX_SEGS_FP8) return fail(ISPA_ERR_INVALID_ARG, "segment count out of range");
   if (n_segs > 0 && !segs) return fail(ISPA_ERR_INVALID_ARG, "null segment table");
   for (int i = 0; i < n_segs; ++i) {
     const ispa_seg_fp8& s = segs[i];
@@ -773,7 +773,7 @@ static ispa_status check_attn_fp8(int64_t n_q, int32_t H, int32_t d, float scale
 ispa_status ispa_local_attn_fp8(int64_t n_q, int32_t H, int32_t d, float scale, const uint8_t* q_codes,
                                 const float* q_scales, const ispa_seg_fp8* segs, int32_t n_segs, void* o,
                                 ispa_dtype o_dt, float* lse, hipStream_t stream) {
-  Attn8Seg s8[ISPA_MAX_SEGS];
+  Attn8Seg s8[ISPA_MAX_SEGS_FP8];
   ispa_status st = check_attn_fp8(n_q, H, d, scale, q_codes, q_scales, segs, n_segs, s8);
   if (st) return st;
   if (!valid_dtype(o_dt)) return fail(ISPA_ERR_UNSUPPORTED, "bad o_dt");
@@ -795,7 +795,7 @@ ispa_status ispa_local_attn_fp8_proj(int64_t n_q, int32_t H, int32_t d, float sc
                                      int64_t q_stride, const ispa_seg_fp8* segs, int32_t n_segs,
                                      const uint8_t* w_codes, const float* w_scales, void* y, ispa_dtype y_dt,
                                      void* ws, size_t ws_bytes, hipStream_t stream) {
-  Attn8Seg s8[ISPA_MAX_SEGS];
+  Attn8Seg s8[ISPA_MAX_SEGS_FP8];
   ispa_status st = check_attn_fp8(n_q, H, d, scale, nullptr, nullptr, segs, n_segs, s8, false);
   if (st) return st;
   if ((st = check_rows_in(q_dt, q, q_stride, (int64_t)H * d, n_q > 0, "q"))) return st;

@@ -314,23 +314,13 @@ __global__ __launch_bounds__(f8::WAVES * 64, 1) void attn_fp8_d128_kernel(const 
     qf[0] = cat8(a[0], a[1]);
     qf[1] = cat8(a[2], a[3]);
   }
-  // the segments' block-scale bytes for this head, four to a register
-  uint32_t ek_lo = 0u, ek_hi = 0u, ev_lo = 0u, ev_hi = 0u;
-  for (int s = 0; s < p.n_segs; ++s) {
-    const uint32_t ek = (uint32_t)e8m0_of(p.ks[s][head]) << (8 * (s & 3));
-    const uint32_t ev = (uint32_t)e8m0_of(p.vs[s][head]) << (8 * (s & 3));
-    if (s < 4) {
-      ek_lo |= ek;
-      ev_lo |= ev;
-    } else {
-      ek_hi |= ek;
-      ev_hi |= ev;
-    }
+  // the segments' block-scale bytes for this head, in LDS (read on segment changes)
+  __shared__ uint8_t e8tab[2][kF8MaxSegs];
+  if (tid < p.n_segs) {
+    e8tab[0][tid] = (uint8_t)e8m0_of(p.ks[tid][head]);
+    e8tab[1][tid] = (uint8_t)e8m0_of(p.vs[tid][head]);
   }
-  ek_lo = __builtin_amdgcn_readfirstlane(ek_lo);
-  ek_hi = __builtin_amdgcn_readfirstlane(ek_hi);
-  ev_lo = __builtin_amdgcn_readfirstlane(ev_lo);
-  ev_hi = __builtin_amdgcn_readfirstlane(ev_hi);
+  __syncthreads();
 
   // Cursors over the tiles in order (every segment has at least one tile: the
   // host drops empty ones).  A load cursor holds its tile's address; past the
@@ -369,9 +359,8 @@ __global__ __launch_bounds__(f8::WAVES * 64, 1) void attn_fp8_d128_kernel(const 
     if (cu.live) {
       cu.left = p.tiles[s];
       cu.nlast = p.nlast[s];
-      const int sh = 8 * (s & 3);
-      cu.ek = (int)(((s < 4 ? ek_lo : ek_hi) >> sh) & 0xffu);
-      cu.ev = (int)(((s < 4 ? ev_lo : ev_hi) >> sh) & 0xffu);
+      cu.ek = __builtin_amdgcn_readfirstlane((int)e8tab[0][s]);
+      cu.ev = __builtin_amdgcn_readfirstlane((int)e8tab[1][s]);
     } else {
       cu.left = 1 << 30;
       cu.nlast = 0;

@@ -9,7 +9,7 @@ namespace ispa {
 constexpr int kF8Keys = 64;                   // keys per cache tile
 constexpr int kF8D = 128;                     // head dimension of the fp8 path
 constexpr int kF8TileBytes = kF8Keys * kF8D;  // 8 KB: one K tile or one V^T tile
-constexpr int kF8MaxSegs = ISPA_MAX_SEGS;
+constexpr int kF8MaxSegs = ISPA_MAX_SEGS_FP8;
 
 inline int64_t f8_tiles(int64_t n) { return (n + kF8Keys - 1) / kF8Keys; }
 

@@ -232,6 +232,7 @@ class IspaStream:
         self.wq = self.wq_scale = None  # W8A8 projection codes and scales, when quantised
         self.sink8 = None  # fp8 caches of the L-Layers' sinks, when their attention is quantised
         self.cur8 = None   # fp8 cache buffers of the current chunk (reused for every layer)
+        self.f8 = None     # per F-Layer, the fp8 caches of its chunks (slot order), when quantised
         self.selected = self.is_local = self.status = None
         self.is_local_host = None
         self.warmups = 1  # warmup phases entered (re-calibration adds one)
@@ -435,35 +436,43 @@ class IspaStream:
             self._ck(L.ispa_quantize_w_fp8(B.ISPA_BF16, D, D, w.data_ptr(), self.wq[layer].data_ptr(),
                                            self.wq_scale[layer].data_ptr(), ws.data_ptr(), need, s))
 
-    def quantize_local_attention(self):
-        """Quantised attention for the L-Layers after the switch: each
-        L-Layer's sink chunk is quantised once here to the fp8 cache format
-        (E4M3 codes, a power-of-two scale per chunk and head), each later
-        current chunk in :meth:`post`; their attention then runs on the fp8
-        matrix core and feeds the W8A8 projection (ispa_local_attn_fp8_proj).
-        F-Layers keep bf16 attention over all their keys.  Needs
-        :meth:`quantize_projections` first and the L-Layers' sinks written
-        (chunk 0); a re-calibration drops the caches."""
+    def quantize_attention(self, f_layers: bool = True):
+        """Quantised post-switch attention (fp8 cache, E4M3 codes with a
+        power-of-two scale per chunk and head; the attention on the fp8
+        matrix core, then the W8A8 projection, ispa_local_attn_fp8_proj).
+
+        L-Layers: each sink is quantised once here, each later current chunk
+        in :meth:`post`.  F-Layers (when ``f_layers``): every chunk the layer
+        holds is quantised once, the chunks held now at their first
+        :meth:`post`, each later chunk at the post() of its own step, and the
+        layer attends over all of them (at most ISPA_MAX_SEGS_FP8 chunks).
+        Needs :meth:`quantize_projections` first and the L-Layers' sinks
+        written (chunk 0); a re-calibration drops the caches."""
         if self.wq is None:
             raise RuntimeError("quantize the projections first")
-        L, s, T, H, d = self.L, self._stream(), self.T, self.H, self.d
-        nb = L.ispa_kv_fp8_bytes(T, H, d)
-        need = L.ispa_quantize_kv_fp8_workspace_bytes(T, H, d)
-        dev = self.device
-
-        def chunk_bufs():
-            return B.Fp8Chunk(torch.empty(nb, dtype=torch.uint8, device=dev),
-                              torch.empty(nb, dtype=torch.uint8, device=dev),
-                              torch.empty(H, dtype=torch.float32, device=dev),
-                              torch.empty(H, dtype=torch.float32, device=dev), T, H)
-
+        s = self._stream()
+        need = self.L.ispa_quantize_kv_fp8_workspace_bytes(self.T, self.H, self.d)
         self.sink8 = {}
         for layer, flag in enumerate(self.is_local_host):
             if flag:
                 k, v = self.kv[layer]._rows(0, 1)
-                self.sink8[layer] = chunk_bufs()
+                self.sink8[layer] = self._chunk_bufs()
                 self._quantize_chunk(k, v, self.sink8[layer], need, s)
-        self.cur8 = chunk_bufs()
+        self.cur8 = self._chunk_bufs()
+        self.f8 = {layer: [] for layer, flag in enumerate(self.is_local_host) if not flag} if f_layers else None
+
+    def quantize_local_attention(self):
+        """:meth:`quantize_attention` for the L-Layers only (F-Layers keep
+        bf16 attention with the W8A8 projection)."""
+        self.quantize_attention(f_layers=False)
+
+    def _chunk_bufs(self):
+        L, T, H, d, dev = self.L, self.T, self.H, self.d, self.device
+        nb = L.ispa_kv_fp8_bytes(T, H, d)
+        return B.Fp8Chunk(torch.empty(nb, dtype=torch.uint8, device=dev),
+                          torch.empty(nb, dtype=torch.uint8, device=dev),
+                          torch.empty(H, dtype=torch.float32, device=dev),
+                          torch.empty(H, dtype=torch.float32, device=dev), T, H)
 
     def _quantize_chunk(self, k, v, c8, need, s):
         ws = self.ws.get(need)
@@ -503,7 +512,7 @@ class IspaStream:
         self.switched = False
         self.selected = self.is_local = self.status = None
         self.wq = self.wq_scale = None
-        self.sink8 = self.cur8 = None
+        self.sink8 = self.cur8 = self.f8 = None
         self.warmups += 1
 
     # ------------------------------------------------------------------ post-switch
@@ -523,6 +532,25 @@ class IspaStream:
                                      s)
                 chunks8.append(self.cur8)
             segs8, ns8 = B._segs_fp8(chunks8)
+            need = L.ispa_local_attn_fp8_proj_workspace_bytes(self.T, self.H, self.d)
+            ws = self.ws.get(need)
+            self._ck(L.ispa_local_attn_fp8_proj(self.T, self.H, self.d, self.scale, B.ISPA_BF16, q.data_ptr(),
+                                                q.stride(0), segs8, ns8, self.wq[layer].data_ptr(),
+                                                self.wq_scale[layer].data_ptr(), self.y.data_ptr(), B.ISPA_BF16,
+                                                ws.data_ptr(), need, s))
+            return self.y
+        if not local and self.f8 is not None:  # fp8 attention over all the F-Layer's chunks, W8A8 projection
+            kvl, chunks8 = self.kv[layer], self.f8[layer]
+            n_slots = kvl.slot(c) + 1
+            if n_slots > B.ISPA_MAX_SEGS_FP8:
+                raise RuntimeError(f"an F-Layer's quantised attention takes at most {B.ISPA_MAX_SEGS_FP8} chunks")
+            need_q = L.ispa_quantize_kv_fp8_workspace_bytes(self.T, self.H, self.d)
+            while len(chunks8) < n_slots:  # chunks not yet in the fp8 cache (written since the last call)
+                k, v = kvl._rows(len(chunks8), len(chunks8) + 1)
+                c8 = self._chunk_bufs()
+                self._quantize_chunk(k, v, c8, need_q, s)
+                chunks8.append(c8)
+            segs8, ns8 = B._segs_fp8(chunks8[:n_slots])
             need = L.ispa_local_attn_fp8_proj_workspace_bytes(self.T, self.H, self.d)
             ws = self.ws.get(need)
             self._ck(L.ispa_local_attn_fp8_proj(self.T, self.H, self.d, self.scale, B.ISPA_BF16, q.data_ptr(),

@@ -262,7 +262,7 @@ def test_fp8_attention_calls_reject_bad_args():
     assert att(d=64) == m.ISPA_ERR_UNSUPPORTED
     assert att(scale=0.0) == m.ISPA_ERR_INVALID_ARG
     assert att(scale=float("inf")) == m.ISPA_ERR_INVALID_ARG
-    assert att(ns=9) == m.ISPA_ERR_INVALID_ARG
+    assert att(ns=65) == m.ISPA_ERR_INVALID_ARG  # above ISPA_MAX_SEGS_FP8
     assert att(ns=-1) == m.ISPA_ERR_INVALID_ARG
     assert att(qc=F + 4) == m.ISPA_ERR_INVALID_ARG
     assert att(o=F + 4) == m.ISPA_ERR_INVALID_ARG

@@ -218,7 +218,8 @@ def test_local_attn_fp8_exact_on_power_of_two_scores():
     (2, 300, (700, 333), torch.float32),          # ragged chunks, a partial query tile
     (3, 257, (64, 1, 65, 0, 129), torch.float32), # tile-edge and empty chunks, 5 segments
     (1, 40, (5000,), torch.bfloat16),             # one long chunk, bf16 output
-    (4, 100, (31,) * 8, torch.float16),           # the most segments, f16 output
+    (4, 100, (31,) * 8, torch.float16),           # 8 segments, f16 output
+    (2, 70, (100,) * 40 + (65,) * 24, torch.float32),  # 64 segments (the limit), the F-Layer form
 ])
 def test_local_attn_fp8_parity(H, n_q, chunks, out_dtype):
     print(f"local_attn_fp8 H={H} n_q={n_q} chunks={chunks} -> {out_dtype}", flush=True)
@@ -289,39 +290,50 @@ def test_local_attn_fp8_proj_matches_its_parts():
     assert torch.equal(y, y2)
 
 
-def test_stream_post_uses_fp8_attention_for_l_layers():
-    """IspaStream after quantize_local_attention: an L-Layer's post-switch
-    output equals, bit for bit, ispa_local_attn_fp8_proj over its sink and
-    current chunk with its W + dW codes; an F-Layer keeps bf16 attention with
-    the W8A8 projection (ispa_local_attn_proj_fp8 over all its keys)."""
+def test_stream_post_uses_fp8_attention():
+    """IspaStream after quantize_attention: an L-Layer's post-switch output
+    equals, bit for bit, ispa_local_attn_fp8_proj over its sink and current
+    chunk with its W + dW codes, and an F-Layer's the same call over all its
+    chunks (each quantised on its own) with W's codes; with
+    quantize_local_attention the F-Layer keeps bf16 attention with the W8A8
+    projection (ispa_local_attn_proj_fp8 over all its keys)."""
     from kv_cache_absorption_amd.stream import IspaStream
     k8 = K()
     H, d, T, N = 4, 128, 300, 2
     D = H * d
     print(f"stream fp8 post H={H} T={T}", flush=True)
-    st = IspaStream(N, H, d, T, [2, 4], DEV, with_stats=False)
     W = synth.normal((N, D, D), 350, DEV, std=D ** -0.5, dtype=torch.bfloat16)
     w_eff = W + synth.normal((N, D, D), 351, DEV, std=1e-3, dtype=torch.bfloat16)
-    st.W = W
     kv = {c: (synth.normal((T, H, d), 360 + c, DEV, dtype=torch.bfloat16),
-              synth.normal((T, H, d), 370 + c, DEV, dtype=torch.bfloat16)) for c in range(4)}
-    st.adopt_switch([1, 0], w_eff)
-    for layer in range(N):
-        for c in range(3):
-            if layer == 1 or c == 0:
-                st.write_kv(layer, c, *kv[c])
-    st.quantize_projections()
-    st.quantize_local_attention()
+              synth.normal((T, H, d), 370 + c, DEV, dtype=torch.bfloat16)) for c in range(5)}
     q = synth.normal((T, H, d), 380, DEV, dtype=torch.bfloat16)
-    for layer in range(N):
-        st.write_kv(layer, 3, *kv[3])
-    y0 = st.post(0, 3, q).clone()
-    y1 = st.post(1, 3, q).clone()
-    chunks = [k8.ispa_quantize_kv_fp8(*kv[0]), k8.ispa_quantize_kv_fp8(*kv[3])]
-    ref0 = k8.ispa_local_attn_fp8_proj(q, chunks, st.wq[0], st.wq_scale[0], out_dtype=torch.bfloat16)
-    ref1 = k8.ispa_local_attn_proj_fp8(q, [(torch.cat([kv[c][0] for c in range(4)]),
-                                            torch.cat([kv[c][1] for c in range(4)]))],
-                                       st.wq[1], st.wq_scale[1], out_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    assert torch.equal(y0, ref0)
-    assert torch.equal(y1, ref1)
+    for f_layers in (True, False):
+        st = IspaStream(N, H, d, T, [2, 5], DEV, with_stats=False)
+        st.W = W
+        st.adopt_switch([1, 0], w_eff)
+        for layer in range(N):
+            for c in range(3):
+                if layer == 1 or c == 0:
+                    st.write_kv(layer, c, *kv[c])
+        st.quantize_projections()
+        if f_layers:
+            st.quantize_attention()
+        else:
+            st.quantize_local_attention()
+        for c in (3, 4):  # two post-switch steps: the F-Layer's chunks are quantised as they are first read
+            for layer in range(N):
+                st.write_kv(layer, c, *kv[c])
+            y0 = st.post(0, c, q).clone()
+            y1 = st.post(1, c, q).clone()
+            chunks = [k8.ispa_quantize_kv_fp8(*kv[0]), k8.ispa_quantize_kv_fp8(*kv[c])]
+            ref0 = k8.ispa_local_attn_fp8_proj(q, chunks, st.wq[0], st.wq_scale[0], out_dtype=torch.bfloat16)
+            if f_layers:
+                all8 = [k8.ispa_quantize_kv_fp8(*kv[i]) for i in range(c + 1)]
+                ref1 = k8.ispa_local_attn_fp8_proj(q, all8, st.wq[1], st.wq_scale[1], out_dtype=torch.bfloat16)
+            else:
+                ref1 = k8.ispa_local_attn_proj_fp8(q, [(torch.cat([kv[i][0] for i in range(c + 1)]),
+                                                        torch.cat([kv[i][1] for i in range(c + 1)]))],
+                                                   st.wq[1], st.wq_scale[1], out_dtype=torch.bfloat16)
+            torch.cuda.synchronize()
+            assert torch.equal(y0, ref0)
+            assert torch.equal(y1, ref1)
