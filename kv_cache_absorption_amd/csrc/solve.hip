@@ -167,65 +167,119 @@ __device__ __forceinline__ void sub_to_lds(const f64x4 (&acc)[2][2], const doubl
   for_acc(acc, [&](int r, int c, double v) { dst[r * LDP + c] = old[(int64_t)r * ld + c] - v; });
 }
 
+// 16 x 16 x 16 product on the fp64 matrix core: acc (+)= A B for 16 x 16 blocks
+// of LDS matrices with pitch LDP; A element (r, k) at a[r * LDP + k], B element
+// (k, c) at b[k * bs_k + c * bs_c] (so B may be read transposed).  Lane l holds
+// result rows l / 16 + 4 e, column l % 16.
+__device__ __forceinline__ f64x4 prod16(const double* a, const double* b, int bs_k, int bs_c, f64x4 acc) {
+  const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const double av = a[li * LDP + 4 * ks + lk];
+    const double bv = b[(4 * ks + lk) * bs_k + li * bs_c];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // Inverse of the Cholesky factor of the SPD 64 x 64 block M (LDS, pitch LDP),
-// by the workgroup's four waves.
-//
-// Lane a of every wave holds column a; wave w holds its rows 16w .. 16w+15.
-// Elimination is right-looking, pivot by pivot, on symmetric Schur
-// complements, so the multipliers of step j are row j.  The wave that holds
-// row j publishes it to LDS twice: as is, for each lane's own multiplier, and
-// with the entries at and above the diagonal zeroed, so that every wave
-// updates all 16 of its rows without a branch.  One barrier per step makes
-// each row visible.  When step j reaches its own column, lane j stops
-// updating: its remaining entries are then column j of the inverse unit
-// factor times -pivot_j, and the later steps update them with the same
-// formula as the matrix columns.  Pivot j is the squared diagonal of the
-// Cholesky factor, so inv(L)[i][a] = E[i][a] / sqrt(pivot_i) with E the
-// inverse unit factor.
-// M is overwritten (it holds the zeroed rows); rows: 64 x 64 doubles of LDS.
-// Writes Li (row-major, 64 wide); returns the first non-positive pivot
-// (1-based) or 0.  Every thread of the workgroup must call it.
-__device__ __forceinline__ int chol_inv64(double* M, double* rows, double* Li) {
-  const int a = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  double c[16];
+// by the workgroup's four waves, blocked in 16 x 16 blocks (k = 0 .. 3):
+//   * the first wave's lanes 0..15 factor the diagonal block M_kk and invert
+//     its factor at once: lane a holds column a, and at step j every lane
+//     publishes its entry of row j to LDS and reads the row back (the
+//     trailing row is also the column of multipliers); lane j stops updating
+//     at its own pivot, after which its entries are column j of the inverse
+//     unit factor times -pivot_j, updated by the same formula; the rows are
+//     scaled by 1/sqrt(pivot) at the end.  The result I_k goes to the
+//     diagonal block of X;
+//   * the panel L_ik = M_ik I_k^T (i > k, one block per wave) and the trailing
+//     update M_ij -= L_ik L_jk^T (k < j <= i) on the fp64 matrix core;
+// then the inverse, block column j by wave j: X_ij = -I_i sum_{t=j}^{i-1} L_it X_tj.
+// One barrier per phase, 11 in all (the unblocked form needed one per pivot).
+// M is overwritten (its lower blocks become L); X: 64 x 64 doubles of LDS
+// (pitch LDP).  Writes Li (row-major, 64 wide); returns the first non-positive
+// pivot (1-based) or 0.  Every thread of the workgroup must call it.
+__device__ __forceinline__ int chol_inv64(double* M, double* X, double* Li) {
+  __shared__ double rowb[2][16];
+  __shared__ int bad_s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  auto blk = [&](double* base, int bi, int bj) { return base + (16 * bi) * LDP + 16 * bj; };
+  if (tid == 0) bad_s = 0;
+  for (int k = 0; k < 4; ++k) {
+    if (w == 0 && lane < 16) {
+      const double* Mkk = blk(M, k, k);
+      double col[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) c[r] = M[(16 * w + r) * LDP + a];
-  __syncthreads();  // every row is in registers: M becomes the zeroed-row table
-  double* mult = M;
-  double* rowv = rows;
-  auto publish = [&](int j, double v) {
-    rowv[j * NB + a] = v;
-    mult[j * NB + a] = a > j ? v : 0.0;
-  };
-  if (w == 0) publish(0, c[0]);
-  int bad = 0;
-#pragma unroll 1
-  for (int j = 0; j < NB; ++j) {
-    __syncthreads();  // row j is published
-    const double piv = rowv[j * NB + j];
-    if (!(piv > 0.0) && bad == 0) bad = j + 1;
-    const double s = a == j ? 0.0 : rowv[j * NB + a] / piv;
-    const double* mj = mult + j * NB + 16 * w;
+      for (int i = 0; i < 16; ++i) col[i] = Mkk[i * LDP + lane];
+      int bad = 0;
+      double my_ea = 0.0, piv_of[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) c[r] = fma(-mj[r], s, c[r]);
-    const int jn = j + 1;
-    if (jn < NB && w == (jn >> 4)) {  // this wave holds row j + 1 (wave-uniform)
-      const int rl = jn & 15;
-      double v = c[0];
+      for (int j = 0; j < 16; ++j) {
+        double* rb = rowb[j & 1];
+        rb[lane] = col[j];
+        const double piv = rb[j];
+        piv_of[j] = piv;
+        if (!(piv > 0.0) && bad == 0) bad = j + 1;
+        // 1 / piv by the hardware reciprocal and two Newton steps (about 1 ulp;
+        // a shorter chain than the IEEE division on the serial path)
+        double inv = __builtin_amdgcn_rcp(piv);
+        inv = fma(inv, fma(-piv, inv, 1.0), inv);
+        inv = fma(inv, fma(-piv, inv, 1.0), inv);
+        const double sc = lane == j ? 0.0 : col[j] * inv;
+        if (lane == j) my_ea = -inv;
 #pragma unroll
-      for (int r = 1; r < 16; ++r) v = rl == r ? c[r] : v;
-      publish(jn, v);
+        for (int i = j + 1; i < 16; ++i) col[i] = fma(-rb[i], sc, col[i]);
+      }
+      // rows scaled by 1 / sqrt(pivot) once the elimination is done (off the serial path)
+      double* Xkk = blk(X, k, k);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const double isq = 1.0 / sqrt(piv_of[i]);
+        Xkk[i * LDP + lane] = i < lane ? 0.0 : (i == lane ? isq : col[i] * isq * my_ea);
+      }
+      if (bad && lane == 0 && bad_s == 0) bad_s = 16 * k + bad;
+    }
+    __syncthreads();  // I_k is in X
+    if (k == 3) break;
+    if (w < 3 - k) {  // panel: L_ik = M_ik I_k^T
+      const int i = k + 1 + w;
+      const f64x4 acc = prod16(blk(M, i, k), blk(X, k, k), 1, LDP, (f64x4){0.0, 0.0, 0.0, 0.0});
+      double* Lik = blk(M, i, k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Lik[(lk + 4 * e) * LDP + li] = acc[e];
+    }
+    __syncthreads();  // the panel is in M
+    int idx = 0;  // trailing blocks (i, j), k < j <= i, round-robin over the waves
+    for (int j = k + 1; j < 4; ++j)
+      for (int i = j; i < 4; ++i, ++idx) {
+        if (idx % 4 != w) continue;
+        const f64x4 acc = prod16(blk(M, i, k), blk(M, j, k), 1, LDP, (f64x4){0.0, 0.0, 0.0, 0.0});
+        double* Mij = blk(M, i, j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mij[(lk + 4 * e) * LDP + li] -= acc[e];
+      }
+    __syncthreads();  // the trailing blocks are updated
+  }
+  {  // block column j = w of the inverse
+    const int j = w;
+    for (int i = j + 1; i < 4; ++i) {
+      f64x4 t = {0.0, 0.0, 0.0, 0.0};
+      for (int u = j; u < i; ++u) t = prod16(blk(M, i, u), blk(X, u, j), LDP, 1, t);
+      double* Xij = blk(X, i, j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Xij[(lk + 4 * e) * LDP + li] = t[e];  // T, then X_ij in its place
+      const f64x4 o = prod16(blk(X, i, i), Xij, LDP, 1, (f64x4){0.0, 0.0, 0.0, 0.0});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Xij[(lk + 4 * e) * LDP + li] = -o[e];
     }
   }
-  __syncthreads();  // the last row is published
-  const double ea = -1.0 / rowv[a * NB + a];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = 16 * w + r;
-    const double isq = 1.0 / sqrt(rowv[i * NB + i]);
-    const double v = i < a ? 0.0 : (i == a ? isq : c[r] * ea * isq);
-    Li[i * NB + a] = bad ? NAN : v;
+  __syncthreads();  // every block of X is written
+  const int bad = bad_s;
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int i = e / NB, a = e % NB;
+    Li[e] = bad ? NAN : ((i >> 4) < (a >> 4) ? 0.0 : X[i * LDP + a]);
   }
   return bad;
 }
