@@ -182,25 +182,50 @@ __device__ __forceinline__ f64x4 prod16(const double* a, const double* b, int bs
   return acc;
 }
 
+// Workgroup barrier that orders LDS only: the global stores of the inverse
+// blocks stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Lane l's value of x (any lane, active or not), as a wave-uniform value.
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Inverse of the Cholesky factor of the SPD 64 x 64 block M (LDS, pitch LDP),
 // by the workgroup's four waves, blocked in 16 x 16 blocks (k = 0 .. 3):
 //   * the first wave's lanes 0..15 factor the diagonal block M_kk and invert
 //     its factor at once: lane a holds column a, and at step j every lane
-//     publishes its entry of row j to LDS and reads the row back (the
-//     trailing row is also the column of multipliers); lane j stops updating
-//     at its own pivot, after which its entries are column j of the inverse
-//     unit factor times -pivot_j, updated by the same formula; the rows are
-//     scaled by 1/sqrt(pivot) at the end.  The result I_k goes to the
-//     diagonal block of X;
+//     publishes its entry of row j to LDS and reads the row back (the trailing
+//     row is also the column of multipliers) while the pivot comes straight
+//     from lane j (readlane), so the reciprocal does not wait for the LDS round
+//     trip; lane j stops updating at its own pivot, after
+//     which its entries are column j of the inverse unit factor times
+//     -pivot_j, updated by the same formula; the rows are scaled by
+//     1/sqrt(pivot) at the end.  The result I_k goes to the diagonal block of X;
 //   * the panel L_ik = M_ik I_k^T (i > k, one block per wave) and the trailing
 //     update M_ij -= L_ik L_jk^T (k < j <= i) on the fp64 matrix core;
-// then the inverse, block column j by wave j: X_ij = -I_i sum_{t=j}^{i-1} L_it X_tj.
-// One barrier per phase, 11 in all (the unblocked form needed one per pivot).
+// then the strictly lower blocks of the inverse from the 2 x 2 split into
+// 32 x 32 halves, inv([[A, 0], [B, C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]]:
+//   stage 1: X_10 = -I_1 L_10 I_0, X_32 = -I_3 L_32 I_2, T01 = L_21 I_1,
+//            T11 = L_31 I_1 and the first terms of T00 and T10 (T = B A^-1);
+//   stage 2: T00 = L_20 I_0 + L_21 X_10, T10 = L_30 I_0 + L_31 X_10;
+//   stage 3: X_20 = -I_2 T00, X_21 = -I_2 T01, X_30 = -(X_32 T00 + I_3 T10),
+//            X_31 = -(X_32 T01 + I_3 T11);
+// five block products on the longest path.  T lives in the unused upper blocks
+// of X.  Every block of the inverse goes to Li (row-major, 64 wide; zeros above
+// the block diagonal, NaN everywhere if a pivot failed) as soon as it is final.
 // M is overwritten (its lower blocks become L); X: 64 x 64 doubles of LDS
-// (pitch LDP).  Writes Li (row-major, 64 wide); returns the first non-positive
-// pivot (1-based) or 0.  Every thread of the workgroup must call it.
+// (pitch LDP).  Returns the first non-positive pivot (1-based) or 0.  Every
+// thread of the workgroup must call it.
 __device__ __forceinline__ int chol_inv64(double* M, double* X, double* Li) {
-  __shared__ double rowb[2][16];
+  __shared__ double rowb[2][16], isq_s[16];
   __shared__ int bad_s;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -214,13 +239,20 @@ __device__ __forceinline__ int chol_inv64(double* M, double* X, double* Li) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) col[i] = Mkk[i * LDP + lane];
       int bad = 0;
-      double my_ea = 0.0, piv_of[16];
+      double my_ea = 0.0, piv_a = 0.0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
+        // row j to LDS for the update; the pivot straight from lane j, so
+        // that the reciprocal starts while the row is in flight
         double* rb = rowb[j & 1];
         rb[lane] = col[j];
-        const double piv = rb[j];
-        piv_of[j] = piv;
+        double r[16];
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) r[i] = rb[i];
+        // the row's reads are in flight before the reciprocal chain starts
+        __builtin_amdgcn_sched_barrier(0);
+        const double piv = readlane_f64(col[j], j);
+        if (lane == j) piv_a = piv;
         if (!(piv > 0.0) && bad == 0) bad = j + 1;
         // 1 / piv by the hardware reciprocal and two Newton steps (about 1 ulp;
         // a shorter chain than the IEEE division on the serial path)
@@ -230,13 +262,15 @@ __device__ __forceinline__ int chol_inv64(double* M, double* X, double* Li) {
         const double sc = lane == j ? 0.0 : col[j] * inv;
         if (lane == j) my_ea = -inv;
 #pragma unroll
-        for (int i = j + 1; i < 16; ++i) col[i] = fma(-rb[i], sc, col[i]);
+        for (int i = j + 1; i < 16; ++i) col[i] = fma(-r[i], sc, col[i]);
       }
-      // rows scaled by 1 / sqrt(pivot) once the elimination is done (off the serial path)
+      // rows scaled by 1 / sqrt(pivot) once the elimination is done (off the
+      // serial path): lane a forms the factor of pivot a and publishes it
+      isq_s[lane] = 1.0 / sqrt(piv_a);
       double* Xkk = blk(X, k, k);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const double isq = 1.0 / sqrt(piv_of[i]);
+        const double isq = isq_s[i];
         Xkk[i * LDP + lane] = i < lane ? 0.0 : (i == lane ? isq : col[i] * isq * my_ea);
       }
       if (bad && lane == 0 && bad_s == 0) bad_s = 16 * k + bad;
@@ -262,24 +296,56 @@ __device__ __forceinline__ int chol_inv64(double* M, double* X, double* Li) {
       }
     __syncthreads();  // the trailing blocks are updated
   }
-  {  // block column j = w of the inverse
-    const int j = w;
-    for (int i = j + 1; i < 4; ++i) {
-      f64x4 t = {0.0, 0.0, 0.0, 0.0};
-      for (int u = j; u < i; ++u) t = prod16(blk(M, i, u), blk(X, u, j), LDP, 1, t);
-      double* Xij = blk(X, i, j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Xij[(lk + 4 * e) * LDP + li] = t[e];  // T, then X_ij in its place
-      const f64x4 o = prod16(blk(X, i, i), Xij, LDP, 1, (f64x4){0.0, 0.0, 0.0, 0.0});
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Xij[(lk + 4 * e) * LDP + li] = -o[e];
-    }
-  }
-  __syncthreads();  // every block of X is written
   const int bad = bad_s;
+  const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
+  // this lane's elements of block (bi, bj) of Li
+  auto put = [&](int bi, int bj, const f64x4 v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Li[(16 * bi + lk + 4 * e) * NB + 16 * bj + li] = bad ? NAN : v[e];
+  };
+  auto put_lds = [&](double* b, const f64x4 v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[(lk + 4 * e) * LDP + li] = v[e];
+  };
+  // the diagonal blocks and the zero blocks above them
   for (int e = tid; e < NB * NB; e += 256) {
     const int i = e / NB, a = e % NB;
-    Li[e] = bad ? NAN : ((i >> 4) < (a >> 4) ? 0.0 : X[i * LDP + a]);
+    if ((i >> 4) <= (a >> 4)) Li[e] = bad ? NAN : ((i >> 4) < (a >> 4) ? 0.0 : X[i * LDP + a]);
+  }
+  double* T00 = blk(X, 0, 2);
+  double* T01 = blk(X, 0, 3);
+  double* T10 = blk(X, 1, 2);
+  double* T11 = blk(X, 1, 3);
+  f64x4 part = zero;
+  if (w == 0) {
+    put_lds(blk(X, 1, 0), prod16(blk(M, 1, 0), blk(X, 0, 0), LDP, 1, zero));  // L_10 I_0, then X_10 in its place
+    const f64x4 x10 = -prod16(blk(X, 1, 1), blk(X, 1, 0), LDP, 1, zero);
+    put_lds(blk(X, 1, 0), x10);
+    put(1, 0, x10);
+  } else if (w == 1) {
+    put_lds(blk(X, 3, 2), prod16(blk(M, 3, 2), blk(X, 2, 2), LDP, 1, zero));
+    const f64x4 x32 = -prod16(blk(X, 3, 3), blk(X, 3, 2), LDP, 1, zero);
+    put_lds(blk(X, 3, 2), x32);
+    put(3, 2, x32);
+  } else if (w == 2) {
+    put_lds(T01, prod16(blk(M, 2, 1), blk(X, 1, 1), LDP, 1, zero));
+    part = prod16(blk(M, 2, 0), blk(X, 0, 0), LDP, 1, zero);
+  } else {
+    put_lds(T11, prod16(blk(M, 3, 1), blk(X, 1, 1), LDP, 1, zero));
+    part = prod16(blk(M, 3, 0), blk(X, 0, 0), LDP, 1, zero);
+  }
+  lds_barrier();  // X_10, X_32, T01, T11 are in X
+  if (w == 2) put_lds(T00, prod16(blk(M, 2, 1), blk(X, 1, 0), LDP, 1, part));
+  if (w == 3) put_lds(T10, prod16(blk(M, 3, 1), blk(X, 1, 0), LDP, 1, part));
+  lds_barrier();  // T00 and T10 are in X
+  if (w == 0) {
+    put(2, 0, -prod16(blk(X, 2, 2), T00, LDP, 1, zero));
+  } else if (w == 1) {
+    put(2, 1, -prod16(blk(X, 2, 2), T01, LDP, 1, zero));
+  } else if (w == 2) {
+    put(3, 0, -prod16(blk(X, 3, 3), T10, LDP, 1, prod16(blk(X, 3, 2), T00, LDP, 1, zero)));
+  } else {
+    put(3, 1, -prod16(blk(X, 3, 3), T11, LDP, 1, prod16(blk(X, 3, 2), T01, LDP, 1, zero)));
   }
   return bad;
 }
