@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
   if (p.ksplit > 1) {
     // partial sums of this split, stored in the output's layout (no triangle mask:
     // the reduction applies it)
-    float* part = p.part + ((int64_t)split * 2 + (kind1 ? 1 : 0)) * p.M * p.ld_out;
+    float* part = p.part + ((int64_t)split * (p.two_kinds ? 2 : 1) + (kind1 ? 1 : 0)) * p.M * p.ld_out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = m0 + wm * 128 + i * 32 + lq;
@@ -660,12 +660,14 @@ __global__ __launch_bounds__(256, 1) void syrk_kernel(const SyrkParams p) {
 // One thread per 4 consecutive columns of one row: the S split copies added;
 // G's upper triangle stored (entries below the diagonal untouched); M split
 // into three bf16 planes whose sum is M to fp32 accuracy (each plane the
-// rounding of what the previous ones left), stored side by side as
-// [D][3 D] for the C = M W product; and this row's share of
-// r2 = <H, W W^T> = sum_i H_ii P_ii + 2 sum_{i<j} H_ij P_ij (P = W W^T) in
-// fp64, one partial per workgroup.
+// rounding of what the previous ones left), stored one after another as
+// [3][D][D] for the C = M W product; and this row's share of
+// r2 = <H, W W^T> = sum_i H_ii P_ii + 2 sum_{i<j} H_ij P_ij (P = W W^T, the
+// sum of its np K-split partial products, upper triangle) in fp64, one
+// partial per workgroup.
 __global__ __launch_bounds__(256) void gram_sum_kernel(const float* state, int64_t split_stride, int S, int32_t D,
-                                                       float* G, const float* P, uint16_t* planes, double* partials) {
+                                                       float* G, const float* P, int np, uint16_t* planes,
+                                                       double* partials) {
   const int64_t vpr = D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t DD = (int64_t)D * D;
@@ -702,11 +704,14 @@ __global__ __launch_bounds__(256) void gram_sum_kernel(const float* state, int64
       }
     }
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) *(u32x2*)(planes + i * 3 * D + pl * D + j) = (u32x2){w[pl][0], w[pl][1]};
-    const f32x4 pv = *(const f32x4*)(P + o);
+    for (int pl = 0; pl < 3; ++pl) *(u32x2*)(planes + pl * DD + o) = (u32x2){w[pl][0], w[pl][1]};
+    if (j + 3 >= i) {
+      f32x4 pv = *(const f32x4*)(P + o);
+      for (int sp = 1; sp < np; ++sp) pv += *(const f32x4*)(P + sp * DD + o);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (j + e >= i) part += (j + e == i ? 1.0 : 2.0) * (double)h[e] * (double)pv[e];
+      for (int e = 0; e < 4; ++e)
+        if (j + e >= i) part += (j + e == i ? 1.0 : 2.0) * (double)h[e] * (double)pv[e];
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
@@ -714,6 +719,13 @@ __global__ __launch_bounds__(256) void gram_sum_kernel(const float* state, int64
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
   __syncthreads();
   if (threadIdx.x == 0) partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// C = c3[0] + c3[1] + c3[2] (the three planes' products), 4 per thread
+__global__ __launch_bounds__(256) void sum3_kernel(const float* c3, int64_t n, float* C) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  *(f32x4*)(C + i) = (*(const f32x4*)(c3 + i) + *(const f32x4*)(c3 + n + i)) + *(const f32x4*)(c3 + 2 * n + i);
 }
 
 // *out = sum of n partials (one workgroup, fixed order: deterministic)
@@ -860,7 +872,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(float* out0, float* o
       if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
       __syncthreads();
     }
-    if (threadIdx.x == 0) *r2 += red[0];
+    if (threadIdx.x == 0 && r2) *r2 += red[0];
     return;
   }
   const int64_t vecs_per_row = N / 4;
@@ -872,7 +884,8 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(float* out0, float* o
   const int64_t m = v / vecs_per_row, n = (v % vecs_per_row) * 4;
   if (kind == 0 && tri && m > n + 3) return;  // entirely below the diagonal
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ksplit; ++s) acc += *(const f32x4*)(part + ((int64_t)s * 2 + kind) * M * ld + m * ld + n);
+  for (int s = 0; s < ksplit; ++s)
+    acc += *(const f32x4*)(part + ((int64_t)s * (two ? 2 : 1) + kind) * M * ld + m * ld + n);
   float* row = (kind ? out1 : out0) + m * ld;
   if (kind == 0 && tri && m > n) {
 #pragma unroll
@@ -965,32 +978,43 @@ ispa_status launch_syrk(const SyrkParams& p, int mfma_dt, hipStream_t stream) {
   return check_launch("syrk_kernel");
 }
 
+// K split of P = W W^T: upper-triangle tiles of 256, split so that the launch
+// fills the chip (1 when the triangle alone does)
+static int finalize_p_split(int32_t D) {
+  const int tm = (D + kNtBM - 1) / kNtBM;
+  const int tiles = tm * (tm + 1) / 2;
+  int ks = std::max(1, std::min(6, 256 / tiles));
+  while (ks > 1 && (D / kNtBK) % ks) --ks;  // K stages divide evenly
+  return ks;
+}
+
 size_t gram_finalize_ws_bytes(int32_t D) {
   const size_t d = (size_t)D;
   const size_t blocks = (d * (d / 4) + 255) / 256;
-  return 2 * align256(d * 3 * d * 2) + align256(d * d * 4) + align256(blocks * 8);
+  const size_t pbuf = std::max<size_t>((size_t)finalize_p_split(D) * d * d * 4, 3 * d * d * 4);
+  return align256(3 * d * d * 2) + align256(d * d * 2) + align256(pbuf) + align256(blocks * 8);
 }
 
 ispa_status launch_gram_finalize(int32_t D, const float* state, int64_t split_stride, int S, const uint16_t* w,
                                  float* G, float* C, double* r2, void* ws, hipStream_t stream) {
   const size_t d = (size_t)D;
   char* wp = (char*)ws;
-  uint16_t* planes = (uint16_t*)wp;  // M as three bf16 planes, [D][3 D]
-  wp += align256(d * 3 * d * 2);
-  uint16_t* wt3 = (uint16_t*)wp;  // W^T three times side by side, [D][3 D]
-  wp += align256(d * 3 * d * 2);
-  float* P = (float*)wp;  // W W^T
-  wp += align256(d * d * 4);
+  uint16_t* planes = (uint16_t*)wp;  // M as three bf16 planes, [3][D][D]
+  wp += align256(3 * d * d * 2);
+  uint16_t* wt = (uint16_t*)wp;  // W^T
+  wp += align256(d * d * 2);
+  float* pbuf = (float*)wp;  // P = W W^T (or its K-split partial sums), then the planes' products [3][D][D]
+  wp += align256(std::max<size_t>((size_t)finalize_p_split(D) * d * d * 4, 3 * d * d * 4));
   double* partials = (double*)wp;
   ispa_status st;
   {
-    const Transpose16 t[2] = {{w, wt3, D, D, D, 3 * (int64_t)D, D, ISPA_BF16, ISPA_BF16},
-                              {w, wt3 + D, D, D, D, 3 * (int64_t)D, D, ISPA_BF16, ISPA_BF16}};
-    if ((st = launch_transpose16(t, 2, stream))) return st;
-    const Transpose16 t3{w, wt3 + 2 * (int64_t)D, D, D, D, 3 * (int64_t)D, D, ISPA_BF16, ISPA_BF16};
-    if ((st = launch_transpose16(&t3, 1, stream))) return st;
+    const Transpose16 t{w, wt, D, D, D, D, D, ISPA_BF16, ISPA_BF16};
+    if ((st = launch_transpose16(&t, 1, stream))) return st;
   }
-  // P = W W^T: rows of W are k-contiguous on both sides
+  // P = W W^T (rows of W are k-contiguous on both sides), upper-triangle tiles;
+  // with a K split each split stores its partial product and gram_sum_kernel
+  // adds them
+  const int ks = finalize_p_split(D);
   NtGemmParams pp{};
   pp.M = D;
   pp.N = D;
@@ -1000,40 +1024,47 @@ ispa_status launch_gram_finalize(int32_t D, const float* state, int64_t split_st
   pp.y = w;
   pp.ldy = D;
   pp.y_rows = D;
-  pp.epi = kNtStore;
-  pp.out = P;
+  pp.epi = ks > 1 ? kNtAccum : kNtStore;
+  pp.out = pbuf;
   pp.out_dt = ISPA_F32;
   pp.ld_out = D;
-  pp.bn = 128;
+  pp.bn = kNtBM;
+  pp.tri = 1;
   pp.tiles_m = (D + kNtBM - 1) / kNtBM;
-  pp.tiles_n = (D + 127) / 128;
-  pp.ksplit = 1;
-  pp.kchunk = D;
+  pp.tiles_n = pp.tiles_m;
+  pp.ksplit = ks;
+  pp.kchunk = D / ks;
+  pp.part = pbuf;
   if ((st = launch_nt_gemm(pp, ISPA_BF16, stream, nullptr))) return st;
   const int64_t blocks = ((int64_t)D * (D / 4) + 255) / 256;
   hipLaunchKernelGGL(gram_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, state, split_stride, S, D, G,
-                     (const float*)P, planes, partials);
+                     (const float*)pbuf, ks, planes, partials);
   if ((st = check_launch("gram_sum_kernel"))) return st;
-  // C = M W as sum over the planes: K = 3 D with W^T repeated
+  // the three planes' products with W in one launch: [3 D][D] x W (the planes
+  // stacked as rows), then C = their sum
   NtGemmParams cp{};
-  cp.M = D;
+  cp.M = 3 * (int64_t)D;
   cp.N = D;
-  cp.K = 3 * (int64_t)D;
+  cp.K = D;
   cp.x = planes;
-  cp.ldx = 3 * (int64_t)D;
-  cp.y = wt3;
-  cp.ldy = 3 * (int64_t)D;
+  cp.ldx = D;
+  cp.y = wt;
+  cp.ldy = D;
   cp.y_rows = D;
   cp.epi = kNtStore;
-  cp.out = C;
+  cp.out = pbuf;
   cp.out_dt = ISPA_F32;
   cp.ld_out = D;
   cp.bn = 128;
-  cp.tiles_m = (D + kNtBM - 1) / kNtBM;
+  cp.tiles_m = (int)((3 * (int64_t)D + kNtBM - 1) / kNtBM);
   cp.tiles_n = (D + 127) / 128;
   cp.ksplit = 1;
-  cp.kchunk = 3 * (int64_t)D;
+  cp.kchunk = D;
   if ((st = launch_nt_gemm(cp, ISPA_BF16, stream, nullptr))) return st;
+  const int64_t n = (int64_t)D * D;
+  hipLaunchKernelGGL(sum3_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, (const float*)pbuf, n,
+                     C);
+  if ((st = check_launch("sum3_kernel"))) return st;
   hipLaunchKernelGGL(sum_set_kernel, dim3(1), dim3(256), 0, stream, (const double*)partials, blocks, r2);
   return check_launch("sum_set_kernel");
 }

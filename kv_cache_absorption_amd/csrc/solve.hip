@@ -10,7 +10,11 @@
 // factorisation of the next diagonal block by the workgroup that updates it).
 // The backward substitution is one launch per block row, whose workgroups of
 // block row kb - 1 also apply inv(L)^T of that row right after its last
-// update.  Block products are 64 x 64 x 64 fp64 MFMA tiles from LDS; a
+// update.  Small solves (one block column per update, where the launch chain's
+// latency is what counts) use an explicit form instead: the forward sweep also
+// carries Z = inv(L) (the identity as more right-hand sides) and adds each
+// finished block row k of Y = inv(L) C to the solution as Z_k^T Y_k, so that
+// dW = Z^T Y = (L L^T)^-1 C is complete when the sweep ends.  Block products are 64 x 64 x 64 fp64 MFMA tiles from LDS; a
 // diagonal block is turned into inv(L_kk) by the workgroup (chol_inv64).  eps uses
 // the identity that holds at the ridge optimum, eps = r2 - <dW, C> -
 // lambda ||dW||^2 (from G dW = C - lambda dW), which is ||A_loc dW - R||^2
@@ -32,8 +36,23 @@ struct SolveWs {
   double* Linv;  // [L][D][NB]
   double* lam;   // [L]
   double* part;  // [L][kEpsBlocks][2]
+  double* Z;     // [L][D][D], explicit form: inv(L) below the block diagonal
+  double* XF;    // [L][D][D], explicit form: the solution inv(L)^T inv(L) C
 };
 constexpr int kEpsBlocks = 1024;  // finalize workgroups per layer
+
+// Block columns per trailing update: deeper updates cut the read-modify-write of
+// the trailing blocks (which bounds large batched solves) but lengthen each
+// workgroup, which a small solve feels as latency.
+int solve_group(int L, int D) {
+  const double blocks = (double)L * (D / NB) * (D / NB);
+  return blocks < 4096.0 ? 1 : D / NB >= 48 ? 8 : 4;
+}
+
+// Small solves (one block column per update) skip the backward substitution:
+// the forward sweep also turns the identity into Z = inv(L) and adds each
+// finished block row's share of inv(L)^T (inv(L) C) to the solution.
+bool explicit_form(int L, int D) { return solve_group(L, D) == 1; }
 
 size_t ws_layout(int L, int D, SolveWs* w, char* base) {
   size_t off = 0;
@@ -47,7 +66,13 @@ size_t ws_layout(int L, int D, SolveWs* w, char* base) {
   double* Li = (double*)take((size_t)L * D * NB * 8);
   double* lam = (double*)take((size_t)L * 8);
   double* part = (double*)take((size_t)L * kEpsBlocks * 2 * 8);
-  if (w) *w = SolveWs{A, X, Li, lam, part};
+  double* Z = nullptr;
+  double* XF = nullptr;
+  if (explicit_form(L, D)) {
+    Z = (double*)take((size_t)L * D * D * 8);
+    XF = (double*)take((size_t)L * D * D * 8);
+  }
+  if (w) *w = SolveWs{A, X, Li, lam, part, Z, XF};
   return off;
 }
 
@@ -97,25 +122,34 @@ struct BlockOp {
   int trans;        // element (r, c) = p[c*ld + r] if trans else p[r*ld + c]
 };
 
-// dst[r][c] = element (r, c) of o; global reads run along o's contiguous dimension
-__device__ __forceinline__ void stage(double* dst, BlockOp o) {
+// A block staged through registers: the loads of a thread (16 elements along
+// o's contiguous dimension), then their LDS stores, so that the global loads of
+// several blocks can be in flight together.
+struct Staged {
+  double x[NB / 4];
+};
+__device__ __forceinline__ Staged stage_load(BlockOp o) {
   const int t = threadIdx.x;
   const int u = t & 63, v0 = t >> 6;
-  double x[NB / 4];
+  Staged r;
+#pragma unroll
+  for (int it = 0; it < NB / 4; ++it) r.x[it] = o.p[(int64_t)(v0 + 4 * it) * o.ld + u];
+  return r;
+}
+// dst[r][c] = element (r, c) of o
+__device__ __forceinline__ void stage_store(double* dst, const Staged& r, int trans) {
+  const int t = threadIdx.x;
+  const int u = t & 63, v0 = t >> 6;
 #pragma unroll
   for (int it = 0; it < NB / 4; ++it) {
     const int v = v0 + 4 * it;
-    x[it] = o.p[(int64_t)v * o.ld + u];
-  }
-#pragma unroll
-  for (int it = 0; it < NB / 4; ++it) {
-    const int v = v0 + 4 * it;
-    if (o.trans)
-      dst[u * LDP + v] = x[it];
+    if (trans)
+      dst[u * LDP + v] = r.x[it];
     else
-      dst[v * LDP + u] = x[it];
+      dst[v * LDP + u] = r.x[it];
   }
 }
+__device__ __forceinline__ void stage(double* dst, BlockOp o) { stage_store(dst, stage_load(o), o.trans); }
 
 // acc = As * Bs for this wave's 32 x 32 quadrant, as 2 x 2 tiles of
 // v_mfma_f64_16x16x4 (A fragment: lane holds A[l % 16][l / 16]; B fragment:
@@ -154,11 +188,12 @@ __device__ __forceinline__ void for_acc(const f64x4 (&acc)[2][2], F f) {
       for (int e = 0; e < 4; ++e) f(r0 + 16 * ti + lk + 4 * e, c0 + 16 * tj + li, acc[ti][tj][e]);
 }
 
-// out (global, ld) = acc, or out - acc
-__device__ __forceinline__ void store_block(const f64x4 (&acc)[2][2], double* out, int64_t ld, bool subtract) {
+// out (global, ld) = acc, out - acc, -acc or out + acc
+enum { kStore = 0, kSub = 1, kStoreNeg = 2, kAdd = 3 };
+__device__ __forceinline__ void store_block(const f64x4 (&acc)[2][2], double* out, int64_t ld, int mode) {
   for_acc(acc, [&](int r, int c, double v) {
     double* o = out + (int64_t)r * ld + c;
-    *o = subtract ? *o - v : v;
+    *o = mode == kStore ? v : mode == kSub ? *o - v : mode == kStoreNeg ? -v : *o + v;
   });
 }
 
@@ -365,6 +400,7 @@ enum { kPotrf0 = 0, kPanel = 1, kUpdate = 2, kBwd = 3 };
 struct StepArgs {
   int kind, kb;
   int k_lo, k_hi, j_lo, j_hi, x_lo, x_hi, diag;
+  int z;  // explicit form (one block column per update, contraction block kb)
 };
 
 // One launch of the blocked solve, batched over layers (blockIdx.y).
@@ -377,25 +413,36 @@ struct StepArgs {
 //                  the block (j_lo, j_lo) then factors it
 //   kBwd         : X_ij -= sum_k L_ki^T X_kj for i in [x_lo, x_hi); for i = diag
 //                  then also X_ij = inv(L_ii)^T X_ij
+// Explicit form (z): the panel also finishes block row kb of Z = inv(L),
+// Z_kb,j = inv(L_kk) Z_kb,j for j < kb (Z_kk = inv(L_kk) is kept in Li), and
+// does not apply inv(L)^T to the last row; the update also carries Z,
+// Z_ij -= L_ik Z_kj for i > k, j <= k (the first touch of Z_ik stores
+// -L_ik inv(L_kk)), and adds the finished row k to the solution,
+// XF_ij += Z_ki^T X_kj for i <= k (the first touch, i = k, stores).  A last
+// update with no trailing, X or Z blocks adds row nb - 1.
 // Diagonal blocks keep only inv(L_kk) (in Li); the strictly lower blocks of A
 // become L.  Every launch writes blocks that no other workgroup of it reads.
 __global__ __launch_bounds__(256, 2) void solve_step_kernel(StepArgs g, int D, double* Aall, double* Xall,
-                                                           double* Liall, int32_t* info) {
+                                                           double* Liall, int32_t* info, double* Zall,
+                                                           double* XFall) {
   __shared__ double As[NB * LDP], Bs[NB * LDP];
   const int l = blockIdx.y;
   const int nb = D / NB;
   const int b = blockIdx.x;
   double* A = Aall + (int64_t)l * D * D;
   double* X = Xall + (int64_t)l * D * D;
+  double* Z = g.z ? Zall + (int64_t)l * D * D : nullptr;
+  double* XF = g.z ? XFall + (int64_t)l * D * D : nullptr;
   double* Li = Liall + (int64_t)l * D * NB;
   auto blk = [&](double* M, int bi, int bj) { return M + (int64_t)bi * NB * D + (int64_t)bj * NB; };
   auto linv = [&](int k) { return Li + (int64_t)k * NB * NB; };
-  f64x4 acc[2][2];
+  f64x4 acc[2][2] = {};
   double* fac_li = nullptr;  // set when this workgroup factors a diagonal block (in As)
   int fac_base = 0;
   auto product = [&](BlockOp x, BlockOp y, bool accumulate) {
-    stage(As, x);
-    stage(Bs, y);
+    const Staged sx = stage_load(x), sy = stage_load(y);  // both blocks' loads in flight together
+    stage_store(As, sx, x.trans);
+    stage_store(Bs, sy, y.trans);
     __syncthreads();
     mma64(As, Bs, acc, accumulate);
   };
@@ -419,18 +466,22 @@ __global__ __launch_bounds__(256, 2) void solve_step_kernel(StepArgs g, int D, d
       if (b < m) {
         const int i = kb + 1 + b;
         product(BlockOp{blk(A, i, kb), D, 0}, BlockOp{linv(kb), NB, 1}, false);
-        store_block(acc, blk(A, i, kb), D, false);
+        store_block(acc, blk(A, i, kb), D, kStore);
+      } else if (b >= m + nb) {  // explicit form: Z_kb,j for j < kb
+        const int j = b - m - nb;
+        product(BlockOp{linv(kb), NB, 0}, BlockOp{blk(Z, kb, j), D, 0}, false);
+        store_block(acc, blk(Z, kb, j), D, kStore);
       } else {
         const int j = b - m;
         product(BlockOp{linv(kb), NB, 0}, BlockOp{blk(X, kb, j), D, 0}, false);
-        if (m == 0) {
+        if (m == 0 && !g.z) {
           __syncthreads();
           for_acc(acc, [&](int r, int c, double v) { Bs[r * LDP + c] = v; });
           stage(As, BlockOp{linv(kb), NB, 1});
           __syncthreads();
           mma64(As, Bs, acc);
         }
-        store_block(acc, blk(X, kb, j), D, false);
+        store_block(acc, blk(X, kb, j), D, kStore);
       }
       break;
     }
@@ -443,22 +494,50 @@ __global__ __launch_bounds__(256, 2) void solve_step_kernel(StepArgs g, int D, d
       }
       if (j < g.j_hi) {
         const int i = j + q;
+        const bool fac = i == g.j_lo && j == g.j_lo;  // the next diagonal block: finish it and factor it here
+        double old[16];  // its elements at this thread's product positions, loaded ahead of the product
+        if (fac) {
+          int e = 0;
+          for_acc(acc, [&](int r, int c, double) { old[e++] = blk(A, i, i)[(int64_t)r * D + c]; });
+        }
         sum_products([&](int k) { return BlockOp{blk(A, i, k), D, 0}; },
                      [&](int k) { return BlockOp{blk(A, j, k), D, 1}; });
-        if (i == g.j_lo && j == g.j_lo) {  // the next diagonal block: finish it and factor it here
+        if (fac) {
           __syncthreads();
-          sub_to_lds(acc, blk(A, i, i), D, As);
+          int e = 0;
+          for_acc(acc, [&](int r, int c, double v) { As[r * LDP + c] = old[e++] - v; });
           __syncthreads();
           fac_li = linv(i);
           fac_base = i * NB;
         } else {
-          store_block(acc, blk(A, i, j), D, true);
+          store_block(acc, blk(A, i, j), D, kSub);
         }
-      } else {
+        break;
+      }
+      const int nx = (g.x_hi - g.x_lo) * nb;
+      if (q < nx) {
         const int i = g.x_lo + q / nb, jx = q % nb;
         sum_products([&](int k) { return BlockOp{blk(A, i, k), D, 0}; },
                      [&](int k) { return BlockOp{blk(X, k, jx), D, 0}; });
-        store_block(acc, blk(X, i, jx), D, true);
+        store_block(acc, blk(X, i, jx), D, kSub);
+        break;
+      }
+      // explicit form, contraction block k = kb
+      q -= nx;
+      const int k = g.kb, nz = (nb - 1 - k) * (k + 1);
+      if (q < nz) {  // Z_i,jz -= L_ik Z_k,jz for i > k, jz <= k
+        const int i = k + 1 + q / (k + 1), jz = q % (k + 1);
+        product(BlockOp{blk(A, i, k), D, 0}, jz == k ? BlockOp{linv(k), NB, 0} : BlockOp{blk(Z, k, jz), D, 0},
+                false);
+        store_block(acc, blk(Z, i, jz), D, jz == k ? kStoreNeg : kSub);
+        break;
+      }
+      q -= nz;
+      {  // XF_i,jx += Z_k,i^T X_k,jx for i <= k
+        const int i = q / nb, jx = q % nb;
+        product(i == k ? BlockOp{linv(k), NB, 1} : BlockOp{blk(Z, k, i), D, 1}, BlockOp{blk(X, k, jx), D, 0},
+                false);
+        store_block(acc, blk(XF, i, jx), D, i == k ? kStore : kAdd);
       }
       break;
     }
@@ -473,9 +552,9 @@ __global__ __launch_bounds__(256, 2) void solve_step_kernel(StepArgs g, int D, d
         stage(As, BlockOp{linv(i), NB, 1});
         __syncthreads();
         mma64(As, Bs, acc);
-        store_block(acc, blk(X, i, j), D, false);
+        store_block(acc, blk(X, i, j), D, kStore);
       } else {
-        store_block(acc, blk(X, i, j), D, true);
+        store_block(acc, blk(X, i, j), D, kSub);
       }
       break;
     }
@@ -547,13 +626,6 @@ __global__ __launch_bounds__(256) void eps_kernel(const double* r2, const double
 
 size_t solve_ws_bytes(int32_t n_layers, int32_t D) { return ws_layout(n_layers, D, nullptr, nullptr); }
 
-// Block columns per trailing update: deeper updates cut the read-modify-write of
-// the trailing blocks (which bounds large batched solves) but lengthen each
-// workgroup, which a small solve feels as latency.
-static int solve_group(int L, int D) {
-  const double blocks = (double)L * (D / NB) * (D / NB);
-  return blocks < 4096.0 ? 1 : D / NB >= 48 ? 8 : 4;
-}
 
 ispa_status run_solve(int32_t L, int32_t D, const float* G, const float* C, const double* r2,
                       int64_t ms, double la, double lr, float* dW, double* eps, int32_t* info,
@@ -569,36 +641,42 @@ ispa_status run_solve(int32_t L, int32_t D, const float* G, const float* C, cons
   // covers only the group's own columns (and X block rows), and the blocks right
   // of (below) the group get the group's P columns in one update of depth P.
   const int P = solve_group(L, D);
+  const int z = explicit_form(L, D) ? 1 : 0;
   auto launch = [&](StepArgs g, int blocks) {
+    g.z = z;
     if (blocks > 0)
       hipLaunchKernelGGL(solve_step_kernel, dim3((unsigned)blocks, (unsigned)L), dim3(256), 0, stream, g, D, s.A,
-                         s.X, s.Linv, info);
+                         s.X, s.Linv, info, s.Z, s.XF);
   };
   auto strip = [&](int j_lo, int j_hi) {  // A blocks on or below the diagonal in columns [j_lo, j_hi)
     int n = 0;
     for (int j = j_lo; j < j_hi; ++j) n += nb - j;
     return n;
   };
+  // explicit form: the Z and solution blocks an update by block column kb adds
+  auto zx = [&](int kb) { return z ? (nb - 1 - kb) * (kb + 1) + (kb + 1) * nb : 0; };
   launch(StepArgs{kPotrf0, 0, 0, 0, 0, 0, 0, 0, -1}, 1);
   for (int g0 = 0; g0 < nb; g0 += P) {
     const int g1 = std::min(g0 + P, nb);
     for (int kb = g0; kb < g1; ++kb) {
-      launch(StepArgs{kPanel, kb, 0, 0, 0, 0, 0, 0, -1}, (nb - 1 - kb) + nb);
+      launch(StepArgs{kPanel, kb, 0, 0, 0, 0, 0, 0, -1}, (nb - 1 - kb) + nb + (z ? kb : 0));
       if (kb + 1 < g1)  // the rest of the group, by column kb
         launch(StepArgs{kUpdate, kb, kb, kb + 1, kb + 1, g1, kb + 1, g1, -1}, strip(kb + 1, g1) + (g1 - kb - 1) * nb);
       else if (g1 < nb)  // everything past the group, by the whole group
-        launch(StepArgs{kUpdate, kb, g0, g1, g1, nb, g1, nb, -1}, strip(g1, nb) + (nb - g1) * nb);
+        launch(StepArgs{kUpdate, kb, g0, g1, g1, nb, g1, nb, -1}, strip(g1, nb) + (nb - g1) * nb + zx(kb));
     }
   }
-  for (int g0 = (nb - 1) / P * P; g0 >= 0; g0 -= P) {
+  if (z)  // the last block row's share of the solution
+    launch(StepArgs{kUpdate, nb - 1, nb - 1, nb, nb, nb, nb, nb, -1}, zx(nb - 1));
+  for (int g0 = (nb - 1) / P * P; g0 >= 0 && !z; g0 -= P) {
     const int g1 = std::min(g0 + P, nb);
     for (int kb = g1 - 1; kb > g0; --kb)  // rows of the group, by row kb
       launch(StepArgs{kBwd, kb, kb, kb + 1, 0, 0, g0, kb, kb - 1}, (kb - g0) * nb);
     if (g0 > 0)  // rows before the group, by the whole group
       launch(StepArgs{kBwd, g0, g0, g1, 0, 0, 0, g0, g0 - 1}, g0 * nb);
   }
-  hipLaunchKernelGGL(finalize_kernel, dim3(kEpsBlocks, L), dim3(256), 0, stream, D, s.X, C, ms, info, dW, w,
-                     w_dt, w_eff, s.part);
+  hipLaunchKernelGGL(finalize_kernel, dim3(kEpsBlocks, L), dim3(256), 0, stream, D, z ? s.XF : s.X, C, ms, info,
+                     dW, w, w_dt, w_eff, s.part);
   hipLaunchKernelGGL(eps_kernel, dim3(L), dim3(256), 0, stream, r2, s.lam, info, s.part, eps);
   return check_launch("solve kernels");
 }
