@@ -390,13 +390,17 @@ __device__ __forceinline__ int swz_mask(int row) { return ((row & 3) << 2) | ((r
 //   1. O += V_{t-1}^T P_{t-1}^T on the matrix core, while the VALU forms
 //      P_t = exp2(S_t c - m) (c = scale * log2(e)) packed to bf16;
 //   2. S_{t+1} = K_{t+1} Q^T on the matrix core (into the registers of S_t,
-//      now consumed), while the VALU adds the row sums of P_t and takes the
-//      row maxima of the first key block of S_{t+1}.
-// Before half 1 the tile's row maxima decide a lazy re-basing: the running
-// maximum m is raised only when the tile exceeds it by more than 8 (log2
-// units), so P < 2^8 and, after the first tile (m starts at -inf), re-basing
-// is rare; it scales l at once and O after half 1.  Any m below the true
-// maximum gives the same result in exact arithmetic.
+//      now consumed), while the VALU adds the row sums of P_t.
+// Lazy re-basing without row maxima in the common path: the reference m is
+// set 7 (log2 units) above the largest scaled score seen, so every P of the
+// keys seen is at most 2^-7, and P_t is formed with the current m before any
+// test.  Half 1 ORs the packed bf16 words of P_t; the exponent's top bit of
+// either half is set exactly when some P >= 2 (or inf / NaN, as in the first
+// tile, where m = -inf), i.e. when a score passes the largest seen by more
+// than 8.  Only then (the first tile, and rarely after it) the tile's row
+// maxima are taken, m is raised, l and O are scaled and P_t is formed again
+// while S_t is still in its registers.  Any m gives the same result in exact
+// arithmetic.
 //   * One iteration form for every tile: iteration 0 multiplies a zeroed
 //     P_{-1} with a zeroed V slot, and keys past the end of a segment (all keys
 //     of the final iteration) are masked to -inf behind a uniform branch.
@@ -777,37 +781,31 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][blk][i]);
     return mx;
   };
-  // Lazy re-basing, decided before P_t is formed from the tile's row maximum
-  // (lanes l and l + 32 hold the two key halves of one query): m is raised to
-  // the row maximum only when that exceeds m by more than kLazy (log2 units),
-  // so P stays below 2^kLazy and re-basing is rare after the first tile (m
-  // starts at -inf, so the first tile always re-bases).  Re-basing scales l at
-  // once and O after this iteration's PV product (which still uses P_{t-1},
-  // formed with the old m).  Returns whether any lane re-based.
-  constexpr float kLazy = 8.0f;
-  float alpha[QB];
-  auto decide = [&](const float (&mx_lane)[QB]) {
-    float mx[QB];
-    bool up[QB], any = false;
+  // Re-basing (the rare path after half 1, entered when some packed P_t >= 2):
+  // the tile's row maxima (lanes l and l + 32 hold the two key halves of one
+  // query) raise m to max + kHead for every row whose maximum passed m - 0.5,
+  // and l and O (which holds P_{t-1} V_{t-1}, formed with the old m) are scaled
+  // by alpha = 2^(m_old - m_new), 0 when m_old = -inf.  P_t is then formed again.
+  constexpr float kHead = 7.0f;
+  auto rebase = [&](const int cb) __attribute__((always_inline)) {
+    float alpha[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const auto r =
-          __builtin_amdgcn_permlane32_swap(__float_as_uint(mx_lane[qb]), __float_as_uint(mx_lane[qb]), false, false);
-      mx[qb] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * c;
-      up[qb] = mx[qb] - m[qb] > kLazy;
-      any = any || up[qb];
+      const float mx_lane = fmaxf(blk_max(qb, 0), blk_max(qb, 1));
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx_lane), __float_as_uint(mx_lane), false, false);
+      const float mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * c;
+      const bool up = mx - m[qb] > 0.5f;
+      alpha[qb] = up ? __builtin_amdgcn_exp2f(m[qb] - (mx + kHead)) : 1.0f;
+      m[qb] = up ? mx + kHead : m[qb];
+      l_part[qb] *= alpha[qb];
     }
-    if (__any(any)) {
-      asm volatile("" ::: "memory");  // keep the rare path a branch (not speculated)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        alpha[qb] = up[qb] ? __builtin_amdgcn_exp2f(m[qb] - mx[qb]) : 1.0f;  // 0 when m = -inf
-        m[qb] = up[qb] ? mx[qb] : m[qb];
-        l_part[qb] *= alpha[qb];
-      }
-      return true;
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) o[qb][dt] *= alpha[qb];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) exp_pair(cb, qb, k);
     }
-    return false;
   };
   // Both halves of an iteration run 16 steps of QB MFMAs each (one per query
   // block, sharing one K or V fragment); the fragment of step i is read LA
@@ -816,10 +814,11 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
   // zeroed P_{-1} with a zeroed V slot, and scores of keys past the end of a
   // segment (all keys of iteration n_tiles) are masked to -inf, which makes
   // their P exactly 0.
-  float mx0[QB];  // this lane's maxima of key block 0 of S_{t+1}, taken in half 2
   // half 1: step i = O^T += V^T P^T for key group i / 4, d-tile i % 4 (P_{t-1})
-  // on the matrix core; P_t pair i on the VALU
-  auto half1 = [&](const int vs, const int ks, const int cb, bf16x8(&kf)[16]) __attribute__((always_inline)) {
+  // on the matrix core; P_t pair i on the VALU, and the OR of its packed words
+  // into orw
+  auto half1 = [&](const int vs, const int ks, const int cb, bf16x8(&kf)[16], uint32_t(&orw)[QB])
+                   __attribute__((always_inline)) {
     bf16x8 vf[16];
 #pragma unroll
     for (int i = 0; i < LA; ++i) vf[i] = v_frag(vs, i >> 2, i & 3);
@@ -831,16 +830,22 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         exp_two(qb, i, e[i & 1][qb]);
-        if (i > 0) P[cb][qb][i - 1] = pack_bf16(e[(i - 1) & 1][qb][0], e[(i - 1) & 1][qb][1]);
-        if (i == 15) P[cb][qb][15] = pack_bf16(e[1][qb][0], e[1][qb][1]);
+        if (i > 0) {
+          P[cb][qb][i - 1] = pack_bf16(e[(i - 1) & 1][qb][0], e[(i - 1) & 1][qb][1]);
+          orw[qb] = i == 1 ? P[cb][qb][0] : orw[qb] | P[cb][qb][i - 1];
+        }
+        if (i == 15) {
+          P[cb][qb][15] = pack_bf16(e[1][qb][0], e[1][qb][1]);
+          orw[qb] |= P[cb][qb][15];
+        }
         o[qb][i & 3] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], p_frag(cb ^ 1, qb, i >> 2), o[qb][i & 3], 0, 0, 0);
       }
-      // QB MFMAs, 2 LDS reads, 5 VALU per query block (2 FMA, 2 exp, pack); the
-      // step boundary keeps each read LA steps ahead of its MFMA
+      // QB MFMAs, 2 LDS reads, 6 VALU per query block (2 FMA, 2 exp, pack, OR);
+      // the step boundary keeps each read LA steps ahead of its MFMA
       __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 5 * QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6 * QB, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // P_t is formed here, not sunk past the re-basing branch into its users
@@ -853,10 +858,9 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     __builtin_amdgcn_sched_barrier(0);
   };
   // half 2: step i = S_{t+1} += K Q^T for key block i / 8, d slice i % 8 on the
-  // matrix core; row sum of P_t pair i on the VALU, and from step 10 (two
-  // MFMAs after block 0 is complete) the maximum of block 0.  The iteration's
-  // loads are issued here, spread over the half so that the waves do not queue
-  // behind each other on the load path.
+  // matrix core; row sum of P_t pair i on the VALU.  The iteration's loads are
+  // issued here, spread over the half so that the waves do not queue behind
+  // each other on the load path.
   auto half2 = [&](const int ks, const int cb, bf16x8(&kf)[16], const Load& lk, const Load& lv)
                    __attribute__((always_inline)) {
     static_assert(LPW == 2, "load placement in half 2");
@@ -866,13 +870,6 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
       if (i == 5) issue_load(lk, 1);
       if (i == 9) issue_load(lv, 0);
       if (i == 13) issue_load(lv, 1);
-      if (i == 10) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          mx0[qb] = blk_max(qb, 0);
-          asm volatile("" ::"v"(mx0[qb]));  // taken here, where the VALU is idle, not at its use
-        }
-      }
       if (i + LA < 16) kf[i + LA] = k_frag(ks, i + LA);
       const int blk = i >> 3, sl = i & 7;
 #pragma unroll
@@ -882,12 +879,10 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
         S[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[qb][sl], sl == 0 ? (f32x16){} : S[qb][blk],
                                                              0, 0, 0);
       }
-      // QB MFMAs, 1 LDS read, the address XOR and a row sum per query block,
-      // then the block-0 maxima
+      // QB MFMAs, 1 LDS read, the address XOR and a row sum per query block
       __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i < 10) __builtin_amdgcn_sched_group_barrier(0x402, 1 + QB, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x402, 1 + 4 * QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 1 + QB, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -909,22 +904,19 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
           for (int i = 0; i < 16; ++i)
             S[qb][blk][i] = ((i >> 2) * 8 + (i & 3) < lim) ? S[qb][blk][i] : -INFINITY;
         }
-        mx0[qb] = blk_max(qb, 0);
       }
     }
-    // row maxima of S_t and the re-basing decision, before P_t is formed
-    float mx[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(mx0[qb], blk_max(qb, 1));
-    const bool resc = decide(mx);
     const int ks = ((u + 1) & 3) * TILEB, vs = ((u + 3) & 3) * TILEB;
     bf16x8 kf[16];
-    half1(vs, ks, cb, kf);
-    if (resc) {
+    uint32_t orw[QB];
+    half1(vs, ks, cb, kf, orw);
+    // some P_t >= 2 (exponent field >= 128 in either bf16 half), inf or NaN
+    bool hot = false;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int dt = 0; dt < DH / 32; ++dt) o[qb][dt] *= alpha[qb];
+    for (int qb = 0; qb < QB; ++qb) hot = hot || (orw[qb] & 0x40004000u) != 0u;
+    if (__any(hot)) {
+      asm volatile("" ::: "memory");  // keep the rare path a branch (not speculated)
+      rebase(cb);
     }
     half2(ks, cb, kf, lk, lv);
     wait_iter();
@@ -963,8 +955,6 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
         S[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[qb][sl], sl == 0 ? (f32x16){} : S[qb][blk],
                                                              0, 0, 0);
     }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mx0[qb] = blk_max(qb, 0);
     __syncthreads();  // every wave has read K_0 before iteration 0 loads K_4 into its slot
     // iterations 0 .. n_tiles, unrolled by the ring size
     for (int t = 0;;) {
