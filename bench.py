@@ -488,6 +488,69 @@ def run_stream(args, name, dev):
     print(json.dumps(out), flush=True)
 
 
+def sdpa_compare(n_calls, seed, dev):
+    """The benchmark chunk's attention through torch's fused scaled-dot-product
+    attention (the vendor path: flash, else memory-efficient backend; the math
+    backend is never used) beside ispa_dual_attn_merge on the same inputs: one
+    key set of sink + current + history (37440 keys) against our two groups
+    and their merge.  Same flops (4 n_q n_k D); mean ms per call with HIP
+    events on the current stream, after one untimed call of each."""
+    import torch
+    import torch.nn.functional as F
+    import synth
+    from kv_cache_absorption_amd import _lib as B
+    L = B.lib()
+    g = synth.wan13b_single_layer(seed=seed, device=dev)
+    n_q, H, d, D = g.n_q, g.H, g.d, g.D
+    q, kc, vc = g.step(0)
+    k_all = torch.cat([g.sink_k, kc, g.hist_k])
+    v_all = torch.cat([g.sink_v, vc, g.hist_v])
+    n_k = k_all.shape[0]
+    flops = 4.0 * n_q * n_k * D
+    qh = q.permute(1, 0, 2).unsqueeze(0).contiguous()
+    kh = k_all.permute(1, 0, 2).unsqueeze(0).contiguous()
+    vh = v_all.permute(1, 0, 2).unsqueeze(0).contiguous()
+    out = {"calls": n_calls, "n_q": n_q, "n_k": n_k, "heads": H, "head_dim": d, "flops_per_call": flops}
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(n_calls):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n_calls
+        return {"ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([be]):
+                out["torch_sdpa_" + name] = timed(lambda: F.scaled_dot_product_attention(qh, kh, vh,
+                                                                                         scale=d ** -0.5))
+        except RuntimeError as e:  # backend not available for these inputs: reported, never replaced
+            out["torch_sdpa_" + name] = {"unavailable": str(e).splitlines()[0][:200]}
+    a_loc = torch.empty((n_q, D), dtype=torch.float16, device=dev)
+    delta = torch.empty_like(a_loc)
+    ls, nl = B._segs([(g.sink_k, g.sink_v), (kc, vc)], H, d)
+    hs, nh = B._segs([(g.hist_k, g.hist_v)], H, d)
+    wsb = L.ispa_dual_attn_merge_workspace_bytes(B.ISPA_BF16, n_q, H, d, ls, nl, hs, nh)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+
+    def ours():
+        st = L.ispa_dual_attn_merge(B.ISPA_BF16, n_q, H, d, d ** -0.5, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
+                                    a_loc.data_ptr(), delta.data_ptr(), B.ISPA_F16, None, ws.data_ptr(),
+                                    ws.numel(), sh)
+        if st:
+            raise B.IspaError(st, L.ispa_last_error().decode())
+    out["ispa_dual_attn_merge"] = timed(ours)
+    return out
+
+
 def proj_compare(n_calls, dev):
     """Post-switch attention + projection of one chunk (4680 queries over the
     sink and current chunk, 9360 keys) with the bf16 projection and with the
@@ -546,6 +609,9 @@ def main():
                          "(counter runs)")
     ap.add_argument("--merge-only", type=int, default=0,
                     help="only run this many two-part LSE merges of the workload (counter runs)")
+    ap.add_argument("--sdpa-compare", type=int, default=0,
+                    help="only time torch's fused attention (flash / memory-efficient backend) and "
+                         "ispa_dual_attn_merge on the benchmark chunk, this many calls each")
     ap.add_argument("--proj-compare", type=int, default=0,
                     help="only time the post-switch projection paths (bf16 and W8A8) at the Wan-1.3B "
                          "and Wan-14B widths, this many calls each")
@@ -580,6 +646,9 @@ def main():
     L = B.lib()  # raises if libispa.so is missing: no fallback path exists
     if args.proj_compare:
         print(json.dumps(proj_compare(args.proj_compare, dev)))
+        return
+    if args.sdpa_compare:
+        print(json.dumps(sdpa_compare(args.sdpa_compare, args.seed, dev)))
         return
     if args.workload != "wan13b_layer":
         run_stream(args, args.workload, dev)
