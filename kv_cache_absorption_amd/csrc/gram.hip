@@ -582,6 +582,18 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
   // wait and barrier for stage s + 1; then stage s + 1's slice 0 is read while
   // slice 1's MFMAs run.  A slot refilled in iteration s held stage s - 2,
   // last read before iteration s - 1's barrier.
+  // One MFMA, then one fragment read of the other slice, 16 times: the reads
+  // of a phase write registers that its MFMAs do not use, so no MFMA waits
+  // for a read issued in its own phase (with all 16 reads first, the LDS
+  // counter cannot tell the older fragments from the new ones, and the first
+  // MFMA waited for two of the new reads).
+  auto interleave = [&]() {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
   int cbuf = 0;
   for (int s = 0; s + 1 < ns; ++s) {
     if (issued < ns) {
@@ -589,16 +601,17 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
       lbuf = lbuf + 1 == SY_NBUF ? 0 : lbuf + 1;
       ++issued;
     }
-    frags(cbuf, 1, fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
+    frags(cbuf, 1, fa1, fb1);
     mfmas(fa0, fb0);
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     const int nbuf = cbuf + 1 == SY_NBUF ? 0 : cbuf + 1;
     wait_stage(issued - (s + 2));  // stage s + 1 is in LDS
     __syncthreads();
     frags(nbuf, 0, fa0, fb0);
-    __builtin_amdgcn_sched_barrier(0);
     mfmas(fa1, fb1);
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     cbuf = nbuf;
   }
@@ -613,6 +626,41 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
   // n = wn*128 + 32 j + 8 g + 4 hh inside the tile.
   const int which = !xb && !yb ? 0 : (!xb ? 1 : 2);  // G, M or H
   float* out = p.state + (int64_t)split * p.split_stride + (int64_t)which * p.D * p.D;
+  const int64_t m0 = cx + wm * 128, n0 = cy + wn * 128;  // this wave's 128 x 128 block
+  if (m0 + 128 <= p.D && n0 + 128 <= p.D) {
+    // The block lies inside D (every block when D is a multiple of 256): no
+    // per-vector checks, the 16 loads of a 32-row block go out together, and
+    // the next block's loads are issued before this one is added and stored.
+    auto ld = [&](int i, f32x4(&c)[4][4]) __attribute__((always_inline)) {
+      const float* row = out + (m0 + i * 32 + lq) * p.D + n0 + hh * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) c[j][g] = *(const f32x4*)(row + j * 32 + g * 8);
+    };
+    auto st = [&](int i, const f32x4(&c)[4][4]) __attribute__((always_inline)) {
+      float* row = out + (m0 + i * 32 + lq) * p.D + n0 + hh * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v = c[j][g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += acc[i][j][g * 4 + e];
+          *(f32x4*)(row + j * 32 + g * 8) = v;
+        }
+    };
+    f32x4 c0[4][4], c1[4][4];
+    ld(0, c0);
+    ld(1, c1);
+    st(0, c0);
+    ld(2, c0);
+    st(1, c1);
+    ld(3, c1);
+    st(2, c0);
+    st(3, c1);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = cx + wm * 128 + i * 32 + lq;
