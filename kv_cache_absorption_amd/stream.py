@@ -184,8 +184,11 @@ class IspaStream:
     Device state per layer: the KV cache, W (bf16 [D, D], y = a W) and the
     warmup statistics.  ``stats="gram"`` (the default) accumulates them in the
     grouping of the printed closed form: one rank-k update of [A_loc | dA]
-    per chunk into a per-layer state (ispa_accum_gram), and G, C = M W and r2
-    formed once at the switch (ispa_gram_finalize).  ``stats="direct"``
+    into a per-layer state (ispa_accum_gram) for every ``stats_chunks``
+    chunks of a layer (their rows wait in a per-layer buffer; the sums do not
+    depend on the grouping, and one update over more rows pays the state's
+    read-modify-write once), and G, C = M W and r2 formed once at the switch
+    (ispa_gram_finalize), after the rows still waiting are added.  ``stats="direct"``
     accumulates G, C = A_loc^T (dA W) and r2 every chunk (ispa_accum_stats).
     For the switch, G, C (fp32 [N, D, D], so that one call solves every
     layer) and r2 (fp64 [N]); after it dW (fp32), eps (fp64), W + dW (bf16),
@@ -195,7 +198,7 @@ class IspaStream:
     def __init__(self, n_layers: int, H: int, d: int, T: int, capacity,
                  device, dtype=torch.bfloat16, stats_dtype=torch.float16,
                  lambda_abs: float = 0.0, lambda_rel: float = 1e-3, scale: float | None = None,
-                 with_stats: bool = True, stats: str = "gram"):
+                 with_stats: bool = True, stats: str = "gram", stats_chunks: int = 2):
         if dtype != torch.bfloat16:
             raise ValueError("streams run on bf16 Q/K/V")
         self.N, self.H, self.d, self.T = n_layers, H, d, T
@@ -214,6 +217,11 @@ class IspaStream:
         if stats not in ("gram", "direct"):
             raise ValueError("stats is 'gram' or 'direct'")
         self.stats = stats
+        if stats_chunks < 1:
+            raise ValueError("stats_chunks must be >= 1")
+        self.stats_chunks = stats_chunks if stats == "gram" else 1
+        self._pend = [None] * n_layers  # per layer: (A_loc, dA) rows of stats_chunks chunks
+        self._npend = [0] * n_layers    # chunks waiting in them
         self.has_stats = with_stats
         self.G = self.C = self.r2 = self.state = None
         if with_stats and stats == "gram":
@@ -274,11 +282,23 @@ class IspaStream:
             need = max(need, L.ispa_accum_stats_workspace_bytes(sdt, n, self.D))
         ws = self.ws.get(need)
         wsp = ws.data_ptr() if ws is not None else None
+        a_loc, delta = self.a_loc, self.delta
+        if self.stats == "gram" and self.stats_chunks > 1:
+            if self._pend[layer] is None:
+                rows = self.stats_chunks * n
+                self._pend[layer] = (torch.empty((rows, self.D), dtype=self.stats_dtype, device=self.device),
+                                     torch.empty((rows, self.D), dtype=self.stats_dtype, device=self.device))
+            off = self._npend[layer] * n
+            a_loc, delta = self._pend[layer][0][off:off + n], self._pend[layer][1][off:off + n]
         self._ck(L.ispa_dual_attn_merge(B.ISPA_BF16, n, self.H, self.d, self.scale, q.data_ptr(), q.stride(0),
-                                        ls, nl, hs, nh, self.a_loc.data_ptr(), self.delta.data_ptr(),
+                                        ls, nl, hs, nh, a_loc.data_ptr(), delta.data_ptr(),
                                         sdt, self.lse_full.data_ptr(), wsp, need, s))
-        if self.stats == "gram":
-            self._ck(L.ispa_accum_gram(sdt, n, self.D, self.a_loc.data_ptr(), self.delta.data_ptr(),
+        if self.stats == "gram" and self.stats_chunks > 1:
+            self._npend[layer] += 1
+            if self._npend[layer] == self.stats_chunks:
+                self._flush_layer(layer)
+        elif self.stats == "gram":
+            self._ck(L.ispa_accum_gram(sdt, n, self.D, a_loc.data_ptr(), delta.data_ptr(),
                                        self.state[layer].data_ptr(), s))
         else:
             self._ck(L.ispa_accum_stats(sdt, B.ISPA_BF16, n, self.D,
@@ -286,7 +306,22 @@ class IspaStream:
                                         self.W[layer].data_ptr(), self.G[layer].data_ptr(),
                                         self.C[layer].data_ptr(), self.r2[layer:layer + 1].data_ptr(),
                                         wsp, need, s))
-        return self.a_loc, self.delta, self.lse_full
+        return a_loc, delta, self.lse_full
+
+    def _flush_layer(self, layer: int):
+        # the rows waiting for this layer's statistics, in one rank-k update
+        k = self._npend[layer]
+        if k:
+            a, dl = self._pend[layer]
+            self._ck(self.L.ispa_accum_gram(B._DT[self.stats_dtype], k * self.T, self.D, a.data_ptr(),
+                                            dl.data_ptr(), self.state[layer].data_ptr(), self._stream()))
+            self._npend[layer] = 0
+
+    def flush_statistics(self):
+        """Add every layer's waiting chunks to its statistics state now."""
+        if self.stats == "gram" and self.state is not None:
+            for layer in range(self.N):
+                self._flush_layer(layer)
 
     def statistics(self):
         """G (upper triangle), C and r2 of every layer from the warmup so far
@@ -295,6 +330,7 @@ class IspaStream:
         if not self.has_stats:
             raise RuntimeError("this stream keeps no statistics")
         if self.stats == "gram":
+            self.flush_statistics()
             self._reserve_stats_out()
             L, N, D = self.L, self.N, self.D
             need = L.ispa_gram_finalize_workspace_bytes(D)
@@ -367,7 +403,8 @@ class IspaStream:
         K lowest-eps layers for each K in ``Ks``, without ending the warmup
         (a budget / warmup-length sweep: the pages' ablation axes x = K / N and
         the warmup length; EN review, Ablation Study).  The statistics are not
-        modified; warmup may continue afterwards.  Returns (eps [N] fp64,
+        modified (chunks still waiting are added to the state first, which
+        leaves the sums as they are); warmup may continue afterwards.  Returns (eps [N] fp64,
         {K: selected int32 [K]}, {K: is_local uint8 [N]}, info [N] int32,
         dW [N, D, D] fp32), all on the device."""
         if self.switched or not self.has_stats:
@@ -400,6 +437,8 @@ class IspaStream:
             if flag:
                 self.kv[layer].evict_history()
         self.G = self.C = self.state = None
+        self._pend = [None] * self.N
+        self._npend = [0] * self.N
         self._solve_ws = self._fin_ws = None
         self.ws.release()
 
@@ -415,6 +454,8 @@ class IspaStream:
             if flag:
                 self.kv[layer].evict_history()
         self.G = self.C = self.state = None
+        self._pend = [None] * self.N
+        self._npend = [0] * self.N
         self.has_stats = False
 
     def quantize_projections(self):
@@ -498,6 +539,7 @@ class IspaStream:
                 self.state = B.gram_state(D, self.N, dev)
             else:
                 self.state.zero_()
+            self._npend = [0] * self.N
         else:
             if self.G is None:
                 self.G = torch.empty((self.N, D, D), dtype=torch.float32, device=dev)
