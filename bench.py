@@ -323,9 +323,18 @@ def _preload_kernels(dev):
     torch.cuda.synchronize()
 
 
+def _kv_stream_bytes(recs, spec):
+    """K and V bytes the pass's attention calls read, each key's K and V row
+    once per call (the kernels read them again for every query tile of a head,
+    from L2 or HBM: this is the algorithmic KV stream, not counter traffic)."""
+    D = spec["H"] * spec["d"]
+    elem = 1 if spec.get("fp8attn") else 2  # the fp8 cache holds 1-byte codes
+    return sum(2.0 * nk * D * elem for r in recs for nk in r["n_keys"])
+
+
 def _pass_figures(recs, spec):
     """ms per chunk and TFLOP/s (attention + statistics + projection flops over
-    the ISPA time) of one stream pass."""
+    the ISPA time) of one stream pass, and its KV streaming rate."""
     N, H, d, T = spec["N"], spec["H"], spec["d"], TOKENS_PER_CHUNK
     D = H * d
     flops = 0.0
@@ -335,8 +344,11 @@ def _pass_figures(recs, spec):
         flops += N * ((4.0 * T * D * D + 2.0 * T * D) if r["warm"] else 2.0 * T * D * D)
     ms = sum(r["ms"] for r in recs)
     tf = flops / (ms * 1e-3) / 1e12
+    kv_gbs = _kv_stream_bytes(recs, spec) / (ms * 1e-3) / 1e9
     out = {"ms/chunk (mean)": round(ms / len(recs), 3), "last chunk ms": round(recs[-1]["ms"], 3),
-           "pass TFLOP/s": round(tf, 1)}
+           "pass TFLOP/s": round(tf, 1),
+           "KV streaming GB/s (K, V bytes read once per call / ISPA time)": round(kv_gbs, 1),
+           "KV streaming frac of HBM 8 TB/s": round(kv_gbs / PEAK_HBM_GBS, 4)}
     if spec.get("fp8attn"):
         out["pass roofline frac (fp8 5 PFLOP/s)"] = round(tf / PEAK_FP8_TFLOPS, 4)
     else:
@@ -473,6 +485,8 @@ def run_stream(args, name, dev):
             "last chunk ms": round(last["ms"], 3),
             "switch ms (solve all layers + select)": round(switch_ms, 3) if switch_ms else None,
             "pass TFLOP/s (attention + statistics + projection flops / ISPA time)": round(achieved, 2),
+            "KV streaming GB/s (K, V bytes read once per call / ISPA time)":
+                round(_kv_stream_bytes(recs, spec) / (pass_ms * 1e-3) / 1e9, 1),
             "kv_bytes_held_last_chunk": last["kv_held"],
             "kv_bytes_all_full_last_chunk": full_bytes,
             "kv_held_fraction": round(last["kv_held"] / full_bytes, 4),
