@@ -6,9 +6,9 @@ One step is one full cycle of the Wan-1.3B-shaped single-layer workload
 28080-key history, fresh current chunk each step):
 
   8 warmup chunk steps, each ispa_dual_attn_merge (dual-stream attention and
-    the LSE merge into A_loc, A_full - A_loc), and after every second chunk
-    ispa_accum_gram (one rank-k update of [A_loc | A_full - A_loc] over both
-    chunks' rows into the layer's statistics state)
+    the LSE merge into A_loc, A_full - A_loc), and after every fourth chunk
+    ispa_accum_gram (one rank-k update of [A_loc | A_full - A_loc] over the
+    four chunks' rows into the layer's statistics state)
   the switch: ispa_gram_finalize (G, C = M W, r2) -> ispa_solve_dw (dW, eps,
     W + dW) -> ispa_select_layers (K = 1 of 1)
   one post-switch chunk of the (local) layer: ispa_local_attn_proj with W + dW
@@ -59,7 +59,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
-STATS_CHUNKS = 2  # warmup chunks per statistics update (their rows in one rank-k update)
+STATS_CHUNKS = 4  # warmup chunks per statistics update (their rows in one rank-k update)
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
@@ -257,6 +257,14 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
                 st.warmup(layer, c, qbuf[layer])
             else:
                 st.post(layer, c, qbuf[layer])
+            e = ev()
+            e.record(stream)
+            marks.append(e)
+        last_warm = warm and (c + 1 == spec["warm"] or (recal is not None and c + 1 == recal + warm2))
+        if last_warm and adopt is None:
+            # the statistics of the chunks still waiting for their update belong
+            # to the warmup, not to the switch that follows
+            st.flush_statistics()
             e = ev()
             e.record(stream)
             marks.append(e)
@@ -687,7 +695,7 @@ def main():
     o_hist = torch.empty_like(o_loc)
     lse_loc = torch.empty((n_q, H), **f32)
     lse_hist = torch.empty_like(lse_loc)
-    # A_loc and dA rows of STATS_CHUNKS chunks: one statistics update per pair
+    # A_loc and dA rows of STATS_CHUNKS chunks: one statistics update for them
     a_loc = torch.empty((STATS_CHUNKS * n_q, D), dtype=torch.float16, device=dev)
     delta = torch.empty_like(a_loc)
     G = torch.zeros((D, D), **f32)
@@ -792,7 +800,7 @@ def main():
         marks = []
         for i, (q, ls, nl, hs, nh) in enumerate(seg_tables):
             e0, e1, e2 = ev(), ev(), ev()
-            off = (i % STATS_CHUNKS) * n_q * D * 2  # this chunk's rows in the pair buffers
+            off = (i % STATS_CHUNKS) * n_q * D * 2  # this chunk's rows in the update buffers
             last = i % STATS_CHUNKS == STATS_CHUNKS - 1
             e0.record(stream)
             ck(L.ispa_dual_attn_merge(B.ISPA_BF16, n_q, H, d, scale, q.data_ptr(), q.stride(0), ls, nl, hs,

@@ -459,7 +459,9 @@ __global__ __launch_bounds__(f8::WAVES * 64, 1) void attn_fp8_d128_kernel(const 
       float e[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(S[kb][4 * j + i], c, -m));
-      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      // both halves of the word are written, so the conversion merges into the
+      // slot's old contents (P_{t-2}, consumed) instead of a zeroed register
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], P[cb][w], false);
       pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
       P[cb][w] = pk;
     };

@@ -184,7 +184,7 @@ class IspaStream:
     Device state per layer: the KV cache, W (bf16 [D, D], y = a W) and the
     warmup statistics.  ``stats="gram"`` (the default) accumulates them in the
     grouping of the printed closed form: one rank-k update of [A_loc | dA]
-    into a per-layer state (ispa_accum_gram) for every ``stats_chunks``
+    into a per-layer state (ispa_accum_gram) for every ``stats_chunks`` (4)
     chunks of a layer (their rows wait in a per-layer buffer; the sums do not
     depend on the grouping, and one update over more rows pays the state's
     read-modify-write once), and G, C = M W and r2 formed once at the switch
@@ -198,7 +198,7 @@ class IspaStream:
     def __init__(self, n_layers: int, H: int, d: int, T: int, capacity,
                  device, dtype=torch.bfloat16, stats_dtype=torch.float16,
                  lambda_abs: float = 0.0, lambda_rel: float = 1e-3, scale: float | None = None,
-                 with_stats: bool = True, stats: str = "gram", stats_chunks: int = 2):
+                 with_stats: bool = True, stats: str = "gram", stats_chunks: int = 4):
         if dtype != torch.bfloat16:
             raise ValueError("streams run on bf16 Q/K/V")
         self.N, self.H, self.d, self.T = n_layers, H, d, T

@@ -606,16 +606,16 @@ def test_end_to_end_dw_deviation(H, T_, chunks):
 
 
 def test_stream_statistics_grouping():
-    """Statistics updates every 1, 2 or 3 chunks of a layer (IspaStream
+    """Statistics updates every 1, 2, 3 or 4 chunks of a layer (IspaStream
     stats_chunks): the sums over the warmup rows do not depend on how the
     rows are grouped into rank-k updates, so G, C and r2 agree to fp32
-    summation order (bar 1e-5), including a pair still waiting at the switch
+    summation order (bar 1e-5), including chunks still waiting at the switch
     (5 chunks) and ragged 300-token chunks."""
     from kv_cache_absorption_amd.stream import IspaStream
     N, H, d, T_, chunks = 2, 2, 128, 300, 5
     si = synth.StreamInputs(N, H, d, T_, torch.bfloat16, 61, DEV, workload=3)
     got = {}
-    for k in (1, 2, 3):
+    for k in (1, 2, 3, 4):
         print(f"statistics every {k} chunk(s)", flush=True)
         st = IspaStream(N, H, d, T_, chunks, DEV, stats_chunks=k)
         for layer in range(N):
@@ -628,7 +628,7 @@ def test_stream_statistics_grouping():
         G, C, r2 = st.statistics()
         torch.cuda.synchronize()
         got[k] = (np.triu(h64(G)), h64(C), h64(r2))
-    for k in (2, 3):
+    for k in (2, 3, 4):
         for layer in range(N):
             assert rel(got[k][0][layer], got[1][0][layer]) <= 1e-5, (k, layer)
             assert rel(got[k][1][layer], got[1][1][layer]) <= 1e-5, (k, layer)
