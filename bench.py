@@ -63,6 +63,7 @@ STATS_CHUNKS = 4  # warmup chunks per statistics update (their rows in one rank-
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
+PEAK_FP64_TFLOPS = 78.6
 
 
 def _fail_multi(n):
@@ -512,6 +513,57 @@ def run_stream(args, name, dev):
     print(json.dumps(out), flush=True)
 
 
+def ceilings(n_calls, dev):
+    """What the machine reaches on plain library work, beside the published
+    peaks the rooflines divide by: large GEMMs through torch (hipBLASLt /
+    rocBLAS) in bf16, fp64 and, where torch offers it, fp8 E4M3 with unit
+    scales; and a 4 GiB device-to-device copy (bytes read + bytes written per
+    second).  Mean over n_calls after one untimed call, HIP events on the
+    current stream.  Operands are contiguous 2-D tensors."""
+    import torch
+    out = {"calls": n_calls}
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(n_calls):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n_calls * 1e-3
+
+    g = torch.Generator(device=dev).manual_seed(5)
+    for name, dt, n, peak in (("bf16 GEMM 8192^3", torch.bfloat16, 8192, PEAK_BF16_TFLOPS),
+                              ("fp64 GEMM 4096^3", torch.float64, 4096, PEAK_FP64_TFLOPS)):
+        x = torch.randn((n, n), device=dev, generator=g).to(dt)
+        y = torch.randn((n, n), device=dev, generator=g).to(dt)
+        t = timed(lambda: torch.matmul(x, y))
+        tf = 2.0 * n ** 3 / t / 1e12
+        out[name] = {"TFLOP/s": round(tf, 1), "frac of published peak": round(tf / peak, 4)}
+        del x, y
+    try:  # fp8 through torch's scaled matmul (second operand column-major, as it requires)
+        n = 8192
+        x = torch.randn((n, n), device=dev, generator=g).to(torch.float8_e4m3fn)
+        y = torch.randn((n, n), device=dev, generator=g).to(torch.float8_e4m3fn).t().contiguous().t()
+        one = torch.ones((), device=dev)
+        t = timed(lambda: torch._scaled_mm(x, y, scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+        tf = 2.0 * n ** 3 / t / 1e12
+        out["fp8 GEMM 8192^3 (torch._scaled_mm)"] = {"TFLOP/s": round(tf, 1),
+                                                    "frac of published peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        del x, y
+    except (RuntimeError, AttributeError, TypeError) as e:  # reported, never replaced
+        out["fp8 GEMM 8192^3 (torch._scaled_mm)"] = {"unavailable": str(e).splitlines()[0][:200]}
+    src = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src))
+    gbs = 2.0 * src.numel() * 4 / t / 1e9
+    out["device copy 4 GiB (read + write)"] = {"GB/s": round(gbs, 1), "frac of published peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def sdpa_compare(n_calls, seed, dev):
     """The benchmark chunk's attention through torch's fused scaled-dot-product
     attention (the vendor path: flash, else memory-efficient backend; the math
@@ -633,6 +685,9 @@ def main():
                          "(counter runs)")
     ap.add_argument("--merge-only", type=int, default=0,
                     help="only run this many two-part LSE merges of the workload (counter runs)")
+    ap.add_argument("--ceilings", type=int, default=0,
+                    help="only time large library GEMMs (bf16, fp64, fp8) and a 4 GiB device copy, this many calls "
+                         "each: what the machine reaches on plain library work")
     ap.add_argument("--sdpa-compare", type=int, default=0,
                     help="only time torch's fused attention (flash / memory-efficient backend) and "
                          "ispa_dual_attn_merge on the benchmark chunk, this many calls each")
@@ -673,6 +728,9 @@ def main():
         return
     if args.sdpa_compare:
         print(json.dumps(sdpa_compare(args.sdpa_compare, args.seed, dev)))
+        return
+    if args.ceilings:
+        print(json.dumps(ceilings(args.ceilings, dev)))
         return
     if args.workload != "wan13b_layer":
         run_stream(args, args.workload, dev)
