@@ -201,6 +201,10 @@ class IspaStream:
                  with_stats: bool = True, stats: str = "gram", stats_chunks: int = 4):
         if dtype != torch.bfloat16:
             raise ValueError("streams run on bf16 Q/K/V")
+        if stats not in ("gram", "direct"):
+            raise ValueError("stats is 'gram' or 'direct'")
+        if stats_chunks < 1:
+            raise ValueError("stats_chunks must be >= 1")
         self.N, self.H, self.d, self.T = n_layers, H, d, T
         self.D = H * d
         self.device, self.dtype, self.stats_dtype = device, dtype, stats_dtype
@@ -214,11 +218,7 @@ class IspaStream:
             raise ValueError("one capacity per layer")
         self.kv = [LayerKV(cap, T, H, d, dtype, dev) for cap in caps]
         self.W = torch.empty((n_layers, D, D), dtype=dtype, device=dev)
-        if stats not in ("gram", "direct"):
-            raise ValueError("stats is 'gram' or 'direct'")
         self.stats = stats
-        if stats_chunks < 1:
-            raise ValueError("stats_chunks must be >= 1")
         self.stats_chunks = stats_chunks if stats == "gram" else 1
         self._pend = [None] * n_layers  # per layer: (A_loc, dA) rows of stats_chunks chunks
         self._npend = [0] * n_layers    # chunks waiting in them

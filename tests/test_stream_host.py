@@ -1,5 +1,6 @@
 """Host logic of the chunked stream (no GPU): cache slots, eviction and the
 key accounting against the oracle's grouping."""
+import pytest
 import torch
 
 import oracle as O
@@ -107,3 +108,14 @@ def test_reentry_right_after_eviction_holds_sink_only():
     for c in range(4, 7):
         _fill(kv, c, T, H, d)
         _check_groups(kv, c, T, *O.stream_groups_kept(c, T, 4))
+
+
+def test_stream_rejects_bad_statistics_options():
+    """The statistics grouping options are checked before anything is
+    allocated (no GPU needed): an unknown form, or fewer than one chunk per
+    rank-k update."""
+    from kv_cache_absorption_amd.stream import IspaStream
+    with pytest.raises(ValueError):
+        IspaStream(1, 2, 128, 64, 2, "cpu", stats="other")
+    with pytest.raises(ValueError):
+        IspaStream(1, 2, 128, 64, 2, "cpu", stats_chunks=0)
