@@ -46,6 +46,14 @@ layers (the chunk's Q, K, V are generated on the GPU before its events):
                  switch, post-switch 6-11, warmup again at 12-17 (statistics
                  from zero, every layer over the keys it still holds), switch,
                  post-switch 18-23
+  wan13b_video   a 30-second video of the wan13b_stream layers: 40 chunks
+                 (120 latent frames), warmup chunks 0-3 (12 latent frames),
+                 switch (K = 15), post-switch chunks 4-39
+  wan13b_video_vanilla  the same 40 chunks without ISPA: every layer attends
+                 to its whole history and projects with W
+
+The default run also times wan13b_video and wan13b_video_vanilla on the same
+inputs and reports ISPA's speed-up over vanilla (``--no-video`` skips them).
 """
 from __future__ import annotations
 
@@ -179,6 +187,10 @@ STREAMS = {
     # 2, 4, 6 and 8 chunks (6-24 frames) for x = 0.3, 0.4, 0.5, 0.7
     "wan13b_sweep": dict(N=30, H=12, d=128, chunks=8, warm=8, K=15, wid=3,
                          evaluate_at=(2, 4, 6, 8), xs=(0.3, 0.4, 0.5, 0.7)),
+    # a 30-second video (40 chunks of 3 latent frames) with the default warmup
+    # of 12 latent frames and ISPA-0.5, and the same chunks without ISPA
+    "wan13b_video": dict(N=30, H=12, d=128, chunks=40, warm=4, K=15, wid=3),
+    "wan13b_video_vanilla": dict(N=30, H=12, d=128, chunks=40, warm=0, K=0, wid=3, vanilla=True),
 }
 TOKENS_PER_CHUNK = 4680  # 3 latent frames of 1560 tokens
 
@@ -397,6 +409,60 @@ def wan14b_figures(seed, dev):
     return out
 
 
+def _vanilla_adopt(spec, dev, seed):
+    """Every layer an F-Layer from chunk 0 on, projecting with its own W: the
+    stream without ISPA."""
+    import torch
+    import synth
+    N, H, d = spec["N"], spec["H"], spec["d"]
+    si = synth.StreamInputs(N, H, d, TOKENS_PER_CHUNK, torch.bfloat16, seed, dev, workload=spec["wid"])
+    W = torch.stack([si.w(layer) for layer in range(N)])
+    return [0] * N, W, W
+
+
+def video_figures(seed, dev):
+    """The 30-second video twice over the same inputs: ISPA-0.5 (warmup
+    chunks 0-3 with dual-stream attention and statistics, the switch, chunks
+    4-39 with 15 L-Layers on sink + current chunk and W + dW) and vanilla
+    (every layer attends to its whole history and projects with W).  Each
+    chunk is timed with HIP events around the ISPA-side calls of all layers
+    (attention, merge, statistics, projection); the switch is timed apart."""
+    import torch
+    _preload_kernels(dev)
+    spec, spec_v = STREAMS["wan13b_video"], STREAMS["wan13b_video_vanilla"]
+    recs_i, switch_ms, st, _ = _stream_pass(spec, dev, seed)
+    W, selected = st.W, [i for i, f in enumerate(st.is_local_host) if f]
+    st.kv = []
+    st.G = st.C = st.dW = st.state = None
+    del st
+    torch.cuda.empty_cache()
+    recs_v, _, st_v, _ = _stream_pass(spec_v, dev, seed, adopt=([0] * spec_v["N"], W, W))
+    st_v.kv = []
+    del st_v, W
+    torch.cuda.empty_cache()
+    warm = spec["warm"]
+    tot = lambda rs, lo=0, hi=None: sum(r["ms"] for r in rs[lo:hi])  # noqa: E731
+    ispa_ms = tot(recs_i) + switch_ms
+    van_ms = tot(recs_v)
+    return {
+        "layers x heads, chunks, warmup chunks, K": f"{spec['N']} x {spec['H']}, {spec['chunks']}, "
+                                                    f"{warm} (12 latent frames), {spec['K']}",
+        "ISPA ms (warmup chunks + switch + post-switch chunks)": round(ispa_ms, 2),
+        "vanilla ms (all chunks)": round(van_ms, 2),
+        "speed-up over the video (vanilla / ISPA)": round(van_ms / ispa_ms, 3),
+        "speed-up over the post-switch chunks": round(tot(recs_v, warm) / tot(recs_i, warm), 3),
+        "speed-up at the last chunk": round(recs_v[-1]["ms"] / recs_i[-1]["ms"], 3),
+        "warmup chunks, ISPA ms / vanilla ms (dual-stream attention + statistics against plain attention)":
+            round(tot(recs_i, 0, warm) / tot(recs_v, 0, warm), 3),
+        "switch ms (finalize + 30 solves + select)": round(switch_ms, 3),
+        "KV held at the last chunk, ISPA / vanilla": round(recs_i[-1]["kv_held"] / recs_v[-1]["kv_held"], 4),
+        "L-Layers": selected,
+        "note": "ISPA-side work only (attention, merge, statistics, output projection); the pages report "
+                "1.89x within attention and 1.35x for the whole model on their GPU and backbones "
+                "(EN review, Key Findings)",
+    }
+
+
 def run_stream(args, name, dev):
     import torch
     spec = STREAMS[name]
@@ -405,6 +471,9 @@ def run_stream(args, name, dev):
     D = H * d
     adopt = None
     pre = {}
+    if spec.get("vanilla"):
+        adopt = _vanilla_adopt(spec, dev, args.seed)
+        pre = {"vanilla": "every layer attends to its whole history and projects with W"}
     if name in ("wan14b_post", "wan14b_post_w8a8", "wan14b_post_fp8"):
         t0 = time.perf_counter()
         _, pre_switch_ms, st4, _ = _stream_pass(STREAMS["wan14b_warmup"], dev, args.seed)
@@ -484,7 +553,9 @@ def run_stream(args, name, dev):
         "data": "synthetic",
         "config": {"workload": name, "layers": N, "heads": H, "head_dim": d, "tokens_per_chunk": T,
                    "chunks": spec["chunks"], "warmup_chunks": spec["warm"], "K": spec["K"],
-                   "stats_operands": "fp16", "statistics": "grouped (accum_gram)", "seed": args.seed,
+                   "stats_operands": "fp16" if spec["warm"] else None,
+                   "statistics": "grouped (accum_gram)" if spec["warm"] else "none (no warmup chunk in the pass)",
+                   "seed": args.seed,
                    "timing": "HIP events around each chunk's ISPA calls of all layers; the chunk's "
                              "synthetic Q/K/V generation sits outside them (ms_per_step is the wall "
                              "time of the whole pass including that generation)"},
@@ -672,6 +743,8 @@ def main():
     ap.add_argument("--workload", default="wan13b_layer", choices=["wan13b_layer"] + sorted(STREAMS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-14b", action="store_true", help="skip the Wan-14B stream passes of the default run")
+    ap.add_argument("--no-video", action="store_true",
+                    help="skip the ISPA-against-vanilla video passes of the default run")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--attn-only", type=int, default=0,
@@ -1038,10 +1111,13 @@ def main():
              "traffic": _traffic("syrk_wan13b_counters.txt", "gram.hip")},
         ],
     }
-    if not args.no_14b:
+    if not (args.no_14b and args.no_video):
         del steps_in, seg_tables, ws
         torch.cuda.empty_cache()
+    if not args.no_14b:
         out["also"]["Wan-14B streams"] = wan14b_figures(args.seed, dev)
+    if not args.no_video:
+        out["also"]["Wan-1.3B 30-second video, ISPA-0.5 against vanilla"] = video_figures(args.seed, dev)
     if not args.no_cpu_baseline:
         q, kc, vc = g.step(0)
         out["cpu_baseline"] = cpu_baseline(g, q, kc, vc)
