@@ -51,9 +51,14 @@ layers (the chunk's Q, K, V are generated on the GPU before its events):
                  switch (K = 15), post-switch chunks 4-39
   wan13b_video_vanilla  the same 40 chunks without ISPA: every layer attends
                  to its whole history and projects with W
+  wan13b_video_fp8  wan13b_video with the quantised post-switch path: at the
+                 switch the projections (W + dW, W) and the L-Layers' sinks are
+                 quantised once (timed apart from the switch), then every layer
+                 attends on the fp8 matrix core and projects with W8A8
 
-The default run also times wan13b_video and wan13b_video_vanilla on the same
-inputs and reports ISPA's speed-up over vanilla (``--no-video`` skips them).
+The default run also times wan13b_video, wan13b_video_fp8 and
+wan13b_video_vanilla on the same inputs and reports ISPA's speed-up over
+vanilla (``--no-video`` skips them).
 """
 from __future__ import annotations
 
@@ -191,6 +196,7 @@ STREAMS = {
     # of 12 latent frames and ISPA-0.5, and the same chunks without ISPA
     "wan13b_video": dict(N=30, H=12, d=128, chunks=40, warm=4, K=15, wid=3),
     "wan13b_video_vanilla": dict(N=30, H=12, d=128, chunks=40, warm=0, K=0, wid=3, vanilla=True),
+    "wan13b_video_fp8": dict(N=30, H=12, d=128, chunks=40, warm=4, K=15, wid=3, w8a8=True, fp8attn=True),
 }
 TOKENS_PER_CHUNK = 4680  # 3 latent frames of 1560 tokens
 
@@ -234,6 +240,7 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     recs = []
     switch_ev = []
+    quant_ev = []
     selections = []
     evaluations = []
     recal, warm2 = spec.get("recal"), spec.get("warm2", 0)
@@ -249,6 +256,17 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
         if evict:
             st.evict()
         selections.append([i for i, f in enumerate(st.is_local_host) if f])
+        if spec.get("w8a8"):
+            # the quantised post-switch path: the projections (and with fp8
+            # attention the L-Layers' sinks) quantised once per switch, timed
+            # apart from the solve and selection
+            q0, q1 = ev(), ev()
+            q0.record(stream)
+            st.quantize_projections()
+            if spec.get("fp8attn"):
+                st.quantize_attention()
+            q1.record(stream)
+            quant_ev.append((q0, q1))
 
     for c in range(spec["chunks"]):
         if adopt is None and (c == spec["warm"] or (recal is not None and c == recal + warm2)):
@@ -305,6 +323,7 @@ def _stream_pass(spec, dev, seed, adopt=None, timed=True):
         r["ms"] = sum(t)
         del r["start"], r["marks"]
     switch_ms = [a.elapsed_time(b) for a, b in switch_ev]
+    st.quantize_ms = [a.elapsed_time(b) for a, b in quant_ev]
     st.selection_history = selections
     st.evaluations = [dict(chunks=e["chunks"], ms=e["ev"][0].elapsed_time(e["ev"][1]),
                            eps=[float(x) for x in e["eps"].cpu()],
@@ -421,12 +440,14 @@ def _vanilla_adopt(spec, dev, seed):
 
 
 def video_figures(seed, dev):
-    """The 30-second video twice over the same inputs: ISPA-0.5 (warmup
-    chunks 0-3 with dual-stream attention and statistics, the switch, chunks
-    4-39 with 15 L-Layers on sink + current chunk and W + dW) and vanilla
-    (every layer attends to its whole history and projects with W).  Each
-    chunk is timed with HIP events around the ISPA-side calls of all layers
-    (attention, merge, statistics, projection); the switch is timed apart."""
+    """The 30-second video three times over the same inputs: ISPA-0.5
+    (warmup chunks 0-3 with dual-stream attention and statistics, the switch,
+    chunks 4-39 with 15 L-Layers on sink + current chunk and W + dW), the same
+    with the quantised post-switch path (fp8 attention, W8A8 projections), and
+    vanilla (every layer attends to its whole history and projects with W).
+    Each chunk is timed with HIP events around the ISPA-side calls of all
+    layers (attention, merge, statistics, projection); the switch and the
+    quantisation at the switch are timed apart and counted on ISPA's side."""
     import torch
     _preload_kernels(dev)
     spec, spec_v = STREAMS["wan13b_video"], STREAMS["wan13b_video_vanilla"]
@@ -436,6 +457,12 @@ def video_figures(seed, dev):
     st.G = st.C = st.dW = st.state = None
     del st
     torch.cuda.empty_cache()
+    recs_q, switch_q, st_q, _ = _stream_pass(STREAMS["wan13b_video_fp8"], dev, seed)
+    quant_ms = st_q.quantize_ms[0]
+    st_q.kv = []
+    st_q.f8 = st_q.sink8 = st_q.wq = None
+    del st_q
+    torch.cuda.empty_cache()
     recs_v, _, st_v, _ = _stream_pass(spec_v, dev, seed, adopt=([0] * spec_v["N"], W, W))
     st_v.kv = []
     del st_v, W
@@ -443,6 +470,7 @@ def video_figures(seed, dev):
     warm = spec["warm"]
     tot = lambda rs, lo=0, hi=None: sum(r["ms"] for r in rs[lo:hi])  # noqa: E731
     ispa_ms = tot(recs_i) + switch_ms
+    ispa8_ms = tot(recs_q) + switch_q + quant_ms
     van_ms = tot(recs_v)
     return {
         "layers x heads, chunks, warmup chunks, K": f"{spec['N']} x {spec['H']}, {spec['chunks']}, "
@@ -456,10 +484,15 @@ def video_figures(seed, dev):
             round(tot(recs_i, 0, warm) / tot(recs_v, 0, warm), 3),
         "switch ms (finalize + 30 solves + select)": round(switch_ms, 3),
         "KV held at the last chunk, ISPA / vanilla": round(recs_i[-1]["kv_held"] / recs_v[-1]["kv_held"], 4),
+        "quantised ISPA ms (fp8 attention and W8A8 projections after the switch)": round(ispa8_ms, 2),
+        "quantisation at the switch ms (30 projections, 15 sinks)": round(quant_ms, 3),
+        "speed-up over the video, quantised ISPA against vanilla bf16": round(van_ms / ispa8_ms, 3),
+        "speed-up over the post-switch chunks, quantised ISPA against vanilla bf16":
+            round(tot(recs_v, warm) / tot(recs_q, warm), 3),
         "L-Layers": selected,
         "note": "ISPA-side work only (attention, merge, statistics, output projection); the pages report "
-                "1.89x within attention and 1.35x for the whole model on their GPU and backbones "
-                "(EN review, Key Findings)",
+                "1.89x within attention, 1.35x for the whole model and 1.86x for the whole model with W8A8, "
+                "on their GPU and backbones (EN review, Key Findings)",
     }
 
 
@@ -494,6 +527,8 @@ def run_stream(args, name, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     recs, switch_ms, st, switches = passes[-1]
+    if st.quantize_ms:
+        pre["quantisation at the switch ms (projections, L-Layer sinks)"] = [round(x, 3) for x in st.quantize_ms]
     all_recs = [r for p in passes for r in p[0]]
     chunk_ms = [r["ms"] for r in all_recs]
     mean = lambda xs: sum(xs) / len(xs) if xs else None  # noqa: E731
