@@ -337,3 +337,49 @@ def test_stream_post_uses_fp8_attention():
             torch.cuda.synchronize()
             assert torch.equal(y0, ref0)
             assert torch.equal(y1, ref1)
+
+
+def test_stream_quantised_after_warmup_and_switch():
+    """The quantised post-switch path entered from a real warmup and switch
+    (the order the video benchmark uses): after switch + eviction,
+    quantize_projections holds the codes of W + dW for the L-Layer and of W
+    for the F-Layer (bit for bit as ispa_quantize_w_fp8), and every post()
+    equals ispa_local_attn_fp8_proj over the chunks the layer keeps (the
+    L-Layer: its sink, kept by the eviction, and the current chunk)."""
+    from kv_cache_absorption_amd.stream import IspaStream
+    k8 = K()
+    H, d, T, N, warm = 2, 128, 300, 2, 3
+    D = H * d
+    print(f"stream warmup -> switch -> fp8 post H={H} T={T}", flush=True)
+    W = [synth.normal((D, D), 390 + i, DEV, std=D ** -0.5, dtype=torch.bfloat16) for i in range(N)]
+    kv = {(i, c): (synth.normal((T, H, d), 400 + 10 * i + c, DEV, dtype=torch.bfloat16),
+                   synth.normal((T, H, d), 500 + 10 * i + c, DEV, dtype=torch.bfloat16))
+          for i in range(N) for c in range(warm + 2)}
+    qs = {(i, c): synth.normal((T, H, d), 600 + 10 * i + c, DEV, dtype=torch.bfloat16)
+          for i in range(N) for c in range(warm + 2)}
+    st = IspaStream(N, H, d, T, warm + 2, DEV)
+    for i in range(N):
+        st.set_w(i, W[i])
+    for c in range(warm):
+        for i in range(N):
+            st.write_kv(i, c, *kv[i, c])
+            st.warmup(i, c, qs[i, c])
+    st.switch(1)
+    st.quantize_projections()
+    st.quantize_attention()
+    loc = [i for i in range(N) if st.is_local_host[i]]
+    assert len(loc) == 1
+    for i in range(N):
+        wc, wsc = k8.ispa_quantize_w_fp8(st.w_eff[i] if st.is_local_host[i] else W[i])
+        torch.cuda.synchronize()
+        assert torch.equal(st.wq[i], wc) and torch.equal(st.wq_scale[i], wsc)
+    for c in range(warm, warm + 2):
+        for i in range(N):
+            st.write_kv(i, c, *kv[i, c])
+            y = st.post(i, c, qs[i, c]).clone()
+            held = [0, c] if st.is_local_host[i] else list(range(c + 1))
+            chunks = [k8.ispa_quantize_kv_fp8(*kv[i, j]) for j in held]
+            ref = k8.ispa_local_attn_fp8_proj(qs[i, c], chunks, st.wq[i], st.wq_scale[i],
+                                              out_dtype=torch.bfloat16)
+            torch.cuda.synchronize()
+            assert torch.equal(y, ref), (i, c)
