@@ -406,7 +406,10 @@ def wan14b_figures(seed, dev):
     t0 = time.perf_counter()
     recs_w, switch_ms, st4, _ = _stream_pass(STREAMS["wan14b_warmup"], dev, seed)
     out = {"wan14b_warmup": {**_pass_figures(recs_w, STREAMS["wan14b_warmup"]),
-                             "switch ms (finalize + 40 solves at D = 5120 + select)": round(switch_ms, 3)}}
+                             "switch ms (finalize + 40 solves at D = 5120 + select)": round(switch_ms, 3),
+                             "traffic": _traffic("attn_dual_single_pass_wan14b_counters.txt", "attn.hip"),
+                             "traffic_kernel": "HBM bytes per launch of the single-pass dual attention at the last "
+                                               "warmup chunk (88920 keys), from counters"}}
     adopt = (list(st4.is_local_host), st4.W, st4.w_eff)
     st4.kv = []
     st4.G = st4.C = st4.dW = st4.state = None
@@ -415,7 +418,10 @@ def wan14b_figures(seed, dev):
     last = recs_p[-1]
     full = 2 * STREAMS["wan14b_post"]["N"] * (last["c"] + 1) * TOKENS_PER_CHUNK * 5120 * 2
     out["wan14b_post"] = {**_pass_figures(recs_p, STREAMS["wan14b_post"]),
-                          "kv_held_fraction_last_chunk": round(last["kv_held"] / full, 4)}
+                          "kv_held_fraction_last_chunk": round(last["kv_held"] / full, 4),
+                          "traffic": _traffic("attn_fpost_wan14b_traffic.txt", "attn.hip"),
+                          "traffic_kernel": "HBM bytes per launch of an F-Layer's attention at the last chunk "
+                                            "(187200 keys), from counters"}
     del st5
     torch.cuda.empty_cache()
     recs_8, _, st6, _ = _stream_pass(STREAMS["wan14b_post_fp8"], dev, seed, adopt)
@@ -494,6 +500,57 @@ def video_figures(seed, dev):
                 "1.89x within attention, 1.35x for the whole model and 1.86x for the whole model with W8A8, "
                 "on their GPU and backbones (EN review, Key Findings)",
     }
+
+
+def wan14b_counter_calls(kind, n_calls, seed, dev):
+    """The dominant attention call of a Wan-14B pass at its largest key set,
+    repeated for counter runs: ``fused`` = the last warmup chunk's
+    ispa_dual_attn_merge (40 heads, 9360 local keys, 17 history chunks =
+    79560 keys); ``fpost`` = the last post-switch chunk of an F-Layer,
+    ispa_local_attn_proj over all 40 chunks (187200 keys) with W.  Prints the
+    mean call time by HIP events over the calls (unprofiled runs)."""
+    import torch
+    import synth
+    import kv_cache_absorption_amd as K
+    from kv_cache_absorption_amd import _lib as B
+    T, H, d = TOKENS_PER_CHUNK, 40, 128
+    n_hist = (17 if kind == "fused" else 38) * T
+    g = synth.GroupInputs(T, H, d, T, n_hist, torch.bfloat16, seed, dev, workload=4)
+    q, kc, vc = g.step(0)
+    L = B.lib()
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    if kind == "fused":
+        ls, nl = B._segs([(g.sink_k, g.sink_v), (kc, vc)], H, d)
+        hs, nh = B._segs([(g.hist_k, g.hist_v)], H, d)
+        need = L.ispa_dual_attn_merge_workspace_bytes(B.ISPA_BF16, T, H, d, ls, nl, hs, nh)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        a_loc = torch.empty((T, H * d), dtype=torch.float16, device=dev)
+        delta = torch.empty_like(a_loc)
+
+        def call():
+            st = L.ispa_dual_attn_merge(B.ISPA_BF16, T, H, d, d ** -0.5, q.data_ptr(), q.stride(0), ls, nl, hs, nh,
+                                        a_loc.data_ptr(), delta.data_ptr(), B.ISPA_F16, None, ws.data_ptr(),
+                                        ws.numel(), sh)
+            if st:
+                raise B.IspaError(st, L.ispa_last_error().decode())
+        n_keys = 2 * T + n_hist
+    else:
+        segs = [(g.sink_k, g.sink_v), (g.hist_k, g.hist_v), (kc, vc)]
+
+        def call():
+            K.ispa_local_attn_proj(q, segs, g.w)
+        n_keys = 2 * T + n_hist
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_calls
+    return {"kind": kind, "calls": n_calls, "heads": H, "keys": n_keys, "call_us": round(ms * 1e3, 1),
+            "attention TFLOP/s": round(4.0 * T * n_keys * H * d / (ms * 1e-3) / 1e12, 1)}
 
 
 def run_stream(args, name, dev):
@@ -791,6 +848,10 @@ def main():
     ap.add_argument("--attn8-only", type=int, default=0,
                     help="only run this many fp8 local-attention calls (post-switch L-Layer) of the workload "
                          "(counter runs)")
+    ap.add_argument("--w14-fused-only", type=int, default=0,
+                    help="only run this many Wan-14B last-warmup-chunk dual-attention calls (counter runs)")
+    ap.add_argument("--w14-fpost-only", type=int, default=0,
+                    help="only run this many Wan-14B last-chunk F-Layer attention + projection calls (counter runs)")
     ap.add_argument("--merge-only", type=int, default=0,
                     help="only run this many two-part LSE merges of the workload (counter runs)")
     ap.add_argument("--ceilings", type=int, default=0,
@@ -831,6 +892,10 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes}))
         return
     L = B.lib()  # raises if libispa.so is missing: no fallback path exists
+    if args.w14_fused_only or args.w14_fpost_only:
+        kind = "fused" if args.w14_fused_only else "fpost"
+        print(json.dumps(wan14b_counter_calls(kind, args.w14_fused_only or args.w14_fpost_only, args.seed, dev)))
+        return
     if args.proj_compare:
         print(json.dumps(proj_compare(args.proj_compare, dev)))
         return
