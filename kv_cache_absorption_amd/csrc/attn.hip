@@ -1029,7 +1029,9 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
     const int64_t qrow = qrow0 + qb * 32;
     if (qrow >= p.n_q) continue;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* op = job.o + (qrow * p.H + head) * (int64_t)DH;
+    const int64_t base = (qrow * p.H + head) * (int64_t)DH;
+    const bool out16 = p.o16 != nullptr && job.group == 0;  // uniform over the workgroup
+    const bool out_bf = p.o16_dt == ISPA_BF16;
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt) {
 #pragma unroll
@@ -1037,7 +1039,11 @@ __global__ __launch_bounds__(a5::WAVES * 64, 1) void attn_bf16_d128_kernel(const
         const int d0 = dt * 32 + g4 * 8 + hh * 4;
         f32x4 v = {o[qb][dt][g4 * 4 + 0] * inv, o[qb][dt][g4 * 4 + 1] * inv, o[qb][dt][g4 * 4 + 2] * inv,
                    o[qb][dt][g4 * 4 + 3] * inv};
-        *(f32x4*)(op + d0) = v;
+        if (out16)
+          *(u32x2*)((uint16_t*)p.o16 + base + d0) = out_bf ? (u32x2){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}
+                                                           : (u32x2){pack_f16(v[0], v[1]), pack_f16(v[2], v[3])};
+        else
+          *(f32x4*)(job.o + base + d0) = v;
       }
     }
     if (hh == 0) job.lse[qrow * p.H + head] = l_tot > 0.0f ? (m[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
@@ -1419,6 +1425,13 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
     }
     two_runs = two_runs && runs <= 2;
   }
+  // an unsplit group 0 asked for as 16-bit rows: the d = 128 kernel writes them
+  // from its epilogue; the other kernels write fp32 and to16_kernel rounds it
+  const bool direct16 = o16_g0 && plan.n_splits[0] == 1 && dt == ISPA_BF16 && d == 128;
+  if (direct16) {
+    p.o16 = o16_g0;
+    p.o16_dt = o16_dt;
+  }
   if (dt == ISPA_BF16) {
     const int64_t blocks = (int64_t)p.n_qtiles * H * nj;
     if (d == 128 && two_runs)
@@ -1441,7 +1454,7 @@ ispa_status run_group_attention(ispa_dtype dt, int64_t n_q, int32_t H, int32_t d
     st = launch_merge(merges[i], stream);
     if (st != ISPA_OK) return st;
   }
-  if (o16_g0 && plan.n_splits[0] == 1) {  // unsplit group 0: its fp32 output, rounded
+  if (o16_g0 && plan.n_splits[0] == 1 && !direct16) {  // unsplit group 0: its fp32 output, rounded
     const int64_t n = n_q * H * d;       // d is a multiple of 4
     hipLaunchKernelGGL(to16_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, o_out[0], n,
                        (uint16_t*)o16_g0, o16_dt);

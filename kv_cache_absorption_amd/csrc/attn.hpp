@@ -45,6 +45,11 @@ struct AttnParams {
   float* lse_full; // [n_q, H] or null
   int32_t out_dt;  // ISPA_BF16 or ISPA_F16
   float* o_stash;  // fp32 [n_q, H, d]: the local group's unnormalised output, from the boundary to the epilogue
+  // per-group form, d = 128 kernel: when set, the job of group 0 (which then
+  // covers the whole group) writes its output here as 16-bit rows [n_q, H, d]
+  // of o16_dt instead of fp32 rows to its job's o (its LSE as before)
+  void* o16;
+  int32_t o16_dt;  // ISPA_BF16 or ISPA_F16
 };
 
 // A group description on the host.
