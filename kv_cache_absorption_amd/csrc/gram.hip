@@ -447,8 +447,9 @@ __global__ __launch_bounds__(256, 1) void nt_gemm_kernel(const NtGemmParams p) {
 //     such reads (tokens +0..3 and +8..11 of a 16-token slice, per wave half
 //     +4) form the 8 k values of a v_mfma_f32_32x32x16 operand, in the same
 //     k order on both sides of the product;
-//   * 4 waves as 2 x 2, each 128 x 128 (16 accumulators of 32 x 32), with the
-//     operands swapped so a lane holds 4 consecutive output columns;
+//   * kSyrkWaves waves: 4 as 2 x 2, each 128 x 128 (16 accumulators of 32 x 32),
+//     or 8 as 2 x 4, each 128 x 64 (8 accumulators), two waves per SIMD; the
+//     operands are swapped so a lane holds 4 consecutive output columns;
 //   * a diagonal tile (I == J) loads one operand and reads both fragments
 //     from it;
 //   * the token range is split S ways (S fixed by D so that the launch fills
@@ -462,14 +463,18 @@ constexpr int SY_ROWB = SY_BM * 2;         // bytes per LDS row of one operand
 constexpr int SY_OPB = SY_BK * SY_ROWB;    // 16 KB per operand and stage
 constexpr int SY_PD = 3, SY_NBUF = 5;      // stages in flight, ring slots
 static_assert(SY_NBUF * 2 * SY_OPB <= 160 * 1024, "LDS budget");
+constexpr int kSyrkWaves = 8;
 
-template <int MT, bool DIAG>
+template <int MT, bool DIAG, int NW>
 __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm, int tn, int split) {
-  constexpr int LOADS = DIAG ? 4 : 8;  // 1 KB loads per wave and stage
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int NJ = NW == 4 ? 4 : 2;         // 32-column blocks per wave
+  constexpr int LPW = 16 / NW;                // 1 KB loads per wave, operand and stage
+  constexpr int LOADS = DIAG ? LPW : 2 * LPW;  // per wave and stage
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hh = lane >> 5, lq = lane & 31, g16 = lane >> 4, s16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = NW == 4 ? wave >> 1 : wave >> 2, wn = NW == 4 ? wave & 1 : wave & 3;
   const int nbh = p.nbh;
   // operand halves and column offsets of the two blocks
   const bool xb = tm >= nbh, yb = tn >= nbh;
@@ -487,14 +492,14 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
   };
   const __amdgpu_buffer_rsrc_t rx = rsrc(xb, cx), ry = rsrc(yb, cy);
-  // this lane's part of load instruction i (0..3) of its wave: LDS row
-  // 2 q + hh (q = 4 wave + i), physical chunk lq holding logical chunk lq ^ 4 (row mod 8)
-  int xo[4], yo[4];
+  // this lane's part of load instruction i (0..LPW-1) of its wave: LDS row
+  // 2 q + hh (q = LPW wave + i), physical chunk lq holding logical chunk lq ^ 4 (row mod 8)
+  int xo[LPW], yo[LPW];
   {
     const int lastx = (int)((p.D - cx) / 8) - 1, lasty = (int)((p.D - cy) / 8) - 1;  // last valid chunk
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 2 * (wave * 4 + i) + hh;
+    for (int i = 0; i < LPW; ++i) {
+      const int row = 2 * (wave * LPW + i) + hh;
       const int lch = lq ^ ((row & 7) << 2);
       xo[i] = row * (int)ldb + min(lch, lastx) * 16;
       yo[i] = row * (int)ldb + min(lch, lasty) * 16;
@@ -508,10 +513,10 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
     const int so = (int)((int64_t)s * SY_BK * ldb);
     const uint32_t xd = lds0 + buf * 2 * SY_OPB, yd = xd + SY_OPB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(rx, xd + (wave * 4 + i) * 1024, xo[i] + so, 0);
+    for (int i = 0; i < LPW; ++i) lds_dma16(rx, xd + (wave * LPW + i) * 1024, xo[i] + so, 0);
     if constexpr (!DIAG) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_dma16(ry, yd + (wave * 4 + i) * 1024, yo[i] + so, 0);
+      for (int i = 0; i < LPW; ++i) lds_dma16(ry, yd + (wave * LPW + i) * 1024, yo[i] + so, 0);
     }
   };
   // wait until at most `newer` stages of loads are outstanding (0 <= newer < SY_PD)
@@ -528,16 +533,15 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
   // second read, +16 per k slice), column block c0 + 32 b: chunk
   // (c0 / 8 + 4 b) ^ 4 (row mod 8), plus (g16 & 1) * 2 + (s16 & 3) / 2 and a
   // half-chunk (s16 & 1) * 8
-  int fx[4], fy[4];
+  int fx[4], fy[NJ];
   {
     const int r = 4 * hh + (s16 >> 2);
     const int fl = r & 7;
     const int low = ((g16 & 1) * 2 + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      fx[b] = r * SY_ROWB + ((((wm * 4 + b) ^ fl) << 2) << 4) + low;
-      fy[b] = r * SY_ROWB + ((((wn * 4 + b) ^ fl) << 2) << 4) + low;
-    }
+    for (int b = 0; b < 4; ++b) fx[b] = r * SY_ROWB + ((((wm * 4 + b) ^ fl) << 2) << 4) + low;
+#pragma unroll
+    for (int b = 0; b < NJ; ++b) fy[b] = r * SY_ROWB + ((((wn * NJ + b) ^ fl) << 2) << 4) + low;
   }
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   auto read8 = [&](const char* base, int off) {
@@ -547,24 +551,24 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(u32x4, v);
   };
-  auto frags = [&](int buf, int ks, u32x4 (&a)[4], u32x4 (&b)[4]) {
+  auto frags = [&](int buf, int ks, u32x4 (&a)[4], u32x4 (&b)[NJ]) {
     const char* xs = lds + buf * 2 * SY_OPB + ks * 16 * SY_ROWB;
     const char* ys = DIAG ? xs : xs + SY_OPB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = read8(xs, fx[i]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = read8(ys, fy[j]);
+    for (int j = 0; j < NJ; ++j) b[j] = read8(ys, fy[j]);
   };
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
-  auto mfmas = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+    for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x16){};
+  auto mfmas = [&](const u32x4 (&a)[4], const u32x4 (&b)[NJ]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma<MT>(b[j], a[i], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma<MT>(b[j], a[i], acc[i][j]);
   };
 
   int issued = 0, lbuf = 0;
@@ -572,7 +576,7 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
     issue(issued, lbuf);
     lbuf = lbuf + 1 == SY_NBUF ? 0 : lbuf + 1;
   }
-  u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  u32x4 fa0[4], fb0[NJ], fa1[4], fb1[NJ];
   if (ns > 0) {
     wait_stage(issued - 1);
     __syncthreads();
@@ -587,11 +591,25 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
   // for a read issued in its own phase (with all 16 reads first, the LDS
   // counter cannot tell the older fragments from the new ones, and the first
   // MFMA waited for two of the new reads).
+  // (8 waves: 8 MFMAs and 12 reads per phase, two reads after each of the first four)
   auto interleave = [&]() {
+    if constexpr (NW == 4) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
   };
   int cbuf = 0;
@@ -626,22 +644,22 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
   // n = wn*128 + 32 j + 8 g + 4 hh inside the tile.
   const int which = !xb && !yb ? 0 : (!xb ? 1 : 2);  // G, M or H
   float* out = p.state + (int64_t)split * p.split_stride + (int64_t)which * p.D * p.D;
-  const int64_t m0 = cx + wm * 128, n0 = cy + wn * 128;  // this wave's 128 x 128 block
-  if (m0 + 128 <= p.D && n0 + 128 <= p.D) {
+  const int64_t m0 = cx + wm * 128, n0 = cy + wn * 32 * NJ;  // this wave's 128 x 32 NJ block
+  if (m0 + 128 <= p.D && n0 + 32 * NJ <= p.D) {
     // The block lies inside D (every block when D is a multiple of 256): no
     // per-vector checks, the 16 loads of a 32-row block go out together, and
     // the next block's loads are issued before this one is added and stored.
-    auto ld = [&](int i, f32x4(&c)[4][4]) __attribute__((always_inline)) {
+    auto ld = [&](int i, f32x4(&c)[NJ][4]) __attribute__((always_inline)) {
       const float* row = out + (m0 + i * 32 + lq) * p.D + n0 + hh * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) c[j][g] = *(const f32x4*)(row + j * 32 + g * 8);
     };
-    auto st = [&](int i, const f32x4(&c)[4][4]) __attribute__((always_inline)) {
+    auto st = [&](int i, const f32x4(&c)[NJ][4]) __attribute__((always_inline)) {
       float* row = out + (m0 + i * 32 + lq) * p.D + n0 + hh * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 v = c[j][g];
@@ -650,7 +668,7 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
           *(f32x4*)(row + j * 32 + g * 8) = v;
         }
     };
-    f32x4 c0[4][4], c1[4][4];
+    f32x4 c0[NJ][4], c1[NJ][4];
     ld(0, c0);
     ld(1, c1);
     st(0, c0);
@@ -666,19 +684,19 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
     const int64_t m = cx + wm * 128 + i * 32 + lq;
     if (m >= p.D) continue;
     float* row = out + m * p.D;
-    f32x4 cur[4][4];
+    f32x4 cur[NJ][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t n = cy + wn * 128 + j * 32 + g * 8 + hh * 4;  // D is a multiple of 64
+        const int64_t n = n0 + j * 32 + g * 8 + hh * 4;  // D is a multiple of 64
         cur[j][g] = n < p.D ? *(const f32x4*)(row + n) : (f32x4){};
       }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t n = cy + wn * 128 + j * 32 + g * 8 + hh * 4;
+        const int64_t n = n0 + j * 32 + g * 8 + hh * 4;
         if (n >= p.D) continue;
         f32x4 v = cur[j][g];
 #pragma unroll
@@ -689,7 +707,7 @@ __device__ __forceinline__ void syrk_tile(const SyrkParams& p, char* lds, int tm
 }
 
 template <int MT>
-__global__ __launch_bounds__(256, 1) void syrk_kernel(const SyrkParams p) {
+__global__ __launch_bounds__(kSyrkWaves * 64, 1) void syrk_kernel(const SyrkParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[SY_NBUF * 2 * SY_OPB];
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int split = (int)(bid / (uint32_t)p.n_tiles);
@@ -699,9 +717,9 @@ __global__ __launch_bounds__(256, 1) void syrk_kernel(const SyrkParams p) {
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
   if (tm == tn)
-    syrk_tile<MT, true>(p, lds, tm, tn, split);
+    syrk_tile<MT, true, kSyrkWaves>(p, lds, tm, tn, split);
   else
-    syrk_tile<MT, false>(p, lds, tm, tn, split);
+    syrk_tile<MT, false, kSyrkWaves>(p, lds, tm, tn, split);
 }
 
 // ---- the statistics at the switch, from the per-layer state ----
@@ -1020,9 +1038,9 @@ ispa_status launch_syrk(const SyrkParams& p, int mfma_dt, hipStream_t stream) {
   }
   if (blocks == 0 || p.n == 0) return ISPA_OK;
   if (mfma_dt == ISPA_BF16)
-    hipLaunchKernelGGL(syrk_kernel<ISPA_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(syrk_kernel<ISPA_BF16>, dim3((unsigned)blocks), dim3(kSyrkWaves * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL(syrk_kernel<ISPA_F16>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(syrk_kernel<ISPA_F16>, dim3((unsigned)blocks), dim3(kSyrkWaves * 64), 0, stream, p);
   return check_launch("syrk_kernel");
 }
 
