@@ -535,7 +535,9 @@ def wan14b_counter_calls(kind, n_calls, seed, dev):
                 raise B.IspaError(st, L.ispa_last_error().decode())
         n_keys = 2 * T + n_hist
     else:
-        segs = [(g.sink_k, g.sink_v), (g.hist_k, g.hist_v), (kc, vc)]
+        # one contiguous run of keys, as a stream's layer cache holds them
+        segs = [(torch.cat([g.sink_k, g.hist_k, kc]), torch.cat([g.sink_v, g.hist_v, vc]))]
+        del g.hist_k, g.hist_v
 
         def call():
             K.ispa_local_attn_proj(q, segs, g.w)
