@@ -1218,12 +1218,18 @@ SplitPlan plan_splits(int bq, int64_t n_q, int32_t H, const HostGroup* groups, i
   if (wgs >= kTargetWgs || nonempty == 0) return plan;
   int64_t piece;
   if (nonempty == 1) {
-    // One key set: the piece count s that minimises the launch's estimated time,
-    // (waves of workgroups over the CUs) x (key tiles per piece + a fixed cost of
-    // about kFillTiles tiles per workgroup: pipeline fill, output store and the
-    // extra merge part).  Both constants are MI355X measurements (256 CUs; the
-    // fixed cost fitted to 1-, 2-, 3- and 4-piece timings of a 9360-key group).
+    // One key set.  A launch that already gives at least half the CUs a
+    // workgroup is not split: the CUs a split would add run at the clock the
+    // chip then falls to, and the parts cost a merge (measured on MI355X at
+    // 4680 queries x 12 heads, 228 workgroups: 93,600 keys whole 2569-2587 us,
+    // in the 10 pieces the model below picks 2655-2662 us; 187,200 keys
+    // 4848-4877 against 4917-4957 us).  Otherwise the piece count s minimises
+    // the launch's estimated time, (waves of workgroups over the CUs) x (key
+    // tiles per piece + a fixed cost of about kFillTiles tiles per workgroup:
+    // pipeline fill, output store and the extra merge part), the fixed cost
+    // fitted to 1-, 2-, 3- and 4-piece timings of a 9360-key group.
     constexpr int64_t kCUs = 256, kFillTiles = 10, kMinTiles = 4;
+    if (2 * wgs >= kCUs) return plan;
     const int64_t tiles = (shortest + kBK - 1) / kBK;
     int64_t s = 1, best = INT64_MAX;
     for (int64_t c = 1; c <= 16 && (c == 1 || tiles / c >= kMinTiles); ++c) {
