@@ -543,6 +543,10 @@ def test_select_parity():
     (2, 128, 130, [64, 500, 700, 130], torch.bfloat16),  # F-layer, several segments
     (4, 64, 200, [5000], torch.float32),             # long single segment (split)
     (12, 128, 600, [4680, 700], torch.bfloat16),     # D = 1536: several GEMM tiles, ragged rows
+    # 8 query tiles x 16 heads = 128 workgroups, half the CUs: the key set runs
+    # whole and the kernel writes its output as bf16 rows from its epilogue
+    (16, 128, 2048, [4680, 700], torch.bfloat16),    # two runs of keys
+    (16, 128, 2048, [1000, 2000, 3000], torch.float32),  # three runs: the segment-cursor form
 ])
 def test_local_attn_proj_parity(H, d, n_q, seg_lens, y_dt):
     print(f"local_attn_proj H={H} d={d} n_q={n_q} segs={seg_lens} {y_dt}", flush=True)
