@@ -258,8 +258,8 @@ ispa_status ispa_select_layers(int32_t n_layers, int32_t K, const double* eps,
  * L-Layer attends to its retained sink and current keys only and projects
  * with W + dW; an F-Layer keeps full attention over its history with W).
  *   y = softmax(scale q k^T) v  over all keys of the segments, then y W.
- * When the launch would leave most CUs idle (fewer than 128 workgroups of
- * 256 queries and one head), a long key set is split into blocks whose
+ * When the launch would leave most CUs idle (fewer than 128 workgroups, one
+ * per query tile and head), a long key set is split into blocks whose
  * partial (o, lse) are merged by the LSE rule before the projection;
  * otherwise it runs whole.
  *   dt      ISPA_BF16 (d in {64,128}) or ISPA_F32.
