@@ -106,6 +106,29 @@ def test_workspace_queries_and_errors():
     assert L.ispa_solve_dw_workspace_bytes(2, 128) >= 2 * 2 * 128 * 128 * 8
 
 
+def test_local_attn_proj_split_rule():
+    """A single key set runs whole when its launch already gives half the CUs a
+    workgroup (no split parts in the workspace), and is split into merged
+    pieces when the launch would leave most CUs idle."""
+    m, L = _lib()
+    a = lambda b: (b + 255) // 256 * 256  # noqa: E731
+
+    def base(n_q, H, d=128):  # fp32 O and LSE, bf16 O, bf16 W^T
+        D = H * d
+        return a(n_q * D * 4) + a(n_q * H * 4) + a(n_q * D * 2) + a(D * D * 2)
+
+    # Wan-1.3B F-Layer at its last chunk: 19 query tiles x 12 heads = 228 workgroups
+    segs = _segarr(m, [_seg(93600, 12, 128, FAKE)])
+    assert L.ispa_local_attn_proj_workspace_bytes(m.ISPA_BF16, 4680, 12, 128, segs, 1) == base(4680, 12)
+    # 8 query tiles x 16 heads = 128: still whole
+    segs16 = _segarr(m, [_seg(93600, 16, 128, FAKE)])
+    assert L.ispa_local_attn_proj_workspace_bytes(m.ISPA_BF16, 2048, 16, 128, segs16, 1) == base(2048, 16)
+    # 3 query tiles x 12 heads = 36: split, each piece with its fp32 (o, lse) part
+    part = a(600 * 12 * 128 * 4) + a(600 * 12 * 4)
+    need = L.ispa_local_attn_proj_workspace_bytes(m.ISPA_BF16, 600, 12, 128, segs, 1)
+    assert need > base(600, 12) and (need - base(600, 12)) % part == 0 and (need - base(600, 12)) // part >= 2
+
+
 def test_stats_solve_select_reject_bad_args():
     m, L = _lib()
     F = FAKE
