@@ -34,6 +34,9 @@
  *  - Stateless and thread-safe: no global flags, no hidden caches.  The one
  *    exception is ispa_w8a8_linear_noalloc, which keeps a fixed scratch
  *    array per device (see there).
+ *  - The header is C as well as C++: a C program compiles it with the ROCm
+ *    include directory and -D__HIP_PLATFORM_AMD__ (for hipStream_t) and links
+ *    -lispa.
  */
 #ifndef ISPA_H
 #define ISPA_H

@@ -106,6 +106,35 @@ def test_workspace_queries_and_errors():
     assert L.ispa_solve_dw_workspace_bytes(2, 128) >= 2 * 2 * 128 * 128 * 8
 
 
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/ispa.h is a C header: a C11 program that includes it compiles
+    with gcc, links against the built library and calls its host-side entry
+    points (version, status strings, a size query)."""
+    import shutil
+    import subprocess
+    m, L = _lib()
+    gcc = shutil.which("gcc")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    if gcc is None or not os.path.isdir(os.path.join(rocm, "include", "hip")):
+        pytest.skip("gcc or the ROCm headers are not available")
+    src = tmp_path / "t.c"
+    src.write_text('#include "ispa.h"\n#include <stdio.h>\n'
+                   'int main(void) {\n'
+                   '  printf("%d\\n%s\\n%zu\\n", ispa_version(), ispa_status_str(ISPA_ERR_WORKSPACE),\n'
+                   '         ispa_gram_state_bytes(1536));\n'
+                   '  return 0;\n}\n')
+    libdir = os.path.dirname(m.LIB_PATH)
+    exe = tmp_path / "t"
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Werror=implicit-function-declaration", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), str(src),
+                    "-L", libdir, "-lispa", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True,
+                   capture_output=True, timeout=120)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=60).stdout.splitlines()
+    assert int(out[0]) == L.ispa_version()
+    assert out[1] == L.ispa_status_str(m.ISPA_ERR_WORKSPACE).decode()
+    assert int(out[2]) == L.ispa_gram_state_bytes(1536)
+
+
 def test_local_attn_proj_split_rule():
     """A single key set runs whole when its launch already gives half the CUs a
     workgroup (no split parts in the workspace), and is split into merged
